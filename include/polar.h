@@ -1,0 +1,159 @@
+/*
+ * libpolar — Polar Attention forward for AMD Instinct MI355X (gfx950).  C ABI, version 1.
+ *
+ * The operation is the attention mixing step of the ATMA hybrid decoder as described in
+ * "ATMA: Length-Invariant Language Modeling via Polar Attention and Gated-Delta
+ * Compression Memory" (gist.science technical summary), section 2.1 "Polar Attention:
+ * A Three-Channel Decomposition", and its kernels in section 2.2 "Hardware-Software
+ * Codesign" (a fused Polar Attention kernel computing participation ratios online in
+ * O(block) memory, and a GQA-grouped decode kernel reading paged KV cache blocks).
+ *
+ * For query row i of head h (KV head g = h / (Hq/Hkv)), seeing n keys j (n = i+1 in causal
+ * prefill, n = seq_len in decode):
+ *   tau    = max(1, ln n / ln train_len)          if POLAR_FLAG_LENGTH_TEMP, else 1
+ *   l_j    = beta_h * tau * <q_i, k_j>             (q, k are unit vectors: caller's job)
+ *   p_j    = softmax_j(l_j);   lse = log sum_j exp(l_j)
+ *   n_eff  = 1 / sum_j p_j^2                        (participation ratio)
+ *   u      = sum_j p_j v_j;    dir = u / |u|        (direction / content channel)
+ *   floor  = b_h + (beta_h * tau / sqrt(d)) * sqrt(2 ln n)   if POLAR_FLAG_NULL_FLOOR,
+ *            else b_h
+ *   gate   = sigmoid(max_j l_j - floor)             (signal-detection confidence)
+ *   count  = gate * tanh(ln n_eff) * w_h            (magnitude / count channel)
+ * The pages give out = content + count + memory; the memory stream is a separate
+ * operation, so dir and count are returned separately and the caller adds them.
+ *
+ * Conventions for every entry point:
+ *  - Pointers to tensors are DEVICE pointers; the params/outputs structs are HOST structs.
+ *  - The caller allocates and owns every buffer.  The library allocates nothing and keeps
+ *    no pointer after a call returns.  Inputs are never written; outputs are fully
+ *    overwritten; inputs and outputs must not alias.
+ *  - Calls are asynchronous and ordered on `stream` (a hipStream_t; NULL = default stream).
+ *  - All validation happens before any launch.  On an error nothing is launched and
+ *    nothing is written; polar_last_error() gives a thread-local description.
+ *  - Launch failures return POLAR_ERR_HIP.  Faults inside kernels surface at the caller's
+ *    next synchronisation.  Nothing throws, aborts or exits across this interface.
+ *  - beta_h must be positive and finite; other values give unspecified (but memory-safe)
+ *    results.
+ */
+#ifndef POLAR_H
+#define POLAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define POLAR_ABI_VERSION 1
+
+#if defined(__GNUC__)
+#define POLAR_API __attribute__((visibility("default")))
+#else
+#define POLAR_API
+#endif
+
+typedef enum {
+  POLAR_OK = 0,
+  POLAR_ERR_NULL_POINTER = 1,       /* a required pointer is NULL                         */
+  POLAR_ERR_BAD_SHAPE = 2,          /* negative size, Hq % Hkv != 0, bad stride, ...      */
+  POLAR_ERR_UNSUPPORTED = 3,        /* head_dim != 64, page_size != 64, unknown dtype ... */
+  POLAR_ERR_MISALIGNED = 4,         /* a tensor pointer is not 16-byte aligned            */
+  POLAR_ERR_WORKSPACE_TOO_SMALL = 5,
+  POLAR_ERR_HIP = 6                 /* the HIP runtime refused a launch                   */
+} polar_status;
+
+typedef enum {
+  POLAR_DTYPE_F32 = 0,              /* q, k, v in float32; MFMA f32                        */
+  POLAR_DTYPE_BF16 = 1              /* q, k, v in bfloat16; MFMA bf16, fp32 accumulation   */
+} polar_dtype;
+
+enum {
+  POLAR_FLAG_LENGTH_TEMP = 1u,      /* apply tau(n)                                       */
+  POLAR_FLAG_NULL_FLOOR = 2u        /* add the sqrt(2 ln n) extreme-value term to b_h      */
+};
+
+typedef struct {
+  int32_t n_q_heads;                /* Hq >= 1                                            */
+  int32_t n_kv_heads;               /* Hkv >= 1, Hq % Hkv == 0                             */
+  int32_t head_dim;                 /* d; must be 64 in version 1                          */
+  int32_t train_len;                /* T_train; must be >= 2 when LENGTH_TEMP is set       */
+  uint32_t flags;                   /* POLAR_FLAG_* bits                                   */
+  const float *beta;                /* device [Hq] logit scale beta_h; NULL -> sqrt(d)     */
+  const float *null_bias;           /* device [Hq] null scalar b_h; NULL -> 0              */
+  const float *count_vec;           /* device [Hq*d] count vectors w_h; required iff
+                                       outputs.count != NULL                             */
+} polar_params;
+
+/* Output tensors, float32, device.  dir and n_eff are required; count, gate and lse may
+ * be NULL (not computed).  Prefill layouts: dir, count [B,T,Hq,d]; n_eff, gate, lse
+ * [B,T,Hq].  Decode layouts: dir, count [B,Hq,d]; n_eff, gate, lse [B,Hq].  dir and count
+ * must be 16-byte aligned. */
+typedef struct {
+  float *dir;
+  float *count;
+  float *n_eff;
+  float *gate;
+  float *lse;
+} polar_outputs;
+
+/*
+ * Causal Polar Attention prefill (the fused kernel of section 2.2: one pass over K/V tiles
+ * with streaming max, sum and sum-of-squares accumulators; the T x T scores are never
+ * stored).
+ *   q  [B,T,Hq,d], k and v [B,T,Hkv,d], row-major contiguous, dtype `dt`, 16-byte aligned.
+ *   Row i of head h attends keys 0..i of KV head h / (Hq/Hkv).
+ *   B == 0 or T == 0 is a valid empty call (nothing is launched).
+ */
+POLAR_API polar_status polar_attn_fwd(const polar_params *p, polar_dtype dt, int32_t B, int32_t T,
+                            const void *q, const void *k, const void *v,
+                            const polar_outputs *out, void *stream);
+
+/*
+ * Workspace bytes polar_attn_decode_paged needs for this batch size and length bound
+ * (0 on invalid arguments).  The value depends only on the arguments.
+ */
+POLAR_API size_t polar_decode_workspace_bytes(const polar_params *p, int32_t B, int32_t max_seq_len,
+                                    int32_t page_size);
+
+/*
+ * One-token GQA-grouped decode over a paged KV cache (section 2.2: the decode kernel reads
+ * paged KV blocks directly; the Hq/Hkv query heads sharing a KV head are served by a
+ * single read of each K/V byte).
+ *   q                [B,Hq,d] dtype `dt`: the newest token of each sequence; its own key
+ *                    and value are already in the cache, so it sees seq_lens[b] keys
+ *                    (the same result as causal prefill row seq_lens[b]-1).
+ *   k_cache, v_cache [num_pages,Hkv,page_size,d] dtype `dt`: page-major pools, one
+ *                    contiguous page_size x d block per (page, KV head).
+ *   page_table       device int32 [B,page_table_stride]: logical page p of sequence b is
+ *                    physical page page_table[b*stride + p].  Ids outside [0,num_pages)
+ *                    are skipped (their keys are masked out) so a bad table cannot read
+ *                    outside the pools.
+ *   seq_lens         device int32 [B], each in [1, max_seq_len]; values outside are
+ *                    clamped to that range.
+ *   max_seq_len      host upper bound of seq_lens; sizes the split-KV grid;
+ *                    page_table_stride >= ceil(max_seq_len / page_size).
+ *   workspace        device scratch of >= polar_decode_workspace_bytes(...) bytes,
+ *                    16-byte aligned; its contents on entry are ignored.
+ *   page_size must be 64 in version 1.
+ */
+POLAR_API polar_status polar_attn_decode_paged(const polar_params *p, polar_dtype dt, int32_t B,
+                                     const void *q, const void *k_cache, const void *v_cache,
+                                     int32_t num_pages, int32_t page_size,
+                                     const int32_t *page_table, int32_t page_table_stride,
+                                     const int32_t *seq_lens, int32_t max_seq_len,
+                                     void *workspace, size_t workspace_bytes,
+                                     const polar_outputs *out, void *stream);
+
+/* Static description of a status code. */
+POLAR_API const char *polar_status_str(polar_status s);
+/* Thread-local detail of the last non-OK return on this thread ("" if none). */
+POLAR_API const char *polar_last_error(void);
+/* POLAR_ABI_VERSION of the loaded library. */
+POLAR_API int32_t polar_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* POLAR_H */

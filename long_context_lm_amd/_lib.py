@@ -1,0 +1,119 @@
+"""ctypes binding of libpolar (include/polar.h): argument marshalling only.
+
+Every step of the computation runs in the HIP kernels of libpolar.so.  torch is used for
+device memory and for the current HIP stream.  There is no fallback: if the library is
+missing or no GPU is present, calls fail loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libpolar.so")
+
+POLAR_OK = 0
+POLAR_ERR_NULL_POINTER = 1
+POLAR_ERR_BAD_SHAPE = 2
+POLAR_ERR_UNSUPPORTED = 3
+POLAR_ERR_MISALIGNED = 4
+POLAR_ERR_WORKSPACE_TOO_SMALL = 5
+POLAR_ERR_HIP = 6
+
+POLAR_DTYPE_F32 = 0
+POLAR_DTYPE_BF16 = 1
+
+POLAR_FLAG_LENGTH_TEMP = 1
+POLAR_FLAG_NULL_FLOOR = 2
+
+EXPORTS = ("polar_attn_fwd", "polar_decode_workspace_bytes", "polar_attn_decode_paged",
+           "polar_status_str", "polar_last_error", "polar_abi_version")
+
+
+class polar_params(ctypes.Structure):
+    _fields_ = [("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("train_len", ctypes.c_int32),
+                ("flags", ctypes.c_uint32), ("beta", ctypes.c_void_p),
+                ("null_bias", ctypes.c_void_p), ("count_vec", ctypes.c_void_p)]
+
+
+class polar_outputs(ctypes.Structure):
+    _fields_ = [("dir", ctypes.c_void_p), ("count", ctypes.c_void_p),
+                ("n_eff", ctypes.c_void_p), ("gate", ctypes.c_void_p),
+                ("lse", ctypes.c_void_p)]
+
+
+class PolarError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"libpolar status {status}: {detail}")
+        self.status = status
+        self.detail = detail
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libpolar.so once and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise FileNotFoundError(f"{path} is missing: build it with "
+                                "`python -m long_context_lm_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I32, SZ, VP = ctypes.POINTER, ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p
+    lib.polar_attn_fwd.restype = I32
+    lib.polar_attn_fwd.argtypes = [P(polar_params), I32, I32, I32, VP, VP, VP, P(polar_outputs),
+                                   VP]
+    lib.polar_decode_workspace_bytes.restype = SZ
+    lib.polar_decode_workspace_bytes.argtypes = [P(polar_params), I32, I32, I32]
+    lib.polar_attn_decode_paged.restype = I32
+    lib.polar_attn_decode_paged.argtypes = [P(polar_params), I32, I32, VP, VP, VP, I32, I32, VP,
+                                            I32, VP, I32, VP, SZ, P(polar_outputs), VP]
+    lib.polar_status_str.restype = ctypes.c_char_p
+    lib.polar_status_str.argtypes = [I32]
+    lib.polar_last_error.restype = ctypes.c_char_p
+    lib.polar_last_error.argtypes = []
+    lib.polar_abi_version.restype = I32
+    lib.polar_abi_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+# ----------------------------------------------------------------- raw C names
+def polar_abi_version() -> int:
+    return load().polar_abi_version()
+
+
+def polar_status_str(status: int) -> str:
+    return load().polar_status_str(status).decode()
+
+
+def polar_last_error() -> str:
+    return load().polar_last_error().decode()
+
+
+def polar_attn_fwd(params, dtype, B, T, q, k, v, outputs, stream) -> int:
+    """Direct call of the C entry point (pointers as ints); returns the status code."""
+    return load().polar_attn_fwd(ctypes.byref(params), dtype, B, T, q, k, v,
+                                 ctypes.byref(outputs), stream)
+
+
+def polar_decode_workspace_bytes(params, B, max_seq_len, page_size) -> int:
+    return load().polar_decode_workspace_bytes(ctypes.byref(params), B, max_seq_len, page_size)
+
+
+def polar_attn_decode_paged(params, dtype, B, q, k_cache, v_cache, num_pages, page_size,
+                            page_table, page_table_stride, seq_lens, max_seq_len, workspace,
+                            workspace_bytes, outputs, stream) -> int:
+    return load().polar_attn_decode_paged(ctypes.byref(params), dtype, B, q, k_cache, v_cache,
+                                          num_pages, page_size, page_table, page_table_stride,
+                                          seq_lens, max_seq_len, workspace, workspace_bytes,
+                                          ctypes.byref(outputs), stream)
+
+
+def check(status: int) -> None:
+    if status != POLAR_OK:
+        raise PolarError(status, f"{polar_status_str(status)}: {polar_last_error()}")

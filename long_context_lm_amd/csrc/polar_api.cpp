@@ -1,0 +1,196 @@
+// C-ABI entry points of libpolar: argument validation, launch geometry, dispatch.
+// Every check runs before any HIP call, so errors are reported without a GPU and
+// nothing is launched or written on an error.
+#include <stdarg.h>
+#include <stdio.h>
+#include <math.h>
+
+#include "../../include/polar.h"
+#include "polar_kernels.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+polar_status fail(polar_status s, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+polar_status check_params(const polar_params *p, polar_dtype dt, const polar_outputs *out) {
+  if (!p) return fail(POLAR_ERR_NULL_POINTER, "params is NULL");
+  if (!out) return fail(POLAR_ERR_NULL_POINTER, "outputs is NULL");
+  if (dt != POLAR_DTYPE_F32 && dt != POLAR_DTYPE_BF16)
+    return fail(POLAR_ERR_UNSUPPORTED, "unknown dtype %d", (int)dt);
+  if (p->n_q_heads < 1 || p->n_kv_heads < 1)
+    return fail(POLAR_ERR_BAD_SHAPE, "head counts must be >= 1 (Hq=%d, Hkv=%d)", p->n_q_heads,
+                p->n_kv_heads);
+  if (p->n_q_heads % p->n_kv_heads != 0)
+    return fail(POLAR_ERR_BAD_SHAPE, "Hq (%d) is not a multiple of Hkv (%d)", p->n_q_heads,
+                p->n_kv_heads);
+  if (p->head_dim != polar::kHeadDim)
+    return fail(POLAR_ERR_UNSUPPORTED, "head_dim %d unsupported (only %d)", p->head_dim,
+                polar::kHeadDim);
+  if (p->flags & ~(uint32_t)(POLAR_FLAG_LENGTH_TEMP | POLAR_FLAG_NULL_FLOOR))
+    return fail(POLAR_ERR_UNSUPPORTED, "unknown flag bits 0x%x", p->flags);
+  if ((p->flags & POLAR_FLAG_LENGTH_TEMP) && p->train_len < 2)
+    return fail(POLAR_ERR_BAD_SHAPE, "train_len must be >= 2 with LENGTH_TEMP (got %d)",
+                p->train_len);
+  if (!out->dir) return fail(POLAR_ERR_NULL_POINTER, "outputs.dir is NULL");
+  if (!out->n_eff) return fail(POLAR_ERR_NULL_POINTER, "outputs.n_eff is NULL");
+  if (out->count && !p->count_vec)
+    return fail(POLAR_ERR_NULL_POINTER, "outputs.count requested but params.count_vec is NULL");
+  if (!aligned16(out->dir) || (out->count && !aligned16(out->count)) ||
+      (out->count && !aligned16(p->count_vec)))
+    return fail(POLAR_ERR_MISALIGNED, "dir, count and count_vec must be 16-byte aligned");
+  return POLAR_OK;
+}
+
+float inv_log_train(const polar_params *p) {
+  return (p->flags & POLAR_FLAG_LENGTH_TEMP) ? (float)(1.0 / log((double)p->train_len)) : 0.f;
+}
+
+}  // namespace
+
+extern "C" {
+
+polar_status polar_attn_fwd(const polar_params *p, polar_dtype dt, int32_t B, int32_t T,
+                            const void *q, const void *k, const void *v,
+                            const polar_outputs *out, void *stream) {
+  polar_status st = check_params(p, dt, out);
+  if (st != POLAR_OK) return st;
+  if (B < 0 || T < 0) return fail(POLAR_ERR_BAD_SHAPE, "B (%d) and T (%d) must be >= 0", B, T);
+  if (!q || !k || !v) return fail(POLAR_ERR_NULL_POINTER, "q, k and v must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v))
+    return fail(POLAR_ERR_MISALIGNED, "q, k and v must be 16-byte aligned");
+  if (B == 0 || T == 0) return POLAR_OK;
+
+  polar::PrefillArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.beta = p->beta;
+  a.null_bias = p->null_bias;
+  a.count_vec = p->count_vec;
+  a.dir = out->dir;
+  a.count = out->count;
+  a.n_eff = out->n_eff;
+  a.gate = out->gate;
+  a.lse = out->lse;
+  a.B = B;
+  a.T = T;
+  a.Hq = p->n_q_heads;
+  a.Hkv = p->n_kv_heads;
+  a.G = a.Hq / a.Hkv;
+  a.hb = polar::prefill_heads_per_block(a.G);
+  const int rows = polar::prefill_rows_per_block((int)dt, a.hb);
+  a.n_row_blocks = (T + rows - 1) / rows;
+  a.inv_log_train = inv_log_train(p);
+  a.null_floor = (p->flags & POLAR_FLAG_NULL_FLOOR) ? 1 : 0;
+  const long long blocks = (long long)a.n_row_blocks * a.Hkv * (a.G / a.hb) * B;
+  if (blocks > 0x7fffffffLL)
+    return fail(POLAR_ERR_BAD_SHAPE, "problem too large for one launch (%lld workgroups)", blocks);
+  hipError_t err = polar::launch_prefill((int)dt, a, (hipStream_t)stream);
+  if (err != hipSuccess) return fail(POLAR_ERR_HIP, "prefill launch: %s", hipGetErrorString(err));
+  return POLAR_OK;
+}
+
+size_t polar_decode_workspace_bytes(const polar_params *p, int32_t B, int32_t max_seq_len,
+                                    int32_t page_size) {
+  if (!p || B < 1 || max_seq_len < 1 || page_size != polar::kPageSize || p->n_kv_heads < 1 ||
+      p->n_q_heads < 1 || p->n_q_heads % p->n_kv_heads != 0)
+    return 0;
+  return polar::decode_ws_bytes(B, p->n_q_heads, p->n_kv_heads, max_seq_len);
+}
+
+polar_status polar_attn_decode_paged(const polar_params *p, polar_dtype dt, int32_t B,
+                                     const void *q, const void *k_cache, const void *v_cache,
+                                     int32_t num_pages, int32_t page_size,
+                                     const int32_t *page_table, int32_t page_table_stride,
+                                     const int32_t *seq_lens, int32_t max_seq_len,
+                                     void *workspace, size_t workspace_bytes,
+                                     const polar_outputs *out, void *stream) {
+  polar_status st = check_params(p, dt, out);
+  if (st != POLAR_OK) return st;
+  if (B < 0) return fail(POLAR_ERR_BAD_SHAPE, "B (%d) must be >= 0", B);
+  if (page_size != polar::kPageSize)
+    return fail(POLAR_ERR_UNSUPPORTED, "page_size %d unsupported (only %d)", page_size,
+                polar::kPageSize);
+  if (B == 0) return POLAR_OK;
+  if (!q || !k_cache || !v_cache || !page_table || !seq_lens || !workspace)
+    return fail(POLAR_ERR_NULL_POINTER,
+                "q, k_cache, v_cache, page_table, seq_lens and workspace must be non-NULL");
+  if (num_pages < 1) return fail(POLAR_ERR_BAD_SHAPE, "num_pages (%d) must be >= 1", num_pages);
+  if (max_seq_len < 1)
+    return fail(POLAR_ERR_BAD_SHAPE, "max_seq_len (%d) must be >= 1", max_seq_len);
+  const int need_pages = (max_seq_len + page_size - 1) / page_size;
+  if (page_table_stride < need_pages)
+    return fail(POLAR_ERR_BAD_SHAPE, "page_table_stride (%d) < ceil(max_seq_len/page_size) (%d)",
+                page_table_stride, need_pages);
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(workspace))
+    return fail(POLAR_ERR_MISALIGNED, "q, caches and workspace must be 16-byte aligned");
+  const size_t need = polar::decode_ws_bytes(B, p->n_q_heads, p->n_kv_heads, max_seq_len);
+  if (workspace_bytes < need)
+    return fail(POLAR_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed",
+                workspace_bytes, need);
+
+  const polar::DecodeGrid grid =
+      polar::decode_grid(B, p->n_q_heads, p->n_kv_heads, max_seq_len);
+  if ((long long)p->n_kv_heads * grid.n_hchunk > 65535 || B > 65535)
+    return fail(POLAR_ERR_BAD_SHAPE, "grid too large (B=%d, Hkv*chunks=%lld)", B,
+                (long long)p->n_kv_heads * grid.n_hchunk);
+  polar::DecodeArgs a;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.page_table = page_table;
+  a.seq_lens = seq_lens;
+  a.beta = p->beta;
+  a.null_bias = p->null_bias;
+  a.count_vec = p->count_vec;
+  a.dir = out->dir;
+  a.count = out->count;
+  a.n_eff = out->n_eff;
+  a.gate = out->gate;
+  a.lse = out->lse;
+  a.ws = (float *)workspace;
+  a.B = B;
+  a.Hq = p->n_q_heads;
+  a.Hkv = p->n_kv_heads;
+  a.G = a.Hq / a.Hkv;
+  a.num_pages = num_pages;
+  a.stride = page_table_stride;
+  a.max_seq_len = max_seq_len;
+  a.n_split = grid.n_split;
+  a.pages_per_split = grid.pages_per_split;
+  a.n_hchunk = grid.n_hchunk;
+  a.inv_log_train = inv_log_train(p);
+  a.null_floor = (p->flags & POLAR_FLAG_NULL_FLOOR) ? 1 : 0;
+  hipError_t err = polar::launch_decode((int)dt, a, (hipStream_t)stream);
+  if (err != hipSuccess) return fail(POLAR_ERR_HIP, "decode launch: %s", hipGetErrorString(err));
+  return POLAR_OK;
+}
+
+const char *polar_status_str(polar_status s) {
+  switch (s) {
+    case POLAR_OK: return "ok";
+    case POLAR_ERR_NULL_POINTER: return "null pointer";
+    case POLAR_ERR_BAD_SHAPE: return "bad shape";
+    case POLAR_ERR_UNSUPPORTED: return "unsupported";
+    case POLAR_ERR_MISALIGNED: return "misaligned pointer";
+    case POLAR_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case POLAR_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char *polar_last_error(void) { return g_last_error; }
+
+int32_t polar_abi_version(void) { return POLAR_ABI_VERSION; }
+
+}  // extern "C"

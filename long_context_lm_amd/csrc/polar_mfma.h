@@ -1,0 +1,102 @@
+// Device building blocks shared by the Polar Attention kernels on gfx950 (CDNA4):
+// MFMA element traits for bf16 and fp32 inputs, wave-half exchanges, fast exp2.
+//
+// MFMA register layouts used throughout (wave64):
+//  * 32x32 output (v_mfma_f32_32x32x16_bf16 / v_mfma_f32_32x32x2_f32): lane l holds
+//    column l%32 and rows 8*(r/4) + 4*(l/32) + r%4 for its 16 accumulators r.
+//  * 16x16 output (v_mfma_f32_16x16x32_bf16 / v_mfma_f32_16x16x4_f32): lane l holds
+//    column l%16 and rows 4*(l/16) + r for its 4 accumulators r.
+//  * A and B operands: lane l supplies KPL consecutive contraction slots of row (A) or
+//    column (B) l%32 (resp. l%16) in slot group l/32 (resp. l/16).  The kernels only rely
+//    on A and B using the same slot numbering, so any contraction order is correct.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace polar {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// x from this lane and from lane l^32, combined in the same order in every lane.
+__device__ __forceinline__ float half_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return __int_as_float(r[0]) + __int_as_float(r[1]);
+}
+__device__ __forceinline__ float half_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+}
+
+// bf16 inputs: 8 contraction slots per lane per MFMA, fp32 accumulation.
+struct Bf16 {
+  using elem_t = uint16_t;                 // storage (bit pattern)
+  using frag_t = bf16x8;
+  static constexpr int kpl = 8;
+  static constexpr int vec = 8;            // elements per 16-byte global access
+
+  __device__ static __forceinline__ f32x16 mma32(frag_t a, frag_t b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ f32x4 mma16(frag_t a, frag_t b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ frag_t load(const elem_t *p) {
+    return *reinterpret_cast<const frag_t *>(p);
+  }
+  __device__ static __forceinline__ frag_t zero() {
+    u32x4 z = {0u, 0u, 0u, 0u};
+    return __builtin_bit_cast(frag_t, z);
+  }
+  // Round kpl probabilities to bf16 (nearest-even) for the P.V product.
+  __device__ static __forceinline__ frag_t pack(const float *x) {
+    frag_t r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = (__bf16)x[e];
+    return r;
+  }
+  // S += sum p, Q += sum p^2 over the rounded probabilities (dot2 per pair).
+  __device__ static __forceinline__ void stats(frag_t f, float &S, float &Q) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    u32x4 w = __builtin_bit_cast(u32x4, f);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      bf16x2 pr = __builtin_bit_cast(bf16x2, w[e]);
+      S = __builtin_amdgcn_fdot2_f32_bf16(pr, one, S, false);
+      Q = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, Q, false);
+    }
+  }
+};
+
+// fp32 inputs: 1 contraction slot per lane per MFMA; probabilities stay fp32.
+struct F32 {
+  using elem_t = float;
+  using frag_t = float;
+  static constexpr int kpl = 1;
+  static constexpr int vec = 4;
+
+  __device__ static __forceinline__ f32x16 mma32(frag_t a, frag_t b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ f32x4 mma16(frag_t a, frag_t b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ frag_t load(const elem_t *p) { return *p; }
+  __device__ static __forceinline__ frag_t zero() { return 0.0f; }
+  __device__ static __forceinline__ frag_t pack(const float *x) { return x[0]; }
+  __device__ static __forceinline__ void stats(frag_t f, float &S, float &Q) {
+    S += f;
+    Q = fmaf(f, f, Q);
+  }
+};
+
+}  // namespace polar

@@ -1,0 +1,111 @@
+"""torch-facing wrappers over libpolar: allocate outputs, pass pointers and the stream.
+
+Nothing here computes: shapes are read, buffers allocated with torch, and the C entry
+points of include/polar.h are called on torch's current HIP stream.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import _lib
+
+_DT = {torch.bfloat16: _lib.POLAR_DTYPE_BF16, torch.float32: _lib.POLAR_DTYPE_F32}
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _params(Hq, Hkv, d, beta, null_bias, count_vec, train_len, flags):
+    return _lib.polar_params(Hq, Hkv, d, train_len, flags, _ptr(beta), _ptr(null_bias),
+                             _ptr(count_vec))
+
+
+def _device_f32(x, device):
+    if x is None:
+        return None
+    return torch.as_tensor(x, dtype=torch.float32, device=device).contiguous()
+
+
+def _check_input(t: torch.Tensor, name: str) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype not in _DT:
+        raise ValueError(f"{name} has dtype {t.dtype}; bfloat16 or float32 expected")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _outputs(lead, Hq, d, device, want_count, want_gate, want_lse):
+    o = dict(dir=torch.empty(*lead, Hq, d, device=device, dtype=torch.float32),
+             n_eff=torch.empty(*lead, Hq, device=device, dtype=torch.float32))
+    o["count"] = (torch.empty(*lead, Hq, d, device=device, dtype=torch.float32)
+                  if want_count else None)
+    o["gate"] = torch.empty(*lead, Hq, device=device, dtype=torch.float32) if want_gate else None
+    o["lse"] = torch.empty(*lead, Hq, device=device, dtype=torch.float32) if want_lse else None
+    c = _lib.polar_outputs(_ptr(o["dir"]), _ptr(o["count"]), _ptr(o["n_eff"]), _ptr(o["gate"]),
+                           _ptr(o["lse"]))
+    return o, c
+
+
+def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta=None, null_bias=None,
+             count_vec=None, train_len: int = 2048,
+             flags: int = _lib.POLAR_FLAG_LENGTH_TEMP | _lib.POLAR_FLAG_NULL_FLOOR,
+             want_gate: bool = True, want_lse: bool = True, stream=None) -> dict:
+    """Causal Polar Attention prefill.  q [B,T,Hq,d], k and v [B,T,Hkv,d] on the GPU."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check_input(t, n)
+    B, T, Hq, d = q.shape
+    Hkv = k.shape[2]
+    if k.shape != (B, T, Hkv, d) or v.shape != k.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("k and v must be [B,T,Hkv,d] with q's dtype")
+    dev = q.device
+    beta, null_bias, count_vec = (_device_f32(beta, dev), _device_f32(null_bias, dev),
+                                  _device_f32(count_vec, dev))
+    prm = _params(Hq, Hkv, d, beta, null_bias, count_vec, train_len, flags)
+    out, cout = _outputs((B, T), Hq, d, dev, count_vec is not None, want_gate, want_lse)
+    s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+    _lib.check(_lib.polar_attn_fwd(prm, _DT[q.dtype], B, T, q.data_ptr(), k.data_ptr(),
+                                   v.data_ptr(), cout, s))
+    return out
+
+
+def decode_workspace_bytes(Hq: int, Hkv: int, B: int, max_seq_len: int, page_size: int = 64,
+                           d: int = 64) -> int:
+    prm = _lib.polar_params(Hq, Hkv, d, 2048, 0, None, None, None)
+    return _lib.polar_decode_workspace_bytes(prm, B, max_seq_len, page_size)
+
+
+def attn_decode_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                      page_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
+                      beta=None, null_bias=None, count_vec=None, train_len: int = 2048,
+                      flags: int = _lib.POLAR_FLAG_LENGTH_TEMP | _lib.POLAR_FLAG_NULL_FLOOR,
+                      workspace: Optional[torch.Tensor] = None, want_gate: bool = True,
+                      want_lse: bool = True, stream=None) -> dict:
+    """GQA paged decode.  q [B,Hq,d]; caches [num_pages,Hkv,page,d]; table [B,stride] int32."""
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _check_input(t, n)
+    B, Hq, d = q.shape
+    num_pages, Hkv, page, d2 = k_cache.shape
+    if d2 != d or v_cache.shape != k_cache.shape:
+        raise ValueError("caches must be [num_pages,Hkv,page,d] matching q")
+    if page_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise ValueError("page_table and seq_lens must be int32")
+    if page_table.dim() != 2 or page_table.shape[0] != B or seq_lens.shape != (B,):
+        raise ValueError("page_table must be [B,stride] and seq_lens [B]")
+    dev = q.device
+    beta, null_bias, count_vec = (_device_f32(beta, dev), _device_f32(null_bias, dev),
+                                  _device_f32(count_vec, dev))
+    prm = _params(Hq, Hkv, d, beta, null_bias, count_vec, train_len, flags)
+    need = _lib.polar_decode_workspace_bytes(prm, B, max_seq_len, page)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    out, cout = _outputs((B,), Hq, d, dev, count_vec is not None, want_gate, want_lse)
+    s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+    _lib.check(_lib.polar_attn_decode_paged(
+        prm, _DT[q.dtype], B, q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), num_pages,
+        page, page_table.data_ptr(), page_table.shape[1], seq_lens.data_ptr(), max_seq_len,
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), cout, s))
+    return out

@@ -1,0 +1,132 @@
+"""libpolar loads, exports every symbol include/polar.h declares, and validates its
+arguments on the host before any HIP call (no GPU needed: no call here launches)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from long_context_lm_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+A = 0x10000            # a 16-byte aligned fake device address (never dereferenced)
+
+
+def declared_symbols():
+    src = open(os.path.join(ROOT, "include", "polar.h")).read()
+    return sorted(set(re.findall(r"POLAR_API\s+[\w\s\*]+?\b(polar_\w+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    names = declared_symbols()
+    assert set(names) == set(_lib.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert _lib.polar_abi_version() == 1
+
+
+def test_status_strings():
+    for code in range(7):
+        assert _lib.polar_status_str(code) not in ("", "unknown status")
+    assert _lib.polar_status_str(99) == "unknown status"
+
+
+def params(**kw):
+    d = dict(n_q_heads=16, n_kv_heads=4, head_dim=64, train_len=2048, flags=3, beta=None,
+             null_bias=None, count_vec=A)
+    d.update(kw)
+    return _lib.polar_params(d["n_q_heads"], d["n_kv_heads"], d["head_dim"], d["train_len"],
+                             d["flags"], d["beta"], d["null_bias"], d["count_vec"])
+
+
+def outs(**kw):
+    d = dict(dir=A, count=A, n_eff=A, gate=A, lse=A)
+    d.update(kw)
+    return _lib.polar_outputs(d["dir"], d["count"], d["n_eff"], d["gate"], d["lse"])
+
+
+def fwd(p=None, dt=1, B=1, T=8, q=A, k=A, v=A, o=None):
+    p = params() if p is None else p
+    o = outs() if o is None else o
+    return _lib.polar_attn_fwd(p, dt, B, T, q, k, v, o, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(p=params(head_dim=128)), _lib.POLAR_ERR_UNSUPPORTED),
+    (dict(dt=7), _lib.POLAR_ERR_UNSUPPORTED),
+    (dict(p=params(n_q_heads=6, n_kv_heads=4)), _lib.POLAR_ERR_BAD_SHAPE),
+    (dict(p=params(n_kv_heads=0)), _lib.POLAR_ERR_BAD_SHAPE),
+    (dict(p=params(train_len=1)), _lib.POLAR_ERR_BAD_SHAPE),
+    (dict(p=params(flags=4)), _lib.POLAR_ERR_UNSUPPORTED),
+    (dict(B=-1), _lib.POLAR_ERR_BAD_SHAPE),
+    (dict(T=-5), _lib.POLAR_ERR_BAD_SHAPE),
+    (dict(q=None), _lib.POLAR_ERR_NULL_POINTER),
+    (dict(o=outs(dir=None)), _lib.POLAR_ERR_NULL_POINTER),
+    (dict(o=outs(n_eff=None)), _lib.POLAR_ERR_NULL_POINTER),
+    (dict(p=params(count_vec=None)), _lib.POLAR_ERR_NULL_POINTER),
+    (dict(k=A + 4), _lib.POLAR_ERR_MISALIGNED),
+    (dict(o=outs(dir=A + 8)), _lib.POLAR_ERR_MISALIGNED),
+])
+def test_prefill_validation_errors(kw, code):
+    assert fwd(**kw) == code
+    assert _lib.polar_last_error() != ""
+
+
+def test_prefill_null_params_and_outputs():
+    lib = _lib.load()
+    assert lib.polar_attn_fwd(None, 1, 1, 8, A, A, A, ctypes.byref(outs()), None) == \
+        _lib.POLAR_ERR_NULL_POINTER
+    assert lib.polar_attn_fwd(ctypes.byref(params()), 1, 1, 8, A, A, A, None, None) == \
+        _lib.POLAR_ERR_NULL_POINTER
+
+
+def test_empty_prefill_is_a_valid_no_op():
+    # nothing is launched for B == 0 or T == 0, so no GPU is touched
+    assert fwd(B=0) == _lib.POLAR_OK
+    assert fwd(T=0) == _lib.POLAR_OK
+    assert fwd(p=params(count_vec=None), o=outs(count=None, gate=None, lse=None), T=0) == \
+        _lib.POLAR_OK
+
+
+def dec(p=None, dt=1, B=2, q=A, kc=A, vc=A, num_pages=10, page=64, table=A, stride=4,
+        lens=A, max_len=256, ws=A, ws_bytes=None, o=None):
+    p = params() if p is None else p
+    o = outs() if o is None else o
+    if ws_bytes is None:
+        ws_bytes = _lib.polar_decode_workspace_bytes(p, B, max_len, page)
+    return _lib.polar_attn_decode_paged(p, dt, B, q, kc, vc, num_pages, page, table, stride,
+                                        lens, max_len, ws, ws_bytes, o, None)
+
+
+def test_workspace_bytes():
+    p = params()
+    n = _lib.polar_decode_workspace_bytes(p, 16, 262144, 64)
+    assert n > 0 and n % 16 == 0
+    assert _lib.polar_decode_workspace_bytes(p, 16, 262144, 32) == 0
+    assert _lib.polar_decode_workspace_bytes(p, 16, 0, 64) == 0
+    assert _lib.polar_decode_workspace_bytes(params(n_q_heads=5), 16, 100, 64) == 0
+    assert _lib.polar_decode_workspace_bytes(p, 0, 100, 64) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(page=32), _lib.POLAR_ERR_UNSUPPORTED),
+    (dict(p=params(head_dim=32)), _lib.POLAR_ERR_UNSUPPORTED),
+    (dict(B=-1), _lib.POLAR_ERR_BAD_SHAPE),
+    (dict(num_pages=0), _lib.POLAR_ERR_BAD_SHAPE),
+    (dict(max_len=0, ws_bytes=1 << 20), _lib.POLAR_ERR_BAD_SHAPE),
+    (dict(stride=3), _lib.POLAR_ERR_BAD_SHAPE),
+    (dict(table=None), _lib.POLAR_ERR_NULL_POINTER),
+    (dict(lens=None), _lib.POLAR_ERR_NULL_POINTER),
+    (dict(ws=None), _lib.POLAR_ERR_NULL_POINTER),
+    (dict(kc=A + 2), _lib.POLAR_ERR_MISALIGNED),
+    (dict(ws=A + 4), _lib.POLAR_ERR_MISALIGNED),
+    (dict(ws_bytes=15), _lib.POLAR_ERR_WORKSPACE_TOO_SMALL),
+])
+def test_decode_validation_errors(kw, code):
+    assert dec(**kw) == code
+    assert _lib.polar_last_error() != ""
+
+
+def test_empty_decode_is_a_valid_no_op():
+    assert dec(B=0, ws_bytes=0) == _lib.POLAR_OK

@@ -1,0 +1,156 @@
+"""GPU parity of polar_attn_fwd (causal prefill) against the CPU oracle.
+
+Element-wise on every output at sizes the oracle finishes in seconds (several row blocks,
+several 64-key tiles, ragged tails), and on sampled rows at the full workload sizes in the
+launch configuration the benchmark uses.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from parity import assert_close, gpu_prefill, oracle_prefill, select
+
+pytestmark = pytest.mark.gpu
+
+ON = synth.FLAG_LENGTH_TEMP | synth.FLAG_NULL_FLOOR
+
+
+def full_check(p, label, **kw):
+    got = gpu_prefill(p, **kw)
+    want = oracle_prefill(p)
+    return assert_close(got, want, p.count_vec, p.dtype, label=label)
+
+
+def test_c1_tiny_fp32_all_rows(gpu_lib):
+    full_check(synth.prefill_inputs("c1"), "c1 fp32 T=256")
+
+
+@pytest.mark.parametrize("T", [1, 2, 31, 63, 64, 65, 129, 300])
+def test_fp32_ragged_lengths(gpu_lib, T):
+    full_check(synth.prefill_inputs("c1", T=T), f"fp32 T={T}")
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (6, 3), (3, 1), (16, 2)])
+def test_fp32_gqa_groupings(gpu_lib, Hq, Hkv):
+    full_check(synth.prefill_inputs("c1", T=150, Hq=Hq, Hkv=Hkv), f"fp32 Hq={Hq} Hkv={Hkv}")
+
+
+def test_c2_structure_bf16_all_rows(gpu_lib):
+    full_check(synth.prefill_inputs("c2", B=2, T=700), "c2-like bf16 B=2 T=700")
+
+
+@pytest.mark.parametrize("T", [1, 5, 64, 127, 128, 129, 257])
+def test_bf16_ragged_lengths(gpu_lib, T):
+    full_check(synth.prefill_inputs("c2", B=1, T=T), f"bf16 T={T}")
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 4), (6, 3), (3, 1), (32, 4)])
+def test_bf16_gqa_groupings(gpu_lib, Hq, Hkv):
+    full_check(synth.prefill_inputs("c2", B=1, T=333, Hq=Hq, Hkv=Hkv), f"bf16 Hq={Hq} Hkv={Hkv}")
+
+
+@pytest.mark.parametrize("flags,train_len", [(0, 2048), (1, 64), (2, 64), (3, 64), (3, 2)])
+def test_bf16_flags_and_temperature(gpu_lib, flags, train_len):
+    # train_len 64 puts the length temperature to work inside a 900-row sequence
+    p = synth.prefill_inputs("c3", T=900, flags=flags, train_len=train_len)
+    full_check(p, f"bf16 flags={flags} train_len={train_len}")
+
+
+def test_fp32_flags_and_temperature(gpu_lib):
+    p = synth.prefill_inputs("c1", T=256, flags=3, train_len=16)
+    full_check(p, "fp32 flags=3 train_len=16")
+
+
+def test_per_head_beta_and_bias(gpu_lib):
+    p = synth.prefill_inputs("c2", B=1, T=400, train_len=32)
+    g = np.random.default_rng(7)
+    p.beta = g.uniform(2.0, 14.0, p.Hq).astype(np.float32)
+    p.null_bias = g.uniform(-1.0, 1.0, p.Hq).astype(np.float32)
+    full_check(p, "bf16 per-head beta/bias")
+    p1 = synth.prefill_inputs("c1", T=200, train_len=32)
+    p1.beta = g.uniform(2.0, 14.0, p1.Hq).astype(np.float32)
+    p1.null_bias = g.uniform(-1.0, 1.0, p1.Hq).astype(np.float32)
+    full_check(p1, "fp32 per-head beta/bias")
+
+
+def test_sharp_rows_large_beta(gpu_lib):
+    # beta 200 makes most rows nearly one-hot: n_eff -> 1, count -> 0
+    p = synth.prefill_inputs("c2", B=1, T=300)
+    p.beta = np.full(p.Hq, 200.0, np.float32)
+    full_check(p, "bf16 beta=200")
+    p1 = synth.prefill_inputs("c1", T=200)
+    p1.beta = np.full(p1.Hq, 200.0, np.float32)
+    full_check(p1, "fp32 beta=200")
+
+
+def test_optional_outputs_absent(gpu_lib):
+    p = synth.prefill_inputs("c2", B=1, T=200)
+    full = gpu_prefill(p)
+    p2 = synth.prefill_inputs("c2", B=1, T=200)
+    p2.count_vec = None
+    from parity import to_dev
+    from long_context_lm_amd import attn_fwd
+    q, k, v = (to_dev(getattr(p2, n), p2.dtype) for n in ("q", "k", "v"))
+    part = attn_fwd(q, k, v, beta=p2.beta, null_bias=p2.null_bias, count_vec=None,
+                    train_len=p2.train_len, flags=p2.flags, want_gate=False, want_lse=False)
+    torch.cuda.synchronize()
+    assert part["count"] is None and part["gate"] is None and part["lse"] is None
+    assert torch.equal(part["dir"], full["dir"]) and torch.equal(part["n_eff"], full["n_eff"])
+
+
+def test_empty_inputs_are_no_ops(gpu_lib):
+    from long_context_lm_amd import attn_fwd
+    for B, T in ((0, 16), (1, 0)):
+        q = torch.zeros(B, T, 16, 64, dtype=torch.bfloat16, device="cuda")
+        k = torch.zeros(B, T, 4, 64, dtype=torch.bfloat16, device="cuda")
+        out = attn_fwd(q, k, k.clone())
+        assert out["dir"].numel() == 0
+
+
+def test_deterministic(gpu_lib):
+    p = synth.prefill_inputs("c2", B=1, T=500)
+    a, b = gpu_prefill(p), gpu_prefill(p)
+    for key in ("dir", "count", "n_eff", "gate", "lse"):
+        assert torch.equal(a[key], b[key]), key
+
+
+def _sampled(name, rows_fn, label):
+    p = synth.prefill_inputs(name)
+    got = gpu_prefill(p)
+    rows = np.unique(np.clip(rows_fn(p.T), 0, p.T - 1))
+    needle_rows = np.unique([i for (_, _, _, i) in p.needles]) if p.needles else np.array([])
+    rows = np.unique(np.concatenate([rows, needle_rows]).astype(np.int64))
+    batches = np.unique([0, p.B - 1])
+    want = oracle_prefill(p, rows=rows, batches=batches)
+    e = assert_close(select(got, batches=batches, rows=rows), want, p.count_vec, p.dtype,
+                     label=label)
+    # every row: finite outputs, unit direction, n_eff within [1, i+1]
+    n = got["n_eff"]
+    i1 = torch.arange(1, p.T + 1, device=n.device, dtype=n.dtype)[None, :, None]
+    assert torch.isfinite(n).all() and (n >= 1 - 1e-3).all() and (n <= i1 * (1 + 1e-3)).all()
+    dn = got["dir"].norm(dim=-1)
+    assert (dn - 1).abs().max().item() < 1e-3
+    return p, got, e
+
+
+def test_c2_full_size_sampled_rows(gpu_lib):
+    rng = np.random.default_rng(2)
+    _sampled("c2", lambda T: np.concatenate([[0, 1, 63, 64, 127, 128, T - 1],
+                                             rng.integers(0, T, 24)]), "c2 full B=8 T=2048")
+
+
+def test_c3_full_size_sampled_rows(gpu_lib):
+    rng = np.random.default_rng(3)
+    _sampled("c3", lambda T: np.concatenate([[0, 2047, 2048, 8191, T - 2, T - 1],
+                                             rng.integers(0, T, 12)]), "c3 full T=16384")
+
+
+def test_c4_full_size_sampled_rows(gpu_lib):
+    rng = np.random.default_rng(4)
+    p, got, _ = _sampled("c4", lambda T: np.concatenate([[0, 2047, 2048, 32767, T - 1],
+                                                        rng.integers(0, T, 6)]),
+                         "c4 full T=65536")
+    # the planted needles dominate the last row: gate near 1, small n_eff
+    for (_, h, _, i) in p.needles:
+        assert got["gate"][0, i, h].item() > 0.9
