@@ -41,6 +41,11 @@ polar_status check_params(const polar_params *p, polar_dtype dt, const polar_out
   if ((p->flags & POLAR_FLAG_LENGTH_TEMP) && p->train_len < 2)
     return fail(POLAR_ERR_BAD_SHAPE, "train_len must be >= 2 with LENGTH_TEMP (got %d)",
                 p->train_len);
+  return POLAR_OK;
+}
+
+// Output pointers are checked only for non-empty calls (empty tensors may be NULL).
+polar_status check_outputs(const polar_params *p, const polar_outputs *out) {
   if (!out->dir) return fail(POLAR_ERR_NULL_POINTER, "outputs.dir is NULL");
   if (!out->n_eff) return fail(POLAR_ERR_NULL_POINTER, "outputs.n_eff is NULL");
   if (out->count && !p->count_vec)
@@ -65,10 +70,12 @@ polar_status polar_attn_fwd(const polar_params *p, polar_dtype dt, int32_t B, in
   polar_status st = check_params(p, dt, out);
   if (st != POLAR_OK) return st;
   if (B < 0 || T < 0) return fail(POLAR_ERR_BAD_SHAPE, "B (%d) and T (%d) must be >= 0", B, T);
+  if (B == 0 || T == 0) return POLAR_OK;
+  st = check_outputs(p, out);
+  if (st != POLAR_OK) return st;
   if (!q || !k || !v) return fail(POLAR_ERR_NULL_POINTER, "q, k and v must be non-NULL");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v))
     return fail(POLAR_ERR_MISALIGNED, "q, k and v must be 16-byte aligned");
-  if (B == 0 || T == 0) return POLAR_OK;
 
   polar::PrefillArgs a;
   a.q = q;
@@ -122,6 +129,8 @@ polar_status polar_attn_decode_paged(const polar_params *p, polar_dtype dt, int3
     return fail(POLAR_ERR_UNSUPPORTED, "page_size %d unsupported (only %d)", page_size,
                 polar::kPageSize);
   if (B == 0) return POLAR_OK;
+  st = check_outputs(p, out);
+  if (st != POLAR_OK) return st;
   if (!q || !k_cache || !v_cache || !page_table || !seq_lens || !workspace)
     return fail(POLAR_ERR_NULL_POINTER,
                 "q, k_cache, v_cache, page_table, seq_lens and workspace must be non-NULL");

@@ -67,10 +67,11 @@ struct Bf16 {
   // S += sum p, Q += sum p^2 over the rounded probabilities (dot2 per pair).
   __device__ static __forceinline__ void stats(frag_t f, float &S, float &Q) {
     const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-    u32x4 w = __builtin_bit_cast(u32x4, f);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      bf16x2 pr = __builtin_bit_cast(bf16x2, w[e]);
+      bf16x2 pr;
+      pr[0] = f[2 * e];
+      pr[1] = f[2 * e + 1];
       S = __builtin_amdgcn_fdot2_f32_bf16(pr, one, S, false);
       Q = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, Q, false);
     }

@@ -87,6 +87,8 @@ def test_empty_prefill_is_a_valid_no_op():
     assert fwd(T=0) == _lib.POLAR_OK
     assert fwd(p=params(count_vec=None), o=outs(count=None, gate=None, lse=None), T=0) == \
         _lib.POLAR_OK
+    # empty tensors may come as NULL pointers
+    assert fwd(B=0, q=None, k=None, v=None, o=outs(dir=None, n_eff=None)) == _lib.POLAR_OK
 
 
 def dec(p=None, dt=1, B=2, q=A, kc=A, vc=A, num_pages=10, page=64, table=A, stride=4,
@@ -130,3 +132,5 @@ def test_decode_validation_errors(kw, code):
 
 def test_empty_decode_is_a_valid_no_op():
     assert dec(B=0, ws_bytes=0) == _lib.POLAR_OK
+    assert dec(B=0, ws_bytes=0, q=None, table=None, lens=None, ws=None,
+               o=outs(dir=None, n_eff=None)) == _lib.POLAR_OK
