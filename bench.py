@@ -1,0 +1,220 @@
+"""Benchmark of the Polar Attention hot path on one MI355X.
+
+One step = one causal prefill of the T=64K extrapolation workload (B=1, T=65536, 16 query /
+4 KV heads, d=64, bf16, length temperature and extreme-value floor on, 8 planted needles)
+followed by one GQA paged decode of the 256K workload (16 sequences x 262144 keys, 64-token
+pages behind a shuffled page table, one needle per (sequence, head)).  Inputs are the seeded
+synthetic workloads of ``synth`` and are resident in HBM before timing starts.
+
+Prints one JSON line.  ``value`` is prefill TFLOP/s over the timed steps, with the
+algorithmic flop count 4*d*Hq*T(T+1)/2 (QK^T and PV over visible pairs only); the decode
+figure (GB/s of K+V read once, plus table, queries and outputs) sits in ``decode``.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       python bench.py --copy-probe BYTES   (plain device copy, for counter calibration)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import glob
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Polar attn fwd TFLOP/s (bf16, T=64K) + paged decode GB/s at 256K KV"
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
+
+
+def src_hash() -> str:
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "long_context_lm_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode())
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def prefill_flops(B, T, Hq, d):
+    return 4.0 * d * B * Hq * T * (T + 1) / 2.0
+
+
+def decode_bytes(B, L, Hq, Hkv, d, page, stride):
+    kv = 2.0 * B * L * Hkv * d * 2            # K and V, bf16, each byte once
+    table = 4.0 * B * stride + 4.0 * B        # page table + seq_lens
+    qb = 2.0 * B * Hq * d
+    outs = 4.0 * B * Hq * (2 * d + 3)         # dir, count, n_eff, gate, lse
+    return kv + table + qb + outs
+
+
+def traffic_record(kind: str):
+    """HBM bytes per launch from the committed counter summary, if the kernels are unchanged."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_src_sha256") != src_hash() or kind not in rec:
+        return None
+    r = rec[kind]
+    return r["fetch_bytes"] * rec["fetch_factor"] + r["write_bytes"] * rec["write_factor"]
+
+
+def cpu_baseline(pre, dec):
+    """The CPU oracle, as it stands, on a bounded sample of the same two workloads."""
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max(i["num_threads"] for i in threadpool_info())
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    rows = np.linspace(0, pre.T - 1, 3072).astype(np.int64)
+    t0 = time.perf_counter()
+    oracle.polar_prefill(pre.as_f32("q"), pre.as_f32("k"), pre.as_f32("v"), pre.beta,
+                         pre.null_bias, pre.count_vec, pre.train_len, pre.flags, rows=rows)
+    t_pre = time.perf_counter() - t0
+    flops = 4.0 * pre.d * pre.Hq * float((rows + 1).sum())
+    batches = list(range(dec.B))
+    t0 = time.perf_counter()
+    oracle.polar_decode_paged(synth.bf16_bits_to_f32(dec.q), dec.k_pool, dec.v_pool,
+                              dec.page_table, dec.seq_lens, dec.page_size, dec.beta,
+                              dec.null_bias, dec.count_vec, dec.train_len, dec.flags,
+                              to_f64=lambda a: synth.bf16_bits_to_f32(a).astype(np.float64),
+                              batches=batches)
+    t_dec = time.perf_counter() - t0
+    dbytes = decode_bytes(len(batches), dec.max_seq_len, dec.Hq, dec.Hkv, dec.d, dec.page_size,
+                          dec.page_table.shape[1])
+    return {"value": flops / t_pre / 1e12, "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"prefill rows {len(rows)} evenly spaced of T=65536, all 16 heads "
+                      f"({t_pre:.1f} s)",
+            "decode": {"value": dbytes / t_dec / 1e9, "unit": "GB/s",
+                       "sample": f"decode, all {len(batches)} sequences ({t_dec:.1f} s)"}}
+
+
+def copy_probe(nbytes: int):
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the Polar Attention path here is a single-GPU "
+              "kernel library (see the sharding notes in DESIGN.md); run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
+
+    import torch
+    import synth
+    from long_context_lm_amd import _lib, attn_decode_paged, attn_fwd
+    _lib.load()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = "cuda"
+
+    def to_dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    pre = synth.prefill_inputs("c4")
+    dec = synth.decode_inputs("c5")
+    q, k, v = to_dev(pre.q), to_dev(pre.k), to_dev(pre.v)
+    pkw = dict(beta=torch.from_numpy(pre.beta).to(dev), null_bias=torch.from_numpy(pre.null_bias).to(dev),
+               count_vec=torch.from_numpy(pre.count_vec).to(dev), train_len=pre.train_len,
+               flags=pre.flags)
+    qd, kc, vc = to_dev(dec.q), to_dev(dec.k_pool), to_dev(dec.v_pool)
+    table = torch.from_numpy(dec.page_table).to(dev)
+    lens = torch.from_numpy(dec.seq_lens).to(dev)
+    dkw = dict(beta=torch.from_numpy(dec.beta).to(dev), null_bias=torch.from_numpy(dec.null_bias).to(dev),
+               count_vec=torch.from_numpy(dec.count_vec).to(dev), train_len=dec.train_len,
+               flags=dec.flags)
+    from long_context_lm_amd import decode_workspace_bytes
+    ws = torch.empty(decode_workspace_bytes(dec.Hq, dec.Hkv, dec.B, dec.max_seq_len),
+                     dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    print(f"[bench] inputs resident: prefill T={pre.T}, decode B={dec.B} L={dec.max_seq_len}",
+          file=sys.stderr, flush=True)
+
+    def step(evs=None):
+        if evs:
+            evs[0].record()
+        attn_fwd(q, k, v, **pkw)
+        if evs:
+            evs[1].record()
+        attn_decode_paged(qd, kc, vc, table, lens, dec.max_seq_len, workspace=ws, **dkw)
+        if evs:
+            evs[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_pre = [e[0].elapsed_time(e[1]) for e in events]
+    t_dec = [e[1].elapsed_time(e[2]) for e in events]
+    F = prefill_flops(pre.B, pre.T, pre.Hq, pre.d)
+    Dbytes = decode_bytes(dec.B, dec.max_seq_len, dec.Hq, dec.Hkv, dec.d, dec.page_size,
+                          dec.page_table.shape[1])
+    pre_ms = float(np.mean(t_pre))
+    dec_ms = float(np.mean(t_dec))
+    tflops = F / (pre_ms * 1e-3) / 1e12
+    gbs = Dbytes / (dec_ms * 1e-3) / 1e9
+    print(f"[bench] prefill mean {pre_ms:.3f} ms (median {np.median(t_pre):.3f}), "
+          f"decode mean {dec_ms:.3f} ms (median {np.median(t_dec):.3f})", file=sys.stderr,
+          flush=True)
+    tr_pre = traffic_record("prefill")
+    tr_dec = traffic_record("decode")
+    rec = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "prefill B=1 T=65536 Hq=16 Hkv=4 d=64 causal bf16 (T=64K, "
+                               "32x train length, 8 needles) + paged decode B=16 L=262144 "
+                               "Hq=16 Hkv=4 d=64 page=64 shuffled table (256K KV)",
+                   "prefill_ms": round(pre_ms, 4), "decode_ms": round(dec_ms, 4)},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": tr_pre},
+        "decode": {"value": round(gbs, 1), "unit": "GB/s", "ms": round(dec_ms, 4),
+                   "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                                "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                                "traffic": tr_dec}},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(pre, dec)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()
