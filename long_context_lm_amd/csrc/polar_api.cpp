@@ -77,6 +77,12 @@ polar_status polar_attn_fwd(const polar_params *p, polar_dtype dt, int32_t B, in
   if (!aligned16(q) || !aligned16(k) || !aligned16(v))
     return fail(POLAR_ERR_MISALIGNED, "q, k and v must be 16-byte aligned");
 
+  // K/V rows are addressed with 32-bit byte offsets (one tile past the end included).
+  const long long elt = dt == POLAR_DTYPE_BF16 ? 2 : 4;
+  if (((long long)T + 64) * p->n_kv_heads * polar::kHeadDim * elt >= 0x7fffffffLL)
+    return fail(POLAR_ERR_BAD_SHAPE, "T*Hkv too large for one sequence (T=%d, Hkv=%d)", T,
+                p->n_kv_heads);
+
   polar::PrefillArgs a;
   a.q = q;
   a.k = k;
