@@ -32,6 +32,11 @@ __device__ __forceinline__ float half_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
   return __int_as_float(r[0]) + __int_as_float(r[1]);
 }
+// The value lane l^32 holds (exact).
+__device__ __forceinline__ float half_other(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return __int_as_float(r[0] == __float_as_int(x) ? r[1] : r[0]);
+}
 __device__ __forceinline__ float half_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
   return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
@@ -56,6 +61,10 @@ struct Bf16 {
   __device__ static __forceinline__ frag_t zero() {
     u32x4 z = {0u, 0u, 0u, 0u};
     return __builtin_bit_cast(frag_t, z);
+  }
+  __device__ static __forceinline__ frag_t ones() {
+    const u32x4 o = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+    return __builtin_bit_cast(frag_t, o);
   }
   // Round kpl probabilities to bf16 (nearest-even) for the P.V product.
   __device__ static __forceinline__ frag_t pack(const float *x) {
@@ -93,6 +102,7 @@ struct F32 {
   }
   __device__ static __forceinline__ frag_t load(const elem_t *p) { return *p; }
   __device__ static __forceinline__ frag_t zero() { return 0.0f; }
+  __device__ static __forceinline__ frag_t ones() { return 1.0f; }
   __device__ static __forceinline__ frag_t pack(const float *x) { return x[0]; }
   __device__ static __forceinline__ void stats(frag_t f, float &S, float &Q) {
     S += f;

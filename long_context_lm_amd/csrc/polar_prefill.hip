@@ -38,6 +38,10 @@
 #ifndef POLAR_PREFILL_KT
 #define POLAR_PREFILL_KT 64
 #endif
+// 1: probability sums on the matrix pipe (ones and Gram products); 0: fp32 adds/FMAs.
+#ifndef POLAR_PREFILL_MSTATS
+#define POLAR_PREFILL_MSTATS 0
+#endif
 
 namespace polar {
 namespace {
@@ -75,8 +79,8 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
   constexpr int KROW = LdsCfg<TR>::krow, VROW = LdsCfg<TR>::vrow;
   constexpr int VEC = TR::vec;                       // elements per 16-byte chunk
   constexpr int CPR = kD / VEC;                      // chunks per key row
-  __shared__ __attribute__((aligned(16))) E Ks[3][kKT * KROW];
-  __shared__ __attribute__((aligned(16))) E Vs[3][kD * VROW];
+  __shared__ __attribute__((aligned(16))) E Ks[4][kKT * KROW];
+  __shared__ __attribute__((aligned(16))) E Vs[4][kD * VROW];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g32 = lane >> 5, c32 = lane & 31;
@@ -132,6 +136,10 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
   }
 
   f32x16 o[QB][2];
+  // Statistics on the matrix pipe: sacc = 1 * P^T (every row holds sum p of the lane's
+  // query), qacc = P P^T (its diagonal holds sum p^2).  Both use the rounded P of the P.V
+  // product.
+  f32x16 sacc[QB], qacc[QB];
   float Mref[QB], smax[QB], Ssum[QB], Qsum[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
@@ -139,6 +147,11 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
     for (int db = 0; db < 2; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[qb][db][r] = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      sacc[qb][r] = 0.f;
+      qacc[qb][r] = 0.f;
+    }
     Mref[qb] = -INFINITY;
     smax[qb] = -INFINITY;
     Ssum[qb] = 0.f;
@@ -291,8 +304,12 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
   auto raise_ref = [&](int qb, float mt) {
     if (mt > Mref[qb] + kLazyTheta) {
       const float alpha = fast_exp2(Mref[qb] - mt);
-      Ssum[qb] *= alpha;
-      Qsum[qb] *= alpha * alpha;
+      const float alpha2 = alpha * alpha;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        sacc[qb][r] *= alpha;
+        qacc[qb][r] *= alpha2;
+      }
 #pragma unroll
       for (int db = 0; db < 2; ++db)
 #pragma unroll
@@ -300,18 +317,18 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
       Mref[qb] = mt;
     }
   };
-  // p = 2^(x - M): rounded for the P.V product; S and Q accumulate the unrounded values
-  // with plain adds and FMAs, which issue alongside the matrix instructions.
+  // p = 2^(x - M), rounded for the P.V product (and the matrix statistics).
   auto probs = [&](const Scores &S, Probs &P) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const float negM = Mref[qb] == -INFINITY ? 0.f : -Mref[qb];
-      float s0 = 0.f, s1 = 0.f, q0 = 0.f, q1 = 0.f;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         float pv[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) pv[r] = fast_exp2(fmaf(S.v[qb][kb][r], cl2[qb], negM));
+#if !POLAR_PREFILL_MSTATS
+        float s0 = 0.f, s1 = 0.f, q0 = 0.f, q1 = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
           s0 += pv[r];
@@ -319,11 +336,12 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
           q0 = fmaf(pv[r], pv[r], q0);
           q1 = fmaf(pv[r + 1], pv[r + 1], q1);
         }
+        Ssum[qb] += s0 + s1;
+        Qsum[qb] += q0 + q1;
+#endif
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) P.v[qb][kb][tt] = TR::pack(pv + tt * KPL);
       }
-      Ssum[qb] += s0 + s1;
-      Qsum[qb] += q0 + q1;
     }
   };
   // O^T += V^T P^T
@@ -339,80 +357,91 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) o[qb][db] = TR::mma32(va, P.v[qb][kb][tt], o[qb][db]);
         }
+#if POLAR_PREFILL_MSTATS
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          sacc[qb] = TR::mma32(TR::ones(), P.v[qb][kb][tt], sacc[qb]);
+          qacc[qb] = TR::mma32(P.v[qb][kb][tt], P.v[qb][kb][tt], qacc[qb]);
+        }
+#endif
   };
 
   // ---- software-pipelined key loop ----
   // On gfx950 a wave waiting to issue an MFMA also holds back VALU issue of the other wave
-  // on its SIMD, so the matrix and vector work overlap inside each wave's own instruction
-  // stream: the scores of tile t+1 are computed (MFMA) while tile t's probabilities are
-  // formed (VALU), then tile t's P.V product runs beside the maximum of tile t+1.  Tiles
-  // fully below the workgroup's first row need no mask; the diagonal tiles run one at a time.
-  // K and V use three LDS slots: tile t+2 is stored while tiles t and t+1 are read.
+  // on its SIMD, so matrix and vector work overlap inside each wave's own instruction
+  // stream.  Step t issues the scores of tile t+2 (MFMA) beside tile t's probabilities
+  // (VALU), then tile t's P.V product beside the maximum of tile t+1, whose scores were
+  // issued a whole step earlier, so no VALU instruction waits on a recent MFMA result.
+  // Tiles fully below the workgroup's first row need no mask; the diagonal tiles run one
+  // at a time.  K and V use four LDS slots: tile t+3 is stored while tiles t..t+2 are live.
   const int nfull = min((row0 + 1) / kKT, ntiles);
 
-  stage_load(0);
-  stage_store(0, 0);
-  if (ntiles > 1) {
-    stage_load(1);
-    stage_store(1, 1);
+  for (int j = 0; j < 3 && j < ntiles; ++j) {
+    stage_load(j);
+    stage_store(j, j);
   }
   __syncthreads();
 
-  Scores Sa, Sb;
+  Scores Sa, Sb, Sc;
   Probs P;
-  if (nfull > 0) {
-    score(0, Sa);
+  auto first_max = [&](const Scores &Sx) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      const float mx = tile_max(Sa, qb);
+      const float mx = tile_max(Sx, qb);
       smax[qb] = fmaxf(smax[qb], mx);
       raise_ref(qb, mx * cl2[qb]);
     }
+  };
+  if (nfull > 0) {
+    score(0, Sa);
+    first_max(Sa);
   }
+  if (nfull > 1) score(1, Sb);
 
-  auto pipe_step = [&](int t, Scores &Scur, Scores &Snext) {
-    const bool stage = t + 2 < ntiles;
-    stage_load(t + 2);       // unconditional: loads past the sequence return zeros
-    score((t + 1) % 3, Snext);
-    probs(Scur, P);
-    pv_mma(t % 3, P);
+  auto pipe_step = [&](int t, Scores &S0, Scores &S1, Scores &S2) {
+    const bool stage = t + 3 < ntiles;
+    stage_load(t + 3);       // unconditional: loads past the sequence return zeros
+    score((t + 2) % 4, S2);
+    probs(S0, P);
+    pv_mma(t % 4, P);
     const bool next_full = t + 1 < nfull;
     float mxs[QB];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) mxs[qb] = tile_max(Snext, qb);
+    for (int qb = 0; qb < QB; ++qb) mxs[qb] = tile_max(S1, qb);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       smax[qb] = next_full ? fmaxf(smax[qb], mxs[qb]) : smax[qb];
       raise_ref(qb, next_full ? mxs[qb] * cl2[qb] : -INFINITY);
     }
-    if (stage) stage_store((t + 2) % 3, (t + 2) % 3);
+    if (stage) stage_store((t + 3) % 4, (t + 3) % 4);
     __syncthreads();
   };
 
   int t = 0;
   while (t < nfull) {
-    pipe_step(t, Sa, Sb);
+    pipe_step(t, Sa, Sb, Sc);
     if (++t >= nfull) break;
-    pipe_step(t, Sb, Sa);
+    pipe_step(t, Sb, Sc, Sa);
+    if (++t >= nfull) break;
+    pipe_step(t, Sc, Sa, Sb);
     ++t;
   }
   for (; t < ntiles; ++t) {
-    const bool stage = t + 2 < ntiles;
-    if (stage) stage_load(t + 2);
+    const bool stage = t + 3 < ntiles;
+    if (stage) stage_load(t + 3);
     const int key0 = t * kKT;
     if (key0 <= w_last) {
-      score(t % 3, Sa);
+      score(t % 4, Sa);
       mask(Sa, key0);
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const float mx = tile_max(Sa, qb);
-        smax[qb] = fmaxf(smax[qb], mx);
-        raise_ref(qb, mx * cl2[qb]);
-      }
+      first_max(Sa);
       probs(Sa, P);
-      pv_mma(t % 3, P);
+      pv_mma(t % 4, P);
     }
-    if (stage) stage_store((t + 2) % 3, (t + 2) % 3);
+    if (stage) stage_store((t + 3) % 4, (t + 3) % 4);
     __syncthreads();
   }
 
@@ -421,8 +450,20 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int row = wrow0 + qb * 32 + c32;
+    // Every register of sacc holds this lane's row sum.  The diagonal of qacc: row c32 of
+    // column c32 sits in the wave half g = (c32/4)%2, register 4*(c32/8) + c32%4.
+#if POLAR_PREFILL_MSTATS
+    const float St = sacc[qb][0];
+    const int rdiag = 4 * (c32 >> 3) + (c32 & 3);
+    float dq = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq = (r == rdiag) ? qacc[qb][r] : dq;
+    const float dq_other = half_other(dq);
+    const float Qt = (g32 == ((c32 >> 2) & 1)) ? dq : dq_other;
+#else
     const float St = half_sum(Ssum[qb]);
     const float Qt = half_sum(Qsum[qb]);
+#endif
     float nrm = 0.f;
 #pragma unroll
     for (int db = 0; db < 2; ++db)
