@@ -159,17 +159,21 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
   }
 
   // ---- K/V staging: global -> registers -> LDS (V transposed) ----
-  // K: 16-byte chunks, copied as is.  V (bf16): tasks of 2 keys x 8 dims, so each pair of
-  // keys lands in one LDS word of the transposed tile.  V (fp32): 16-byte chunks scattered
-  // element by element.  Three LDS slots per tensor: at tile t the loop reads K of t+1
-  // (pipelined) or t (masked tail) and V of t, and writes tile t+2 into the third slot.
+  // K: 16-byte chunks, copied as is.  V (bf16): tasks of 2 keys x 4 dims (two 8-byte loads)
+  // so every thread of a 512-thread workgroup does one V task and one K chunk per tile, and
+  // each pair of keys lands in one LDS word of the transposed tile.  Keys vary fastest
+  // across lanes, which keeps the transposed writes on distinct banks.  V (fp32): 16-byte
+  // chunks scattered element by element.
   constexpr int KTASKS = kKT * CPR;
-  constexpr int VTASKS = KPL == 8 ? (kKT / 2) * CPR : kKT * CPR;
+  constexpr int VDIMS = KPL == 8 ? 4 : VEC;          // dims per V task
+  constexpr int VKEYS = KPL == 8 ? 2 : 1;            // keys per V task
+  constexpr int VKG = kKT / VKEYS;                   // V tasks per dim group
+  constexpr int VTASKS = VKG * (kD / VDIMS);
   constexpr int NK = (KTASKS + kThreads - 1) / kThreads;
   constexpr int NV = (VTASKS + kThreads - 1) / kThreads;
-  constexpr int VREG = KPL == 8 ? 2 : 1;             // 16-byte registers per V task
-  constexpr int VKG = kKT / VREG;                    // V tasks per 16-byte column of a tile
-  u32x4 kst[NK], vst[NV][VREG];
+  typedef uint32_t vchunk_t __attribute__((ext_vector_type(KPL == 8 ? 2 : 4)));
+  u32x4 kst[NK];
+  vchunk_t vst[NV][VKEYS];
   auto stage_load = [&](int t) {
     const int key0 = t * kKT;
 #pragma unroll
@@ -185,11 +189,15 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
       const int ti = min(tid + kThreads * j, VTASKS - 1);
       const int part = ti / VKG;
 #pragma unroll
-      for (int r = 0; r < VREG; ++r) {
-        const int key = (ti % VKG) * VREG + r;
-        vst[j][r] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                       vrsrc, (int)((size_t)(key0 + key) * kv_row_bytes) + part * 16, 0, 0));
+      for (int r = 0; r < VKEYS; ++r) {
+        const int key = (ti % VKG) * VKEYS + r;
+        const int off = (int)((size_t)(key0 + key) * kv_row_bytes) + part * VDIMS * (int)sizeof(E);
+        if constexpr (KPL == 8)
+          vst[j][r] = __builtin_bit_cast(vchunk_t,
+                                         __builtin_amdgcn_raw_buffer_load_b64(vrsrc, off, 0, 0));
+        else
+          vst[j][r] = __builtin_bit_cast(vchunk_t,
+                                         __builtin_amdgcn_raw_buffer_load_b128(vrsrc, off, 0, 0));
       }
     }
   };
@@ -206,15 +214,15 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
       const int ti = tid + kThreads * j;
       if (NV * kThreads != VTASKS && ti >= VTASKS) continue;
       const int part = ti / VKG;
-      const int key = (ti % VKG) * VREG;
+      const int key = (ti % VKG) * VKEYS;
       const int pos = (key >> 5) * 32 + vpos32<KPL>(key & 31);
       if constexpr (KPL == 8) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < 4; ++e) {
           const uint32_t w0 = vst[j][0][e >> 1], w1 = vst[j][1][e >> 1];
           const uint32_t word = (e & 1) ? ((w0 >> 16) | (w1 & 0xFFFF0000u))
                                         : ((w0 & 0xFFFFu) | (w1 << 16));
-          *(uint32_t *)&Vs[vslot][(part * 8 + e) * VROW + pos] = word;
+          *(uint32_t *)&Vs[vslot][(part * 4 + e) * VROW + pos] = word;
         }
       } else {
 #pragma unroll
@@ -305,11 +313,15 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
     if (mt > Mref[qb] + kLazyTheta) {
       const float alpha = fast_exp2(Mref[qb] - mt);
       const float alpha2 = alpha * alpha;
+      Ssum[qb] *= alpha;
+      Qsum[qb] *= alpha2;
+#if POLAR_PREFILL_MSTATS
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         sacc[qb][r] *= alpha;
         qacc[qb][r] *= alpha2;
       }
+#endif
 #pragma unroll
       for (int db = 0; db < 2; ++db)
 #pragma unroll
