@@ -222,6 +222,19 @@ __global__ void __launch_bounds__(64) polar_decode_split_kernel(DecodeArgs a) {
   }
 }
 
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) x = fmaxf(x, __shfl_xor(x, m));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m);
+  return x;
+}
+
+// One wave per (sequence, query head).  Lanes own splits for the scalar merge; the value
+// merge walks the splits 64 at a time with each split's weight read from a lane register.
 __global__ void __launch_bounds__(256) polar_decode_combine_kernel(DecodeArgs a) {
   const int lane = threadIdx.x & 63;
   const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -229,27 +242,43 @@ __global__ void __launch_bounds__(256) polar_decode_combine_kernel(DecodeArgs a)
   const int b = pair / a.Hq, h = pair % a.Hq;
   const float *e = a.ws + (size_t)pair * a.n_split * kEntry;
   float R = -INFINITY, smax = -INFINITY;
-  for (int s = 0; s < a.n_split; ++s) {
+  for (int s = lane; s < a.n_split; s += 64) {
     R = fmaxf(R, e[s * kEntry + 0]);
     smax = fmaxf(smax, e[s * kEntry + 1]);
   }
+  R = wave_max(R);
+  smax = wave_max(smax);
   float S = 0.f, Q = 0.f, u = 0.f;
-  for (int s = 0; s < a.n_split; ++s) {
-    const float Ms = e[s * kEntry + 0];
-    if (Ms == -INFINITY) continue;
-    const float w = fast_exp2(Ms - R);
-    S = fmaf(e[s * kEntry + 2], w, S);
-    Q = fmaf(e[s * kEntry + 3], w * w, Q);
-    u = fmaf(e[s * kEntry + 4 + lane], w, u);
+  for (int s0 = 0; s0 < a.n_split; s0 += 64) {
+    const int s = s0 + lane;
+    float w = 0.f;
+    if (s < a.n_split) {
+      const float Ms = e[s * kEntry + 0];
+      w = Ms == -INFINITY ? 0.f : fast_exp2(Ms - R);
+      S = fmaf(e[s * kEntry + 2], w, S);
+      Q = fmaf(e[s * kEntry + 3], w * w, Q);
+    }
+    const int cnt = min(64, a.n_split - s0);
+    const float *us = e + (size_t)s0 * kEntry + 4 + lane;
+    int j = 0;
+    for (; j + 4 <= cnt; j += 4) {
+      const float u0 = us[(j + 0) * kEntry], u1 = us[(j + 1) * kEntry];
+      const float u2 = us[(j + 2) * kEntry], u3 = us[(j + 3) * kEntry];
+      u = fmaf(u0, __shfl(w, j + 0), u);
+      u = fmaf(u1, __shfl(w, j + 1), u);
+      u = fmaf(u2, __shfl(w, j + 2), u);
+      u = fmaf(u3, __shfl(w, j + 3), u);
+    }
+    for (; j < cnt; ++j) u = fmaf(us[j * kEntry], __shfl(w, j), u);
   }
+  S = wave_sum(S);
+  Q = wave_sum(Q);
   const int L = min(max(a.seq_lens[b], 1), a.max_seq_len);
   const float beta = a.beta ? a.beta[h] : 8.0f;
   const float tau =
       a.inv_log_train > 0.f ? fmaxf(1.0f, logf((float)L) * a.inv_log_train) : 1.0f;
   const float cnat = beta * tau;
-  float nrm = u * u;
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) nrm += __shfl_xor(nrm, m);
+  const float nrm = wave_sum(u * u);
   const float neff = S * S / Q;
   const float lse = (R + log2f(S)) * kLn2;
   const float m_nat = smax * cnat;
