@@ -33,11 +33,18 @@ PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
 
 
-def src_hash() -> str:
+# Sources each timed kernel is built from; a counter record stays valid while these are unchanged.
+KERNEL_SOURCES = {
+    "prefill": ["polar_prefill.hip", "polar_mfma.h", "polar_kernels.h"],
+    "decode": ["polar_decode.hip", "polar_mfma.h", "polar_kernels.h"],
+}
+
+
+def src_hash(kind: str) -> str:
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "long_context_lm_amd", "csrc", "*"))):
-        with open(f, "rb") as fh:
-            h.update(os.path.basename(f).encode())
+    for name in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, "long_context_lm_amd", "csrc", name), "rb") as fh:
+            h.update(name.encode())
             h.update(fh.read())
     return h.hexdigest()
 
@@ -61,9 +68,9 @@ def traffic_record(kind: str):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_src_sha256") != src_hash() or kind not in rec:
+    r = rec.get(kind)
+    if r is None or r.get("src_sha256") != src_hash(kind):
         return None
-    r = rec[kind]
     return r["fetch_bytes"] * rec["fetch_factor"] + r["write_bytes"] * rec["write_factor"]
 
 
