@@ -6,5 +6,7 @@ may import this package.  The product path (``long_context_lm_amd``) never does.
 from .polar_oracle import (length_temperature, null_floor, polar_prefill, polar_decode_paged,
                            gather_pages, FLAG_LENGTH_TEMP, FLAG_NULL_FLOOR)
 
-__all__ = ["length_temperature", "null_floor", "polar_prefill", "polar_decode_paged",
+from .polar_grad import polar_prefill_grad, arg_max_keys
+
+__all__ = ["polar_prefill_grad", "arg_max_keys", "length_temperature", "null_floor", "polar_prefill", "polar_decode_paged",
            "gather_pages", "FLAG_LENGTH_TEMP", "FLAG_NULL_FLOOR"]

@@ -1,0 +1,144 @@
+"""Float64 reverse-mode oracle of the causal Polar Attention prefill (the backward pass).
+
+TEST INFRASTRUCTURE: imported only by tests/ and bench.py's ``cpu_baseline`` leg.  It
+shares no code with the HIP path.
+
+The forward is written out again with torch CPU tensors in float64 (the definitions of
+the "ATMA: Length-Invariant Language Modeling via Polar Attention and Gated-Delta
+Compression Memory" technical summary, section 2.1, under the readings of the numpy
+oracle in ``polar_oracle``: length temperature, extreme-value floor, sigmoid gate,
+tanh(log n_eff) count).  Gradients come from ``torch.autograd`` on the scalar
+
+    L = sum(c_dir * dir) + sum(c_count * count) + sum(c_n_eff * n_eff)
+        + sum(c_gate * gate) + sum(c_lse * lse)
+
+for caller-given cotangents c_*, with respect to q, k, v and the per-head parameters
+beta, null_bias and count_vec.
+
+The row maximum m = max_j l_j that drives the gate is non-differentiable at ties; the
+reading taken is the usual subgradient that routes d m entirely to the first key (lowest
+position) attaining the maximum.
+
+Pins (tests/test_oracle_grad.py): central finite differences of the independent numpy
+oracle on tiny inputs, torch's own scaled-dot-product-attention backward at tau = 1, and
+closed forms (a single visible key; identical keys, where the direction and n_eff terms
+cancel from dq).
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import numpy as np
+import torch
+
+FLAG_LENGTH_TEMP = 1
+FLAG_NULL_FLOOR = 2
+
+_OUT = ("dir", "count", "n_eff", "gate", "lse")
+
+
+def _rows_forward(Qr, K, V, n_vis, beta_h, bias_h, w_h, train_len: int, flags: int):
+    """Polar outputs of rows Qr [R,d] over keys K[:n_vis[r]], as torch float64 graphs."""
+    R, d = Qr.shape
+    nmax = int(n_vis.max())
+    n = torch.as_tensor(n_vis, dtype=torch.float64)
+    if flags & FLAG_LENGTH_TEMP:
+        tau = torch.clamp(torch.log(n) / math.log(train_len), min=1.0)
+    else:
+        tau = torch.ones_like(n)
+    S = Qr @ K[:nmax].T
+    logits = (beta_h * tau)[:, None] * S
+    visible = torch.arange(nmax)[None, :] < torch.as_tensor(n_vis)[:, None]
+    logits = logits.masked_fill(~visible, float("-inf"))
+    jstar = torch.as_tensor(np.argmax(logits.detach().numpy(), axis=1))   # first maximum
+    m = logits.gather(1, jstar[:, None])[:, 0]
+    e = torch.exp(logits - m[:, None])
+    Z = e.sum(dim=1)
+    p = e / Z[:, None]
+    lse = m + torch.log(Z)
+    n_eff = 1.0 / (p * p).sum(dim=1)
+    u = p @ V[:nmax]
+    norm = torch.sqrt((u * u).sum(dim=1))
+    dir_ = u / norm[:, None]
+    floor = bias_h + torch.zeros_like(n)
+    if flags & FLAG_NULL_FLOOR:
+        floor = floor + (beta_h * tau / math.sqrt(d)) * torch.sqrt(2.0 * torch.log(n))
+    gate = torch.sigmoid(m - floor)
+    count = (gate * torch.tanh(torch.log(n_eff)))[:, None] * w_h[None, :]
+    return dict(dir=dir_, count=count, n_eff=n_eff, gate=gate, lse=lse)
+
+
+def polar_prefill_grad(q, k, v, cot: dict, beta=None, null_bias=None, count_vec=None,
+                       train_len: int = 2048, flags: int = FLAG_LENGTH_TEMP | FLAG_NULL_FLOOR,
+                       max_elems: int = 1 << 21, return_outputs: bool = False) -> dict:
+    """Gradients of the causal prefill with respect to q, k, v, beta, null_bias, count_vec.
+
+    q [B,T,Hq,d], k and v [B,T,Hkv,d]; ``cot`` maps output names ("dir", "count",
+    "n_eff", "gate", "lse") to cotangents of the output shapes (a missing name means
+    zero).  Rows are processed in blocks of about ``max_elems`` scores, each block's
+    graph differentiated on its own; gradients accumulate in the leaves.
+    Returns float64 numpy arrays dq, dk, dv, d_beta [Hq], d_null_bias [Hq],
+    d_count_vec [Hq,d] (and the forward outputs when ``return_outputs``).
+    """
+    q = np.asarray(q)
+    B, T, Hq, d = q.shape
+    Hkv = k.shape[2]
+    G = Hq // Hkv
+    f64 = lambda a: torch.tensor(np.asarray(a, np.float64))
+    qt = f64(q).requires_grad_(True)
+    kt = f64(k).requires_grad_(True)
+    vt = f64(v).requires_grad_(True)
+    bt = f64(np.full(Hq, math.sqrt(d)) if beta is None else beta).requires_grad_(True)
+    nb = f64(np.zeros(Hq) if null_bias is None else null_bias).requires_grad_(True)
+    wt = f64(np.zeros((Hq, d)) if count_vec is None
+             else np.asarray(count_vec).reshape(Hq, d)).requires_grad_(True)
+    cts = {name: f64(cot[name]) for name in _OUT if cot.get(name) is not None}
+    outs = {name: np.zeros((B, T, Hq, d) if name in ("dir", "count") else (B, T, Hq))
+            for name in _OUT} if return_outputs else None
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            r0 = 0
+            while r0 < T:
+                r1 = min(T, r0 + max(1, max_elems // max(1, T)))
+                rows = np.arange(r0, r1)
+                res = _rows_forward(qt[b, r0:r1, h], kt[b, :, g], vt[b, :, g], rows + 1,
+                                    bt[h], nb[h], wt[h], train_len, flags)
+                loss = torch.zeros((), dtype=torch.float64)
+                for name, c in cts.items():
+                    loss = loss + (c[b, r0:r1, h] * res[name]).sum()
+                if loss.requires_grad:
+                    loss.backward()
+                if outs is not None:
+                    for name in _OUT:
+                        outs[name][b, r0:r1, h] = res[name].detach().numpy()
+                r0 = r1
+
+    def grad(t):
+        return np.zeros(tuple(t.shape)) if t.grad is None else t.grad.numpy().copy()
+
+    r = dict(dq=grad(qt), dk=grad(kt), dv=grad(vt), d_beta=grad(bt), d_null_bias=grad(nb),
+             d_count_vec=grad(wt))
+    if outs is not None:
+        r["outputs"] = outs
+    return r
+
+
+def arg_max_keys(q, k, beta=None, train_len: int = 2048,
+                 flags: int = FLAG_LENGTH_TEMP | FLAG_NULL_FLOOR) -> np.ndarray:
+    """First key position attaining each row's maximum logit, [B,T,Hq] int64 (float64)."""
+    q = np.asarray(q, np.float64)
+    B, T, Hq, d = q.shape
+    G = Hq // k.shape[2]
+    beta = np.full(Hq, math.sqrt(d)) if beta is None else np.asarray(beta, np.float64)
+    out = np.zeros((B, T, Hq), np.int64)
+    n = np.arange(1, T + 1, dtype=np.float64)
+    tau = np.maximum(1.0, np.log(n) / math.log(train_len)) if flags & FLAG_LENGTH_TEMP else np.ones(T)
+    for b in range(B):
+        for h in range(Hq):
+            S = q[b, :, h] @ np.asarray(k[b, :, h // G], np.float64).T
+            L = (beta[h] * tau)[:, None] * S
+            L[np.triu_indices(T, 1)] = -np.inf
+            out[b, :, h] = np.argmax(L, axis=1)
+    return out

@@ -292,3 +292,27 @@ def decode_inputs(name: str = "c5", B: Optional[int] = None, L: Optional[int] = 
                         beta=np.full(Hq, BETA_DEFAULT, np.float32),
                         null_bias=np.zeros(Hq, np.float32), count_vec=w, train_len=train_len,
                         flags=flags, needles=needles)
+
+
+# --------------------------------------------------------------------------- gradients
+@dataclasses.dataclass
+class Cotangents:
+    """Upstream gradients of the five prefill outputs (float32, standard normal)."""
+    d_dir: np.ndarray          # [B,T,Hq,d]
+    d_count: np.ndarray        # [B,T,Hq,d]
+    d_n_eff: np.ndarray        # [B,T,Hq]
+    d_gate: np.ndarray         # [B,T,Hq]
+    d_lse: np.ndarray          # [B,T,Hq]
+
+    def as_dict(self) -> dict:
+        return dict(dir=self.d_dir, count=self.d_count, n_eff=self.d_n_eff, gate=self.d_gate,
+                    lse=self.d_lse)
+
+
+def cotangents(B: int, T: int, Hq: int, d: int = 64, seed: int = 2001,
+               n_eff_scale: float = 1.0) -> Cotangents:
+    """Seeded upstream gradients for the backward pass: one child stream per output."""
+    s = np.random.SeedSequence(seed).spawn(5)
+    return Cotangents(d_dir=_normal(s[0], (B, T, Hq, d)), d_count=_normal(s[1], (B, T, Hq, d)),
+                      d_n_eff=(np.float32(n_eff_scale) * _normal(s[2], (B, T, Hq))).astype(np.float32),
+                      d_gate=_normal(s[3], (B, T, Hq)), d_lse=_normal(s[4], (B, T, Hq)))
