@@ -145,6 +145,79 @@ POLAR_API polar_status polar_attn_decode_paged(const polar_params *p, polar_dtyp
                                      void *workspace, size_t workspace_bytes,
                                      const polar_outputs *out, void *stream);
 
+/* ---------------------------------------------------------------------------------
+ * Training: forward with residuals, and the backward pass of the causal prefill.
+ *
+ * The backward differentiates the prefill definitions above with respect to q, k, v and
+ * the per-head parameters beta, null_bias and count_vec, for caller-given upstream
+ * gradients of the five outputs.  max_j l_j (through the gate) is differentiated as the
+ * subgradient that sends its whole gradient to the lowest key position attaining the
+ * maximum (the forward records that key).  The pages train at 2K context; the backward
+ * is what makes the fused kernel of section 2.2 usable for training.
+ * --------------------------------------------------------------------------------- */
+
+/* Per-row residuals of the forward pass that the backward reads, device, [B,T,Hq]. */
+typedef struct {
+  float *u_norm;                    /* |u|, the norm of the softmax-weighted value sum     */
+  int32_t *arg_max;                 /* lowest key position j attaining max_j l_j           */
+} polar_saved;
+
+/* Upstream gradients of the outputs, float32, device, in the polar_outputs layouts
+ * ([B,T,Hq,d] for dir and count, [B,T,Hq] for the rest).  NULL means zero.  dir and
+ * count must be 16-byte aligned; count != NULL needs params.count_vec. */
+typedef struct {
+  const float *dir;
+  const float *count;
+  const float *n_eff;
+  const float *gate;
+  const float *lse;
+} polar_cotangents;
+
+/* Gradients written by polar_attn_bwd, float32, device.  dq [B,T,Hq,d], dk and dv
+ * [B,T,Hkv,d] are required and 16-byte aligned; d_beta [Hq], d_null_bias [Hq] and
+ * d_count_vec [Hq*d] may be NULL (not computed).  All are fully overwritten. */
+typedef struct {
+  float *dq;
+  float *dk;
+  float *dv;
+  float *d_beta;
+  float *d_null_bias;
+  float *d_count_vec;
+} polar_grads;
+
+/*
+ * polar_attn_fwd plus the residuals of the backward pass.  Same arguments, outputs and
+ * results as polar_attn_fwd; additionally out->gate and out->lse are required, and
+ * saved->u_norm and saved->arg_max are written.
+ */
+POLAR_API polar_status polar_attn_fwd_train(const polar_params *p, polar_dtype dt, int32_t B,
+                                  int32_t T, const void *q, const void *k, const void *v,
+                                  const polar_outputs *out, const polar_saved *saved,
+                                  void *stream);
+
+/* Workspace bytes polar_attn_bwd needs (0 on invalid arguments); depends only on the
+ * arguments. */
+POLAR_API size_t polar_bwd_workspace_bytes(const polar_params *p, int32_t B, int32_t T);
+
+/*
+ * Backward pass of the causal prefill.  bf16 inputs only in version 1
+ * (POLAR_ERR_UNSUPPORTED for float32).
+ *   p, dt, B, T, q, k, v  exactly as passed to polar_attn_fwd_train.
+ *   fwd                   its outputs: dir, n_eff, gate and lse are read (count unused).
+ *   saved                 its residuals.
+ *   cot                   upstream gradients (fields may be NULL).
+ *   grads                 outputs (see polar_grads).
+ *   workspace             device scratch of >= polar_bwd_workspace_bytes bytes, 256-byte
+ *                         aligned; contents on entry are ignored.
+ * Results are deterministic: no atomics; every reduction has a fixed order.
+ * B == 0 or T == 0 writes zeros to the requested parameter gradients and nothing else.
+ */
+POLAR_API polar_status polar_attn_bwd(const polar_params *p, polar_dtype dt, int32_t B,
+                            int32_t T, const void *q, const void *k, const void *v,
+                            const polar_outputs *fwd, const polar_saved *saved,
+                            const polar_cotangents *cot, const polar_grads *grads,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
 /* Static description of a status code. */
 POLAR_API const char *polar_status_str(polar_status s);
 /* Thread-local detail of the last non-OK return on this thread ("" if none). */

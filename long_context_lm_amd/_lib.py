@@ -28,6 +28,7 @@ POLAR_FLAG_LENGTH_TEMP = 1
 POLAR_FLAG_NULL_FLOOR = 2
 
 EXPORTS = ("polar_attn_fwd", "polar_decode_workspace_bytes", "polar_attn_decode_paged",
+           "polar_attn_fwd_train", "polar_bwd_workspace_bytes", "polar_attn_bwd",
            "polar_status_str", "polar_last_error", "polar_abi_version")
 
 
@@ -42,6 +43,22 @@ class polar_outputs(ctypes.Structure):
     _fields_ = [("dir", ctypes.c_void_p), ("count", ctypes.c_void_p),
                 ("n_eff", ctypes.c_void_p), ("gate", ctypes.c_void_p),
                 ("lse", ctypes.c_void_p)]
+
+
+class polar_saved(ctypes.Structure):
+    _fields_ = [("u_norm", ctypes.c_void_p), ("arg_max", ctypes.c_void_p)]
+
+
+class polar_cotangents(ctypes.Structure):
+    _fields_ = [("dir", ctypes.c_void_p), ("count", ctypes.c_void_p),
+                ("n_eff", ctypes.c_void_p), ("gate", ctypes.c_void_p),
+                ("lse", ctypes.c_void_p)]
+
+
+class polar_grads(ctypes.Structure):
+    _fields_ = [("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p),
+                ("d_beta", ctypes.c_void_p), ("d_null_bias", ctypes.c_void_p),
+                ("d_count_vec", ctypes.c_void_p)]
 
 
 class PolarError(RuntimeError):
@@ -72,6 +89,15 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.polar_attn_decode_paged.restype = I32
     lib.polar_attn_decode_paged.argtypes = [P(polar_params), I32, I32, VP, VP, VP, I32, I32, VP,
                                             I32, VP, I32, VP, SZ, P(polar_outputs), VP]
+    lib.polar_attn_fwd_train.restype = I32
+    lib.polar_attn_fwd_train.argtypes = [P(polar_params), I32, I32, I32, VP, VP, VP,
+                                         P(polar_outputs), P(polar_saved), VP]
+    lib.polar_bwd_workspace_bytes.restype = SZ
+    lib.polar_bwd_workspace_bytes.argtypes = [P(polar_params), I32, I32]
+    lib.polar_attn_bwd.restype = I32
+    lib.polar_attn_bwd.argtypes = [P(polar_params), I32, I32, I32, VP, VP, VP, P(polar_outputs),
+                                   P(polar_saved), P(polar_cotangents), P(polar_grads), VP, SZ,
+                                   VP]
     lib.polar_status_str.restype = ctypes.c_char_p
     lib.polar_status_str.argtypes = [I32]
     lib.polar_last_error.restype = ctypes.c_char_p
@@ -112,6 +138,22 @@ def polar_attn_decode_paged(params, dtype, B, q, k_cache, v_cache, num_pages, pa
                                           num_pages, page_size, page_table, page_table_stride,
                                           seq_lens, max_seq_len, workspace, workspace_bytes,
                                           ctypes.byref(outputs), stream)
+
+
+def polar_attn_fwd_train(params, dtype, B, T, q, k, v, outputs, saved, stream) -> int:
+    return load().polar_attn_fwd_train(ctypes.byref(params), dtype, B, T, q, k, v,
+                                       ctypes.byref(outputs), ctypes.byref(saved), stream)
+
+
+def polar_bwd_workspace_bytes(params, B, T) -> int:
+    return load().polar_bwd_workspace_bytes(ctypes.byref(params), B, T)
+
+
+def polar_attn_bwd(params, dtype, B, T, q, k, v, fwd, saved, cot, grads, workspace,
+                   workspace_bytes, stream) -> int:
+    return load().polar_attn_bwd(ctypes.byref(params), dtype, B, T, q, k, v, ctypes.byref(fwd),
+                                 ctypes.byref(saved), ctypes.byref(cot), ctypes.byref(grads),
+                                 workspace, workspace_bytes, stream)
 
 
 def check(status: int) -> None:

@@ -64,9 +64,13 @@ float inv_log_train(const polar_params *p) {
 
 extern "C" {
 
-polar_status polar_attn_fwd(const polar_params *p, polar_dtype dt, int32_t B, int32_t T,
-                            const void *q, const void *k, const void *v,
-                            const polar_outputs *out, void *stream) {
+}  // extern "C"
+
+namespace {
+
+polar_status prefill(const polar_params *p, polar_dtype dt, int32_t B, int32_t T, const void *q,
+                     const void *k, const void *v, const polar_outputs *out,
+                     const polar_saved *saved, void *stream) {
   polar_status st = check_params(p, dt, out);
   if (st != POLAR_OK) return st;
   if (B < 0 || T < 0) return fail(POLAR_ERR_BAD_SHAPE, "B (%d) and T (%d) must be >= 0", B, T);
@@ -76,6 +80,12 @@ polar_status polar_attn_fwd(const polar_params *p, polar_dtype dt, int32_t B, in
   if (!q || !k || !v) return fail(POLAR_ERR_NULL_POINTER, "q, k and v must be non-NULL");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v))
     return fail(POLAR_ERR_MISALIGNED, "q, k and v must be 16-byte aligned");
+  if (saved) {
+    if (!saved->u_norm || !saved->arg_max)
+      return fail(POLAR_ERR_NULL_POINTER, "saved.u_norm and saved.arg_max must be non-NULL");
+    if (!out->gate || !out->lse)
+      return fail(POLAR_ERR_NULL_POINTER, "training forward needs outputs.gate and outputs.lse");
+  }
 
   // K/V rows are addressed with 32-bit byte offsets (one tile past the end included).
   const long long elt = dt == POLAR_DTYPE_BF16 ? 2 : 4;
@@ -95,6 +105,8 @@ polar_status polar_attn_fwd(const polar_params *p, polar_dtype dt, int32_t B, in
   a.n_eff = out->n_eff;
   a.gate = out->gate;
   a.lse = out->lse;
+  a.u_norm = saved ? saved->u_norm : nullptr;
+  a.arg_max = saved ? saved->arg_max : nullptr;
   a.B = B;
   a.T = T;
   a.Hq = p->n_q_heads;
@@ -110,6 +122,136 @@ polar_status polar_attn_fwd(const polar_params *p, polar_dtype dt, int32_t B, in
     return fail(POLAR_ERR_BAD_SHAPE, "problem too large for one launch (%lld workgroups)", blocks);
   hipError_t err = polar::launch_prefill((int)dt, a, (hipStream_t)stream);
   if (err != hipSuccess) return fail(POLAR_ERR_HIP, "prefill launch: %s", hipGetErrorString(err));
+  return POLAR_OK;
+}
+
+// Shape limits of the backward: 32-bit byte offsets over q/du rows and K/V rows.
+bool bwd_shape_ok(int32_t B, int32_t T, int32_t Hq, int32_t Hkv) {
+  const long long d2 = polar::kHeadDim * 2;
+  return ((long long)T + 64) * Hq * d2 < 0x7fffffffLL &&
+         ((long long)T + 64) * Hkv * d2 < 0x7fffffffLL &&
+         (long long)B * T * Hq < (1LL << 34);
+}
+
+}  // namespace
+
+extern "C" {
+
+polar_status polar_attn_fwd(const polar_params *p, polar_dtype dt, int32_t B, int32_t T,
+                            const void *q, const void *k, const void *v,
+                            const polar_outputs *out, void *stream) {
+  return prefill(p, dt, B, T, q, k, v, out, nullptr, stream);
+}
+
+polar_status polar_attn_fwd_train(const polar_params *p, polar_dtype dt, int32_t B, int32_t T,
+                                  const void *q, const void *k, const void *v,
+                                  const polar_outputs *out, const polar_saved *saved,
+                                  void *stream) {
+  if (!saved) return fail(POLAR_ERR_NULL_POINTER, "saved is NULL");
+  return prefill(p, dt, B, T, q, k, v, out, saved, stream);
+}
+
+size_t polar_bwd_workspace_bytes(const polar_params *p, int32_t B, int32_t T) {
+  if (!p || B < 1 || T < 1 || p->n_kv_heads < 1 || p->n_q_heads < 1 ||
+      p->n_q_heads % p->n_kv_heads != 0 || !bwd_shape_ok(B, T, p->n_q_heads, p->n_kv_heads))
+    return 0;
+  return polar::bwd_ws_bytes(B, T, p->n_q_heads);
+}
+
+polar_status polar_attn_bwd(const polar_params *p, polar_dtype dt, int32_t B, int32_t T,
+                            const void *q, const void *k, const void *v,
+                            const polar_outputs *fwd, const polar_saved *saved,
+                            const polar_cotangents *cot, const polar_grads *grads,
+                            void *workspace, size_t workspace_bytes, void *stream) {
+  polar_status st = check_params(p, dt, fwd);
+  if (st != POLAR_OK) return st;
+  if (dt != POLAR_DTYPE_BF16)
+    return fail(POLAR_ERR_UNSUPPORTED, "the backward pass takes bf16 inputs only");
+  if (!saved || !cot || !grads)
+    return fail(POLAR_ERR_NULL_POINTER, "saved, cot and grads must be non-NULL");
+  if (B < 0 || T < 0) return fail(POLAR_ERR_BAD_SHAPE, "B (%d) and T (%d) must be >= 0", B, T);
+  if (cot->count && !p->count_vec)
+    return fail(POLAR_ERR_NULL_POINTER, "cot.count given but params.count_vec is NULL");
+  const int Hq = p->n_q_heads;
+  if (B == 0 || T == 0) {
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = hipSuccess;
+    if (grads->d_beta && e == hipSuccess) e = hipMemsetAsync(grads->d_beta, 0, Hq * 4, s);
+    if (grads->d_null_bias && e == hipSuccess)
+      e = hipMemsetAsync(grads->d_null_bias, 0, Hq * 4, s);
+    if (grads->d_count_vec && e == hipSuccess)
+      e = hipMemsetAsync(grads->d_count_vec, 0, (size_t)Hq * p->head_dim * 4, s);
+    if (e != hipSuccess) return fail(POLAR_ERR_HIP, "memset: %s", hipGetErrorString(e));
+    return POLAR_OK;
+  }
+  if (!q || !k || !v) return fail(POLAR_ERR_NULL_POINTER, "q, k and v must be non-NULL");
+  if (!fwd->dir || !fwd->n_eff || !fwd->gate || !fwd->lse)
+    return fail(POLAR_ERR_NULL_POINTER, "fwd.dir, fwd.n_eff, fwd.gate and fwd.lse are required");
+  if (!saved->u_norm || !saved->arg_max)
+    return fail(POLAR_ERR_NULL_POINTER, "saved.u_norm and saved.arg_max must be non-NULL");
+  if (!grads->dq || !grads->dk || !grads->dv)
+    return fail(POLAR_ERR_NULL_POINTER, "grads.dq, grads.dk and grads.dv are required");
+  if (!workspace) return fail(POLAR_ERR_NULL_POINTER, "workspace is NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(fwd->dir) ||
+      !aligned16(grads->dq) || !aligned16(grads->dk) || !aligned16(grads->dv) ||
+      (cot->dir && !aligned16(cot->dir)) || (cot->count && !aligned16(cot->count)) ||
+      (cot->count && !aligned16(p->count_vec)))
+    return fail(POLAR_ERR_MISALIGNED,
+                "q, k, v, fwd.dir, cot.dir, cot.count, count_vec, dq, dk, dv must be 16-byte "
+                "aligned");
+  if (((uintptr_t)workspace & 255u) != 0)
+    return fail(POLAR_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+  if (!bwd_shape_ok(B, T, Hq, p->n_kv_heads))
+    return fail(POLAR_ERR_BAD_SHAPE, "T*Hq too large for the backward (B=%d, T=%d, Hq=%d)", B,
+                T, Hq);
+  const size_t need = polar::bwd_ws_bytes(B, T, Hq);
+  if (workspace_bytes < need)
+    return fail(POLAR_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed",
+                workspace_bytes, need);
+
+  polar::BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.beta = p->beta;
+  a.null_bias = p->null_bias;
+  a.count_vec = p->count_vec;
+  a.dir = fwd->dir;
+  a.n_eff = fwd->n_eff;
+  a.gate = fwd->gate;
+  a.lse = fwd->lse;
+  a.u_norm = saved->u_norm;
+  a.arg_max = saved->arg_max;
+  a.c_dir = cot->dir;
+  a.c_count = cot->count;
+  a.c_n_eff = cot->n_eff;
+  a.c_gate = cot->gate;
+  a.c_lse = cot->lse;
+  a.dq = grads->dq;
+  a.dk = grads->dk;
+  a.dv = grads->dv;
+  a.d_beta = grads->d_beta;
+  a.d_null_bias = grads->d_null_bias;
+  a.d_count_vec = grads->d_count_vec;
+  a.B = B;
+  a.T = T;
+  a.Hq = Hq;
+  a.Hkv = p->n_kv_heads;
+  a.G = a.Hq / a.Hkv;
+  a.hb = polar::prefill_heads_per_block(a.G);
+  const int rows = polar::bwd_rows_per_block(a.hb);
+  a.n_row_blocks = (T + rows - 1) / rows;
+  const int keys = polar::bwd_keys_per_block();
+  a.n_key_blocks = (T + keys - 1) / keys;
+  a.inv_log_train = inv_log_train(p);
+  a.null_floor = (p->flags & POLAR_FLAG_NULL_FLOOR) ? 1 : 0;
+  polar::bwd_ws_layout(a, workspace);
+  const long long dq_blocks = (long long)a.n_row_blocks * a.Hkv * (a.G / a.hb) * B;
+  const long long dkv_blocks = (long long)a.n_key_blocks * a.Hkv * B;
+  if (dq_blocks > 0x7fffffffLL || dkv_blocks > 0x7fffffffLL)
+    return fail(POLAR_ERR_BAD_SHAPE, "problem too large for one launch");
+  hipError_t err = polar::launch_bwd(a, (hipStream_t)stream);
+  if (err != hipSuccess) return fail(POLAR_ERR_HIP, "backward launch: %s", hipGetErrorString(err));
   return POLAR_OK;
 }
 

@@ -1,0 +1,633 @@
+// Backward pass of the causal Polar Attention prefill for gfx950 (bf16 inputs, fp32
+// gradients).
+//
+// The forward is section 2.1 of the ATMA technical summary (gist.science), "Polar
+// Attention: A Three-Channel Decomposition", as fused in section 2.2.  Differentiating it
+// row by row (row i of head h, c = beta_h * tau(i+1), l_j = c <q_i, k_j>, p = softmax(l)):
+//   du    = (I - dir dir^T) d_dir / |u|                      (dir = u/|u|)
+//   th    = tanh(ln n_eff) = (n^2-1)/(n^2+1);  gc = d_count . w_h
+//   dgate = d_gate + gc th;  dn = d_n_eff + gc gate 4n/(n^2+1)^2
+//   dm    = dgate gate (1-gate)                              (gate = sigmoid(m - floor))
+//   A     = d_lse + 2 n dn;   E = -2 n^2 dn                  (n_eff = 1/sum p^2)
+//   dl_j  = p_j (v_j . du + A + E p_j) + [j = j*] dm         (j* = first arg-max key)
+//   dq_i  = c sum_j dl_j k_j;  dk_j = sum_i c dl_ij q_i;  dv_j = sum_i p_ij du_i
+//   dbeta = sum_i [tau (q_i . sum_j dl_ij k_j) - dm (tau/sqrt(d)) sqrt(2 ln n)],
+//   dnull_bias = -sum_i dm,   dcount_vec = sum_i d_count_i gate th.
+// (u . du = 0, so the value term needs no row constant.)  p is recomputed from the saved
+// log-sum-exp, so no T x T quantity is stored.
+//
+// Kernels, in launch order:
+//  1. prep:  one 16-lane group per row: du (bf16), c*du (bf16) and the row scalars.
+//  2. dq:    one wave per 32 rows of a head (lane = query, as in the forward): per 64-key
+//            tile S^T = K Q^T and dP^T = V du^T on MFMA, dl on the VALU, then
+//            dq^T += K^T dl^T with K^T from a transposed LDS tile.
+//  3. dk/dv: one wave per 32 keys (lane = key), keys and values resident in registers;
+//            the workgroup walks every query tile of the G heads sharing the KV head that
+//            can see its keys.  S' = Q K^T and c dP' = (c du) V^T on MFMA, then
+//            dv^T += du^T P and dk^T += Q^T dS with du^T and Q^T from transposed tiles.
+//            Each key has one owner, so dk and dv need no atomics.
+//  4. parameter gradients: fixed-order two-level reductions over rows.
+#include "polar_kernels.h"
+#include "polar_mfma.h"
+
+namespace polar {
+namespace {
+
+constexpr int kD = kHeadDim;
+constexpr int kBufferFlags = 0x00020000;   // gfx9 buffer resource word 3 (raw dword access)
+constexpr int kDqWaves = 8;
+constexpr int kDkvWaves = 4;
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+using F = bf16x8;
+
+__device__ __forceinline__ float tau_of(int row, float inv_log_train) {
+  return inv_log_train > 0.f ? fmaxf(1.0f, logf((float)(row + 1)) * inv_log_train) : 1.0f;
+}
+
+__device__ __forceinline__ const uint16_t *lds_at(const uint16_t *base, uint32_t off) {
+  asm volatile("" : "+v"(off));
+  return reinterpret_cast<const uint16_t *>(reinterpret_cast<const char *>(base) + off);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Interleave two rows' 4 bf16 values (two dwords each) into 4 dwords: dword e holds
+// element e of the first row in its low half and of the second row in its high half.
+__device__ __forceinline__ uint32_t pair_word(u32x2 w0, u32x2 w1, int e) {
+  return (e & 1) ? ((w0[e >> 1] >> 16) | (w1[e >> 1] & 0xFFFF0000u))
+                 : ((w0[e >> 1] & 0xFFFFu) | (w1[e >> 1] << 16));
+}
+
+// ------------------------------------------------------------------ 1. per-row prep
+__global__ void __launch_bounds__(256) polar_bwd_prep_kernel(BwdArgs a) {
+  const int tid = threadIdx.x, l16 = tid & 15;
+  const long long nrows = (long long)a.B * a.T * a.Hq;
+  const long long R = (long long)blockIdx.x * 16 + (tid >> 4);
+  const bool ok = R < nrows;
+  const long long Rc = ok ? R : nrows - 1;
+  const int h = (int)(Rc % a.Hq);
+  const int i = (int)((Rc / a.Hq) % a.T);
+  const size_t e0 = (size_t)Rc * kD + 4 * l16;
+  const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+  const f32x4 dir = *(const f32x4 *)(a.dir + e0);
+  const f32x4 cd = a.c_dir ? *(const f32x4 *)(a.c_dir + e0) : z4;
+  const f32x4 cc = a.c_count ? *(const f32x4 *)(a.c_count + e0) : z4;
+  const f32x4 w = a.c_count ? *(const f32x4 *)(a.count_vec + (size_t)h * kD + 4 * l16) : z4;
+  float dd = 0.f, gc = 0.f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    dd = fmaf(dir[c], cd[c], dd);
+    gc = fmaf(cc[c], w[c], gc);
+  }
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) {
+    dd += __shfl_xor(dd, m);
+    gc += __shfl_xor(gc, m);
+  }
+  const float U = a.u_norm[Rc], n = a.n_eff[Rc], gate = a.gate[Rc], lse = a.lse[Rc];
+  const float inv = U > 0.f ? 1.0f / U : 0.f;
+  const float n2 = n * n;
+  const float th = (n2 - 1.f) / (n2 + 1.f);
+  const float dth_dn = 4.f * n / ((n2 + 1.f) * (n2 + 1.f));
+  const float dgate = (a.c_gate ? a.c_gate[Rc] : 0.f) + gc * th;
+  const float dn = (a.c_n_eff ? a.c_n_eff[Rc] : 0.f) + gc * gate * dth_dn;
+  const float dm = dgate * gate * (1.f - gate);
+  const float A = (a.c_lse ? a.c_lse[Rc] : 0.f) + 2.f * n * dn;
+  const float E = -2.f * n2 * dn;
+  const float beta = a.beta ? a.beta[h] : 8.0f;
+  const float tau = tau_of(i, a.inv_log_train);
+  const float c = beta * tau;
+  if (!ok) return;
+  bf16x4 o1, o2;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float du = (cd[k] - dir[k] * dd) * inv;
+    o1[k] = (__bf16)du;
+    o2[k] = (__bf16)(c * du);
+  }
+  *(bf16x4 *)(a.du + e0) = o1;
+  *(bf16x4 *)(a.cdu + e0) = o2;
+  if (l16 == 0) {
+    const f32x4 r0 = {c * kLog2e, lse * kLog2e, c * A, c * E};
+    const f32x4 r1 = {A, E, dm, __int_as_float(a.arg_max[Rc])};
+    const float fl =
+        a.null_floor ? -dm * tau * 0.125f * sqrtf(2.f * logf((float)(i + 1))) : 0.f;
+    const f32x4 rp = {0.f, -dm, gate * th, fl};
+    *(f32x4 *)(a.r0 + 4 * Rc) = r0;
+    *(f32x4 *)(a.r1 + 4 * Rc) = r1;
+    *(f32x4 *)(a.rp + 4 * Rc) = rp;
+  }
+}
+
+// ------------------------------------------------------------------ 2. dq
+template <int kWaves>
+__global__ void __launch_bounds__(64 * kWaves) polar_bwd_dq_kernel(BwdArgs a) {
+  constexpr int kThreads = 64 * kWaves;
+  constexpr int KT = 64, KROW = 72, TROW = 72;
+  constexpr int NTASK = 512;                        // 16-byte chunks (or pair tasks) per tile
+  constexpr int NPER = (NTASK + kThreads - 1) / kThreads;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KT * KROW];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][KT * KROW];
+  __shared__ __attribute__((aligned(16))) uint16_t Kt[2][kD * TROW];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g32 = lane >> 5, c32 = lane & 31;
+  const int n_hc = a.G / a.hb;
+  const int NY = a.Hkv * n_hc;
+  int id = blockIdx.x;
+  const int b = id % a.B;
+  id /= a.B;
+  const int y = id % NY;
+  const int rb = a.n_row_blocks - 1 - id / NY;
+  const int g = y / n_hc, hc = y % n_hc;
+  const int h = g * a.G + hc * a.hb + (wave % a.hb);
+  const int WR = (kWaves / a.hb) * 32;
+  const int row0 = rb * WR;
+  const int wrow0 = row0 + (wave / a.hb) * 32;
+  const int wg_last = min(row0 + WR, a.T) - 1;
+  const int w_last = wrow0 < a.T ? min(wrow0 + 32, a.T) - 1 : -1;
+  const int ntiles = wg_last / KT + 1;
+  const int row = wrow0 + c32;
+  const bool valid = row < a.T;
+
+  const size_t row_bytes = (size_t)a.Hkv * kD * 2;
+  const size_t kv_base = ((size_t)b * a.T * a.Hkv + g) * kD;
+  const int kv_bytes = (int)(((size_t)a.T * a.Hkv - g) * kD * 2);
+  const auto krsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)((const uint16_t *)a.k + kv_base), 0, kv_bytes, kBufferFlags);
+  const auto vrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)((const uint16_t *)a.v + kv_base), 0, kv_bytes, kBufferFlags);
+
+  // Row scalars; rows past T get p = 0 (lse2 = +inf) and zero coefficients.
+  const size_t rr = ((size_t)b * a.T + (valid ? row : 0)) * a.Hq + h;
+  float cl2 = 1.f, lse2 = INFINITY, A = 0.f, E = 0.f, dm = 0.f;
+  int js = 0;
+  if (valid) {
+    const f32x4 r0 = *(const f32x4 *)(a.r0 + 4 * rr);
+    const f32x4 r1 = *(const f32x4 *)(a.r1 + 4 * rr);
+    cl2 = r0[0];
+    lse2 = r0[1];
+    A = r1[0];
+    E = r1[1];
+    dm = r1[2];
+    js = min(max(__float_as_int(r1[3]), 0), a.T - 1);   // memory-safe on a corrupt table
+  }
+  // Q and du fragments: B operands of S^T = K Q^T and dP^T = V du^T.
+  F qf[4], df[4];
+  {
+    const uint16_t *qp = (const uint16_t *)a.q + rr * kD + g32 * 8;
+    const uint16_t *dp = a.du + rr * kD + g32 * 8;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      qf[ks] = valid ? *(const F *)(qp + ks * 16) : Bf16::zero();
+      df[ks] = valid ? *(const F *)(dp + ks * 16) : Bf16::zero();
+    }
+  }
+  f32x16 o[2];
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+
+  // Staging: K and V rows as 16-byte chunks; K^T from 2-key x 4-dim tasks whose pairs of
+  // keys land in one LDS word of the transposed tile.
+  u32x4 kst[NPER], vst[NPER];
+  u32x2 tst[NPER][2];
+  auto stage_load = [&](int t) {
+    const int key0 = t * KT;
+#pragma unroll
+    for (int j = 0; j < NPER; ++j) {
+      const int ch = min(tid + kThreads * j, NTASK - 1);
+      const int key = ch >> 3, part = ch & 7;
+      const int off = (int)((size_t)(key0 + key) * row_bytes) + part * 16;
+      kst[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krsrc, off, 0, 0));
+      vst[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrsrc, off, 0, 0));
+      const int kp = ch & 31, dg = ch >> 5;
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+        tst[j][r] = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                       krsrc, (int)((size_t)(key0 + 2 * kp + r) * row_bytes) + dg * 8, 0, 0));
+    }
+  };
+  auto stage_store = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < NPER; ++j) {
+      const int ch = tid + kThreads * j;
+      if (NPER * kThreads != NTASK && ch >= NTASK) continue;
+      const int key = ch >> 3, part = ch & 7;
+      *(u32x4 *)&Ks[buf][key * KROW + part * 8] = kst[j];
+      *(u32x4 *)&Vs[buf][key * KROW + part * 8] = vst[j];
+      const int kp = ch & 31, dg = ch >> 5;
+      const int pos = ((2 * kp) >> 5) * 32 + vpos32<8>((2 * kp) & 31);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        *(uint32_t *)&Kt[buf][(dg * 4 + e) * TROW + pos] = pair_word(tst[j][0], tst[j][1], e);
+    }
+  };
+
+  const uint32_t k_lane = (uint32_t)((c32 * KROW + g32 * 8) * 2);
+  const uint32_t t_lane = (uint32_t)((c32 * TROW + g32 * 8) * 2);
+  constexpr uint32_t KBUF = KT * KROW * 2, TBUF = kD * TROW * 2;
+
+  stage_load(0);
+  stage_store(0);
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    const bool more = t + 1 < ntiles;
+    if (more) stage_load(t + 1);
+    const int key0 = t * KT;
+    if (key0 <= w_last) {
+      const uint16_t *Kb = lds_at(&Ks[0][0], k_lane + buf * KBUF);
+      const uint16_t *Vb = lds_at(&Vs[0][0], k_lane + buf * KBUF);
+      const f32x16 zero = {};
+      f32x16 S[2], P[2];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const F ka = *(const F *)(Kb + kb * 32 * KROW + ks * 16);
+          S[kb] = Bf16::mma32(ka, qf[ks], ks == 0 ? zero : S[kb]);
+          const F va = *(const F *)(Vb + kb * 32 * KROW + ks * 16);
+          P[kb] = Bf16::mma32(va, df[ks], ks == 0 ? zero : P[kb]);
+        }
+      const bool diag = key0 + KT - 1 > wrow0;
+      F dl[2][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float s = S[kb][r];
+          if (diag) {
+            const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * g32 + (r & 3);
+            if (key > row) s = -INFINITY;
+          }
+          const float p = fast_exp2(fmaf(s, cl2, -lse2));
+          x[r] = p * (P[kb][r] + fmaf(E, p, A));
+        }
+        dl[kb][0] = Bf16::pack(x);
+        dl[kb][1] = Bf16::pack(x + 8);
+      }
+      const uint16_t *Tb = lds_at(&Kt[0][0], t_lane + buf * TBUF);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int db = 0; db < 2; ++db) {
+            const F ta = *(const F *)(Tb + db * 32 * TROW + kb * 32 + tt * 16);
+            o[db] = Bf16::mma32(ta, dl[kb][tt], o[db]);
+          }
+    }
+    if (more) stage_store(buf ^ 1);
+    __syncthreads();
+  }
+
+  // Epilogue: the arg-max key's share of dl, the dbeta row term, dq = c * sum dl k.
+  if (valid && dm != 0.f) {
+    const uint16_t *kr = (const uint16_t *)a.k + (((size_t)b * a.T + js) * a.Hkv + g) * kD;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4) {
+        const u32x2 w = *(const u32x2 *)(kr + db * 32 + 8 * j4 + 4 * g32);
+        o[db][4 * j4 + 0] = fmaf(dm, bf16_lo(w[0]), o[db][4 * j4 + 0]);
+        o[db][4 * j4 + 1] = fmaf(dm, bf16_hi(w[0]), o[db][4 * j4 + 1]);
+        o[db][4 * j4 + 2] = fmaf(dm, bf16_lo(w[1]), o[db][4 * j4 + 2]);
+        o[db][4 * j4 + 3] = fmaf(dm, bf16_hi(w[1]), o[db][4 * j4 + 3]);
+      }
+  }
+  const float tau = tau_of(valid ? row : 0, a.inv_log_train);
+  if (a.d_beta) {
+    float qd = 0.f;
+    if (valid) {
+      const uint16_t *qr = (const uint16_t *)a.q + rr * kD;
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int j4 = 0; j4 < 4; ++j4) {
+          const u32x2 w = *(const u32x2 *)(qr + db * 32 + 8 * j4 + 4 * g32);
+          qd = fmaf(bf16_lo(w[0]), o[db][4 * j4 + 0], qd);
+          qd = fmaf(bf16_hi(w[0]), o[db][4 * j4 + 1], qd);
+          qd = fmaf(bf16_lo(w[1]), o[db][4 * j4 + 2], qd);
+          qd = fmaf(bf16_hi(w[1]), o[db][4 * j4 + 3], qd);
+        }
+    }
+    qd = half_sum(qd);
+    if (valid && g32 == 0) a.rp[4 * rr] = tau * qd;
+  }
+  if (valid) {
+    const float c = (a.beta ? a.beta[h] : 8.0f) * tau;
+    float *dqp = a.dq + rr * kD;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4) {
+        f32x4 val;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) val[e] = o[db][4 * j4 + e] * c;
+        *(f32x4 *)(dqp + db * 32 + 8 * j4 + 4 * g32) = val;
+      }
+  }
+}
+
+// ------------------------------------------------------------------ 3. dk / dv
+template <int kWaves>
+__global__ void __launch_bounds__(64 * kWaves) polar_bwd_dkv_kernel(BwdArgs a) {
+  constexpr int kThreads = 64 * kWaves;
+  static_assert(kThreads == 256, "one staging task per thread");
+  constexpr int KB = 32 * kWaves;                   // keys per workgroup
+  constexpr int QROW = 72, TROW = 40;
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[2][32 * QROW];   // q rows
+  __shared__ __attribute__((aligned(16))) uint16_t Cs[2][32 * QROW];   // c*du rows
+  __shared__ __attribute__((aligned(16))) uint16_t Qt[2][kD * TROW];   // q^T
+  __shared__ __attribute__((aligned(16))) uint16_t Dt[2][kD * TROW];   // du^T
+  // Row scalars: cl2, lse2, c*A, c*E, dm, arg-max key (bits).
+  __shared__ __attribute__((aligned(16))) float Sc[2][6][32];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g32 = lane >> 5, c32 = lane & 31;
+  int id = blockIdx.x;
+  const int b = id % a.B;
+  id /= a.B;
+  const int g = id % a.Hkv;
+  const int kblk = a.n_key_blocks - 1 - id / a.Hkv;   // heaviest (lowest keys) first
+  const int k0 = kblk * KB;
+  const int kw0 = k0 + wave * 32;
+  const int key = kw0 + c32;
+  const bool kvalid = key < a.T;
+
+  F kf[4], vf[4];
+  {
+    const size_t kb = (((size_t)b * a.T + (kvalid ? key : 0)) * a.Hkv + g) * kD + g32 * 8;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      kf[ks] = kvalid ? *(const F *)((const uint16_t *)a.k + kb + ks * 16) : Bf16::zero();
+      vf[ks] = kvalid ? *(const F *)((const uint16_t *)a.v + kb + ks * 16) : Bf16::zero();
+    }
+  }
+  f32x16 dK[2], dV[2];
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dK[db][r] = 0.f;
+      dV[db][r] = 0.f;
+    }
+
+  const int rt0 = k0 / 32;
+  const int nrt = (a.T + 31) / 32;
+  const int nsteps = (nrt - rt0) * a.G;
+  const int rs = a.Hq * kD * 2;                     // bytes between rows of q / du
+
+  u32x4 qst, cst;
+  u32x2 qtst[2], dtst[2];
+  f32x4 sst;
+  auto stage_load = [&](int s) {
+    const int r0row = (rt0 + s / a.G) * 32;
+    const int h = g * a.G + s % a.G;
+    const size_t base = ((size_t)b * a.T * a.Hq + h) * kD;
+    const int nbytes = (int)(((size_t)a.T * a.Hq - h) * kD * 2);
+    const auto qr = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)((const uint16_t *)a.q + base), 0, nbytes, kBufferFlags);
+    const auto dr = __builtin_amdgcn_make_buffer_rsrc((void *)(a.du + base), 0, nbytes,
+                                                      kBufferFlags);
+    const auto cr = __builtin_amdgcn_make_buffer_rsrc((void *)(a.cdu + base), 0, nbytes,
+                                                      kBufferFlags);
+    const int rw = tid >> 3, part = tid & 7;
+    const int off = (r0row + rw) * rs + part * 16;
+    qst = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(qr, off, 0, 0));
+    cst = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(cr, off, 0, 0));
+    const int rp = tid & 15, dg = tid >> 4;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int o2 = (r0row + 2 * rp + r) * rs + dg * 8;
+      qtst[r] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(qr, o2, 0, 0));
+      dtst[r] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(dr, o2, 0, 0));
+    }
+    if (tid < 64) {
+      const int ri = tid & 31;
+      const int row = r0row + ri;
+      const size_t rr = ((size_t)b * a.T + min(row, a.T - 1)) * a.Hq + h;
+      if (tid < 32) {
+        const f32x4 pad = {1.f, INFINITY, 0.f, 0.f};
+        sst = row < a.T ? *(const f32x4 *)(a.r0 + 4 * rr) : pad;
+      } else {
+        const f32x4 pad = {0.f, 0.f, 0.f, __int_as_float(-1)};
+        sst = row < a.T ? *(const f32x4 *)(a.r1 + 4 * rr) : pad;
+      }
+    }
+  };
+  auto stage_store = [&](int buf) {
+    const int rw = tid >> 3, part = tid & 7;
+    *(u32x4 *)&Qs[buf][rw * QROW + part * 8] = qst;
+    *(u32x4 *)&Cs[buf][rw * QROW + part * 8] = cst;
+    const int rp = tid & 15, dg = tid >> 4;
+    const int pos = vpos32<8>(2 * rp);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      *(uint32_t *)&Qt[buf][(dg * 4 + e) * TROW + pos] = pair_word(qtst[0], qtst[1], e);
+      *(uint32_t *)&Dt[buf][(dg * 4 + e) * TROW + pos] = pair_word(dtst[0], dtst[1], e);
+    }
+    if (tid < 32) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) Sc[buf][q][tid] = sst[q];
+    } else if (tid < 64) {
+      Sc[buf][4][tid - 32] = sst[2];
+      Sc[buf][5][tid - 32] = sst[3];
+    }
+  };
+
+  const uint32_t q_lane = (uint32_t)((c32 * QROW + g32 * 8) * 2);
+  const uint32_t t_lane = (uint32_t)((c32 * TROW + g32 * 8) * 2);
+  constexpr uint32_t QBUF = 32 * QROW * 2, TBUF = kD * TROW * 2;
+
+  if (nsteps > 0) {
+    stage_load(0);
+    stage_store(0);
+  }
+  __syncthreads();
+  for (int s = 0; s < nsteps; ++s) {
+    const int buf = s & 1;
+    const bool more = s + 1 < nsteps;
+    if (more) stage_load(s + 1);
+    const int r0row = (rt0 + s / a.G) * 32;
+    if (r0row + 31 >= kw0 && kw0 < a.T) {
+      const uint16_t *Qb = lds_at(&Qs[0][0], q_lane + buf * QBUF);
+      const uint16_t *Cb = lds_at(&Cs[0][0], q_lane + buf * QBUF);
+      const f32x16 zero = {};
+      f32x16 S, P;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        S = Bf16::mma32(*(const F *)(Qb + ks * 16), kf[ks], ks == 0 ? zero : S);
+        P = Bf16::mma32(*(const F *)(Cb + ks * 16), vf[ks], ks == 0 ? zero : P);
+      }
+      const bool diag = r0row < kw0 + 31;
+      float pv[16], dsv[16];
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const int ri0 = 8 * a4 + 4 * g32;
+        const f32x4 cl = *(const f32x4 *)&Sc[buf][0][ri0];
+        const f32x4 ls = *(const f32x4 *)&Sc[buf][1][ri0];
+        const f32x4 ac = *(const f32x4 *)&Sc[buf][2][ri0];
+        const f32x4 ec = *(const f32x4 *)&Sc[buf][3][ri0];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int r = 4 * a4 + c;
+          float p = fast_exp2(fmaf(S[r], cl[c], -ls[c]));
+          if (diag && r0row + ri0 + c < key) p = 0.f;
+          pv[r] = p;
+          dsv[r] = p * (P[r] + fmaf(ec[c], p, ac[c]));
+        }
+      }
+      // Rows whose arg-max key belongs to this wave (rare): add c*dm at that key.
+      const int jl = __float_as_int(Sc[buf][5][c32]);
+      if (__ballot(jl >= kw0 && jl < kw0 + 32) != 0) {
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const int ri0 = 8 * a4 + 4 * g32;
+          const f32x4 jv = *(const f32x4 *)&Sc[buf][5][ri0];
+          const f32x4 dmv = *(const f32x4 *)&Sc[buf][4][ri0];
+          const f32x4 cl = *(const f32x4 *)&Sc[buf][0][ri0];
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            if (__float_as_int(jv[c]) == key) dsv[4 * a4 + c] += dmv[c] * cl[c] * kLn2;
+        }
+      }
+      const F pp0 = Bf16::pack(pv), pp1 = Bf16::pack(pv + 8);
+      const F dp0 = Bf16::pack(dsv), dp1 = Bf16::pack(dsv + 8);
+      const uint16_t *Db = lds_at(&Dt[0][0], t_lane + buf * TBUF);
+      const uint16_t *Tb = lds_at(&Qt[0][0], t_lane + buf * TBUF);
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        dV[db] = Bf16::mma32(*(const F *)(Db + db * 32 * TROW), pp0, dV[db]);
+        dK[db] = Bf16::mma32(*(const F *)(Tb + db * 32 * TROW), dp0, dK[db]);
+        dV[db] = Bf16::mma32(*(const F *)(Db + db * 32 * TROW + 16), pp1, dV[db]);
+        dK[db] = Bf16::mma32(*(const F *)(Tb + db * 32 * TROW + 16), dp1, dK[db]);
+      }
+    }
+    if (more) stage_store(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (kvalid) {
+    const size_t ob = (((size_t)b * a.T + key) * a.Hkv + g) * kD;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4) {
+        const int d0 = db * 32 + 8 * j4 + 4 * g32;
+        f32x4 kv, vv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          kv[e] = dK[db][4 * j4 + e];
+          vv[e] = dV[db][4 * j4 + e];
+        }
+        *(f32x4 *)(a.dk + ob + d0) = kv;
+        *(f32x4 *)(a.dv + ob + d0) = vv;
+      }
+  }
+}
+
+// ------------------------------------------------------------------ 4. parameter grads
+// Stage 1: workgroup (chunk p, head h) sums its rows in a fixed order.
+__global__ void __launch_bounds__(256) polar_bwd_param_kernel(BwdArgs a) {
+  const int p = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int dim = tid & 63, sub = tid >> 6;
+  const long long nr = (long long)a.B * a.T;
+  const long long chunk = (nr + a.n_part - 1) / a.n_part;
+  const long long lo = (long long)p * chunk;
+  const long long hi = min(nr, lo + chunk);
+  float dw = 0.f, dbeta = 0.f, dbias = 0.f;
+  for (long long rho = lo + sub; rho < hi; rho += 4) {
+    const size_t rr = (size_t)rho * a.Hq + h;
+    const f32x4 rp = *(const f32x4 *)(a.rp + 4 * rr);
+    if (a.c_count) dw = fmaf(rp[2], a.c_count[rr * kD + dim], dw);
+    dbeta += rp[0] + rp[3];
+    dbias += rp[1];
+  }
+  __shared__ float red[4][66];
+  red[sub][dim] = dw;
+  if (dim == 0) {
+    red[sub][64] = dbeta;
+    red[sub][65] = dbias;
+  }
+  __syncthreads();
+  if (tid < 66)
+    a.part[((size_t)h * a.n_part + p) * kPartStride + tid] =
+        (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
+}
+
+// Stage 2: one workgroup per head adds the chunks in order.
+__global__ void __launch_bounds__(128) polar_bwd_param_final_kernel(BwdArgs a) {
+  const int h = blockIdx.x, tid = threadIdx.x;
+  if (tid >= 66) return;
+  float s = 0.f;
+  for (int p = 0; p < a.n_part; ++p) s += a.part[((size_t)h * a.n_part + p) * kPartStride + tid];
+  if (tid < 64) {
+    if (a.d_count_vec) a.d_count_vec[(size_t)h * kD + tid] = s;
+  } else if (tid == 64) {
+    if (a.d_beta) a.d_beta[h] = s;
+  } else {
+    if (a.d_null_bias) a.d_null_bias[h] = s;
+  }
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int n_parts(int B, int T) {
+  const long long nr = (long long)B * T;
+  return (int)max(1LL, min(256LL, (nr + 255) / 256));
+}
+
+}  // namespace
+
+size_t bwd_ws_bytes(int B, int T, int Hq) {
+  const size_t nrows = (size_t)B * T * Hq;
+  return 2 * align256(nrows * kD * 2) + 3 * align256(nrows * 16) +
+         align256((size_t)Hq * n_parts(B, T) * kPartStride * 4);
+}
+
+void bwd_ws_layout(BwdArgs &a, void *ws) {
+  const size_t nrows = (size_t)a.B * a.T * a.Hq;
+  char *p = (char *)ws;
+  a.du = (uint16_t *)p;
+  p += align256(nrows * kD * 2);
+  a.cdu = (uint16_t *)p;
+  p += align256(nrows * kD * 2);
+  a.r0 = (float *)p;
+  p += align256(nrows * 16);
+  a.r1 = (float *)p;
+  p += align256(nrows * 16);
+  a.rp = (float *)p;
+  p += align256(nrows * 16);
+  a.part = (float *)p;
+  a.n_part = n_parts(a.B, a.T);
+}
+
+int bwd_rows_per_block(int hb) { return (kDqWaves / hb) * 32; }
+int bwd_keys_per_block() { return 32 * kDkvWaves; }
+
+hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream) {
+  const long long nrows = (long long)a.B * a.T * a.Hq;
+  if (nrows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(polar_bwd_prep_kernel, dim3((unsigned)((nrows + 15) / 16)), dim3(256), 0,
+                     stream, a);
+  const long long dq_blocks = (long long)a.n_row_blocks * a.Hkv * (a.G / a.hb) * a.B;
+  hipLaunchKernelGGL((polar_bwd_dq_kernel<kDqWaves>), dim3((unsigned)dq_blocks),
+                     dim3(64 * kDqWaves), 0, stream, a);
+  const long long dkv_blocks = (long long)a.n_key_blocks * a.Hkv * a.B;
+  hipLaunchKernelGGL((polar_bwd_dkv_kernel<kDkvWaves>), dim3((unsigned)dkv_blocks),
+                     dim3(64 * kDkvWaves), 0, stream, a);
+  if (a.d_beta || a.d_null_bias || a.d_count_vec) {
+    hipLaunchKernelGGL(polar_bwd_param_kernel, dim3(a.n_part, a.Hq), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(polar_bwd_param_final_kernel, dim3(a.Hq), dim3(128), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace polar

@@ -14,6 +14,8 @@ struct PrefillArgs {
   const void *q, *k, *v;                  // [B,T,Hq,d], [B,T,Hkv,d] x2
   const float *beta, *null_bias, *count_vec;
   float *dir, *count, *n_eff, *gate, *lse;
+  float *u_norm;                          // [B,T,Hq] |u| for the backward pass, or NULL
+  int32_t *arg_max;                       // [B,T,Hq] first key of the row maximum (with u_norm)
   int B, T, Hq, Hkv, G;                   // G = Hq / Hkv
   int hb;                                 // query heads per workgroup (divides G, <= 4)
   int n_row_blocks;                       // ceil(T / rows per workgroup)
@@ -46,5 +48,36 @@ struct DecodeGrid {
 DecodeGrid decode_grid(int B, int Hq, int Hkv, int max_seq_len);
 size_t decode_ws_bytes(int B, int Hq, int Hkv, int max_seq_len);
 hipError_t launch_decode(int dtype, const DecodeArgs &a, hipStream_t stream);
+
+// Backward pass of the causal prefill (bf16 inputs).  Per-row quantities (float4 each):
+//   r0 = {c*log2(e), lse*log2(e), c*A, c*E}   r1 = {A, E, dm, arg-max key (int bits)}
+//   rp = {dbeta contribution of the dq kernel, -dm, gate*tanh(ln n_eff), floor term of dbeta}
+// with c = beta*tau and dl_j = p_j (v_j.du + A + E p_j) + [j = arg-max] dm.
+struct BwdArgs {
+  const void *q, *k, *v;                  // bf16 [B,T,Hq,d], [B,T,Hkv,d] x2
+  const float *beta, *null_bias, *count_vec;
+  const float *dir, *n_eff, *gate, *lse;  // forward outputs
+  const float *u_norm;                    // forward residuals
+  const int32_t *arg_max;
+  const float *c_dir, *c_count, *c_n_eff, *c_gate, *c_lse;   // cotangents (NULL = 0)
+  float *dq, *dk, *dv;                    // fp32 [B,T,Hq,d], [B,T,Hkv,d] x2
+  float *d_beta, *d_null_bias, *d_count_vec;
+  uint16_t *du, *cdu;                     // workspace: bf16 du and c*du [B,T,Hq,d]
+  float *r0, *r1, *rp;                    // workspace: per-row float4
+  float *part;                            // workspace: [Hq][n_part][kPartStride]
+  int B, T, Hq, Hkv, G;
+  int hb, n_row_blocks;                   // dq kernel: heads per workgroup, row blocks
+  int n_key_blocks;                       // dk/dv kernel: key blocks per (b, KV head)
+  int n_part;                             // parameter reduction: row chunks per head
+  float inv_log_train;
+  int null_floor;
+};
+constexpr int kPartStride = 68;           // dw[64], dbeta, dbias, pad
+
+size_t bwd_ws_bytes(int B, int T, int Hq);
+void bwd_ws_layout(BwdArgs &a, void *ws);  // sets du, cdu, r0, r1, rp, part, n_part
+int bwd_rows_per_block(int hb);
+int bwd_keys_per_block();
+hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream);
 
 }  // namespace polar

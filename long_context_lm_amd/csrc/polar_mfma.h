@@ -42,6 +42,18 @@ __device__ __forceinline__ float half_max(float x) {
   return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
 }
 
+// Position of key k32 (0..31 inside a 32-key block) in a transposed V row: the kpl keys
+// that one lane feeds to one P.V MFMA sit next to each other.  Lane group g of MFMA t
+// supplies slots e = 0..kpl-1 for keys 8*(i/4) + 4*g + i%4 with i = t*kpl + e (the keys
+// that the score MFMA left in that lane).  The same order serves any 32-long
+// contraction whose B operand comes straight out of a 32x32 MFMA result.
+template <int KPL>
+__device__ __forceinline__ int vpos32(int k32) {
+  const int a = k32 >> 3, gg = (k32 >> 2) & 1, cc = k32 & 3;
+  const int i = 4 * a + cc;
+  return (i / KPL) * (2 * KPL) + gg * KPL + (i % KPL);
+}
+
 // bf16 inputs: 8 contraction slots per lane per MFMA, fp32 accumulation.
 struct Bf16 {
   using elem_t = uint16_t;                 // storage (bit pattern)

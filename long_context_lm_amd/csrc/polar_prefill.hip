@@ -20,7 +20,10 @@
 //      S = sum 2^(x-M), Q = sum 2^(2(x-M)), u = sum 2^(x-M) v, and the exact row maximum.
 //    Raising the reference rescales S and u by 2^(M_old-M_new) and Q by its square, the
 //    squared correction factor of section 2.2;
-//  * epilogue: n_eff = S^2/Q, lse, the floor gate, dir = u/|u|, count.
+//  * epilogue: n_eff = S^2/Q, lse, the floor gate, dir = u/|u|, count;
+//  * training instances (kSave) also keep, per lane, the first key attaining the lane's
+//    running maximum score and write |u| and that key (the row's arg-max) for the
+//    backward pass.
 #include "polar_kernels.h"
 #include "polar_mfma.h"
 
@@ -57,18 +60,7 @@ template <> struct LdsCfg<Bf16> {
 };
 template <> struct LdsCfg<F32> { static constexpr int kt = 64, krow = 68, vrow = 65; };
 
-// Position of key k32 (0..31 inside a 32-key block) in a transposed V row: the kpl keys
-// that one lane feeds to one P.V MFMA sit next to each other.  Lane group g of MFMA t
-// supplies slots e = 0..kpl-1 for keys 8*(i/4) + 4*g + i%4 with i = t*kpl + e (the keys
-// that the score MFMA left in that lane).
-template <int KPL>
-__device__ __forceinline__ int vpos32(int k32) {
-  const int a = k32 >> 3, gg = (k32 >> 2) & 1, cc = k32 & 3;
-  const int i = 4 * a + cc;
-  return (i / KPL) * (2 * KPL) + gg * KPL + (i % KPL);
-}
-
-template <class TR, int QB, int kWaves>
+template <class TR, int QB, int kWaves, bool kSave>
 __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs a) {
   constexpr int kThreads = 64 * kWaves;
   constexpr int kKT = LdsCfg<TR>::kt;                // keys per tile
@@ -141,6 +133,8 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
   // product.
   f32x16 sacc[QB], qacc[QB];
   float Mref[QB], smax[QB], Ssum[QB], Qsum[QB];
+  float lbest[QB];                          // kSave: this lane's best score so far
+  int lkey[QB];                             // kSave: first key attaining it
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
@@ -154,6 +148,8 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
     }
     Mref[qb] = -INFINITY;
     smax[qb] = -INFINITY;
+    lbest[qb] = -INFINITY;
+    lkey[qb] = 0;
     Ssum[qb] = 0.f;
     Qsum[qb] = 0.f;
   }
@@ -307,6 +303,28 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S.v[qb][kb][r]);
     return half_max(mx);
   };
+  // kSave: keep the lowest key attaining this lane's maximum.  Tiles arrive in key order
+  // and a lane's registers in increasing key order, so a strict improvement picks the
+  // first occurrence.  Lanes rarely improve after the first tiles.
+  auto track = [&](const Scores &S, int qb, int key0) {
+    if constexpr (kSave) {
+      float mx = S.v[qb][0][0];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S.v[qb][kb][r]);
+      if (mx > lbest[qb]) {
+        int key = 0;
+#pragma unroll
+        for (int kb = NKB - 1; kb >= 0; --kb)
+#pragma unroll
+          for (int r = 15; r >= 0; --r)
+            if (S.v[qb][kb][r] == mx) key = key0 + kb * 32 + 8 * (r >> 2) + 4 * g32 + (r & 3);
+        lbest[qb] = mx;
+        lkey[qb] = key;
+      }
+    }
+  };
   // Raise the reference when the tile maximum passes it by more than the lazy threshold:
   // u and S scale by 2^(M_old - M_new), Q by the square of that factor.
   auto raise_ref = [&](int qb, float mt) {
@@ -400,9 +418,10 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
 
   Scores Sa, Sb, Sc;
   Probs P;
-  auto first_max = [&](const Scores &Sx) {
+  auto first_max = [&](const Scores &Sx, int key0) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
+      track(Sx, qb, key0);
       const float mx = tile_max(Sx, qb);
       smax[qb] = fmaxf(smax[qb], mx);
       raise_ref(qb, mx * cl2[qb]);
@@ -410,7 +429,7 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
   };
   if (nfull > 0) {
     score(0, Sa);
-    first_max(Sa);
+    first_max(Sa, 0);
   }
   if (nfull > 1) score(1, Sb);
 
@@ -424,6 +443,10 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
     float mxs[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) mxs[qb] = tile_max(S1, qb);
+    if (next_full) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) track(S1, qb, (t + 1) * kKT);
+    }
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       smax[qb] = next_full ? fmaxf(smax[qb], mxs[qb]) : smax[qb];
@@ -449,7 +472,7 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
     if (key0 <= w_last) {
       score(t % 4, Sa);
       mask(Sa, key0);
-      first_max(Sa);
+      first_max(Sa, key0);
       probs(Sa, P);
       pv_mma(t % 4, P);
     }
@@ -517,6 +540,16 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
             *(f32x4 *)(cp + dim0) = w * cg;
           }
       }
+      if constexpr (kSave) {
+        // Arg-max over the two wave halves: larger score, then lower key.
+        const float ob = __shfl_xor(lbest[qb], 32);
+        const int ok = __shfl_xor(lkey[qb], 32);
+        const int key = (ob > lbest[qb] || (ob == lbest[qb] && ok < lkey[qb])) ? ok : lkey[qb];
+        if (g32 == 0) {
+          a.u_norm[obase] = sqrtf(nrm) / St;
+          a.arg_max[obase] = key;
+        }
+      }
       if (g32 == 0) {
         a.n_eff[obase] = neff;
         if (a.gate) a.gate[obase] = gate;
@@ -551,11 +584,18 @@ hipError_t launch_prefill(int dtype, const PrefillArgs &a, hipStream_t stream) {
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   dim3 grid((unsigned)blocks);
-  if (dtype == 1)
-    hipLaunchKernelGGL((polar_prefill_kernel<Bf16, kQbBf16, kWavesBf16>), grid,
+  const bool save = a.u_norm != nullptr;
+  if (dtype == 1 && !save)
+    hipLaunchKernelGGL((polar_prefill_kernel<Bf16, kQbBf16, kWavesBf16, false>), grid,
                        dim3(64 * kWavesBf16), 0, stream, a);
+  else if (dtype == 1)
+    hipLaunchKernelGGL((polar_prefill_kernel<Bf16, kQbBf16, kWavesBf16, true>), grid,
+                       dim3(64 * kWavesBf16), 0, stream, a);
+  else if (!save)
+    hipLaunchKernelGGL((polar_prefill_kernel<F32, kQbF32, kWavesF32, false>), grid,
+                       dim3(64 * kWavesF32), 0, stream, a);
   else
-    hipLaunchKernelGGL((polar_prefill_kernel<F32, kQbF32, kWavesF32>), grid,
+    hipLaunchKernelGGL((polar_prefill_kernel<F32, kQbF32, kWavesF32, true>), grid,
                        dim3(64 * kWavesF32), 0, stream, a);
   return hipGetLastError();
 }

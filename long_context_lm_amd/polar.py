@@ -72,6 +72,85 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta=None, null_
     return out
 
 
+def _prefill_args(q, k, v, beta, null_bias, count_vec, train_len, flags):
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check_input(t, n)
+    B, T, Hq, d = q.shape
+    Hkv = k.shape[2]
+    if k.shape != (B, T, Hkv, d) or v.shape != k.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("k and v must be [B,T,Hkv,d] with q's dtype")
+    dev = q.device
+    beta, null_bias, count_vec = (_device_f32(beta, dev), _device_f32(null_bias, dev),
+                                  _device_f32(count_vec, dev))
+    prm = _params(Hq, Hkv, d, beta, null_bias, count_vec, train_len, flags)
+    return prm, (beta, null_bias, count_vec), (B, T, Hq, Hkv, d)
+
+
+def attn_fwd_train(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta=None,
+                   null_bias=None, count_vec=None, train_len: int = 2048,
+                   flags: int = _lib.POLAR_FLAG_LENGTH_TEMP | _lib.POLAR_FLAG_NULL_FLOOR,
+                   stream=None) -> dict:
+    """Prefill that also returns the residuals of the backward pass ("u_norm", "arg_max")."""
+    prm, keep, (B, T, Hq, Hkv, d) = _prefill_args(q, k, v, beta, null_bias, count_vec,
+                                                  train_len, flags)
+    dev = q.device
+    out, cout = _outputs((B, T), Hq, d, dev, keep[2] is not None, True, True)
+    out["u_norm"] = torch.empty(B, T, Hq, device=dev, dtype=torch.float32)
+    out["arg_max"] = torch.empty(B, T, Hq, device=dev, dtype=torch.int32)
+    saved = _lib.polar_saved(_ptr(out["u_norm"]), _ptr(out["arg_max"]))
+    s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+    _lib.check(_lib.polar_attn_fwd_train(prm, _DT[q.dtype], B, T, q.data_ptr(), k.data_ptr(),
+                                         v.data_ptr(), cout, saved, s))
+    return out
+
+
+def bwd_workspace_bytes(Hq: int, Hkv: int, B: int, T: int, d: int = 64) -> int:
+    prm = _lib.polar_params(Hq, Hkv, d, 2048, 0, None, None, None)
+    return _lib.polar_bwd_workspace_bytes(prm, B, T)
+
+
+def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, fwd: dict, cot: dict,
+             beta=None, null_bias=None, count_vec=None, train_len: int = 2048,
+             flags: int = _lib.POLAR_FLAG_LENGTH_TEMP | _lib.POLAR_FLAG_NULL_FLOOR,
+             param_grads: bool = True, workspace: Optional[torch.Tensor] = None,
+             stream=None) -> dict:
+    """Backward of the causal prefill.
+
+    ``fwd`` is what attn_fwd_train returned for the same arguments; ``cot`` maps output
+    names ("dir", "count", "n_eff", "gate", "lse") to float32 upstream gradients (missing
+    names are zero).  Returns float32 dq, dk, dv and, with ``param_grads``, d_beta,
+    d_null_bias and d_count_vec.
+    """
+    prm, keep, (B, T, Hq, Hkv, d) = _prefill_args(q, k, v, beta, null_bias, count_vec,
+                                                  train_len, flags)
+    dev = q.device
+    cts = {}
+    for name in ("dir", "count", "n_eff", "gate", "lse"):
+        c = cot.get(name)
+        cts[name] = None if c is None else torch.as_tensor(
+            c, dtype=torch.float32, device=dev).contiguous()
+    f32 = dict(device=dev, dtype=torch.float32)
+    g = dict(dq=torch.empty(B, T, Hq, d, **f32), dk=torch.empty(B, T, Hkv, d, **f32),
+             dv=torch.empty(B, T, Hkv, d, **f32))
+    if param_grads:
+        g.update(d_beta=torch.empty(Hq, **f32), d_null_bias=torch.empty(Hq, **f32),
+                 d_count_vec=torch.empty(Hq, d, **f32))
+    need = _lib.polar_bwd_workspace_bytes(prm, B, T)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    fo = _lib.polar_outputs(_ptr(fwd["dir"]), None, _ptr(fwd["n_eff"]), _ptr(fwd["gate"]),
+                            _ptr(fwd["lse"]))
+    sv = _lib.polar_saved(_ptr(fwd["u_norm"]), _ptr(fwd["arg_max"]))
+    co = _lib.polar_cotangents(*(_ptr(cts[n]) for n in ("dir", "count", "n_eff", "gate", "lse")))
+    go = _lib.polar_grads(_ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g.get("d_beta")),
+                          _ptr(g.get("d_null_bias")), _ptr(g.get("d_count_vec")))
+    s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+    _lib.check(_lib.polar_attn_bwd(prm, _DT[q.dtype], B, T, q.data_ptr(), k.data_ptr(),
+                                   v.data_ptr(), fo, sv, co, go, workspace.data_ptr(),
+                                   workspace.numel() * workspace.element_size(), s))
+    return g
+
+
 def decode_workspace_bytes(Hq: int, Hkv: int, B: int, max_seq_len: int, page_size: int = 64,
                            d: int = 64) -> int:
     prm = _lib.polar_params(Hq, Hkv, d, 2048, 0, None, None, None)

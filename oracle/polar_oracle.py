@@ -100,7 +100,7 @@ def _polar_rows(Qr: np.ndarray, K: np.ndarray, V: np.ndarray, n_vis: np.ndarray,
     floor = null_floor(n_vis, beta_h, tau, d, null_bias_h, bool(flags & FLAG_NULL_FLOOR))
     gate = expit(m - floor)
     count = (gate * np.tanh(np.log(n_eff)))[:, None] * np.asarray(w_h, np.float64)[None, :]
-    return dict(dir=dir_, count=count, n_eff=n_eff, gate=gate, lse=lse)
+    return dict(dir=dir_, count=count, n_eff=n_eff, gate=gate, lse=lse, u_norm=norm)
 
 
 def _params(Hq, d, beta, null_bias, count_vec):
@@ -121,7 +121,8 @@ def polar_prefill(q, k, v, beta=None, null_bias=None, count_vec=None, train_len:
     Row i of head h sees keys 0..i of KV head h // (Hq // Hkv).
     ``rows``/``heads``/``batches`` restrict the computation to a sample; the outputs are
     then indexed [len(batches), len(rows), len(heads), ...].
-    Returns float64 dir, count [B,R,H,d] and n_eff, gate, lse [B,R,H].
+    Returns float64 dir, count [B,R,H,d] and n_eff, gate, lse [B,R,H], plus u_norm [B,R,H],
+    the norm |u| of the matched value sum (a residual of the backward pass).
     """
     q = np.asarray(q)
     B, T, Hq, d = q.shape
@@ -134,7 +135,8 @@ def polar_prefill(q, k, v, beta=None, null_bias=None, count_vec=None, train_len:
     batches = np.arange(B) if batches is None else np.asarray(batches, np.int64)
     R, H, Bs = len(rows), len(heads), len(batches)
     out = dict(dir=np.zeros((Bs, R, H, d)), count=np.zeros((Bs, R, H, d)),
-               n_eff=np.zeros((Bs, R, H)), gate=np.zeros((Bs, R, H)), lse=np.zeros((Bs, R, H)))
+               n_eff=np.zeros((Bs, R, H)), gate=np.zeros((Bs, R, H)), lse=np.zeros((Bs, R, H)),
+               u_norm=np.zeros((Bs, R, H)))
     for bi, b in enumerate(batches):
         for hi, h in enumerate(heads):
             g = h // G

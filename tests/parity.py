@@ -112,3 +112,61 @@ def select(out: dict, batches=None, rows=None, heads=None) -> dict:
             t = t[:, :, torch.as_tensor(heads, device=t.device)]
         res[k] = t
     return res
+
+
+# ------------------------------------------------------------------ backward pass
+# Gradient error metric, per tensor: max |g^ - g| / max |g| (the largest gradient entry
+# sets the scale, so near-zero entries are not judged by their own size), and the
+# relative Frobenius error |g^ - g|_F / |g|_F.  Bound for bfloat16 inputs: 2e-2 on the
+# first, 1e-2 on the second (the P, dS and du operands of the MFMA products are rounded to
+# bfloat16, a relative 2^-9 per element, summed over up to T terms in fp32).
+GRAD_TOL = {"max": 2e-2, "fro": 1e-2}
+GRAD_KEYS = ("dq", "dk", "dv", "d_beta", "d_null_bias", "d_count_vec")
+
+
+def gpu_forward_train(p: synth.PrefillInputs):
+    from long_context_lm_amd import attn_fwd_train
+    q, k, v = (to_dev(getattr(p, n), p.dtype) for n in ("q", "k", "v"))
+    out = attn_fwd_train(q, k, v, beta=p.beta, null_bias=p.null_bias, count_vec=p.count_vec,
+                         train_len=p.train_len, flags=p.flags)
+    torch.cuda.synchronize()
+    return (q, k, v), out
+
+
+def gpu_backward(p: synth.PrefillInputs, cot: dict, param_grads: bool = True):
+    from long_context_lm_amd import attn_bwd
+    (q, k, v), fwd = gpu_forward_train(p)
+    g = attn_bwd(q, k, v, fwd, cot, beta=p.beta, null_bias=p.null_bias, count_vec=p.count_vec,
+                 train_len=p.train_len, flags=p.flags, param_grads=param_grads)
+    torch.cuda.synchronize()
+    return g
+
+
+def oracle_backward(p: synth.PrefillInputs, cot: dict, batches=None) -> dict:
+    sl = slice(None) if batches is None else list(batches)
+    c = {n: (None if x is None else np.asarray(x)[sl]) for n, x in cot.items()}
+    return oracle.polar_prefill_grad(p.as_f32("q")[sl], p.as_f32("k")[sl], p.as_f32("v")[sl],
+                                     c, p.beta, p.null_bias, p.count_vec, p.train_len, p.flags)
+
+
+def grad_errors(got: dict, want: dict, keys=GRAD_KEYS) -> dict:
+    e = {}
+    for n in keys:
+        g = host(got[n]) if isinstance(got[n], torch.Tensor) else np.asarray(got[n])
+        w = np.asarray(want[n], np.float64)
+        scale = float(np.max(np.abs(w)))
+        if scale == 0.0:
+            e[n] = (float(np.max(np.abs(g))), 0.0)
+            continue
+        e[n] = (float(np.max(np.abs(g - w))) / scale,
+                float(np.linalg.norm(g - w) / max(np.linalg.norm(w), 1e-300)))
+    return e
+
+
+def assert_grads_close(got: dict, want: dict, keys=GRAD_KEYS, label=""):
+    e = grad_errors(got, want, keys)
+    print(f"[grad] {label} " + " ".join(f"{n}={m:.1e}/{f:.1e}" for n, (m, f) in e.items()),
+          flush=True)
+    bad = {n: v for n, v in e.items() if not (v[0] <= GRAD_TOL["max"] and v[1] <= GRAD_TOL["fro"])}
+    assert not bad, f"{label}: gradient errors above {GRAD_TOL}: {bad}"
+    return e

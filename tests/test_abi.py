@@ -134,3 +134,93 @@ def test_empty_decode_is_a_valid_no_op():
     assert dec(B=0, ws_bytes=0) == _lib.POLAR_OK
     assert dec(B=0, ws_bytes=0, q=None, table=None, lens=None, ws=None,
                o=outs(dir=None, n_eff=None)) == _lib.POLAR_OK
+
+
+# ------------------------------------------------------------------ training entry points
+WS = 0x100000          # 256-byte aligned fake workspace address
+
+
+def saved(**kw):
+    d = dict(u_norm=A, arg_max=A)
+    d.update(kw)
+    return _lib.polar_saved(d["u_norm"], d["arg_max"])
+
+
+def cots(**kw):
+    d = dict(dir=A, count=A, n_eff=A, gate=A, lse=A)
+    d.update(kw)
+    return _lib.polar_cotangents(d["dir"], d["count"], d["n_eff"], d["gate"], d["lse"])
+
+
+def grads(**kw):
+    d = dict(dq=A, dk=A, dv=A, d_beta=None, d_null_bias=None, d_count_vec=None)
+    d.update(kw)
+    return _lib.polar_grads(d["dq"], d["dk"], d["dv"], d["d_beta"], d["d_null_bias"],
+                            d["d_count_vec"])
+
+
+def bwd(p=None, dt=1, B=1, T=100, q=A, k=A, v=A, o=None, s=None, c=None, g=None, ws=WS,
+        ws_bytes=None):
+    p = params() if p is None else p
+    if ws_bytes is None:
+        ws_bytes = _lib.polar_bwd_workspace_bytes(p, max(B, 1), max(T, 1))
+    return _lib.polar_attn_bwd(p, dt, B, T, q, k, v, outs() if o is None else o,
+                               saved() if s is None else s, cots() if c is None else c,
+                               grads() if g is None else g, ws, ws_bytes, None)
+
+
+def test_bwd_workspace_bytes():
+    p = params()
+    n = _lib.polar_bwd_workspace_bytes(p, 8, 2048)
+    assert n >= 8 * 2048 * 16 * (2 * 64 * 2 + 3 * 16) and n % 256 == 0
+    assert _lib.polar_bwd_workspace_bytes(p, 0, 2048) == 0
+    assert _lib.polar_bwd_workspace_bytes(p, 8, 0) == 0
+    assert _lib.polar_bwd_workspace_bytes(params(n_q_heads=6), 8, 64) == 0
+    assert _lib.polar_bwd_workspace_bytes(p, 1, 1 << 30) == 0       # 32-bit offsets
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=0), _lib.POLAR_ERR_UNSUPPORTED),                        # bf16 only
+    (dict(p=params(head_dim=128)), _lib.POLAR_ERR_UNSUPPORTED),
+    (dict(T=-1), _lib.POLAR_ERR_BAD_SHAPE),
+    (dict(g=grads(dq=None)), _lib.POLAR_ERR_NULL_POINTER),
+    (dict(g=grads(dv=None)), _lib.POLAR_ERR_NULL_POINTER),
+    (dict(s=saved(arg_max=None)), _lib.POLAR_ERR_NULL_POINTER),
+    (dict(o=outs(lse=None)), _lib.POLAR_ERR_NULL_POINTER),
+    (dict(o=outs(gate=None)), _lib.POLAR_ERR_NULL_POINTER),
+    (dict(p=params(count_vec=None), o=outs(count=None)), _lib.POLAR_ERR_NULL_POINTER),
+    (dict(ws=None), _lib.POLAR_ERR_NULL_POINTER),
+    (dict(ws=WS + 16), _lib.POLAR_ERR_MISALIGNED),
+    (dict(g=grads(dk=A + 4)), _lib.POLAR_ERR_MISALIGNED),
+    (dict(c=cots(dir=A + 8)), _lib.POLAR_ERR_MISALIGNED),
+    (dict(ws_bytes=1024), _lib.POLAR_ERR_WORKSPACE_TOO_SMALL),
+])
+def test_bwd_validation_errors(kw, code):
+    assert bwd(**kw) == code
+    assert _lib.polar_last_error() != ""
+
+
+def test_bwd_null_structs():
+    lib = _lib.load()
+    p = params()
+    n = _lib.polar_bwd_workspace_bytes(p, 1, 100)
+    assert lib.polar_attn_bwd(ctypes.byref(p), 1, 1, 100, A, A, A, ctypes.byref(outs()), None,
+                              ctypes.byref(cots()), ctypes.byref(grads()), WS, n, None) == \
+        _lib.POLAR_ERR_NULL_POINTER
+
+
+def test_empty_bwd_without_parameter_grads_is_a_no_op():
+    assert bwd(B=0, q=None, k=None, v=None, ws=None, ws_bytes=0) == _lib.POLAR_OK
+    assert bwd(T=0, g=grads(dq=None, dk=None, dv=None), ws=None, ws_bytes=0) == _lib.POLAR_OK
+
+
+def test_fwd_train_validation():
+    lib = _lib.load()
+    p = params()
+    assert lib.polar_attn_fwd_train(ctypes.byref(p), 1, 1, 8, A, A, A, ctypes.byref(outs()),
+                                    None, None) == _lib.POLAR_ERR_NULL_POINTER
+    assert _lib.polar_attn_fwd_train(p, 1, 1, 8, A, A, A, outs(), saved(u_norm=None),
+                                     None) == _lib.POLAR_ERR_NULL_POINTER
+    assert _lib.polar_attn_fwd_train(p, 1, 1, 8, A, A, A, outs(gate=None), saved(),
+                                     None) == _lib.POLAR_ERR_NULL_POINTER
+    assert _lib.polar_attn_fwd_train(p, 1, 0, 8, A, A, A, outs(), saved(), None) == _lib.POLAR_OK

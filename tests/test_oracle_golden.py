@@ -20,7 +20,8 @@ def test_oracle_matches_committed_fixture():
                                  **kw)
         o = oracle.polar_prefill(p.as_f32("q"), p.as_f32("k"), p.as_f32("v"), p.beta,
                                  p.null_bias, p.count_vec, p.train_len, p.flags)
-        for key, val in o.items():
+        for key in ("dir", "count", "n_eff", "gate", "lse"):
+            val = o[key]
             if val.ndim == 4:
                 val = val[..., :8]
             assert np.abs(val - np.array(entry[key])).max() < 1e-12, (case, key)
