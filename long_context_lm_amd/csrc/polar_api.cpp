@@ -247,7 +247,7 @@ polar_status polar_attn_bwd(const polar_params *p, polar_dtype dt, int32_t B, in
   a.null_floor = (p->flags & POLAR_FLAG_NULL_FLOOR) ? 1 : 0;
   polar::bwd_ws_layout(a, workspace);
   const long long dq_blocks = (long long)a.n_row_blocks * a.Hkv * (a.G / a.hb) * B;
-  const long long dkv_blocks = (long long)a.n_key_blocks * a.Hkv * B;
+  const long long dkv_blocks = (long long)((a.n_key_blocks + 1) / 2) * a.Hkv * B;
   if (dq_blocks > 0x7fffffffLL || dkv_blocks > 0x7fffffffLL)
     return fail(POLAR_ERR_BAD_SHAPE, "problem too large for one launch");
   hipError_t err = polar::launch_bwd(a, (hipStream_t)stream);

@@ -22,8 +22,9 @@
 //            tile S^T = K Q^T and dP^T = V du^T on MFMA, dl on the VALU, then
 //            dq^T += K^T dl^T with K^T from a transposed LDS tile.
 //  3. dk/dv: one wave per 32 keys (lane = key), keys and values resident in registers;
-//            the workgroup walks every query tile of the G heads sharing the KV head that
-//            can see its keys.  S' = Q K^T and c dP' = (c du) V^T on MFMA, then
+//            a workgroup owns two key blocks (i and its mirror, for causal balance) and
+//            walks, from the last one down, every query tile of the G heads sharing the KV
+//            head that can see their keys.  S' = Q K^T and c dP' = (c du) V^T on MFMA, then
 //            dv^T += du^T P and dk^T += Q^T dS with du^T and Q^T from transposed tiles.
 //            Each key has one owner, so dk and dv need no atomics.
 //  4. parameter gradients: fixed-order two-level reductions over rows.
@@ -115,8 +116,8 @@ __global__ void __launch_bounds__(256) polar_bwd_prep_kernel(BwdArgs a) {
     const float fl =
         a.null_floor ? -dm * tau * 0.125f * sqrtf(2.f * logf((float)(i + 1))) : 0.f;
     const f32x4 rp = {0.f, -dm, gate * th, fl};
-    *(f32x4 *)(a.r0 + 4 * Rc) = r0;
-    *(f32x4 *)(a.r1 + 4 * Rc) = r1;
+    *(f32x4 *)(a.rows + 8 * Rc) = r0;
+    *(f32x4 *)(a.rows + 8 * Rc + 4) = r1;
     *(f32x4 *)(a.rp + 4 * Rc) = rp;
   }
 }
@@ -165,8 +166,8 @@ __global__ void __launch_bounds__(64 * kWaves) polar_bwd_dq_kernel(BwdArgs a) {
   float cl2 = 1.f, lse2 = INFINITY, A = 0.f, E = 0.f, dm = 0.f;
   int js = 0;
   if (valid) {
-    const f32x4 r0 = *(const f32x4 *)(a.r0 + 4 * rr);
-    const f32x4 r1 = *(const f32x4 *)(a.r1 + 4 * rr);
+    const f32x4 r0 = *(const f32x4 *)(a.rows + 8 * rr);
+    const f32x4 r1 = *(const f32x4 *)(a.rows + 8 * rr + 4);
     cl2 = r0[0];
     lse2 = r0[1];
     A = r1[0];
@@ -337,10 +338,11 @@ __global__ void __launch_bounds__(64 * kWaves) polar_bwd_dq_kernel(BwdArgs a) {
 
 // ------------------------------------------------------------------ 3. dk / dv
 template <int kWaves>
-__global__ void __launch_bounds__(64 * kWaves) polar_bwd_dkv_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+polar_bwd_dkv_kernel(BwdArgs a) {
   constexpr int kThreads = 64 * kWaves;
   static_assert(kThreads == 256, "one staging task per thread");
-  constexpr int KB = 32 * kWaves;                   // keys per workgroup
+  constexpr int KB = 32 * kWaves;                   // keys per key block
   constexpr int QROW = 72, TROW = 40;
   __shared__ __attribute__((aligned(16))) uint16_t Qs[2][32 * QROW];   // q rows
   __shared__ __attribute__((aligned(16))) uint16_t Cs[2][32 * QROW];   // c*du rows
@@ -351,82 +353,65 @@ __global__ void __launch_bounds__(64 * kWaves) polar_bwd_dkv_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g32 = lane >> 5, c32 = lane & 31;
-  int id = blockIdx.x;
-  const int b = id % a.B;
-  id /= a.B;
-  const int g = id % a.Hkv;
-  const int kblk = a.n_key_blocks - 1 - id / a.Hkv;   // heaviest (lowest keys) first
-  const int k0 = kblk * KB;
-  const int kw0 = k0 + wave * 32;
-  const int key = kw0 + c32;
-  const bool kvalid = key < a.T;
-
-  F kf[4], vf[4];
-  {
-    const size_t kb = (((size_t)b * a.T + (kvalid ? key : 0)) * a.Hkv + g) * kD + g32 * 8;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      kf[ks] = kvalid ? *(const F *)((const uint16_t *)a.k + kb + ks * 16) : Bf16::zero();
-      vf[ks] = kvalid ? *(const F *)((const uint16_t *)a.v + kb + ks * 16) : Bf16::zero();
-    }
-  }
-  f32x16 dK[2], dV[2];
-#pragma unroll
-  for (int db = 0; db < 2; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      dK[db][r] = 0.f;
-      dV[db][r] = 0.f;
-    }
-
-  const int rt0 = k0 / 32;
+  // Causal balance: a workgroup owns key blocks i and nkb-1-i, whose query-tile counts
+  // add up to the same total for every i.  Workgroups are dealt to the 8 XCDs
+  // round-robin by block index; each XCD gets a contiguous range of (sequence, KV head,
+  // pair) units, pair fastest, so the workgroups of one (sequence, KV head) share an L2
+  // and, all walking the query tiles top-down, read each tile at about the same time.
+  const int nblk = gridDim.x;
+  const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+  const int unit = xcd * (nblk >> 3) + min(xcd, nblk & 7) + local;
+  const int npair = (a.n_key_blocks + 1) >> 1;
+  const int pair = unit % npair;
+  const int bg = unit / npair;
+  const int g = bg % a.Hkv, b = bg / a.Hkv;
   const int nrt = (a.T + 31) / 32;
-  const int nsteps = (nrt - rt0) * a.G;
   const int rs = a.Hq * kD * 2;                     // bytes between rows of q / du
+
+  // Loop-invariant per-thread buffer offsets; the row tile and head move the resource
+  // base, so rows past T fall outside the resource and load zeros.
+  const int rw = tid >> 3, part = tid & 7, rp = tid & 15, dg = tid >> 4;
+  const int voff_c = rw * rs + part * 16;
+  const int voff_p0 = 2 * rp * rs + dg * 8;
+  const int voff_p1 = voff_p0 + rs;
+  const int voff_s = (tid & 31) * a.Hq * 32 + (tid >> 5) * 16;   // r0 (tid < 32) or r1
 
   u32x4 qst, cst;
   u32x2 qtst[2], dtst[2];
   f32x4 sst;
   auto stage_load = [&](int s) {
-    const int r0row = (rt0 + s / a.G) * 32;
+    const int r0row = (nrt - 1 - s / a.G) * 32;
     const int h = g * a.G + s % a.G;
-    const size_t base = ((size_t)b * a.T * a.Hq + h) * kD;
-    const int nbytes = (int)(((size_t)a.T * a.Hq - h) * kD * 2);
+    const size_t row0 = ((size_t)b * a.T + r0row) * a.Hq + h;
+    const int nbytes = (int)(((size_t)(a.T - r0row) * a.Hq - h) * kD * 2);
     const auto qr = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)((const uint16_t *)a.q + base), 0, nbytes, kBufferFlags);
-    const auto dr = __builtin_amdgcn_make_buffer_rsrc((void *)(a.du + base), 0, nbytes,
+        (void *)((const uint16_t *)a.q + row0 * kD), 0, nbytes, kBufferFlags);
+    const auto dr = __builtin_amdgcn_make_buffer_rsrc((void *)(a.du + row0 * kD), 0, nbytes,
                                                       kBufferFlags);
-    const auto cr = __builtin_amdgcn_make_buffer_rsrc((void *)(a.cdu + base), 0, nbytes,
+    const auto cr = __builtin_amdgcn_make_buffer_rsrc((void *)(a.cdu + row0 * kD), 0, nbytes,
                                                       kBufferFlags);
-    const int rw = tid >> 3, part = tid & 7;
-    const int off = (r0row + rw) * rs + part * 16;
-    qst = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(qr, off, 0, 0));
-    cst = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(cr, off, 0, 0));
-    const int rp = tid & 15, dg = tid >> 4;
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int o2 = (r0row + 2 * rp + r) * rs + dg * 8;
-      qtst[r] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(qr, o2, 0, 0));
-      dtst[r] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(dr, o2, 0, 0));
-    }
+    qst = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(qr, voff_c, 0, 0));
+    cst = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(cr, voff_c, 0, 0));
+    qtst[0] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(qr, voff_p0, 0, 0));
+    qtst[1] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(qr, voff_p1, 0, 0));
+    dtst[0] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(dr, voff_p0, 0, 0));
+    dtst[1] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(dr, voff_p1, 0, 0));
     if (tid < 64) {
-      const int ri = tid & 31;
-      const int row = r0row + ri;
-      const size_t rr = ((size_t)b * a.T + min(row, a.T - 1)) * a.Hq + h;
-      if (tid < 32) {
-        const f32x4 pad = {1.f, INFINITY, 0.f, 0.f};
-        sst = row < a.T ? *(const f32x4 *)(a.r0 + 4 * rr) : pad;
-      } else {
-        const f32x4 pad = {0.f, 0.f, 0.f, __int_as_float(-1)};
-        sst = row < a.T ? *(const f32x4 *)(a.r1 + 4 * rr) : pad;
-      }
+      const int sbytes = (int)(((size_t)(a.T - r0row) * a.Hq - h) * 32);
+      const auto sr = __builtin_amdgcn_make_buffer_rsrc((void *)(a.rows + row0 * 8), 0, sbytes,
+                                                        kBufferFlags);
+      sst = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(sr, voff_s, 0, 0));
     }
   };
-  auto stage_store = [&](int buf) {
-    const int rw = tid >> 3, part = tid & 7;
+  // Rows past T: p = 0 (lse2 = +inf), zero coefficients, no arg-max key.
+  auto stage_store = [&](int buf, int s) {
+    if (tid < 64 && (nrt - 1 - s / a.G) * 32 + (tid & 31) >= a.T) {
+      const f32x4 pad0 = {1.f, INFINITY, 0.f, 0.f};
+      const f32x4 pad1 = {0.f, 0.f, 0.f, __int_as_float(-1)};
+      sst = tid < 32 ? pad0 : pad1;
+    }
     *(u32x4 *)&Qs[buf][rw * QROW + part * 8] = qst;
     *(u32x4 *)&Cs[buf][rw * QROW + part * 8] = cst;
-    const int rp = tid & 15, dg = tid >> 4;
     const int pos = vpos32<8>(2 * rp);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -446,90 +431,121 @@ __global__ void __launch_bounds__(64 * kWaves) polar_bwd_dkv_kernel(BwdArgs a) {
   const uint32_t t_lane = (uint32_t)((c32 * TROW + g32 * 8) * 2);
   constexpr uint32_t QBUF = 32 * QROW * 2, TBUF = kD * TROW * 2;
 
-  if (nsteps > 0) {
-    stage_load(0);
-    stage_store(0);
-  }
-  __syncthreads();
-  for (int s = 0; s < nsteps; ++s) {
-    const int buf = s & 1;
-    const bool more = s + 1 < nsteps;
-    if (more) stage_load(s + 1);
-    const int r0row = (rt0 + s / a.G) * 32;
-    if (r0row + 31 >= kw0 && kw0 < a.T) {
-      const uint16_t *Qb = lds_at(&Qs[0][0], q_lane + buf * QBUF);
-      const uint16_t *Cb = lds_at(&Cs[0][0], q_lane + buf * QBUF);
-      const f32x16 zero = {};
-      f32x16 S, P;
+  for (int half = 0; half < 2; ++half) {
+    const int kblk = half == 0 ? pair : a.n_key_blocks - 1 - pair;
+    if (half == 1 && kblk == pair) break;            // odd count: the middle block once
+    const int k0 = kblk * KB;
+    const int kw0 = k0 + wave * 32;
+    const int key = kw0 + c32;
+    const bool kvalid = key < a.T;
+
+    F kf[4], vf[4];
+    {
+      const size_t kb = (((size_t)b * a.T + (kvalid ? key : 0)) * a.Hkv + g) * kD + g32 * 8;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        S = Bf16::mma32(*(const F *)(Qb + ks * 16), kf[ks], ks == 0 ? zero : S);
-        P = Bf16::mma32(*(const F *)(Cb + ks * 16), vf[ks], ks == 0 ? zero : P);
+        kf[ks] = kvalid ? *(const F *)((const uint16_t *)a.k + kb + ks * 16) : Bf16::zero();
+        vf[ks] = kvalid ? *(const F *)((const uint16_t *)a.v + kb + ks * 16) : Bf16::zero();
       }
-      const bool diag = r0row < kw0 + 31;
-      float pv[16], dsv[16];
-#pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4) {
-        const int ri0 = 8 * a4 + 4 * g32;
-        const f32x4 cl = *(const f32x4 *)&Sc[buf][0][ri0];
-        const f32x4 ls = *(const f32x4 *)&Sc[buf][1][ri0];
-        const f32x4 ac = *(const f32x4 *)&Sc[buf][2][ri0];
-        const f32x4 ec = *(const f32x4 *)&Sc[buf][3][ri0];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int r = 4 * a4 + c;
-          float p = fast_exp2(fmaf(S[r], cl[c], -ls[c]));
-          if (diag && r0row + ri0 + c < key) p = 0.f;
-          pv[r] = p;
-          dsv[r] = p * (P[r] + fmaf(ec[c], p, ac[c]));
-        }
-      }
-      // Rows whose arg-max key belongs to this wave (rare): add c*dm at that key.
-      const int jl = __float_as_int(Sc[buf][5][c32]);
-      if (__ballot(jl >= kw0 && jl < kw0 + 32) != 0) {
-#pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
-          const int ri0 = 8 * a4 + 4 * g32;
-          const f32x4 jv = *(const f32x4 *)&Sc[buf][5][ri0];
-          const f32x4 dmv = *(const f32x4 *)&Sc[buf][4][ri0];
-          const f32x4 cl = *(const f32x4 *)&Sc[buf][0][ri0];
-#pragma unroll
-          for (int c = 0; c < 4; ++c)
-            if (__float_as_int(jv[c]) == key) dsv[4 * a4 + c] += dmv[c] * cl[c] * kLn2;
-        }
-      }
-      const F pp0 = Bf16::pack(pv), pp1 = Bf16::pack(pv + 8);
-      const F dp0 = Bf16::pack(dsv), dp1 = Bf16::pack(dsv + 8);
-      const uint16_t *Db = lds_at(&Dt[0][0], t_lane + buf * TBUF);
-      const uint16_t *Tb = lds_at(&Qt[0][0], t_lane + buf * TBUF);
-#pragma unroll
-      for (int db = 0; db < 2; ++db) {
-        dV[db] = Bf16::mma32(*(const F *)(Db + db * 32 * TROW), pp0, dV[db]);
-        dK[db] = Bf16::mma32(*(const F *)(Tb + db * 32 * TROW), dp0, dK[db]);
-        dV[db] = Bf16::mma32(*(const F *)(Db + db * 32 * TROW + 16), pp1, dV[db]);
-        dK[db] = Bf16::mma32(*(const F *)(Tb + db * 32 * TROW + 16), dp1, dK[db]);
-      }
+      // Settle these loads here, on every path into the key loop, so the loop's first
+      // MFMA does not wait on the staging loads issued in the same step.
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     }
-    if (more) stage_store(buf ^ 1);
-    __syncthreads();
-  }
-
-  if (kvalid) {
-    const size_t ob = (((size_t)b * a.T + key) * a.Hkv + g) * kD;
+    f32x16 dK[2], dV[2];
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
-      for (int j4 = 0; j4 < 4; ++j4) {
-        const int d0 = db * 32 + 8 * j4 + 4 * g32;
-        f32x4 kv, vv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          kv[e] = dK[db][4 * j4 + e];
-          vv[e] = dV[db][4 * j4 + e];
-        }
-        *(f32x4 *)(a.dk + ob + d0) = kv;
-        *(f32x4 *)(a.dv + ob + d0) = vv;
+      for (int r = 0; r < 16; ++r) {
+        dK[db][r] = 0.f;
+        dV[db][r] = 0.f;
       }
+
+    const int nsteps = (nrt - k0 / 32) * a.G;
+    if (nsteps > 0) {
+      stage_load(0);
+      stage_store(0, 0);
+    }
+    __syncthreads();
+    for (int s = 0; s < nsteps; ++s) {
+      const int buf = s & 1;
+      const bool more = s + 1 < nsteps;
+      if (more) stage_load(s + 1);
+      const int r0row = (nrt - 1 - s / a.G) * 32;
+      if (r0row + 31 >= kw0 && kw0 < a.T) {
+        const uint16_t *Qb = lds_at(&Qs[0][0], q_lane + buf * QBUF);
+        const uint16_t *Cb = lds_at(&Cs[0][0], q_lane + buf * QBUF);
+        const f32x16 zero = {};
+        f32x16 S, P;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          S = Bf16::mma32(*(const F *)(Qb + ks * 16), kf[ks], ks == 0 ? zero : S);
+          P = Bf16::mma32(*(const F *)(Cb + ks * 16), vf[ks], ks == 0 ? zero : P);
+        }
+        const bool diag = r0row < kw0 + 31;
+        float pv[16], dsv[16];
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const int ri0 = 8 * a4 + 4 * g32;
+          const f32x4 cl = *(const f32x4 *)&Sc[buf][0][ri0];
+          const f32x4 ls = *(const f32x4 *)&Sc[buf][1][ri0];
+          const f32x4 ac = *(const f32x4 *)&Sc[buf][2][ri0];
+          const f32x4 ec = *(const f32x4 *)&Sc[buf][3][ri0];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int r = 4 * a4 + c;
+            float p = fast_exp2(fmaf(S[r], cl[c], -ls[c]));
+            if (diag && r0row + ri0 + c < key) p = 0.f;
+            pv[r] = p;
+            dsv[r] = p * (P[r] + fmaf(ec[c], p, ac[c]));
+          }
+        }
+        // Rows whose arg-max key belongs to this wave (rare): add c*dm at that key.
+        const int jl = __float_as_int(Sc[buf][5][c32]);
+        if (__ballot(jl >= kw0 && jl < kw0 + 32) != 0) {
+#pragma unroll
+          for (int a4 = 0; a4 < 4; ++a4) {
+            const int ri0 = 8 * a4 + 4 * g32;
+            const f32x4 jv = *(const f32x4 *)&Sc[buf][5][ri0];
+            const f32x4 dmv = *(const f32x4 *)&Sc[buf][4][ri0];
+            const f32x4 cl = *(const f32x4 *)&Sc[buf][0][ri0];
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+              if (__float_as_int(jv[c]) == key) dsv[4 * a4 + c] += dmv[c] * cl[c] * kLn2;
+          }
+        }
+        const F pp0 = Bf16::pack(pv), pp1 = Bf16::pack(pv + 8);
+        const F dp0 = Bf16::pack(dsv), dp1 = Bf16::pack(dsv + 8);
+        const uint16_t *Db = lds_at(&Dt[0][0], t_lane + buf * TBUF);
+        const uint16_t *Tb = lds_at(&Qt[0][0], t_lane + buf * TBUF);
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+          dV[db] = Bf16::mma32(*(const F *)(Db + db * 32 * TROW), pp0, dV[db]);
+          dK[db] = Bf16::mma32(*(const F *)(Tb + db * 32 * TROW), dp0, dK[db]);
+          dV[db] = Bf16::mma32(*(const F *)(Db + db * 32 * TROW + 16), pp1, dV[db]);
+          dK[db] = Bf16::mma32(*(const F *)(Tb + db * 32 * TROW + 16), dp1, dK[db]);
+        }
+      }
+      if (more) stage_store(buf ^ 1, s + 1);
+      __syncthreads();
+    }
+
+    if (kvalid) {
+      const size_t ob = (((size_t)b * a.T + key) * a.Hkv + g) * kD;
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int j4 = 0; j4 < 4; ++j4) {
+          const int d0 = db * 32 + 8 * j4 + 4 * g32;
+          f32x4 kv, vv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            kv[e] = dK[db][4 * j4 + e];
+            vv[e] = dV[db][4 * j4 + e];
+          }
+          *(f32x4 *)(a.dk + ob + d0) = kv;
+          *(f32x4 *)(a.dv + ob + d0) = vv;
+        }
+    }
   }
 }
 
@@ -588,7 +604,7 @@ int n_parts(int B, int T) {
 
 size_t bwd_ws_bytes(int B, int T, int Hq) {
   const size_t nrows = (size_t)B * T * Hq;
-  return 2 * align256(nrows * kD * 2) + 3 * align256(nrows * 16) +
+  return 2 * align256(nrows * kD * 2) + align256(nrows * 32) + align256(nrows * 16) +
          align256((size_t)Hq * n_parts(B, T) * kPartStride * 4);
 }
 
@@ -599,10 +615,8 @@ void bwd_ws_layout(BwdArgs &a, void *ws) {
   p += align256(nrows * kD * 2);
   a.cdu = (uint16_t *)p;
   p += align256(nrows * kD * 2);
-  a.r0 = (float *)p;
-  p += align256(nrows * 16);
-  a.r1 = (float *)p;
-  p += align256(nrows * 16);
+  a.rows = (float *)p;
+  p += align256(nrows * 32);
   a.rp = (float *)p;
   p += align256(nrows * 16);
   a.part = (float *)p;
@@ -620,7 +634,7 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream) {
   const long long dq_blocks = (long long)a.n_row_blocks * a.Hkv * (a.G / a.hb) * a.B;
   hipLaunchKernelGGL((polar_bwd_dq_kernel<kDqWaves>), dim3((unsigned)dq_blocks),
                      dim3(64 * kDqWaves), 0, stream, a);
-  const long long dkv_blocks = (long long)a.n_key_blocks * a.Hkv * a.B;
+  const long long dkv_blocks = (long long)((a.n_key_blocks + 1) / 2) * a.Hkv * a.B;
   hipLaunchKernelGGL((polar_bwd_dkv_kernel<kDkvWaves>), dim3((unsigned)dkv_blocks),
                      dim3(64 * kDkvWaves), 0, stream, a);
   if (a.d_beta || a.d_null_bias || a.d_count_vec) {

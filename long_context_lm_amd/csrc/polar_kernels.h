@@ -49,7 +49,8 @@ DecodeGrid decode_grid(int B, int Hq, int Hkv, int max_seq_len);
 size_t decode_ws_bytes(int B, int Hq, int Hkv, int max_seq_len);
 hipError_t launch_decode(int dtype, const DecodeArgs &a, hipStream_t stream);
 
-// Backward pass of the causal prefill (bf16 inputs).  Per-row quantities (float4 each):
+// Backward pass of the causal prefill (bf16 inputs).  Per-row quantities (float4 each;
+// r0 and r1 of a row are adjacent in `rows`):
 //   r0 = {c*log2(e), lse*log2(e), c*A, c*E}   r1 = {A, E, dm, arg-max key (int bits)}
 //   rp = {dbeta contribution of the dq kernel, -dm, gate*tanh(ln n_eff), floor term of dbeta}
 // with c = beta*tau and dl_j = p_j (v_j.du + A + E p_j) + [j = arg-max] dm.
@@ -63,7 +64,8 @@ struct BwdArgs {
   float *dq, *dk, *dv;                    // fp32 [B,T,Hq,d], [B,T,Hkv,d] x2
   float *d_beta, *d_null_bias, *d_count_vec;
   uint16_t *du, *cdu;                     // workspace: bf16 du and c*du [B,T,Hq,d]
-  float *r0, *r1, *rp;                    // workspace: per-row float4
+  float *rows;                            // workspace: per-row r0, r1 (8 floats)
+  float *rp;                              // workspace: per-row float4
   float *part;                            // workspace: [Hq][n_part][kPartStride]
   int B, T, Hq, Hkv, G;
   int hb, n_row_blocks;                   // dq kernel: heads per workgroup, row blocks
