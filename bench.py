@@ -8,7 +8,10 @@ synthetic workloads of ``synth`` and are resident in HBM before timing starts.
 
 Prints one JSON line.  ``value`` is prefill TFLOP/s over the timed steps, with the
 algorithmic flop count 4*d*Hq*T(T+1)/2 (QK^T and PV over visible pairs only); the decode
-figure (GB/s of K+V read once, plus table, queries and outputs) sits in ``decode``.
+figure (GB/s of K+V read once, plus table, queries and outputs) sits in ``decode``.  After
+the timed steps, the backward pass is timed on its own at the 2K training shape and
+reported in ``backward`` (TFLOP/s over the five products of the gradient, 2.5x the
+forward count).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
        python bench.py --copy-probe BYTES   (plain device copy, for counter calibration)
@@ -37,6 +40,7 @@ PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
 KERNEL_SOURCES = {
     "prefill": ["polar_prefill.hip", "polar_mfma.h", "polar_kernels.h"],
     "decode": ["polar_decode.hip", "polar_mfma.h", "polar_kernels.h"],
+    "backward": ["polar_backward.hip", "polar_mfma.h", "polar_kernels.h"],
 }
 
 
@@ -51,6 +55,11 @@ def src_hash(kind: str) -> str:
 
 def prefill_flops(B, T, Hq, d):
     return 4.0 * d * B * Hq * T * (T + 1) / 2.0
+
+
+def backward_flops(B, T, Hq, d):
+    """Five products over visible pairs (S = QK^T, dP = du V^T, dV, dK, dQ): 2.5x forward."""
+    return 2.5 * prefill_flops(B, T, Hq, d)
 
 
 def decode_bytes(B, L, Hq, Hkv, d, page, stride):
@@ -105,6 +114,62 @@ def cpu_baseline(pre, dec):
                       f"({t_pre:.1f} s)",
             "decode": {"value": dbytes / t_dec / 1e9, "unit": "GB/s",
                        "sample": f"decode, all {len(batches)} sequences ({t_dec:.1f} s)"}}
+
+
+def measure_backward(dev, steps: int, warmup: int, with_cpu: bool):
+    """Training forward + backward at the 2K training shape (B=8, T=2048, 16/4 heads)."""
+    import torch
+    import synth
+    from long_context_lm_amd import attn_bwd, attn_fwd_train, bwd_workspace_bytes
+    p = synth.prefill_inputs("c2")
+
+    def to_dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = to_dev(p.q), to_dev(p.k), to_dev(p.v)
+    kw = dict(beta=torch.from_numpy(p.beta).to(dev), null_bias=torch.from_numpy(p.null_bias).to(dev),
+              count_vec=torch.from_numpy(p.count_vec).to(dev), train_len=p.train_len, flags=p.flags)
+    cot_np = synth.cotangents(p.B, p.T, p.Hq, p.d).as_dict()
+    cot = {n: torch.from_numpy(x).to(dev) for n, x in cot_np.items()}
+    ws = torch.empty(bwd_workspace_bytes(p.Hq, p.Hkv, p.B, p.T), dtype=torch.uint8, device=dev)
+    fwd = attn_fwd_train(q, k, v, **kw)
+    for _ in range(warmup):
+        attn_fwd_train(q, k, v, **kw)
+        attn_bwd(q, k, v, fwd, cot, workspace=ws, **kw)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for e in ev:
+        e[0].record()
+        fwd = attn_fwd_train(q, k, v, **kw)
+        e[1].record()
+        attn_bwd(q, k, v, fwd, cot, workspace=ws, **kw)
+        e[2].record()
+    torch.cuda.synchronize()
+    f_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    b_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    Fb = backward_flops(p.B, p.T, p.Hq, p.d)
+    tf = Fb / (b_ms * 1e-3) / 1e12
+    rec = {"workload": "backward of the causal prefill, B=8 T=2048 Hq=16 Hkv=4 d=64 bf16 "
+                       "(2K training shape), all five cotangents, parameter gradients on",
+           "value": round(tf, 2), "unit": "TFLOP/s", "bwd_ms": round(b_ms, 4),
+           "fwd_train_ms": round(f_ms, 4),
+           "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                        "traffic": traffic_record("backward")}}
+    print(f"[bench] backward mean {b_ms:.3f} ms ({tf:.1f} TFLOP/s), training forward "
+          f"{f_ms:.3f} ms", file=sys.stderr, flush=True)
+    if with_cpu:
+        import oracle
+        t0 = time.perf_counter()
+        oracle.polar_prefill_grad(p.as_f32("q"), p.as_f32("k"), p.as_f32("v"), cot_np, p.beta,
+                                  p.null_bias, p.count_vec, p.train_len, p.flags)
+        t = time.perf_counter() - t0
+        rec["cpu_baseline"] = {"value": round(backward_flops(p.B, p.T, p.Hq, p.d) / t / 1e12, 5),
+                               "unit": "TFLOP/s", "cores": int(torch.get_num_threads()),
+                               "kind": "oracle",
+                               "sample": f"float64 autograd backward of the whole workload, "
+                                         f"all 8 sequences ({t:.1f} s)"}
+    return rec
 
 
 def copy_probe(nbytes: int):
@@ -215,6 +280,10 @@ def main():
                                 "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                                 "traffic": tr_dec}},
     }
+    del q, k, v, qd, kc, vc, table, lens, ws
+    torch.cuda.empty_cache()
+    rec["backward"] = measure_backward(dev, max(1, args.steps // 2), args.warmup,
+                                       not args.no_cpu_baseline)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(pre, dec)
