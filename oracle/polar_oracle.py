@@ -75,18 +75,23 @@ def null_floor(n, beta_h: float, tau, d: int, null_bias_h: float, on: bool) -> n
 
 def _polar_rows(Qr: np.ndarray, K: np.ndarray, V: np.ndarray, n_vis: np.ndarray,
                 beta_h: float, null_bias_h: float, w_h: np.ndarray, train_len: int,
-                flags: int) -> dict:
-    """Polar outputs for query rows Qr [R,d] attending keys K[:n_vis[r]] (float64).
+                flags: int, lo: Optional[np.ndarray] = None) -> dict:
+    """Polar outputs for query rows Qr [R,d] attending keys K[lo[r]:n_vis[r]] (float64).
 
-    Full score rows are formed (no streaming): scores, mask, max, exponentials, then the
-    normalised probabilities in a second pass.
+    ``lo`` (default 0) is the first visible key of each row; the row sees n = n_vis - lo
+    keys, and that n drives the temperature and the floor.  Full score rows are formed (no
+    streaming): scores, mask, max, exponentials, then the normalised probabilities in a
+    second pass.
     """
     R, d = Qr.shape
+    lo = np.zeros_like(n_vis) if lo is None else np.asarray(lo)
+    n_keys = n_vis - lo
     nmax = int(n_vis.max())
     S = Qr @ K[:nmax].T                                        # raw cosines [R, nmax]
-    tau = length_temperature(n_vis, train_len, bool(flags & FLAG_LENGTH_TEMP))
+    tau = length_temperature(n_keys, train_len, bool(flags & FLAG_LENGTH_TEMP))
     logits = (beta_h * tau)[:, None] * S
-    visible = np.arange(nmax)[None, :] < n_vis[:, None]
+    cols = np.arange(nmax)[None, :]
+    visible = (cols < n_vis[:, None]) & (cols >= lo[:, None])
     logits = np.where(visible, logits, -np.inf)
     m = logits.max(axis=1)                                     # row maximum logit
     e = np.exp(logits - m[:, None])                            # masked entries -> 0
@@ -97,10 +102,28 @@ def _polar_rows(Qr: np.ndarray, K: np.ndarray, V: np.ndarray, n_vis: np.ndarray,
     u = p @ V[:nmax]                                           # matched value sum
     norm = np.sqrt(np.sum(u * u, axis=1))
     dir_ = np.divide(u, norm[:, None], out=np.zeros_like(u), where=norm[:, None] > 0)
-    floor = null_floor(n_vis, beta_h, tau, d, null_bias_h, bool(flags & FLAG_NULL_FLOOR))
+    floor = null_floor(n_keys, beta_h, tau, d, null_bias_h, bool(flags & FLAG_NULL_FLOOR))
     gate = expit(m - floor)
     count = (gate * np.tanh(np.log(n_eff)))[:, None] * np.asarray(w_h, np.float64)[None, :]
-    return dict(dir=dir_, count=count, n_eff=n_eff, gate=gate, lse=lse, u_norm=norm)
+    return dict(dir=dir_, count=count, n_eff=n_eff, gate=gate, lse=lse, u_norm=norm, attn=u)
+
+
+def rope(x: np.ndarray, theta: float, positions: Optional[np.ndarray] = None) -> np.ndarray:
+    """Rotary position embedding of RoFormer (Su et al.): for each pair of dimensions
+    (2t, 2t+1) a rotation by the angle pos * theta**(-2t/d).  x [B,T,H,d]; position of
+    row t is t unless ``positions`` [T] says otherwise.  float64."""
+    x = np.asarray(x, np.float64)
+    d = x.shape[-1]
+    pos = np.arange(x.shape[1], dtype=np.float64) if positions is None else \
+        np.asarray(positions, np.float64)
+    freq = theta ** (-np.arange(0, d, 2, dtype=np.float64) / d)          # [d/2]
+    ang = pos[:, None] * freq[None, :]                                    # [T, d/2]
+    c, s = np.cos(ang)[None, :, None, :], np.sin(ang)[None, :, None, :]
+    x0, x1 = x[..., 0::2], x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = x0 * c - x1 * s
+    out[..., 1::2] = x0 * s + x1 * c
+    return out
 
 
 def _params(Hq, d, beta, null_bias, count_vec):
@@ -114,16 +137,23 @@ def _params(Hq, d, beta, null_bias, count_vec):
 def polar_prefill(q, k, v, beta=None, null_bias=None, count_vec=None, train_len: int = 2048,
                   flags: int = FLAG_LENGTH_TEMP | FLAG_NULL_FLOOR,
                   rows: Optional[np.ndarray] = None, heads: Optional[np.ndarray] = None,
-                  batches: Optional[np.ndarray] = None, max_elems: int = 1 << 24) -> dict:
+                  batches: Optional[np.ndarray] = None, max_elems: int = 1 << 24,
+                  window: int = 0, rope_theta: float = 0.0) -> dict:
     """Causal Polar Attention prefill.
+
+    Variants: ``window`` W >= 1 restricts row i to keys max(0, i-W+1)..i (so it sees
+    n = min(i+1, W) keys); ``rope_theta`` > 0 rotates q and k by RoPE at their positions
+    before the scores.  ``attn`` is the plain softmax attention output sum_j p_j v_j.
 
     q [B,T,Hq,d], k and v [B,T,Hkv,d] (any float dtype; computed in float64).
     Row i of head h sees keys 0..i of KV head h // (Hq // Hkv).
     ``rows``/``heads``/``batches`` restrict the computation to a sample; the outputs are
     then indexed [len(batches), len(rows), len(heads), ...].
-    Returns float64 dir, count [B,R,H,d] and n_eff, gate, lse [B,R,H], plus u_norm [B,R,H],
-    the norm |u| of the matched value sum (a residual of the backward pass).
+    Returns float64 dir, count, attn [B,R,H,d] and n_eff, gate, lse [B,R,H], plus u_norm
+    [B,R,H], the norm |u| of the matched value sum (a residual of the backward pass).
     """
+    if rope_theta > 0:
+        q, k = rope(q, rope_theta), rope(k, rope_theta)
     q = np.asarray(q)
     B, T, Hq, d = q.shape
     Hkv = k.shape[2]
@@ -136,7 +166,7 @@ def polar_prefill(q, k, v, beta=None, null_bias=None, count_vec=None, train_len:
     R, H, Bs = len(rows), len(heads), len(batches)
     out = dict(dir=np.zeros((Bs, R, H, d)), count=np.zeros((Bs, R, H, d)),
                n_eff=np.zeros((Bs, R, H)), gate=np.zeros((Bs, R, H)), lse=np.zeros((Bs, R, H)),
-               u_norm=np.zeros((Bs, R, H)))
+               u_norm=np.zeros((Bs, R, H)), attn=np.zeros((Bs, R, H, d)))
     for bi, b in enumerate(batches):
         for hi, h in enumerate(heads):
             g = h // G
@@ -151,8 +181,9 @@ def polar_prefill(q, k, v, beta=None, null_bias=None, count_vec=None, train_len:
                     n_hi = max(n_hi, int(rows[r1]) + 1)
                     r1 += 1
                 sel = rows[r0:r1]
+                lo = np.maximum(0, sel - window + 1) if window > 0 else None
                 res = _polar_rows(np.asarray(q[b, sel, h], np.float64), K, V, sel + 1,
-                                  beta[h], null_bias[h], count_vec[h], train_len, flags)
+                                  beta[h], null_bias[h], count_vec[h], train_len, flags, lo)
                 for key in out:
                     out[key][bi, r0:r1, hi] = res[key]
                 r0 = r1
