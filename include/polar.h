@@ -110,6 +110,34 @@ POLAR_API polar_status polar_attn_fwd(const polar_params *p, polar_dtype dt, int
                             const polar_outputs *out, void *stream);
 
 /*
+ * Variant modes of the prefill (the comparison arms and position schemes the pages
+ * evaluate alongside Polar Attention: a plain softmax read-out, RoPE, sliding-window
+ * attention).
+ *   window      W >= 1: row i attends keys max(0, i-W+1)..i and n = min(i+1, W) is the key
+ *               count that drives tau and the floor; 0 = all earlier keys.
+ *   rope_theta  > 0: q and k are rotated on load by rotary position embeddings (RoFormer
+ *               form: the pair of dimensions (2t, 2t+1) of the vector at position p turns
+ *               by the angle p * rope_theta^(-2t/d)); positions are the row indices 0..T-1.
+ *               0 = no rotation.
+ *   attn        optional device float32 [B,T,Hq,d], 16-byte aligned: the plain softmax
+ *               attention output u = sum_j p_j v_j.  NULL = not written.
+ */
+typedef struct {
+  int32_t window;
+  float rope_theta;
+  float *attn;
+} polar_variant;
+
+/*
+ * polar_attn_fwd with the variant modes above.  Same arguments, outputs and conventions
+ * as polar_attn_fwd; var == NULL, or all fields zero, gives polar_attn_fwd's results.
+ */
+POLAR_API polar_status polar_attn_fwd_variant(const polar_params *p, const polar_variant *var,
+                                    polar_dtype dt, int32_t B, int32_t T, const void *q,
+                                    const void *k, const void *v, const polar_outputs *out,
+                                    void *stream);
+
+/*
  * Workspace bytes polar_attn_decode_paged needs for this batch size and length bound
  * (0 on invalid arguments).  The value depends only on the arguments.
  */

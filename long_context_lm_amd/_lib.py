@@ -29,6 +29,7 @@ POLAR_FLAG_NULL_FLOOR = 2
 
 EXPORTS = ("polar_attn_fwd", "polar_decode_workspace_bytes", "polar_attn_decode_paged",
            "polar_attn_fwd_train", "polar_bwd_workspace_bytes", "polar_attn_bwd",
+           "polar_attn_fwd_variant",
            "polar_status_str", "polar_last_error", "polar_abi_version")
 
 
@@ -43,6 +44,11 @@ class polar_outputs(ctypes.Structure):
     _fields_ = [("dir", ctypes.c_void_p), ("count", ctypes.c_void_p),
                 ("n_eff", ctypes.c_void_p), ("gate", ctypes.c_void_p),
                 ("lse", ctypes.c_void_p)]
+
+
+class polar_variant(ctypes.Structure):
+    _fields_ = [("window", ctypes.c_int32), ("rope_theta", ctypes.c_float),
+                ("attn", ctypes.c_void_p)]
 
 
 class polar_saved(ctypes.Structure):
@@ -98,6 +104,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.polar_attn_bwd.argtypes = [P(polar_params), I32, I32, I32, VP, VP, VP, P(polar_outputs),
                                    P(polar_saved), P(polar_cotangents), P(polar_grads), VP, SZ,
                                    VP]
+    lib.polar_attn_fwd_variant.restype = I32
+    lib.polar_attn_fwd_variant.argtypes = [P(polar_params), P(polar_variant), I32, I32, I32, VP,
+                                           VP, VP, P(polar_outputs), VP]
     lib.polar_status_str.restype = ctypes.c_char_p
     lib.polar_status_str.argtypes = [I32]
     lib.polar_last_error.restype = ctypes.c_char_p
@@ -143,6 +152,12 @@ def polar_attn_decode_paged(params, dtype, B, q, k_cache, v_cache, num_pages, pa
 def polar_attn_fwd_train(params, dtype, B, T, q, k, v, outputs, saved, stream) -> int:
     return load().polar_attn_fwd_train(ctypes.byref(params), dtype, B, T, q, k, v,
                                        ctypes.byref(outputs), ctypes.byref(saved), stream)
+
+
+def polar_attn_fwd_variant(params, variant, dtype, B, T, q, k, v, outputs, stream) -> int:
+    return load().polar_attn_fwd_variant(ctypes.byref(params),
+                                         None if variant is None else ctypes.byref(variant),
+                                         dtype, B, T, q, k, v, ctypes.byref(outputs), stream)
 
 
 def polar_bwd_workspace_bytes(params, B, T) -> int:

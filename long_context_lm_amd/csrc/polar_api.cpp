@@ -70,9 +70,17 @@ namespace {
 
 polar_status prefill(const polar_params *p, polar_dtype dt, int32_t B, int32_t T, const void *q,
                      const void *k, const void *v, const polar_outputs *out,
-                     const polar_saved *saved, void *stream) {
+                     const polar_saved *saved, const polar_variant *var, void *stream) {
   polar_status st = check_params(p, dt, out);
   if (st != POLAR_OK) return st;
+  if (var) {
+    if (var->window < 0) return fail(POLAR_ERR_BAD_SHAPE, "window (%d) must be >= 0", var->window);
+    if (!(var->rope_theta >= 0.f) || !isfinite(var->rope_theta) ||
+        (var->rope_theta > 0.f && var->rope_theta <= 1.f))
+      return fail(POLAR_ERR_BAD_SHAPE, "rope_theta must be 0 or a finite value > 1");
+    if (var->attn && !aligned16(var->attn))
+      return fail(POLAR_ERR_MISALIGNED, "variant attn output must be 16-byte aligned");
+  }
   if (B < 0 || T < 0) return fail(POLAR_ERR_BAD_SHAPE, "B (%d) and T (%d) must be >= 0", B, T);
   if (B == 0 || T == 0) return POLAR_OK;
   st = check_outputs(p, out);
@@ -107,6 +115,20 @@ polar_status prefill(const polar_params *p, polar_dtype dt, int32_t B, int32_t T
   a.lse = out->lse;
   a.u_norm = saved ? saved->u_norm : nullptr;
   a.arg_max = saved ? saved->arg_max : nullptr;
+  a.attn = var ? var->attn : nullptr;
+  a.window = var ? var->window : 0;
+  a.rope = (var && var->rope_theta > 0.f) ? 1 : 0;
+  a.variant = (a.attn || a.window > 0 || a.rope) ? 1 : 0;
+  for (int t = 0; t < polar::kHeadDim / 2; ++t) {
+    a.rope_f[t] = 0;
+    if (a.rope) {
+      // revolutions per position of pair t, rounded to 2^-64 units (< 1/(2 pi), fits)
+      const long double f = powl((long double)var->rope_theta,
+                                 -2.0L * t / polar::kHeadDim) /
+                            (2.0L * 3.14159265358979323846264338327950288L);
+      a.rope_f[t] = (uint64_t)(f * 18446744073709551616.0L + 0.5L);
+    }
+  }
   a.B = B;
   a.T = T;
   a.Hq = p->n_q_heads;
@@ -140,7 +162,14 @@ extern "C" {
 polar_status polar_attn_fwd(const polar_params *p, polar_dtype dt, int32_t B, int32_t T,
                             const void *q, const void *k, const void *v,
                             const polar_outputs *out, void *stream) {
-  return prefill(p, dt, B, T, q, k, v, out, nullptr, stream);
+  return prefill(p, dt, B, T, q, k, v, out, nullptr, nullptr, stream);
+}
+
+polar_status polar_attn_fwd_variant(const polar_params *p, const polar_variant *var,
+                                    polar_dtype dt, int32_t B, int32_t T, const void *q,
+                                    const void *k, const void *v, const polar_outputs *out,
+                                    void *stream) {
+  return prefill(p, dt, B, T, q, k, v, out, nullptr, var, stream);
 }
 
 polar_status polar_attn_fwd_train(const polar_params *p, polar_dtype dt, int32_t B, int32_t T,
@@ -148,7 +177,7 @@ polar_status polar_attn_fwd_train(const polar_params *p, polar_dtype dt, int32_t
                                   const polar_outputs *out, const polar_saved *saved,
                                   void *stream) {
   if (!saved) return fail(POLAR_ERR_NULL_POINTER, "saved is NULL");
-  return prefill(p, dt, B, T, q, k, v, out, saved, stream);
+  return prefill(p, dt, B, T, q, k, v, out, saved, nullptr, stream);
 }
 
 size_t polar_bwd_workspace_bytes(const polar_params *p, int32_t B, int32_t T) {

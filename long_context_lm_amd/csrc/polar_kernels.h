@@ -16,6 +16,12 @@ struct PrefillArgs {
   float *dir, *count, *n_eff, *gate, *lse;
   float *u_norm;                          // [B,T,Hq] |u| for the backward pass, or NULL
   int32_t *arg_max;                       // [B,T,Hq] first key of the row maximum (with u_norm)
+  // Variant modes (variant instances only):
+  float *attn;                            // [B,T,Hq,d] plain softmax output sum p v, or NULL
+  int variant;                            // 1: launch the variant instance
+  int window;                             // W >= 1: row i sees keys i-W+1..i; 0: all
+  int rope;                               // 1: rotate q and k by RoPE on load
+  uint64_t rope_f[kHeadDim / 2];          // revolutions per position of pair t, 2^-64 units
   int B, T, Hq, Hkv, G;                   // G = Hq / Hkv
   int hb;                                 // query heads per workgroup (divides G, <= 4)
   int n_row_blocks;                       // ceil(T / rows per workgroup)

@@ -21,9 +21,12 @@
 //    Raising the reference rescales S and u by 2^(M_old-M_new) and Q by its square, the
 //    squared correction factor of section 2.2;
 //  * epilogue: n_eff = S^2/Q, lse, the floor gate, dir = u/|u|, count;
-//  * training instances (kSave) also keep, per lane, the first key attaining the lane's
-//    running maximum score and write |u| and that key (the row's arg-max) for the
-//    backward pass.
+//  * training instances (kMode == kModeSave) also keep, per lane, the first key attaining
+//    the lane's running maximum score and write |u| and that key (the row's arg-max) for
+//    the backward pass;
+//  * variant instances (kMode == kModeVariant) add a sliding window, RoPE applied to q at
+//    load and to each K tile while it is staged into LDS, and the plain softmax output;
+//    every tile goes through the masked path.
 #include "polar_kernels.h"
 #include "polar_mfma.h"
 
@@ -60,8 +63,19 @@ template <> struct LdsCfg<Bf16> {
 };
 template <> struct LdsCfg<F32> { static constexpr int kt = 64, krow = 68, vrow = 65; };
 
-template <class TR, int QB, int kWaves, bool kSave>
+constexpr int kModePlain = 0, kModeSave = 1, kModeVariant = 2;
+
+// RoPE rotation angle of pair t at position pos: revolutions = frac(pos * f_t) taken
+// exactly from the 64-bit fixed-point product, then sin/cos of 2*pi*revolutions.
+__device__ __forceinline__ void rope_cs(uint64_t f, int pos, float &c, float &s) {
+  const uint32_t hi = (uint32_t)(((uint64_t)(uint32_t)pos * f) >> 32);
+  sincospif(2.0f * ((float)hi * 2.3283064365386963e-10f), &s, &c);
+}
+
+template <class TR, int QB, int kWaves, int kMode>
 __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs a) {
+  constexpr bool kSave = kMode == kModeSave;
+  constexpr bool kVar = kMode == kModeVariant;
   constexpr int kThreads = 64 * kWaves;
   constexpr int kKT = LdsCfg<TR>::kt;                // keys per tile
   constexpr int NKB = kKT / 32;                      // 32-key MFMA blocks per tile
@@ -110,8 +124,9 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int row = wrow0 + qb * 32 + c32;
+    const int nk = (kVar && a.window > 0) ? min(row + 1, a.window) : row + 1;
     const float tau =
-        a.inv_log_train > 0.f ? fmaxf(1.0f, logf((float)(row + 1)) * a.inv_log_train) : 1.0f;
+        a.inv_log_train > 0.f ? fmaxf(1.0f, logf((float)nk) * a.inv_log_train) : 1.0f;
     cnat[qb] = beta * tau;
     cl2[qb] = cnat[qb] * kLog2e;
   }
@@ -125,6 +140,29 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
     const E *qp = (const E *)a.q + (((size_t)b * a.T + (ok ? row : 0)) * a.Hq + h) * kD + g32 * KPL;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) qf[qb][ks] = ok ? TR::load(qp + ks * KSTEP) : TR::zero();
+    if constexpr (kVar) {
+      if (a.rope) {
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          if constexpr (KPL == 8) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+              float c, sn;
+              rope_cs(a.rope_f[ks * 8 + g32 * 4 + m], row, c, sn);
+              const float x0 = (float)qf[qb][ks][2 * m], x1 = (float)qf[qb][ks][2 * m + 1];
+              qf[qb][ks][2 * m] = (__bf16)(x0 * c - x1 * sn);
+              qf[qb][ks][2 * m + 1] = (__bf16)(x0 * sn + x1 * c);
+            }
+          } else {
+            // fp32: lanes l and l^32 hold the two elements of pair ks.
+            float c, sn;
+            rope_cs(a.rope_f[ks], row, c, sn);
+            const float x = qf[qb][ks], other = half_other(x);
+            qf[qb][ks] = x * c + (g32 ? other * sn : -other * sn);
+          }
+        }
+      }
+    }
   }
 
   f32x16 o[QB][2];
@@ -170,8 +208,10 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
   typedef uint32_t vchunk_t __attribute__((ext_vector_type(KPL == 8 ? 2 : 4)));
   u32x4 kst[NK];
   vchunk_t vst[NV][VKEYS];
+  int staged_key0 = 0;                               // variant: position of the staged tile
   auto stage_load = [&](int t) {
     const int key0 = t * kKT;
+    staged_key0 = key0;
 #pragma unroll
     for (int j = 0; j < NK; ++j) {
       const int ch = min(tid + kThreads * j, KTASKS - 1);
@@ -202,6 +242,29 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
     for (int j = 0; j < NK; ++j) {
       const int ch = tid + kThreads * j;
       const int key = ch / CPR, part = ch % CPR;
+      if constexpr (kVar) {
+        if (a.rope) {
+          // Rotate the staged chunk: pairs (2t, 2t+1) of key position staged_key0 + key.
+          const int pos = staged_key0 + key;
+#pragma unroll
+          for (int m = 0; m < (KPL == 8 ? 4 : 2); ++m) {
+            float c, sn, x0, x1;
+            if constexpr (KPL == 8) {
+              rope_cs(a.rope_f[part * 4 + m], pos, c, sn);
+              x0 = __uint_as_float(kst[j][m] << 16);
+              x1 = __uint_as_float(kst[j][m] & 0xFFFF0000u);
+              const bf16x2 r = {(__bf16)(x0 * c - x1 * sn), (__bf16)(x0 * sn + x1 * c)};
+              kst[j][m] = __builtin_bit_cast(uint32_t, r);
+            } else {
+              rope_cs(a.rope_f[part * 2 + m], pos, c, sn);
+              x0 = __uint_as_float(kst[j][2 * m]);
+              x1 = __uint_as_float(kst[j][2 * m + 1]);
+              kst[j][2 * m] = __float_as_uint(x0 * c - x1 * sn);
+              kst[j][2 * m + 1] = __float_as_uint(x0 * sn + x1 * c);
+            }
+          }
+        }
+      }
       if (NK * kThreads == KTASKS || ch < KTASKS)
         *(u32x4 *)&Ks[slot][key * KROW + part * VEC] = kst[j];
     }
@@ -290,7 +353,9 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * g32 + (r & 3);
-          if (key > row) S.v[qb][kb][r] = -INFINITY;
+          bool masked = key > row;
+          if constexpr (kVar) masked = masked || (a.window > 0 && key <= row - a.window);
+          if (masked) S.v[qb][kb][r] = -INFINITY;
         }
     }
   };
@@ -408,11 +473,14 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
   // issued a whole step earlier, so no VALU instruction waits on a recent MFMA result.
   // Tiles fully below the workgroup's first row need no mask; the diagonal tiles run one
   // at a time.  K and V use four LDS slots: tile t+3 is stored while tiles t..t+2 are live.
-  const int nfull = min((row0 + 1) / kKT, ntiles);
+  // Variant instances start at the first tile any row of the workgroup can see and run
+  // every tile through the masked path.
+  const int t0 = (kVar && a.window > 0) ? max(0, row0 - a.window + 1) / kKT : 0;
+  const int nfull = kVar ? 0 : min((row0 + 1) / kKT, ntiles);
 
-  for (int j = 0; j < 3 && j < ntiles; ++j) {
+  for (int j = t0; j < t0 + 3 && j < ntiles; ++j) {
     stage_load(j);
-    stage_store(j, j);
+    stage_store(j % 4, j % 4);
   }
   __syncthreads();
 
@@ -456,7 +524,7 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
     __syncthreads();
   };
 
-  int t = 0;
+  int t = t0;
   while (t < nfull) {
     pipe_step(t, Sa, Sb, Sc);
     if (++t >= nfull) break;
@@ -469,7 +537,9 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
     const bool stage = t + 3 < ntiles;
     if (stage) stage_load(t + 3);
     const int key0 = t * kKT;
-    if (key0 <= w_last) {
+    bool live = key0 <= w_last;
+    if constexpr (kVar) live = live && (a.window == 0 || key0 + kKT > wrow0 - a.window + 1);
+    if (live) {
       score(t % 4, Sa);
       mask(Sa, key0);
       first_max(Sa, key0);
@@ -510,7 +580,8 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
       const float lse = (Mref[qb] + log2f(St)) * kLn2;
       const float m_nat = smax[qb] * cnat[qb];
       float floor_ = bias;
-      if (a.null_floor) floor_ += cnat[qb] * 0.125f * sqrtf(2.0f * logf((float)(row + 1)));
+      const int nk = (kVar && a.window > 0) ? min(row + 1, a.window) : row + 1;
+      if (a.null_floor) floor_ += cnat[qb] * 0.125f * sqrtf(2.0f * logf((float)nk));
       const float gate = 1.0f / (1.0f + expf(floor_ - m_nat));
       const float n2 = neff * neff;
       const float th = (n2 - 1.0f) / (n2 + 1.0f);
@@ -527,6 +598,22 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
           for (int c = 0; c < 4; ++c) val[c] = o[qb][db][4 * j4 + c] * inv;
           *(f32x4 *)(dp + dim0) = val;
         }
+      if constexpr (kVar) {
+        if (a.attn) {
+          const float is = 1.0f / St;
+          float *ap = a.attn + obase * kD;
+#pragma unroll
+          for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int j4 = 0; j4 < 4; ++j4) {
+              const int dim0 = db * 32 + 8 * j4 + 4 * g32;
+              f32x4 val;
+#pragma unroll
+              for (int c = 0; c < 4; ++c) val[c] = o[qb][db][4 * j4 + c] * is;
+              *(f32x4 *)(ap + dim0) = val;
+            }
+        }
+      }
       if (a.count) {
         const float cg = gate * th;
         const float *wp = a.count_vec + (size_t)h * kD;
@@ -584,19 +671,29 @@ hipError_t launch_prefill(int dtype, const PrefillArgs &a, hipStream_t stream) {
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   dim3 grid((unsigned)blocks);
-  const bool save = a.u_norm != nullptr;
-  if (dtype == 1 && !save)
-    hipLaunchKernelGGL((polar_prefill_kernel<Bf16, kQbBf16, kWavesBf16, false>), grid,
-                       dim3(64 * kWavesBf16), 0, stream, a);
-  else if (dtype == 1)
-    hipLaunchKernelGGL((polar_prefill_kernel<Bf16, kQbBf16, kWavesBf16, true>), grid,
-                       dim3(64 * kWavesBf16), 0, stream, a);
-  else if (!save)
-    hipLaunchKernelGGL((polar_prefill_kernel<F32, kQbF32, kWavesF32, false>), grid,
-                       dim3(64 * kWavesF32), 0, stream, a);
-  else
-    hipLaunchKernelGGL((polar_prefill_kernel<F32, kQbF32, kWavesF32, true>), grid,
-                       dim3(64 * kWavesF32), 0, stream, a);
+  const int mode = a.variant ? kModeVariant : (a.u_norm != nullptr ? kModeSave : kModePlain);
+  const dim3 bb(64 * kWavesBf16), bf(64 * kWavesF32);
+  if (dtype == 1) {
+    if (mode == kModePlain)
+      hipLaunchKernelGGL((polar_prefill_kernel<Bf16, kQbBf16, kWavesBf16, kModePlain>), grid, bb,
+                         0, stream, a);
+    else if (mode == kModeSave)
+      hipLaunchKernelGGL((polar_prefill_kernel<Bf16, kQbBf16, kWavesBf16, kModeSave>), grid, bb,
+                         0, stream, a);
+    else
+      hipLaunchKernelGGL((polar_prefill_kernel<Bf16, kQbBf16, kWavesBf16, kModeVariant>), grid,
+                         bb, 0, stream, a);
+  } else {
+    if (mode == kModePlain)
+      hipLaunchKernelGGL((polar_prefill_kernel<F32, kQbF32, kWavesF32, kModePlain>), grid, bf, 0,
+                         stream, a);
+    else if (mode == kModeSave)
+      hipLaunchKernelGGL((polar_prefill_kernel<F32, kQbF32, kWavesF32, kModeSave>), grid, bf, 0,
+                         stream, a);
+    else
+      hipLaunchKernelGGL((polar_prefill_kernel<F32, kQbF32, kWavesF32, kModeVariant>), grid, bf,
+                         0, stream, a);
+  }
   return hipGetLastError();
 }
 

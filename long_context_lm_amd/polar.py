@@ -104,6 +104,26 @@ def attn_fwd_train(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta=None,
     return out
 
 
+def attn_fwd_variant(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, window: int = 0,
+                     rope_theta: float = 0.0, want_attn: bool = True, beta=None,
+                     null_bias=None, count_vec=None, train_len: int = 2048,
+                     flags: int = _lib.POLAR_FLAG_LENGTH_TEMP | _lib.POLAR_FLAG_NULL_FLOOR,
+                     stream=None) -> dict:
+    """Prefill with the variant modes: sliding ``window``, RoPE on load (``rope_theta``) and
+    the plain softmax output ("attn", when ``want_attn``)."""
+    prm, keep, (B, T, Hq, Hkv, d) = _prefill_args(q, k, v, beta, null_bias, count_vec,
+                                                  train_len, flags)
+    dev = q.device
+    out, cout = _outputs((B, T), Hq, d, dev, keep[2] is not None, True, True)
+    out["attn"] = (torch.empty(B, T, Hq, d, device=dev, dtype=torch.float32)
+                   if want_attn else None)
+    var = _lib.polar_variant(window, rope_theta, _ptr(out["attn"]))
+    s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+    _lib.check(_lib.polar_attn_fwd_variant(prm, var, _DT[q.dtype], B, T, q.data_ptr(),
+                                           k.data_ptr(), v.data_ptr(), cout, s))
+    return out
+
+
 def bwd_workspace_bytes(Hq: int, Hkv: int, B: int, T: int, d: int = 64) -> int:
     prm = _lib.polar_params(Hq, Hkv, d, 2048, 0, None, None, None)
     return _lib.polar_bwd_workspace_bytes(prm, B, T)

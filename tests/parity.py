@@ -34,10 +34,12 @@ def gpu_prefill(p: synth.PrefillInputs, **kw) -> dict:
     return out
 
 
-def oracle_prefill(p: synth.PrefillInputs, rows=None, heads=None, batches=None) -> dict:
+def oracle_prefill(p: synth.PrefillInputs, rows=None, heads=None, batches=None, window=0,
+                   rope_theta=0.0) -> dict:
     return oracle.polar_prefill(p.as_f32("q"), p.as_f32("k"), p.as_f32("v"), p.beta,
                                 p.null_bias, p.count_vec, p.train_len, p.flags, rows=rows,
-                                heads=heads, batches=batches)
+                                heads=heads, batches=batches, window=window,
+                                rope_theta=rope_theta)
 
 
 def gpu_decode(d: synth.DecodeInputs, **kw) -> dict:

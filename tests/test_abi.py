@@ -224,3 +224,28 @@ def test_fwd_train_validation():
     assert _lib.polar_attn_fwd_train(p, 1, 1, 8, A, A, A, outs(gate=None), saved(),
                                      None) == _lib.POLAR_ERR_NULL_POINTER
     assert _lib.polar_attn_fwd_train(p, 1, 0, 8, A, A, A, outs(), saved(), None) == _lib.POLAR_OK
+
+
+# ------------------------------------------------------------------ variant modes
+def var_fwd(window=0, theta=0.0, attn=None, **kw):
+    return _lib.polar_attn_fwd_variant(params(), _lib.polar_variant(window, theta, attn), 1,
+                                       kw.get("B", 1), kw.get("T", 8), A, A, A, outs(), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(window=-1), _lib.POLAR_ERR_BAD_SHAPE),
+    (dict(theta=-2.0), _lib.POLAR_ERR_BAD_SHAPE),
+    (dict(theta=0.5), _lib.POLAR_ERR_BAD_SHAPE),
+    (dict(theta=float("inf")), _lib.POLAR_ERR_BAD_SHAPE),
+    (dict(theta=float("nan")), _lib.POLAR_ERR_BAD_SHAPE),
+    (dict(attn=A + 4), _lib.POLAR_ERR_MISALIGNED),
+])
+def test_variant_validation_errors(kw, code):
+    assert var_fwd(**kw) == code
+    assert _lib.polar_last_error() != ""
+
+
+def test_variant_empty_calls():
+    assert var_fwd(window=16, theta=10000.0, attn=A, B=0) == _lib.POLAR_OK
+    assert _lib.polar_attn_fwd_variant(params(), None, 1, 1, 0, A, A, A, outs(), None) == \
+        _lib.POLAR_OK

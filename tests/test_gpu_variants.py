@@ -1,0 +1,64 @@
+"""GPU parity of the variant modes (sliding window, RoPE on load, plain softmax output)
+against the float64 oracle, through the C ABI.  Tolerances as in tests/parity.py; the
+plain softmax output uses the direction metric scaled by |attn|."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from parity import TOL, assert_close, gpu_prefill, host, oracle_prefill, select, to_dev
+from long_context_lm_amd import attn_fwd_variant
+
+pytestmark = pytest.mark.gpu
+
+
+def run(p, **var):
+    q, k, v = (to_dev(getattr(p, n), p.dtype) for n in ("q", "k", "v"))
+    out = attn_fwd_variant(q, k, v, beta=p.beta, null_bias=p.null_bias, count_vec=p.count_vec,
+                           train_len=p.train_len, flags=p.flags, **var)
+    torch.cuda.synchronize()
+    return out
+
+
+def check(p, got, want, label, heads=None):
+    assert_close(got, want, p.count_vec, p.dtype, heads=heads, label=label)
+    a, w = host(got["attn"]), want["attn"]
+    err = float(np.max(np.linalg.norm(a - w, axis=-1) / np.linalg.norm(w, axis=-1)))
+    print(f"[variant] {label} attn {err:.2e}", flush=True)
+    assert err <= TOL[p.dtype], (label, err)
+
+
+@pytest.mark.parametrize("cfg,B,T,Hq,Hkv,window,theta", [
+    ("c2", 2, 300, 8, 2, 100, 0.0),          # window only, ragged
+    ("c2", 1, 257, 4, 4, 1, 0.0),            # window 1: closed forms
+    ("c2", 1, 200, 8, 2, 0, 10000.0),        # RoPE only
+    ("c2", 1, 333, 16, 4, 64, 500.0),        # window + RoPE, GQA 4
+    ("c2", 1, 130, 4, 2, 200, 0.0),          # window >= T
+    ("c1", 1, 256, 4, 4, 37, 10000.0),       # float32 inputs
+    ("c1", 1, 100, 4, 2, 0, 0.0),            # float32, softmax output only
+])
+def test_variant_parity(gpu_lib, cfg, B, T, Hq, Hkv, window, theta):
+    print(f"[case] variant {cfg} B={B} T={T} {Hq}/{Hkv} W={window} theta={theta}", flush=True)
+    p = synth.prefill_inputs(cfg, B=B, T=T, Hq=Hq, Hkv=Hkv, train_len=64)
+    got = run(p, window=window, rope_theta=theta)
+    want = oracle_prefill(p, window=window, rope_theta=theta)
+    check(p, got, want, f"{cfg} W={window} theta={theta}")
+
+
+def test_variant_without_modes_equals_plain_forward(gpu_lib):
+    p = synth.prefill_inputs("c2", B=1, T=200, Hq=8, Hkv=2, train_len=64)
+    a = run(p, want_attn=False)
+    b = gpu_prefill(p)
+    for n in ("dir", "count", "n_eff", "gate", "lse"):
+        assert torch.equal(a[n], b[n]), n
+
+
+def test_variant_full_size_sampled(gpu_lib):
+    """T = 64K extrapolation workload with RoPE and a 4096-key window, sampled rows."""
+    print("[case] variant C4 W=4096 theta=10000 sampled", flush=True)
+    p = synth.prefill_inputs("c4")
+    got = run(p, window=4096, rope_theta=10000.0)
+    rows = np.array([0, 1, 63, 64, 4095, 4096, 4097, 30000, 65534, 65535])
+    heads = np.array([0, 5, 10, 15])
+    want = oracle_prefill(p, rows=rows, heads=heads, window=4096, rope_theta=10000.0)
+    check(p, select(got, rows=rows, heads=heads), want, "C4 W=4096 rope", heads=heads)
