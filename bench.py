@@ -172,6 +172,45 @@ def measure_backward(dev, steps: int, warmup: int, with_cpu: bool):
     return rec
 
 
+def visible_pairs(T: int, window: int) -> float:
+    """Sum over rows i of the keys row i sees: i+1, or min(i+1, W) with a window."""
+    if window <= 0 or window >= T:
+        return T * (T + 1) / 2.0
+    return window * (window + 1) / 2.0 + float(T - window) * window
+
+
+def measure_variants(dev, q, k, v, pkw, pre, steps: int, warmup: int):
+    """The variant modes on the T=64K workload: RoPE + softmax output over the full causal
+    range, and RoPE with a 4096-key sliding window."""
+    import torch
+    from long_context_lm_amd import attn_fwd_variant
+    res = {}
+    for name, var in (("rope_softmax_out", dict(window=0, rope_theta=10000.0)),
+                      ("rope_window4096", dict(window=4096, rope_theta=10000.0))):
+        for _ in range(warmup):
+            attn_fwd_variant(q, k, v, **var, **pkw)
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        for e in ev:
+            e[0].record()
+            attn_fwd_variant(q, k, v, **var, **pkw)
+            e[1].record()
+        torch.cuda.synchronize()
+        ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+        F = 4.0 * pre.d * pre.B * pre.Hq * visible_pairs(pre.T, var["window"])
+        tf = F / (ms * 1e-3) / 1e12
+        res[name] = {"window": var["window"], "rope_theta": var["rope_theta"], "attn_out": True,
+                     "ms": round(ms, 4), "value": round(tf, 2), "unit": "TFLOP/s",
+                     "roofline": {"bound": "mfma", "achieved": round(tf, 2),
+                                  "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                  "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None}}
+        print(f"[bench] variant {name}: {ms:.3f} ms ({tf:.1f} TFLOP/s)", file=sys.stderr,
+              flush=True)
+    res["workload"] = ("prefill variants at B=1 T=65536 Hq=16 Hkv=4 d=64 bf16: flops over the "
+                       "visible pairs of each mode")
+    return res
+
+
 def copy_probe(nbytes: int):
     import torch
     a = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
@@ -280,6 +319,8 @@ def main():
                                 "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                                 "traffic": tr_dec}},
     }
+    rec["variants"] = measure_variants(dev, q, k, v, pkw, pre, max(1, args.steps // 4),
+                                       min(args.warmup, 2))
     del q, k, v, qd, kc, vc, table, lens, ws
     torch.cuda.empty_cache()
     rec["backward"] = measure_backward(dev, max(1, args.steps // 2), args.warmup,
