@@ -4,9 +4,11 @@ Only the tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``be
 may import this package.  The product path (``long_context_lm_amd``) never does.
 """
 from .polar_oracle import (length_temperature, null_floor, polar_prefill, polar_decode_paged,
-                           gather_pages, rope, FLAG_LENGTH_TEMP, FLAG_NULL_FLOOR)
+                           gather_pages, rope, kv_append, polar_prefill_paged,
+                           FLAG_LENGTH_TEMP, FLAG_NULL_FLOOR)
 
 from .polar_grad import polar_prefill_grad, arg_max_keys
 
 __all__ = ["polar_prefill_grad", "arg_max_keys", "length_temperature", "null_floor", "polar_prefill", "polar_decode_paged",
-           "gather_pages", "rope", "FLAG_LENGTH_TEMP", "FLAG_NULL_FLOOR"]
+           "gather_pages", "rope", "kv_append", "polar_prefill_paged",
+           "FLAG_LENGTH_TEMP", "FLAG_NULL_FLOOR"]

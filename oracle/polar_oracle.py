@@ -235,3 +235,58 @@ def polar_decode_paged(q, k_pool, v_pool, page_table, seq_lens, page_size: int, 
                 for key in out:
                     out[key][bi, h] = res[key][0]
     return out
+
+
+def kv_append(k_pool: np.ndarray, v_pool: np.ndarray, page_table: np.ndarray,
+              start_pos: np.ndarray, k_new: np.ndarray, v_new: np.ndarray, page_size: int,
+              max_seq_len: int):
+    """Write a chunk of new keys and values into the paged pools (returns new pools).
+
+    Token t of sequence b goes to logical position start_pos[b] + t, i.e. physical page
+    page_table[b, pos // page_size], slot pos % page_size, for every KV head.  Tokens whose
+    position reaches max_seq_len or whose page id is outside the pool are dropped.
+    """
+    k_pool, v_pool = k_pool.copy(), v_pool.copy()
+    B, C = k_new.shape[:2]
+    num_pages = k_pool.shape[0]
+    for b in range(B):
+        for t in range(C):
+            pos = int(start_pos[b]) + t
+            if pos >= max_seq_len:
+                continue
+            page = int(page_table[b, pos // page_size])
+            if not 0 <= page < num_pages:
+                continue
+            k_pool[page, :, pos % page_size] = k_new[b, t]
+            v_pool[page, :, pos % page_size] = v_new[b, t]
+    return k_pool, v_pool
+
+
+def polar_prefill_paged(q, k_pool, v_pool, page_table, start_pos, page_size: int, beta=None,
+                        null_bias=None, count_vec=None, train_len: int = 2048,
+                        flags: int = FLAG_LENGTH_TEMP | FLAG_NULL_FLOOR,
+                        to_f64=lambda a: np.asarray(a, np.float64)) -> dict:
+    """Chunked prefill over a paged cache: row t of sequence b is the token at position
+    start_pos[b] + t and attends the logical keys 0..start_pos[b] + t (the cached prefix
+    and the chunk up to itself), gathered through the page table.
+    q [B,C,Hq,d]; returns float64 dir, count [B,C,Hq,d] and n_eff, gate, lse [B,C,Hq].
+    """
+    q = np.asarray(q, np.float64)
+    B, C, Hq, d = q.shape
+    Hkv = k_pool.shape[1]
+    G = Hq // Hkv
+    beta, null_bias, count_vec = _params(Hq, d, beta, null_bias, count_vec)
+    out = dict(dir=np.zeros((B, C, Hq, d)), count=np.zeros((B, C, Hq, d)),
+               n_eff=np.zeros((B, C, Hq)), gate=np.zeros((B, C, Hq)), lse=np.zeros((B, C, Hq)))
+    for b in range(B):
+        L = int(start_pos[b]) + C
+        pos = int(start_pos[b]) + np.arange(C)
+        for g in range(Hkv):
+            K = to_f64(gather_pages(k_pool, page_table[b], g, L, page_size))
+            V = to_f64(gather_pages(v_pool, page_table[b], g, L, page_size))
+            for h in range(g * G, (g + 1) * G):
+                res = _polar_rows(q[b, :, h], K, V, pos + 1, beta[h], null_bias[h],
+                                  count_vec[h], train_len, flags)
+                for key in out:
+                    out[key][b, :, h] = res[key]
+    return out

@@ -316,3 +316,54 @@ def cotangents(B: int, T: int, Hq: int, d: int = 64, seed: int = 2001,
     return Cotangents(d_dir=_normal(s[0], (B, T, Hq, d)), d_count=_normal(s[1], (B, T, Hq, d)),
                       d_n_eff=(np.float32(n_eff_scale) * _normal(s[2], (B, T, Hq))).astype(np.float32),
                       d_gate=_normal(s[3], (B, T, Hq)), d_lse=_normal(s[4], (B, T, Hq)))
+
+
+
+# --------------------------------------------------------------------------- paged chunks
+@dataclasses.dataclass
+class ChunkInputs:
+    """A chunked-prefill step: sequences whose first start_pos[b] tokens are cached in
+    shuffled pages, plus a chunk of C new tokens (queries, keys, values)."""
+    full: PrefillInputs         # the contiguous sequences (T = max start + C)
+    start_pos: np.ndarray       # [B] int32
+    C: int
+    page_size: int
+    k_pool: np.ndarray          # [num_pages, Hkv, page, d], prefix already written
+    v_pool: np.ndarray
+    page_table: np.ndarray      # [B, stride] int32 (-1 past the end)
+    max_seq_len: int
+
+    def chunk(self, name: str) -> np.ndarray:
+        """q, k or v of the new tokens, [B,C,H,d] (storage dtype)."""
+        a = getattr(self.full, name)
+        return np.stack([a[b, s:s + self.C] for b, s in enumerate(self.start_pos)])
+
+
+def chunk_inputs(cfg: str = "c2", B: int = 2, C: int = 256, starts=(0, 700), Hq=None, Hkv=None,
+                 train_len: int = TRAIN_LEN, extra_pages: int = 3, seed: int = 3001,
+                 page_size: int = 64) -> ChunkInputs:
+    """Contiguous sequences of length max(starts) + C drawn like ``cfg``; the prefix of each
+    (tokens before its start) is scattered into a shuffled page pool, the rest left out."""
+    starts = np.asarray(starts, np.int32)[:B]
+    T = int(starts.max()) + C
+    full = prefill_inputs(cfg, B=B, T=T, Hq=Hq, Hkv=Hkv, train_len=train_len)
+    max_seq_len = T
+    stride = -(-max_seq_len // page_size)
+    num_pages = B * stride + extra_pages
+    g = np.random.Generator(np.random.PCG64(seed))
+    perm = g.permutation(num_pages)
+    table = np.full((B, stride), -1, np.int32)
+    k_pool = np.zeros((num_pages, full.Hkv, page_size, full.d), full.k.dtype)
+    v_pool = np.zeros_like(k_pool)
+    nxt = 0
+    for b in range(B):
+        L = int(starts[b]) + C
+        for pg in range(-(-L // page_size)):
+            table[b, pg] = perm[nxt]
+            nxt += 1
+        for t in range(int(starts[b])):
+            pid = table[b, t // page_size]
+            k_pool[pid, :, t % page_size] = full.k[b, t]
+            v_pool[pid, :, t % page_size] = full.v[b, t]
+    return ChunkInputs(full=full, start_pos=starts, C=C, page_size=page_size, k_pool=k_pool,
+                       v_pool=v_pool, page_table=table, max_seq_len=max_seq_len)

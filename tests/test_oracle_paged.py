@@ -1,0 +1,73 @@
+"""Pins of the chunked-prefill and KV-append oracles.
+
+* after appending the chunk, chunked prefill rows equal the contiguous causal prefill rows
+  start..start+C-1 of the same sequence (the page indirection and the prefix split change
+  nothing);
+* a chunk of one token equals paged decode of that sequence;
+* appending into pages and gathering back returns the contiguous keys and values exactly;
+  dropped tokens (past max_seq_len, invalid pages) leave the pool unchanged.
+"""
+import numpy as np
+
+import oracle
+import synth
+
+
+def _f(a):
+    return synth.bf16_bits_to_f32(a).astype(np.float64)
+
+
+def test_chunked_prefill_equals_contiguous_rows():
+    ci = synth.chunk_inputs("c2", B=2, C=40, starts=(0, 77), Hq=8, Hkv=2, train_len=16)
+    kp, vp = oracle.kv_append(ci.k_pool, ci.v_pool, ci.page_table, ci.start_pos,
+                              ci.chunk("k"), ci.chunk("v"), ci.page_size, ci.max_seq_len)
+    p = ci.full
+    got = oracle.polar_prefill_paged(_f(ci.chunk("q")), kp, vp, ci.page_table, ci.start_pos,
+                                     ci.page_size, p.beta, p.null_bias, p.count_vec,
+                                     p.train_len, p.flags, to_f64=_f)
+    full = oracle.polar_prefill(p.as_f32("q"), p.as_f32("k"), p.as_f32("v"), p.beta,
+                                p.null_bias, p.count_vec, p.train_len, p.flags)
+    for b, s in enumerate(ci.start_pos):
+        for n in ("dir", "count", "n_eff", "gate", "lse"):
+            np.testing.assert_allclose(got[n][b], full[n][b, s:s + ci.C], rtol=1e-12, atol=1e-12)
+
+
+def test_one_token_chunk_equals_decode():
+    ci = synth.chunk_inputs("c2", B=2, C=1, starts=(130, 5), Hq=4, Hkv=1, train_len=16)
+    kp, vp = oracle.kv_append(ci.k_pool, ci.v_pool, ci.page_table, ci.start_pos,
+                              ci.chunk("k"), ci.chunk("v"), ci.page_size, ci.max_seq_len)
+    p = ci.full
+    got = oracle.polar_prefill_paged(_f(ci.chunk("q")), kp, vp, ci.page_table, ci.start_pos,
+                                     ci.page_size, p.beta, p.null_bias, p.count_vec,
+                                     p.train_len, p.flags, to_f64=_f)
+    dec = oracle.polar_decode_paged(_f(ci.chunk("q"))[:, 0], kp, vp, ci.page_table,
+                                    ci.start_pos + 1, ci.page_size, p.beta, p.null_bias,
+                                    p.count_vec, p.train_len, p.flags, to_f64=_f)
+    for n in ("dir", "count", "n_eff", "gate", "lse"):
+        np.testing.assert_allclose(got[n][:, 0], dec[n], rtol=1e-13, atol=1e-13)
+
+
+def test_append_then_gather_round_trips():
+    ci = synth.chunk_inputs("c2", B=2, C=70, starts=(10, 200), Hq=4, Hkv=2)
+    kp, vp = oracle.kv_append(ci.k_pool, ci.v_pool, ci.page_table, ci.start_pos,
+                              ci.chunk("k"), ci.chunk("v"), ci.page_size, ci.max_seq_len)
+    for b, s in enumerate(ci.start_pos):
+        L = int(s) + ci.C
+        for g in range(2):
+            np.testing.assert_array_equal(
+                oracle.gather_pages(kp, ci.page_table[b], g, L, ci.page_size), ci.full.k[b, :L, g])
+            np.testing.assert_array_equal(
+                oracle.gather_pages(vp, ci.page_table[b], g, L, ci.page_size), ci.full.v[b, :L, g])
+
+
+def test_append_drops_out_of_range_tokens():
+    ci = synth.chunk_inputs("c2", B=1, C=64, starts=(0,), Hq=4, Hkv=1)
+    table = ci.page_table.copy()
+    table[0, 0] = -1                                       # invalid page: tokens dropped
+    kp, vp = oracle.kv_append(ci.k_pool, ci.v_pool, table, ci.start_pos, ci.chunk("k"),
+                              ci.chunk("v"), ci.page_size, ci.max_seq_len)
+    np.testing.assert_array_equal(kp, ci.k_pool)
+    kp2, _ = oracle.kv_append(ci.k_pool, ci.v_pool, ci.page_table, ci.start_pos, ci.chunk("k"),
+                              ci.chunk("v"), ci.page_size, max_seq_len=32)
+    changed = np.any(kp2 != ci.k_pool, axis=(1, 3))      # [pages, slots]
+    assert changed.sum() <= 32                              # only positions < 32 written
