@@ -246,6 +246,44 @@ POLAR_API polar_status polar_attn_bwd(const polar_params *p, polar_dtype dt, int
                             const polar_cotangents *cot, const polar_grads *grads,
                             void *workspace, size_t workspace_bytes, void *stream);
 
+/* ---------------------------------------------------------------------------------
+ * Paged KV cache: append and chunked prefill (the step before decode in section 2.2: new
+ * keys and values are written into cache pages, then the new tokens attend the paged
+ * prefix).  Pools, page table and page_size are as for polar_attn_decode_paged.
+ *   start_pos   device int32 [B]: position of the chunk's first token in its sequence
+ *               (the number of tokens already cached).  Values are clamped to
+ *               [0, max_seq_len - C].
+ *   max_seq_len host bound: start_pos[b] + C <= max_seq_len;
+ *               page_table_stride >= ceil(max_seq_len / page_size).
+ * --------------------------------------------------------------------------------- */
+
+/*
+ * Writes k_new, v_new [B,C,Hkv,d] (dtype `dt`, 16-byte aligned) into the pools: token t of
+ * sequence b goes to position start_pos[b] + t, page page_table[b, pos / page_size], slot
+ * pos % page_size.  Tokens whose page id lies outside [0, num_pages) are dropped.  The
+ * pools are the only memory written.  Only n_kv_heads and head_dim of `p` are used.
+ */
+POLAR_API polar_status polar_kv_append(const polar_params *p, polar_dtype dt, int32_t B, int32_t C,
+                             const void *k_new, const void *v_new, void *k_cache,
+                             void *v_cache, int32_t num_pages, int32_t page_size,
+                             const int32_t *page_table, int32_t page_table_stride,
+                             const int32_t *start_pos, int32_t max_seq_len, void *stream);
+
+/*
+ * Chunked causal prefill over the paged cache: q [B,C,Hq,d] are the queries of C new
+ * tokens per sequence; row t (position pos = start_pos[b] + t) attends keys 0..pos of its
+ * sequence, read from the pools through the page table (append the chunk's own keys and
+ * values first).  n = pos + 1 drives tau and the floor, so the rows equal causal prefill
+ * rows start_pos[b]..start_pos[b]+C-1 of the whole sequence.  Keys on pages with ids
+ * outside [0, num_pages) are masked out.  Outputs as for polar_attn_fwd with T = C.
+ */
+POLAR_API polar_status polar_attn_prefill_paged(const polar_params *p, polar_dtype dt, int32_t B,
+                                      int32_t C, const void *q, const void *k_cache,
+                                      const void *v_cache, int32_t num_pages, int32_t page_size,
+                                      const int32_t *page_table, int32_t page_table_stride,
+                                      const int32_t *start_pos, int32_t max_seq_len,
+                                      const polar_outputs *out, void *stream);
+
 /* Static description of a status code. */
 POLAR_API const char *polar_status_str(polar_status s);
 /* Thread-local detail of the last non-OK return on this thread ("" if none). */

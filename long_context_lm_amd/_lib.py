@@ -29,7 +29,7 @@ POLAR_FLAG_NULL_FLOOR = 2
 
 EXPORTS = ("polar_attn_fwd", "polar_decode_workspace_bytes", "polar_attn_decode_paged",
            "polar_attn_fwd_train", "polar_bwd_workspace_bytes", "polar_attn_bwd",
-           "polar_attn_fwd_variant",
+           "polar_attn_fwd_variant", "polar_kv_append", "polar_attn_prefill_paged",
            "polar_status_str", "polar_last_error", "polar_abi_version")
 
 
@@ -107,6 +107,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.polar_attn_fwd_variant.restype = I32
     lib.polar_attn_fwd_variant.argtypes = [P(polar_params), P(polar_variant), I32, I32, I32, VP,
                                            VP, VP, P(polar_outputs), VP]
+    lib.polar_kv_append.restype = I32
+    lib.polar_kv_append.argtypes = [P(polar_params), I32, I32, I32, VP, VP, VP, VP, I32, I32, VP,
+                                    I32, VP, I32, VP]
+    lib.polar_attn_prefill_paged.restype = I32
+    lib.polar_attn_prefill_paged.argtypes = [P(polar_params), I32, I32, I32, VP, VP, VP, I32, I32,
+                                             VP, I32, VP, I32, P(polar_outputs), VP]
     lib.polar_status_str.restype = ctypes.c_char_p
     lib.polar_status_str.argtypes = [I32]
     lib.polar_last_error.restype = ctypes.c_char_p
@@ -158,6 +164,20 @@ def polar_attn_fwd_variant(params, variant, dtype, B, T, q, k, v, outputs, strea
     return load().polar_attn_fwd_variant(ctypes.byref(params),
                                          None if variant is None else ctypes.byref(variant),
                                          dtype, B, T, q, k, v, ctypes.byref(outputs), stream)
+
+
+def polar_kv_append(params, dtype, B, C, k_new, v_new, k_cache, v_cache, num_pages, page_size,
+                    page_table, stride, start_pos, max_seq_len, stream) -> int:
+    return load().polar_kv_append(ctypes.byref(params), dtype, B, C, k_new, v_new, k_cache,
+                                  v_cache, num_pages, page_size, page_table, stride, start_pos,
+                                  max_seq_len, stream)
+
+
+def polar_attn_prefill_paged(params, dtype, B, C, q, k_cache, v_cache, num_pages, page_size,
+                             page_table, stride, start_pos, max_seq_len, outputs, stream) -> int:
+    return load().polar_attn_prefill_paged(ctypes.byref(params), dtype, B, C, q, k_cache,
+                                           v_cache, num_pages, page_size, page_table, stride,
+                                           start_pos, max_seq_len, ctypes.byref(outputs), stream)
 
 
 def polar_bwd_workspace_bytes(params, B, T) -> int:

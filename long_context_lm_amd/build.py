@@ -13,7 +13,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libpolar.so")
-SOURCES = ["polar_api.cpp", "polar_prefill.hip", "polar_decode.hip", "polar_backward.hip"]
+SOURCES = ["polar_api.cpp", "polar_prefill.hip", "polar_decode.hip", "polar_backward.hip",
+           "polar_paged.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -68,9 +68,15 @@ extern "C" {
 
 namespace {
 
+struct PagedSrc {
+  const int32_t *page_table, *start_pos;
+  int stride, num_pages, max_seq_len;
+};
+
 polar_status prefill(const polar_params *p, polar_dtype dt, int32_t B, int32_t T, const void *q,
                      const void *k, const void *v, const polar_outputs *out,
-                     const polar_saved *saved, const polar_variant *var, void *stream) {
+                     const polar_saved *saved, const polar_variant *var, void *stream,
+                     const PagedSrc *paged = nullptr) {
   polar_status st = check_params(p, dt, out);
   if (st != POLAR_OK) return st;
   if (var) {
@@ -97,7 +103,7 @@ polar_status prefill(const polar_params *p, polar_dtype dt, int32_t B, int32_t T
 
   // K/V rows are addressed with 32-bit byte offsets (one tile past the end included).
   const long long elt = dt == POLAR_DTYPE_BF16 ? 2 : 4;
-  if (((long long)T + 64) * p->n_kv_heads * polar::kHeadDim * elt >= 0x7fffffffLL)
+  if (!paged && ((long long)T + 64) * p->n_kv_heads * polar::kHeadDim * elt >= 0x7fffffffLL)
     return fail(POLAR_ERR_BAD_SHAPE, "T*Hkv too large for one sequence (T=%d, Hkv=%d)", T,
                 p->n_kv_heads);
 
@@ -119,6 +125,12 @@ polar_status prefill(const polar_params *p, polar_dtype dt, int32_t B, int32_t T
   a.window = var ? var->window : 0;
   a.rope = (var && var->rope_theta > 0.f) ? 1 : 0;
   a.variant = (a.attn || a.window > 0 || a.rope) ? 1 : 0;
+  a.paged = paged ? 1 : 0;
+  a.page_table = paged ? paged->page_table : nullptr;
+  a.start_pos = paged ? paged->start_pos : nullptr;
+  a.stride = paged ? paged->stride : 0;
+  a.num_pages = paged ? paged->num_pages : 0;
+  a.max_seq_len = paged ? paged->max_seq_len : 0;
   for (int t = 0; t < polar::kHeadDim / 2; ++t) {
     a.rope_f[t] = 0;
     if (a.rope) {
@@ -360,6 +372,77 @@ polar_status polar_attn_decode_paged(const polar_params *p, polar_dtype dt, int3
   hipError_t err = polar::launch_decode((int)dt, a, (hipStream_t)stream);
   if (err != hipSuccess) return fail(POLAR_ERR_HIP, "decode launch: %s", hipGetErrorString(err));
   return POLAR_OK;
+}
+
+polar_status polar_kv_append(const polar_params *p, polar_dtype dt, int32_t B, int32_t C,
+                             const void *k_new, const void *v_new, void *k_cache,
+                             void *v_cache, int32_t num_pages, int32_t page_size,
+                             const int32_t *page_table, int32_t page_table_stride,
+                             const int32_t *start_pos, int32_t max_seq_len, void *stream) {
+  if (!p) return fail(POLAR_ERR_NULL_POINTER, "params is NULL");
+  if (dt != POLAR_DTYPE_F32 && dt != POLAR_DTYPE_BF16)
+    return fail(POLAR_ERR_UNSUPPORTED, "unknown dtype %d", (int)dt);
+  if (p->n_kv_heads < 1) return fail(POLAR_ERR_BAD_SHAPE, "Hkv must be >= 1");
+  if (p->head_dim != polar::kHeadDim)
+    return fail(POLAR_ERR_UNSUPPORTED, "head_dim %d unsupported (only %d)", p->head_dim,
+                polar::kHeadDim);
+  if (page_size != polar::kPageSize)
+    return fail(POLAR_ERR_UNSUPPORTED, "page_size %d unsupported (only %d)", page_size,
+                polar::kPageSize);
+  if (B < 0 || C < 0) return fail(POLAR_ERR_BAD_SHAPE, "B (%d) and C (%d) must be >= 0", B, C);
+  if (B == 0 || C == 0) return POLAR_OK;
+  if (!k_new || !v_new || !k_cache || !v_cache || !page_table || !start_pos)
+    return fail(POLAR_ERR_NULL_POINTER, "tensors, page_table and start_pos must be non-NULL");
+  if (num_pages < 1) return fail(POLAR_ERR_BAD_SHAPE, "num_pages (%d) must be >= 1", num_pages);
+  if (max_seq_len < C)
+    return fail(POLAR_ERR_BAD_SHAPE, "max_seq_len (%d) < C (%d)", max_seq_len, C);
+  if (page_table_stride < (max_seq_len + page_size - 1) / page_size)
+    return fail(POLAR_ERR_BAD_SHAPE, "page_table_stride (%d) < ceil(max_seq_len/page_size)",
+                page_table_stride);
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(POLAR_ERR_MISALIGNED, "k_new, v_new and the pools must be 16-byte aligned");
+  polar::AppendArgs a;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.page_table = page_table;
+  a.start_pos = start_pos;
+  a.B = B;
+  a.C = C;
+  a.Hkv = p->n_kv_heads;
+  a.stride = page_table_stride;
+  a.num_pages = num_pages;
+  a.max_seq_len = max_seq_len;
+  a.row_bytes = polar::kHeadDim * (dt == POLAR_DTYPE_BF16 ? 2 : 4);
+  hipError_t err = polar::launch_kv_append(a, (hipStream_t)stream);
+  if (err != hipSuccess) return fail(POLAR_ERR_HIP, "append launch: %s", hipGetErrorString(err));
+  return POLAR_OK;
+}
+
+polar_status polar_attn_prefill_paged(const polar_params *p, polar_dtype dt, int32_t B,
+                                      int32_t C, const void *q, const void *k_cache,
+                                      const void *v_cache, int32_t num_pages, int32_t page_size,
+                                      const int32_t *page_table, int32_t page_table_stride,
+                                      const int32_t *start_pos, int32_t max_seq_len,
+                                      const polar_outputs *out, void *stream) {
+  polar_status st = check_params(p, dt, out);
+  if (st != POLAR_OK) return st;
+  if (page_size != polar::kPageSize)
+    return fail(POLAR_ERR_UNSUPPORTED, "page_size %d unsupported (only %d)", page_size,
+                polar::kPageSize);
+  if (B < 0 || C < 0) return fail(POLAR_ERR_BAD_SHAPE, "B (%d) and C (%d) must be >= 0", B, C);
+  if (B == 0 || C == 0) return POLAR_OK;
+  if (!page_table || !start_pos)
+    return fail(POLAR_ERR_NULL_POINTER, "page_table and start_pos must be non-NULL");
+  if (num_pages < 1) return fail(POLAR_ERR_BAD_SHAPE, "num_pages (%d) must be >= 1", num_pages);
+  if (max_seq_len < C)
+    return fail(POLAR_ERR_BAD_SHAPE, "max_seq_len (%d) < C (%d)", max_seq_len, C);
+  if (page_table_stride < (max_seq_len + page_size - 1) / page_size)
+    return fail(POLAR_ERR_BAD_SHAPE, "page_table_stride (%d) < ceil(max_seq_len/page_size)",
+                page_table_stride);
+  const PagedSrc src{page_table, start_pos, page_table_stride, num_pages, max_seq_len};
+  return prefill(p, dt, B, C, q, k_cache, v_cache, out, nullptr, nullptr, stream, &src);
 }
 
 const char *polar_status_str(polar_status s) {

@@ -27,6 +27,12 @@ struct PrefillArgs {
   int n_row_blocks;                       // ceil(T / rows per workgroup)
   float inv_log_train;                    // 1/ln(train_len) with the length temperature, else 0
   int null_floor;                         // 1: add the extreme-value term to the floor
+  // Paged chunk instances: q holds C = T rows per sequence at positions start_pos[b]..;
+  // k and v are the page pools [num_pages,Hkv,kPageSize,d] read through page_table.
+  int paged;
+  const int32_t *page_table;              // [B,stride]
+  const int32_t *start_pos;               // [B]
+  int stride, num_pages, max_seq_len;
 };
 
 // dtype: 0 = f32, 1 = bf16 (same numbering as polar_dtype).
@@ -54,6 +60,16 @@ struct DecodeGrid {
 DecodeGrid decode_grid(int B, int Hq, int Hkv, int max_seq_len);
 size_t decode_ws_bytes(int B, int Hq, int Hkv, int max_seq_len);
 hipError_t launch_decode(int dtype, const DecodeArgs &a, hipStream_t stream);
+
+// Writes a chunk of new keys/values into the page pools.
+struct AppendArgs {
+  const void *k_new, *v_new;              // [B,C,Hkv,d]
+  void *k_cache, *v_cache;                // [num_pages,Hkv,kPageSize,d]
+  const int32_t *page_table, *start_pos;
+  int B, C, Hkv, stride, num_pages, max_seq_len;
+  int row_bytes;                          // d * element size
+};
+hipError_t launch_kv_append(const AppendArgs &a, hipStream_t stream);
 
 // Backward pass of the causal prefill (bf16 inputs).  Per-row quantities (float4 each;
 // r0 and r1 of a row are adjacent in `rows`):

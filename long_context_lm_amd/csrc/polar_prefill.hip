@@ -26,7 +26,10 @@
 //    the backward pass;
 //  * variant instances (kMode == kModeVariant) add a sliding window, RoPE applied to q at
 //    load and to each K tile while it is staged into LDS, and the plain softmax output;
-//    every tile goes through the masked path.
+//    every tile goes through the masked path;
+//  * paged instances (kMode == kModePaged) serve chunked prefill over a paged KV cache: the
+//    rows are C new tokens at positions start_pos[b].., and a 64-key tile is one page,
+//    read through the page table (pages with invalid ids are masked out).
 #include "polar_kernels.h"
 #include "polar_mfma.h"
 
@@ -63,7 +66,7 @@ template <> struct LdsCfg<Bf16> {
 };
 template <> struct LdsCfg<F32> { static constexpr int kt = 64, krow = 68, vrow = 65; };
 
-constexpr int kModePlain = 0, kModeSave = 1, kModeVariant = 2;
+constexpr int kModePlain = 0, kModeSave = 1, kModeVariant = 2, kModePaged = 3;
 
 // RoPE rotation angle of pair t at position pos: revolutions = frac(pos * f_t) taken
 // exactly from the 64-bit fixed-point product, then sin/cos of 2*pi*revolutions.
@@ -76,6 +79,8 @@ template <class TR, int QB, int kWaves, int kMode>
 __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs a) {
   constexpr bool kSave = kMode == kModeSave;
   constexpr bool kVar = kMode == kModeVariant;
+  constexpr bool kPaged = kMode == kModePaged;
+  static_assert(!kPaged || LdsCfg<TR>::kt == kPageSize, "a key tile is one page");
   constexpr int kThreads = 64 * kWaves;
   constexpr int kKT = LdsCfg<TR>::kt;                // keys per tile
   constexpr int NKB = kKT / 32;                      // 32-key MFMA blocks per tile
@@ -104,9 +109,11 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
   const int WR = (kWaves / a.hb) * 32 * QB;
   const int row0 = rb * WR;
   const int wrow0 = row0 + (wave / a.hb) * 32 * QB;
+  // Row r of this sequence sits at position pbase + r (pbase = 0 outside paged instances).
+  const int pbase = kPaged ? min(max(a.start_pos[b], 0), a.max_seq_len - a.T) : 0;
   const int wg_last = min(row0 + WR, a.T) - 1;
-  const int w_last = wrow0 < a.T ? min(wrow0 + 32 * QB, a.T) - 1 : -1;
-  const int ntiles = wg_last / kKT + 1;
+  const int w_last = wrow0 < a.T ? pbase + min(wrow0 + 32 * QB, a.T) - 1 : -1;
+  const int ntiles = (pbase + wg_last) / kKT + 1;
 
   // K and V rows of this (b, g) through buffer resources sized to the sequence, so loads
   // of keys >= T return zeros without a branch.
@@ -124,7 +131,7 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int row = wrow0 + qb * 32 + c32;
-    const int nk = (kVar && a.window > 0) ? min(row + 1, a.window) : row + 1;
+    const int nk = (kVar && a.window > 0) ? min(row + 1, a.window) : pbase + row + 1;
     const float tau =
         a.inv_log_train > 0.f ? fmaxf(1.0f, logf((float)nk) * a.inv_log_train) : 1.0f;
     cnat[qb] = beta * tau;
@@ -209,16 +216,31 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
   u32x4 kst[NK];
   vchunk_t vst[NV][VKEYS];
   int staged_key0 = 0;                               // variant: position of the staged tile
+  int tok[4] = {1, 1, 1, 1};                         // paged: slot holds a valid page
   auto stage_load = [&](int t) {
     const int key0 = t * kKT;
     staged_key0 = key0;
+    // Tile source: rows of this (b, g) in place, or (paged) one page of the pools.
+    auto rk = krsrc, rv = vrsrc;
+    int base = (int)((size_t)key0 * kv_row_bytes), rstride = (int)kv_row_bytes;
+    if constexpr (kPaged) {
+      const int npg = min(a.stride, (pbase + a.T + kPageSize - 1) / kPageSize);
+      const int page = t < npg ? a.page_table[(size_t)b * a.stride + t] : -1;
+      const bool pok = page >= 0 && page < a.num_pages;
+      tok[t & 3] = pok;
+      const size_t pe = ((size_t)(pok ? page : 0) * a.Hkv + g) * kPageSize * kD;
+      const int nb = pok ? kPageSize * kD * (int)sizeof(E) : 0;
+      rk = __builtin_amdgcn_make_buffer_rsrc((void *)((const E *)a.k + pe), 0, nb, kBufferFlags);
+      rv = __builtin_amdgcn_make_buffer_rsrc((void *)((const E *)a.v + pe), 0, nb, kBufferFlags);
+      base = 0;
+      rstride = kD * (int)sizeof(E);
+    }
 #pragma unroll
     for (int j = 0; j < NK; ++j) {
       const int ch = min(tid + kThreads * j, KTASKS - 1);
       const int key = ch / CPR, part = ch % CPR;
       kst[j] = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                     krsrc, (int)((size_t)(key0 + key) * kv_row_bytes) + part * 16, 0, 0));
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, base + key * rstride + part * 16, 0, 0));
     }
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
@@ -227,13 +249,13 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
 #pragma unroll
       for (int r = 0; r < VKEYS; ++r) {
         const int key = (ti % VKG) * VKEYS + r;
-        const int off = (int)((size_t)(key0 + key) * kv_row_bytes) + part * VDIMS * (int)sizeof(E);
+        const int off = base + key * rstride + part * VDIMS * (int)sizeof(E);
         if constexpr (KPL == 8)
           vst[j][r] = __builtin_bit_cast(vchunk_t,
-                                         __builtin_amdgcn_raw_buffer_load_b64(vrsrc, off, 0, 0));
+                                         __builtin_amdgcn_raw_buffer_load_b64(rv, off, 0, 0));
         else
           vst[j][r] = __builtin_bit_cast(vchunk_t,
-                                         __builtin_amdgcn_raw_buffer_load_b128(vrsrc, off, 0, 0));
+                                         __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
       }
     }
   };
@@ -342,6 +364,16 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
           S.v[qb][kb] = TR::mma32(ka, qf[qb][ks], ks == 0 ? zero : S.v[qb][kb]);
       }
 #endif
+    if constexpr (kPaged) {
+      if (!tok[slot]) {                               // a page with an invalid id
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) S.v[qb][kb][r] = -INFINITY;
+      }
+    }
   };
   // Causal mask: key > row -> -inf.
   auto mask = [&](Scores &S, int key0) {
@@ -353,7 +385,7 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * g32 + (r & 3);
-          bool masked = key > row;
+          bool masked = key > pbase + row;
           if constexpr (kVar) masked = masked || (a.window > 0 && key <= row - a.window);
           if (masked) S.v[qb][kb][r] = -INFINITY;
         }
@@ -476,7 +508,7 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
   // Variant instances start at the first tile any row of the workgroup can see and run
   // every tile through the masked path.
   const int t0 = (kVar && a.window > 0) ? max(0, row0 - a.window + 1) / kKT : 0;
-  const int nfull = kVar ? 0 : min((row0 + 1) / kKT, ntiles);
+  const int nfull = kVar ? 0 : min((pbase + row0 + 1) / kKT, ntiles);
 
   for (int j = t0; j < t0 + 3 && j < ntiles; ++j) {
     stage_load(j);
@@ -580,7 +612,7 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
       const float lse = (Mref[qb] + log2f(St)) * kLn2;
       const float m_nat = smax[qb] * cnat[qb];
       float floor_ = bias;
-      const int nk = (kVar && a.window > 0) ? min(row + 1, a.window) : row + 1;
+      const int nk = (kVar && a.window > 0) ? min(row + 1, a.window) : pbase + row + 1;
       if (a.null_floor) floor_ += cnat[qb] * 0.125f * sqrtf(2.0f * logf((float)nk));
       const float gate = 1.0f / (1.0f + expf(floor_ - m_nat));
       const float n2 = neff * neff;
@@ -671,7 +703,8 @@ hipError_t launch_prefill(int dtype, const PrefillArgs &a, hipStream_t stream) {
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   dim3 grid((unsigned)blocks);
-  const int mode = a.variant ? kModeVariant : (a.u_norm != nullptr ? kModeSave : kModePlain);
+  const int mode = a.paged ? kModePaged
+                 : a.variant ? kModeVariant : (a.u_norm != nullptr ? kModeSave : kModePlain);
   const dim3 bb(64 * kWavesBf16), bf(64 * kWavesF32);
   if (dtype == 1) {
     if (mode == kModePlain)
@@ -680,8 +713,11 @@ hipError_t launch_prefill(int dtype, const PrefillArgs &a, hipStream_t stream) {
     else if (mode == kModeSave)
       hipLaunchKernelGGL((polar_prefill_kernel<Bf16, kQbBf16, kWavesBf16, kModeSave>), grid, bb,
                          0, stream, a);
-    else
+    else if (mode == kModeVariant)
       hipLaunchKernelGGL((polar_prefill_kernel<Bf16, kQbBf16, kWavesBf16, kModeVariant>), grid,
+                         bb, 0, stream, a);
+    else
+      hipLaunchKernelGGL((polar_prefill_kernel<Bf16, kQbBf16, kWavesBf16, kModePaged>), grid,
                          bb, 0, stream, a);
   } else {
     if (mode == kModePlain)
@@ -690,9 +726,12 @@ hipError_t launch_prefill(int dtype, const PrefillArgs &a, hipStream_t stream) {
     else if (mode == kModeSave)
       hipLaunchKernelGGL((polar_prefill_kernel<F32, kQbF32, kWavesF32, kModeSave>), grid, bf, 0,
                          stream, a);
-    else
+    else if (mode == kModeVariant)
       hipLaunchKernelGGL((polar_prefill_kernel<F32, kQbF32, kWavesF32, kModeVariant>), grid, bf,
                          0, stream, a);
+    else
+      hipLaunchKernelGGL((polar_prefill_kernel<F32, kQbF32, kWavesF32, kModePaged>), grid, bf, 0,
+                         stream, a);
   }
   return hipGetLastError();
 }

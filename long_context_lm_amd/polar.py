@@ -208,3 +208,59 @@ def attn_decode_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
         page, page_table.data_ptr(), page_table.shape[1], seq_lens.data_ptr(), max_seq_len,
         workspace.data_ptr(), workspace.numel() * workspace.element_size(), cout, s))
     return out
+
+
+def _paged_args(k_cache, v_cache, page_table, start_pos, B):
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        _check_input(t, n)
+    num_pages, Hkv, page, d = k_cache.shape
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise ValueError("caches must match")
+    if page_table.dtype != torch.int32 or start_pos.dtype != torch.int32:
+        raise ValueError("page_table and start_pos must be int32")
+    if page_table.dim() != 2 or page_table.shape[0] != B or start_pos.shape != (B,):
+        raise ValueError("page_table must be [B,stride] and start_pos [B]")
+    return num_pages, Hkv, page, d
+
+
+def kv_append(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor,
+              v_cache: torch.Tensor, page_table: torch.Tensor, start_pos: torch.Tensor,
+              max_seq_len: int, stream=None) -> None:
+    """Write k_new, v_new [B,C,Hkv,d] into the page pools in place (see polar_kv_append)."""
+    for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+        _check_input(t, n)
+    B, C, Hkv, d = k_new.shape
+    num_pages, Hkv2, page, d2 = _paged_args(k_cache, v_cache, page_table, start_pos, B)
+    if (Hkv2, d2) != (Hkv, d) or v_new.shape != k_new.shape or k_new.dtype != k_cache.dtype:
+        raise ValueError("k_new/v_new must be [B,C,Hkv,d] matching the pools")
+    prm = _lib.polar_params(Hkv, Hkv, d, 2048, 0, None, None, None)
+    s = torch.cuda.current_stream(k_new.device).cuda_stream if stream is None else stream
+    _lib.check(_lib.polar_kv_append(prm, _DT[k_new.dtype], B, C, k_new.data_ptr(),
+                                    v_new.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                    num_pages, page, page_table.data_ptr(), page_table.shape[1],
+                                    start_pos.data_ptr(), max_seq_len, s))
+
+
+def attn_prefill_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                       page_table: torch.Tensor, start_pos: torch.Tensor, max_seq_len: int,
+                       beta=None, null_bias=None, count_vec=None, train_len: int = 2048,
+                       flags: int = _lib.POLAR_FLAG_LENGTH_TEMP | _lib.POLAR_FLAG_NULL_FLOOR,
+                       want_gate: bool = True, want_lse: bool = True, stream=None) -> dict:
+    """Chunked prefill over the paged cache.  q [B,C,Hq,d]: row t is the token at position
+    start_pos[b] + t; its keys come from the pools (append the chunk first)."""
+    _check_input(q, "q")
+    B, C, Hq, d = q.shape
+    num_pages, Hkv, page, d2 = _paged_args(k_cache, v_cache, page_table, start_pos, B)
+    if d2 != d or k_cache.dtype != q.dtype:
+        raise ValueError("caches must match q's head_dim and dtype")
+    dev = q.device
+    beta, null_bias, count_vec = (_device_f32(beta, dev), _device_f32(null_bias, dev),
+                                  _device_f32(count_vec, dev))
+    prm = _params(Hq, Hkv, d, beta, null_bias, count_vec, train_len, flags)
+    out, cout = _outputs((B, C), Hq, d, dev, count_vec is not None, want_gate, want_lse)
+    s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+    _lib.check(_lib.polar_attn_prefill_paged(
+        prm, _DT[q.dtype], B, C, q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), num_pages,
+        page, page_table.data_ptr(), page_table.shape[1], start_pos.data_ptr(), max_seq_len,
+        cout, s))
+    return out

@@ -249,3 +249,55 @@ def test_variant_empty_calls():
     assert var_fwd(window=16, theta=10000.0, attn=A, B=0) == _lib.POLAR_OK
     assert _lib.polar_attn_fwd_variant(params(), None, 1, 1, 0, A, A, A, outs(), None) == \
         _lib.POLAR_OK
+
+
+# ------------------------------------------------------------------ paged append / chunks
+def app(p=None, dt=1, B=2, C=16, kn=A, vn=A, kc=A, vc=A, num_pages=10, page=64, table=A,
+        stride=4, start=A, max_len=256):
+    return _lib.polar_kv_append(params() if p is None else p, dt, B, C, kn, vn, kc, vc,
+                                num_pages, page, table, stride, start, max_len, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(page=32), _lib.POLAR_ERR_UNSUPPORTED),
+    (dict(dt=5), _lib.POLAR_ERR_UNSUPPORTED),
+    (dict(p=params(head_dim=32)), _lib.POLAR_ERR_UNSUPPORTED),
+    (dict(C=-1), _lib.POLAR_ERR_BAD_SHAPE),
+    (dict(num_pages=0), _lib.POLAR_ERR_BAD_SHAPE),
+    (dict(max_len=8), _lib.POLAR_ERR_BAD_SHAPE),
+    (dict(stride=3), _lib.POLAR_ERR_BAD_SHAPE),
+    (dict(table=None), _lib.POLAR_ERR_NULL_POINTER),
+    (dict(start=None), _lib.POLAR_ERR_NULL_POINTER),
+    (dict(kc=A + 8), _lib.POLAR_ERR_MISALIGNED),
+])
+def test_append_validation_errors(kw, code):
+    assert app(**kw) == code
+    assert _lib.polar_last_error() != ""
+
+
+def chunk(p=None, dt=1, B=2, C=16, q=A, kc=A, vc=A, num_pages=10, page=64, table=A, stride=4,
+          start=A, max_len=256, o=None):
+    return _lib.polar_attn_prefill_paged(params() if p is None else p, dt, B, C, q, kc, vc,
+                                         num_pages, page, table, stride, start, max_len,
+                                         outs() if o is None else o, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(page=16), _lib.POLAR_ERR_UNSUPPORTED),
+    (dict(p=params(n_q_heads=5)), _lib.POLAR_ERR_BAD_SHAPE),
+    (dict(C=-2), _lib.POLAR_ERR_BAD_SHAPE),
+    (dict(max_len=4), _lib.POLAR_ERR_BAD_SHAPE),
+    (dict(stride=2), _lib.POLAR_ERR_BAD_SHAPE),
+    (dict(start=None), _lib.POLAR_ERR_NULL_POINTER),
+    (dict(q=None), _lib.POLAR_ERR_NULL_POINTER),
+    (dict(o=outs(dir=None)), _lib.POLAR_ERR_NULL_POINTER),
+    (dict(kc=A + 2), _lib.POLAR_ERR_MISALIGNED),
+])
+def test_chunked_prefill_validation_errors(kw, code):
+    assert chunk(**kw) == code
+    assert _lib.polar_last_error() != ""
+
+
+def test_empty_append_and_chunk():
+    assert app(C=0, kn=None, vn=None) == _lib.POLAR_OK
+    assert chunk(B=0, q=None) == _lib.POLAR_OK

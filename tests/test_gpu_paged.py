@@ -1,0 +1,104 @@
+"""GPU parity of the paged-cache write (KV append: bit-exact) and of chunked prefill over the
+paged cache (float tolerances of tests/parity.py) against the oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from parity import assert_close, host, select, to_dev
+from long_context_lm_amd import attn_prefill_paged, kv_append
+
+pytestmark = pytest.mark.gpu
+
+
+def _f(a):
+    return synth.bf16_bits_to_f32(a).astype(np.float64)
+
+
+def _setup(ci):
+    dt = ci.full.dtype
+    kc, vc = to_dev(ci.k_pool, dt), to_dev(ci.v_pool, dt)
+    table = torch.from_numpy(ci.page_table).cuda()
+    start = torch.from_numpy(ci.start_pos).cuda()
+    return kc, vc, table, start
+
+
+def _append_and_run(ci):
+    dt = ci.full.dtype
+    kc, vc, table, start = _setup(ci)
+    kv_append(to_dev(ci.chunk("k"), dt), to_dev(ci.chunk("v"), dt), kc, vc, table, start,
+              ci.max_seq_len)
+    p = ci.full
+    out = attn_prefill_paged(to_dev(ci.chunk("q"), dt), kc, vc, table, start, ci.max_seq_len,
+                             beta=p.beta, null_bias=p.null_bias, count_vec=p.count_vec,
+                             train_len=p.train_len, flags=p.flags)
+    torch.cuda.synchronize()
+    return kc, vc, out
+
+
+def _oracle(ci, kp, vp, rows=None):
+    p = ci.full
+    conv = _f if p.dtype == "bf16" else (lambda a: np.asarray(a, np.float64))
+    q = conv(ci.chunk("q"))
+    return oracle.polar_prefill_paged(q, kp, vp, ci.page_table, ci.start_pos, ci.page_size,
+                                      p.beta, p.null_bias, p.count_vec, p.train_len, p.flags,
+                                      to_f64=conv)
+
+
+def _bits(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16) if t.dtype == torch.bfloat16 \
+        else t.cpu().numpy()
+
+
+@pytest.mark.parametrize("B,C,starts,Hq,Hkv", [
+    (2, 256, (0, 700), 16, 4),       # a first chunk and a later chunk
+    (2, 100, (37, 64), 8, 2),        # ragged chunk, unaligned starts
+    (1, 1, (500,), 4, 1),            # one token (the decode case)
+    (3, 64, (0, 1, 130), 4, 4),      # no GQA
+])
+def test_append_bit_exact_and_chunked_prefill_parity(gpu_lib, B, C, starts, Hq, Hkv):
+    print(f"[case] paged B={B} C={C} starts={starts} {Hq}/{Hkv}", flush=True)
+    ci = synth.chunk_inputs("c2", B=B, C=C, starts=starts, Hq=Hq, Hkv=Hkv, train_len=64)
+    kc, vc, out = _append_and_run(ci)
+    kp, vp = oracle.kv_append(ci.k_pool, ci.v_pool, ci.page_table, ci.start_pos, ci.chunk("k"),
+                              ci.chunk("v"), ci.page_size, ci.max_seq_len)
+    np.testing.assert_array_equal(_bits(kc), kp)
+    np.testing.assert_array_equal(_bits(vc), vp)
+    want = _oracle(ci, kp, vp)
+    assert_close(out, want, ci.full.count_vec, "bf16", label=f"chunk C={C} starts={starts}")
+
+
+def test_append_drops_tokens_on_invalid_pages(gpu_lib):
+    ci = synth.chunk_inputs("c2", B=1, C=128, starts=(0,), Hq=4, Hkv=1)
+    ci.page_table[0, 1] = -1                       # tokens 64..127 have nowhere to go
+    kc, vc, table, start = _setup(ci)
+    kv_append(to_dev(ci.chunk("k"), "bf16"), to_dev(ci.chunk("v"), "bf16"), kc, vc, table, start,
+              ci.max_seq_len)
+    torch.cuda.synchronize()
+    kp, _ = oracle.kv_append(ci.k_pool, ci.v_pool, ci.page_table, ci.start_pos, ci.chunk("k"),
+                             ci.chunk("v"), ci.page_size, ci.max_seq_len)
+    np.testing.assert_array_equal(_bits(kc), kp)
+
+
+def test_chunked_prefill_float32(gpu_lib):
+    ci = synth.chunk_inputs("c1", B=2, C=96, starts=(0, 150), Hq=4, Hkv=2, train_len=64)
+    kc, vc, out = _append_and_run(ci)
+    kp, vp = oracle.kv_append(ci.k_pool, ci.v_pool, ci.page_table, ci.start_pos, ci.chunk("k"),
+                              ci.chunk("v"), ci.page_size, ci.max_seq_len)
+    assert_close(out, _oracle(ci, kp, vp), ci.full.count_vec, "f32", label="chunk f32")
+
+
+def test_last_chunk_of_64k_sequence_sampled(gpu_lib):
+    """The final 4096-token chunk of the T=64K workload over a shuffled page pool."""
+    print("[case] paged last chunk of C4", flush=True)
+    ci = synth.chunk_inputs("c4", B=1, C=4096, starts=(61440,))
+    kc, vc, out = _append_and_run(ci)
+    kp, vp = oracle.kv_append(ci.k_pool, ci.v_pool, ci.page_table, ci.start_pos, ci.chunk("k"),
+                              ci.chunk("v"), ci.page_size, ci.max_seq_len)
+    rows = np.array([0, 1, 2047, 4094, 4095])
+    p = ci.full
+    full = oracle.polar_prefill(p.as_f32("q"), p.as_f32("k"), p.as_f32("v"), p.beta,
+                                p.null_bias, p.count_vec, p.train_len, p.flags,
+                                rows=rows + 61440)
+    assert_close(select(out, rows=rows), full, p.count_vec, "bf16", label="C4 last chunk")
