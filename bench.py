@@ -211,6 +211,57 @@ def measure_variants(dev, q, k, v, pkw, pre, steps: int, warmup: int):
     return res
 
 
+def measure_paged(dev, pre, steps: int, warmup: int):
+    """The last 4096-token chunk of the T=64K sequence over a shuffled page pool: KV append
+    of the chunk, then its chunked prefill over the 61440 cached tokens and itself."""
+    import torch
+    import synth
+    from long_context_lm_amd import attn_prefill_paged, kv_append
+    C, start = 4096, pre.T - 4096
+    ci = synth.chunk_inputs(B=1, C=C, starts=(start,), full=pre)
+
+    def to_dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    kc, vc = to_dev(ci.k_pool), to_dev(ci.v_pool)
+    table = torch.from_numpy(ci.page_table).to(dev)
+    sp = torch.from_numpy(ci.start_pos).to(dev)
+    qn, kn, vn = to_dev(ci.chunk("q")), to_dev(ci.chunk("k")), to_dev(ci.chunk("v"))
+    kw = dict(beta=torch.from_numpy(pre.beta).to(dev), count_vec=torch.from_numpy(pre.count_vec).to(dev),
+              null_bias=torch.from_numpy(pre.null_bias).to(dev), train_len=pre.train_len,
+              flags=pre.flags)
+    for _ in range(warmup):
+        kv_append(kn, vn, kc, vc, table, sp, ci.max_seq_len)
+        attn_prefill_paged(qn, kc, vc, table, sp, ci.max_seq_len, **kw)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for e in ev:
+        e[0].record()
+        kv_append(kn, vn, kc, vc, table, sp, ci.max_seq_len)
+        e[1].record()
+        attn_prefill_paged(qn, kc, vc, table, sp, ci.max_seq_len, **kw)
+        e[2].record()
+    torch.cuda.synchronize()
+    a_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    p_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    F = 4.0 * pre.d * pre.Hq * float(np.sum(start + np.arange(C) + 1.0))
+    tf = F / (p_ms * 1e-3) / 1e12
+    a_bytes = 2.0 * 2 * C * pre.Hkv * pre.d * 2            # K and V, read and written once
+    gbs = a_bytes / (a_ms * 1e-3) / 1e9
+    print(f"[bench] paged: append {a_ms * 1e3:.1f} us ({gbs:.0f} GB/s), chunked prefill "
+          f"{p_ms:.3f} ms ({tf:.1f} TFLOP/s)", file=sys.stderr, flush=True)
+    return {"workload": "last 4096-token chunk of the B=1 T=65536 Hq=16 Hkv=4 d=64 bf16 sequence "
+                        "(61440 tokens cached in shuffled 64-token pages)",
+            "value": round(tf, 2), "unit": "TFLOP/s", "prefill_ms": round(p_ms, 4),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                         "traffic": None},
+            "append": {"us": round(a_ms * 1e3, 2), "value": round(gbs, 1), "unit": "GB/s",
+                       "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
+                                    "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                    "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}}}
+
+
 def copy_probe(nbytes: int):
     import torch
     a = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
@@ -321,6 +372,7 @@ def main():
     }
     rec["variants"] = measure_variants(dev, q, k, v, pkw, pre, max(1, args.steps // 4),
                                        min(args.warmup, 2))
+    rec["paged"] = measure_paged(dev, pre, max(1, args.steps // 2), min(args.warmup, 2))
     del q, k, v, qd, kc, vc, table, lens, ws
     torch.cuda.empty_cache()
     rec["backward"] = measure_backward(dev, max(1, args.steps // 2), args.warmup,

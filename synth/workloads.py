@@ -341,12 +341,15 @@ class ChunkInputs:
 
 def chunk_inputs(cfg: str = "c2", B: int = 2, C: int = 256, starts=(0, 700), Hq=None, Hkv=None,
                  train_len: int = TRAIN_LEN, extra_pages: int = 3, seed: int = 3001,
-                 page_size: int = 64) -> ChunkInputs:
-    """Contiguous sequences of length max(starts) + C drawn like ``cfg``; the prefix of each
-    (tokens before its start) is scattered into a shuffled page pool, the rest left out."""
+                 page_size: int = 64, full: Optional[PrefillInputs] = None) -> ChunkInputs:
+    """Contiguous sequences of length max(starts) + C drawn like ``cfg`` (or the given
+    ``full`` sequences); the prefix of each (tokens before its start) is scattered into a
+    shuffled page pool, the rest left out."""
     starts = np.asarray(starts, np.int32)[:B]
     T = int(starts.max()) + C
-    full = prefill_inputs(cfg, B=B, T=T, Hq=Hq, Hkv=Hkv, train_len=train_len)
+    if full is None:
+        full = prefill_inputs(cfg, B=B, T=T, Hq=Hq, Hkv=Hkv, train_len=train_len)
+    assert full.T >= T and full.B >= B
     max_seq_len = T
     stride = -(-max_seq_len // page_size)
     num_pages = B * stride + extra_pages
@@ -361,9 +364,11 @@ def chunk_inputs(cfg: str = "c2", B: int = 2, C: int = 256, starts=(0, 700), Hq=
         for pg in range(-(-L // page_size)):
             table[b, pg] = perm[nxt]
             nxt += 1
-        for t in range(int(starts[b])):
-            pid = table[b, t // page_size]
-            k_pool[pid, :, t % page_size] = full.k[b, t]
-            v_pool[pid, :, t % page_size] = full.v[b, t]
+        for pg in range(int(starts[b]) // page_size + 1):
+            lo, hi = pg * page_size, min((pg + 1) * page_size, int(starts[b]))
+            if hi > lo:
+                pid = table[b, pg]
+                k_pool[pid, :, :hi - lo] = full.k[b, lo:hi].transpose(1, 0, 2)
+                v_pool[pid, :, :hi - lo] = full.v[b, lo:hi].transpose(1, 0, 2)
     return ChunkInputs(full=full, start_pos=starts, C=C, page_size=page_size, k_pool=k_pool,
                        v_pool=v_pool, page_table=table, max_seq_len=max_seq_len)
