@@ -8,7 +8,9 @@ from .polar_oracle import (length_temperature, null_floor, polar_prefill, polar_
                            FLAG_LENGTH_TEMP, FLAG_NULL_FLOOR)
 
 from .polar_grad import polar_prefill_grad, arg_max_keys
+from .delta_oracle import delta_step, delta_step_pool, l2_normalize
 
-__all__ = ["polar_prefill_grad", "arg_max_keys", "length_temperature", "null_floor", "polar_prefill", "polar_decode_paged",
+__all__ = ["polar_prefill_grad", "arg_max_keys", "delta_step", "delta_step_pool", "l2_normalize",
+           "length_temperature", "null_floor", "polar_prefill", "polar_decode_paged",
            "gather_pages", "rope", "kv_append", "polar_prefill_paged",
            "FLAG_LENGTH_TEMP", "FLAG_NULL_FLOOR"]

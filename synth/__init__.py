@@ -8,8 +8,9 @@ arithmetic; both the CPU oracle and the GPU path consume what it returns.
 from .workloads import (CONFIGS, PrefillInputs, DecodeInputs, prefill_inputs,
                         decode_inputs, round_bf16, bf16_bits_to_f32, FLAG_LENGTH_TEMP,
                         FLAG_NULL_FLOOR, Cotangents, cotangents, ChunkInputs,
-                        chunk_inputs)
+                        chunk_inputs, DeltaInputs, delta_inputs)
 
 __all__ = ["CONFIGS", "PrefillInputs", "DecodeInputs", "prefill_inputs", "decode_inputs",
            "round_bf16", "bf16_bits_to_f32", "FLAG_LENGTH_TEMP", "FLAG_NULL_FLOOR", "Cotangents",
-           "cotangents", "ChunkInputs", "chunk_inputs"]
+           "cotangents", "ChunkInputs", "chunk_inputs",
+           "DeltaInputs", "delta_inputs"]

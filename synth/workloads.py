@@ -372,3 +372,40 @@ def chunk_inputs(cfg: str = "c2", B: int = 2, C: int = 256, starts=(0, 700), Hq=
                 v_pool[pid, :, :hi - lo] = full.v[b, lo:hi].transpose(1, 0, 2)
     return ChunkInputs(full=full, start_pos=starts, C=C, page_size=page_size, k_pool=k_pool,
                        v_pool=v_pool, page_table=table, max_seq_len=max_seq_len)
+
+
+# --------------------------------------------------------------------------- memory step
+@dataclasses.dataclass
+class DeltaInputs:
+    """One gated-delta memory step for B sequences whose states live in a slot pool."""
+    dtype: str                 # q, k, v storage: "bf16" (bit patterns) or "f32"
+    pool: np.ndarray           # [num_slots, H, d_v, d_k] float32
+    slots: np.ndarray          # [B] int32, distinct
+    q: np.ndarray              # [B, H, d_k]
+    k: np.ndarray              # [B, H, d_k]
+    v: np.ndarray              # [B, H, d_v]
+    alpha: np.ndarray          # [B, H] float32 gate in (0, 1]
+    beta: np.ndarray           # [B, H] float32 write strength in (0, 1)
+
+    def as_f32(self, name: str) -> np.ndarray:
+        a = getattr(self, name)
+        return bf16_bits_to_f32(a) if self.dtype == "bf16" else a
+
+
+def delta_inputs(B: int = 256, H: int = 16, num_slots: int = 1024, d_k: int = 64, d_v: int = 64,
+                 dtype: str = "bf16", seed: int = 4001) -> DeltaInputs:
+    """States N(0, 1/d_k) (a memory of unit-scale writes), q, k, v N(0, 1) (the kernel
+    normalises q and k), gates alpha ~ U(0.9, 1) and beta ~ U(0, 1), and a random choice
+    of B distinct pool slots."""
+    s = np.random.SeedSequence(seed).spawn(6)
+    pool = (_normal(s[0], (num_slots, H, d_v, d_k)) / np.float32(np.sqrt(d_k))).astype(np.float32)
+    q = _normal(s[1], (B, H, d_k))
+    k = _normal(s[2], (B, H, d_k))
+    v = _normal(s[3], (B, H, d_v))
+    g = np.random.Generator(np.random.PCG64(s[4]))
+    alpha = g.uniform(0.9, 1.0, (B, H)).astype(np.float32)
+    beta = g.uniform(0.0, 1.0, (B, H)).astype(np.float32)
+    slots = np.random.Generator(np.random.PCG64(s[5])).permutation(num_slots)[:B].astype(np.int32)
+    if dtype == "bf16":
+        q, k, v = round_bf16(q), round_bf16(k), round_bf16(v)
+    return DeltaInputs(dtype=dtype, pool=pool, slots=slots, q=q, k=k, v=v, alpha=alpha, beta=beta)
