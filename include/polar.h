@@ -284,6 +284,41 @@ POLAR_API polar_status polar_attn_prefill_paged(const polar_params *p, polar_dty
                                       const int32_t *start_pos, int32_t max_seq_len,
                                       const polar_outputs *out, void *stream);
 
+/* ---------------------------------------------------------------------------------
+ * Recurrent memory stream: the in-place gated-delta step (section 2.1's third channel, a
+ * gated-delta memory derived from gated DeltaNet with L2-normalised keys and queries; its
+ * step kernel of section 2.2 updates the recurrent state in place, without gathering
+ * states into a batch and scattering them back).  The pages print no update rule; this is
+ * the gated delta rule, one token per sequence:
+ *   k <- k/|k|, q <- q/|q|            (when POLAR_DELTA_NORMALIZE_QK; |x| = sqrt(x.x + 1e-12))
+ *   S' = alpha S (I - beta k k^T) + beta v k^T,   o = S' q
+ * with S the [d_v, d_k] state of one (sequence, head).
+ * --------------------------------------------------------------------------------- */
+enum { POLAR_DELTA_NORMALIZE_QK = 1u };
+
+typedef struct {
+  int32_t n_heads;                  /* H >= 1                                              */
+  int32_t key_dim;                  /* d_k; must be 64 in version 1                        */
+  int32_t value_dim;                /* d_v; must be 64 in version 1                        */
+  uint32_t flags;                   /* POLAR_DELTA_* bits                                  */
+} polar_delta_params;
+
+/*
+ * One step for B sequences.
+ *   state_pool  device float32 [num_slots, H, d_v, d_k], row-major; sequence b's state is
+ *               slot slots[b] and is updated in place.  Slots outside [0, num_slots) are
+ *               skipped (their outputs are zero, no state is touched).  Two sequences
+ *               naming the same slot race (unspecified result).
+ *   slots       device int32 [B].
+ *   q, k        [B,H,d_k] and v [B,H,d_v], dtype `dt`, 16-byte aligned.
+ *   alpha, beta device float32 [B,H]: gate and write strength (normally in [0, 1]).
+ *   out         device float32 [B,H,d_v], 16-byte aligned: o = S' q.
+ */
+POLAR_API polar_status polar_delta_step(const polar_delta_params *p, polar_dtype dt, int32_t B,
+                              float *state_pool, int32_t num_slots, const int32_t *slots,
+                              const void *q, const void *k, const void *v, const float *alpha,
+                              const float *beta, float *out, void *stream);
+
 /* Static description of a status code. */
 POLAR_API const char *polar_status_str(polar_status s);
 /* Thread-local detail of the last non-OK return on this thread ("" if none). */

@@ -26,10 +26,12 @@ POLAR_DTYPE_BF16 = 1
 
 POLAR_FLAG_LENGTH_TEMP = 1
 POLAR_FLAG_NULL_FLOOR = 2
+POLAR_DELTA_NORMALIZE_QK = 1
 
 EXPORTS = ("polar_attn_fwd", "polar_decode_workspace_bytes", "polar_attn_decode_paged",
            "polar_attn_fwd_train", "polar_bwd_workspace_bytes", "polar_attn_bwd",
            "polar_attn_fwd_variant", "polar_kv_append", "polar_attn_prefill_paged",
+           "polar_delta_step",
            "polar_status_str", "polar_last_error", "polar_abi_version")
 
 
@@ -44,6 +46,11 @@ class polar_outputs(ctypes.Structure):
     _fields_ = [("dir", ctypes.c_void_p), ("count", ctypes.c_void_p),
                 ("n_eff", ctypes.c_void_p), ("gate", ctypes.c_void_p),
                 ("lse", ctypes.c_void_p)]
+
+
+class polar_delta_params(ctypes.Structure):
+    _fields_ = [("n_heads", ctypes.c_int32), ("key_dim", ctypes.c_int32),
+                ("value_dim", ctypes.c_int32), ("flags", ctypes.c_uint32)]
 
 
 class polar_variant(ctypes.Structure):
@@ -113,6 +120,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.polar_attn_prefill_paged.restype = I32
     lib.polar_attn_prefill_paged.argtypes = [P(polar_params), I32, I32, I32, VP, VP, VP, I32, I32,
                                              VP, I32, VP, I32, P(polar_outputs), VP]
+    lib.polar_delta_step.restype = I32
+    lib.polar_delta_step.argtypes = [P(polar_delta_params), I32, I32, VP, I32, VP, VP, VP, VP, VP,
+                                     VP, VP, VP]
     lib.polar_status_str.restype = ctypes.c_char_p
     lib.polar_status_str.argtypes = [I32]
     lib.polar_last_error.restype = ctypes.c_char_p
@@ -178,6 +188,12 @@ def polar_attn_prefill_paged(params, dtype, B, C, q, k_cache, v_cache, num_pages
     return load().polar_attn_prefill_paged(ctypes.byref(params), dtype, B, C, q, k_cache,
                                            v_cache, num_pages, page_size, page_table, stride,
                                            start_pos, max_seq_len, ctypes.byref(outputs), stream)
+
+
+def polar_delta_step(params, dtype, B, state_pool, num_slots, slots, q, k, v, alpha, beta, out,
+                     stream) -> int:
+    return load().polar_delta_step(ctypes.byref(params), dtype, B, state_pool, num_slots, slots,
+                                   q, k, v, alpha, beta, out, stream)
 
 
 def polar_bwd_workspace_bytes(params, B, T) -> int:

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libpolar.so")
 SOURCES = ["polar_api.cpp", "polar_prefill.hip", "polar_decode.hip", "polar_backward.hip",
-           "polar_paged.hip"]
+           "polar_paged.hip", "polar_delta.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -71,6 +71,17 @@ struct AppendArgs {
 };
 hipError_t launch_kv_append(const AppendArgs &a, hipStream_t stream);
 
+// In-place gated-delta memory step (states [num_slots,H,d,d] fp32, d = kHeadDim).
+struct DeltaArgs {
+  float *pool;
+  const int32_t *slots;                   // [B]
+  const void *q, *k, *v;                  // [B,H,d]
+  const float *alpha, *beta;              // [B,H]
+  float *out;                             // [B,H,d]
+  int B, H, num_slots, normalize;
+};
+hipError_t launch_delta_step(int dtype, const DeltaArgs &a, hipStream_t stream);
+
 // Backward pass of the causal prefill (bf16 inputs).  Per-row quantities (float4 each;
 // r0 and r1 of a row are adjacent in `rows`):
 //   r0 = {c*log2(e), lse*log2(e), c*A, c*E}   r1 = {A, E, dm, arg-max key (int bits)}

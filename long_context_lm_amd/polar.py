@@ -264,3 +264,30 @@ def attn_prefill_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Te
         page, page_table.data_ptr(), page_table.shape[1], start_pos.data_ptr(), max_seq_len,
         cout, s))
     return out
+
+
+def delta_step(state_pool: torch.Tensor, slots: torch.Tensor, q: torch.Tensor, k: torch.Tensor,
+               v: torch.Tensor, alpha: torch.Tensor, beta: torch.Tensor,
+               normalize_qk: bool = True, stream=None) -> torch.Tensor:
+    """In-place gated-delta memory step (see polar_delta_step): updates
+    state_pool[slots[b]] for every sequence b and returns o [B,H,d_v] (float32)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check_input(t, n)
+    if state_pool.dtype != torch.float32 or not state_pool.is_contiguous():
+        raise ValueError("state_pool must be a contiguous float32 tensor")
+    num_slots, H, dv, dk = state_pool.shape
+    B = q.shape[0]
+    if q.shape != (B, H, dk) or k.shape != q.shape or v.shape != (B, H, dv):
+        raise ValueError("q, k must be [B,H,d_k] and v [B,H,d_v] matching the pool")
+    if slots.dtype != torch.int32 or slots.shape != (B,):
+        raise ValueError("slots must be int32 [B]")
+    dev = q.device
+    alpha = torch.as_tensor(alpha, dtype=torch.float32, device=dev).contiguous()
+    beta = torch.as_tensor(beta, dtype=torch.float32, device=dev).contiguous()
+    out = torch.empty(B, H, dv, device=dev, dtype=torch.float32)
+    prm = _lib.polar_delta_params(H, dk, dv, _lib.POLAR_DELTA_NORMALIZE_QK if normalize_qk else 0)
+    s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+    _lib.check(_lib.polar_delta_step(prm, _DT[q.dtype], B, state_pool.data_ptr(), num_slots,
+                                     slots.data_ptr(), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                     alpha.data_ptr(), beta.data_ptr(), out.data_ptr(), s))
+    return out

@@ -301,3 +301,35 @@ def test_chunked_prefill_validation_errors(kw, code):
 def test_empty_append_and_chunk():
     assert app(C=0, kn=None, vn=None) == _lib.POLAR_OK
     assert chunk(B=0, q=None) == _lib.POLAR_OK
+
+
+# ------------------------------------------------------------------ gated-delta memory step
+def dstep(H=4, dk=64, dv=64, flags=1, dt=1, B=3, pool=A, num_slots=8, slots=A, q=A, k=A, v=A,
+          al=A, be=A, out=A):
+    prm = _lib.polar_delta_params(H, dk, dv, flags)
+    return _lib.polar_delta_step(prm, dt, B, pool, num_slots, slots, q, k, v, al, be, out, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dk=32), _lib.POLAR_ERR_UNSUPPORTED),
+    (dict(dv=128), _lib.POLAR_ERR_UNSUPPORTED),
+    (dict(flags=2), _lib.POLAR_ERR_UNSUPPORTED),
+    (dict(dt=3), _lib.POLAR_ERR_UNSUPPORTED),
+    (dict(H=0), _lib.POLAR_ERR_BAD_SHAPE),
+    (dict(B=-1), _lib.POLAR_ERR_BAD_SHAPE),
+    (dict(num_slots=0), _lib.POLAR_ERR_BAD_SHAPE),
+    (dict(slots=None), _lib.POLAR_ERR_NULL_POINTER),
+    (dict(be=None), _lib.POLAR_ERR_NULL_POINTER),
+    (dict(pool=A + 4), _lib.POLAR_ERR_MISALIGNED),
+    (dict(out=A + 8), _lib.POLAR_ERR_MISALIGNED),
+])
+def test_delta_step_validation_errors(kw, code):
+    assert dstep(**kw) == code
+    assert _lib.polar_last_error() != ""
+
+
+def test_delta_step_empty_and_null_params():
+    assert dstep(B=0, pool=None, slots=None, q=None) == _lib.POLAR_OK
+    lib = _lib.load()
+    assert lib.polar_delta_step(None, 1, 1, A, 1, A, A, A, A, A, A, A, None) == \
+        _lib.POLAR_ERR_NULL_POINTER
