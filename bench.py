@@ -15,6 +15,8 @@ forward count).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
        python bench.py --copy-probe BYTES   (plain device copy, for counter calibration)
+       python bench.py --memory-step-probe fused|ref --steps K
+                                            (one form of the memory step, for counters)
 """
 from __future__ import annotations
 
@@ -41,6 +43,7 @@ KERNEL_SOURCES = {
     "prefill": ["polar_prefill.hip", "polar_mfma.h", "polar_kernels.h"],
     "decode": ["polar_decode.hip", "polar_mfma.h", "polar_kernels.h"],
     "backward": ["polar_backward.hip", "polar_mfma.h", "polar_kernels.h"],
+    "memory_step": ["polar_delta.hip", "polar_kernels.h"],
 }
 
 
@@ -262,6 +265,95 @@ def measure_paged(dev, pre, steps: int, warmup: int):
                                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}}}
 
 
+def _delta_setup(dev):
+    import torch
+    import synth
+    d = synth.delta_inputs()                     # B=256 sequences, H=16, 1024-slot pool
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    return d, (torch.from_numpy(d.pool).to(dev), torch.from_numpy(d.slots).to(dev), bf(d.q),
+               bf(d.k), bf(d.v), torch.from_numpy(d.alpha).to(dev), torch.from_numpy(d.beta).to(dev))
+
+
+def delta_step_reference(pool, slots, q, k, v, alpha, beta):
+    """The same step written as separate torch operations on a gathered batch and scattered
+    back (the gather-scatter form the pages' in-place kernel replaces).  Measurement aid."""
+    import torch
+    idx = slots.long()
+    S = pool[idx]                                            # gather  [B,H,dv,dk]
+    qn = torch.nn.functional.normalize(q.float(), dim=-1, eps=1e-6)
+    kn = torch.nn.functional.normalize(k.float(), dim=-1, eps=1e-6)
+    Sk = torch.matmul(S, kn.unsqueeze(-1)).squeeze(-1)
+    Sq = torch.matmul(S, qn.unsqueeze(-1)).squeeze(-1)
+    u = beta.unsqueeze(-1) * (v.float() - alpha.unsqueeze(-1) * Sk)
+    S = alpha[..., None, None] * S + u.unsqueeze(-1) * kn.unsqueeze(-2)
+    o = alpha.unsqueeze(-1) * Sq + u * (kn * qn).sum(-1, keepdim=True)
+    pool[idx] = S                                            # scatter
+    return o
+
+
+def measure_memory_step(dev, steps: int, warmup: int, with_cpu: bool = False):
+    """In-place gated-delta step for 256 sequences x 16 heads (64x64 fp32 states in a
+    1024-slot pool), and the gather-scatter torch form of the same step beside it."""
+    import torch
+    from long_context_lm_amd import delta_step
+    d, (pool, sl, q, k, v, al, be) = _delta_setup(dev)
+    B, H = d.q.shape[:2]
+    times = {}
+    for name, fn in (("fused", lambda: delta_step(pool, sl, q, k, v, al, be)),
+                     ("reference", lambda: delta_step_reference(pool, sl, q, k, v, al, be))):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        for e in ev:
+            e[0].record()
+            fn()
+            e[1].record()
+        torch.cuda.synchronize()
+        times[name] = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    state = B * H * 64 * 64 * 4
+    algo = 2.0 * state + B * H * 64 * (3 * 2 + 4) + B * H * 8 + B * 4
+    gbs = algo / (times["fused"] * 1e-3) / 1e9
+    print(f"[bench] memory step: fused {times['fused'] * 1e3:.1f} us ({gbs:.0f} GB/s), "
+          f"gather-scatter torch form {times['reference'] * 1e3:.1f} us", file=sys.stderr,
+          flush=True)
+    rec = {"workload": "in-place gated-delta memory step, 256 sequences x 16 heads, 64x64 fp32 "
+                       "states in a 1024-slot pool, bf16 q/k/v",
+           "value": round(gbs, 1), "unit": "GB/s", "us": round(times["fused"] * 1e3, 2),
+           "reference_us": round(times["reference"] * 1e3, 2),
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                        "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                        "traffic": traffic_record("memory_step")}}
+    if with_cpu:
+        import oracle
+        t0 = time.perf_counter()
+        oracle.delta_step_pool(d.pool, d.slots, d.as_f32("q"), d.as_f32("k"), d.as_f32("v"),
+                               d.alpha, d.beta)
+        t = time.perf_counter() - t0
+        rec["cpu_baseline"] = {"value": round(algo / t / 1e9, 3), "unit": "GB/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"float64 step of all 256 x 16 states ({t:.1f} s)"}
+    return rec
+
+
+def memory_step_probe(which: str, steps: int):
+    """Run only one form of the memory step (for per-step HBM counters)."""
+    import torch
+    from long_context_lm_amd import _lib, delta_step
+    _lib.load()
+    d, (pool, sl, q, k, v, al, be) = _delta_setup("cuda")
+    fn = (lambda: delta_step(pool, sl, q, k, v, al, be)) if which == "fused" else \
+        (lambda: delta_step_reference(pool, sl, q, k, v, al, be))
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    print(json.dumps({"memory_step_probe": which, "steps": steps}))
+
+
 def copy_probe(nbytes: int):
     import torch
     a = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
@@ -279,6 +371,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0)
+    ap.add_argument("--memory-step-probe", choices=("fused", "ref"), default=None)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the Polar Attention path here is a single-GPU "
@@ -287,6 +380,9 @@ def main():
         sys.exit(2)
     if args.copy_probe:
         copy_probe(args.copy_probe)
+        return
+    if args.memory_step_probe:
+        memory_step_probe(args.memory_step_probe, args.steps)
         return
 
     import torch
@@ -377,6 +473,8 @@ def main():
     torch.cuda.empty_cache()
     rec["backward"] = measure_backward(dev, max(1, args.steps // 2), args.warmup,
                                        not args.no_cpu_baseline)
+    rec["memory_step"] = measure_memory_step(dev, args.steps, args.warmup,
+                                             not args.no_cpu_baseline)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(pre, dec)
