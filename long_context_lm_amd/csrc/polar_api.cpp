@@ -196,7 +196,7 @@ size_t polar_bwd_workspace_bytes(const polar_params *p, int32_t B, int32_t T) {
   if (!p || B < 1 || T < 1 || p->n_kv_heads < 1 || p->n_q_heads < 1 ||
       p->n_q_heads % p->n_kv_heads != 0 || !bwd_shape_ok(B, T, p->n_q_heads, p->n_kv_heads))
     return 0;
-  return polar::bwd_ws_bytes(B, T, p->n_q_heads);
+  return polar::bwd_ws_bytes(B, T, p->n_q_heads, p->n_kv_heads);
 }
 
 polar_status polar_attn_bwd(const polar_params *p, polar_dtype dt, int32_t B, int32_t T,
@@ -245,7 +245,7 @@ polar_status polar_attn_bwd(const polar_params *p, polar_dtype dt, int32_t B, in
   if (!bwd_shape_ok(B, T, Hq, p->n_kv_heads))
     return fail(POLAR_ERR_BAD_SHAPE, "T*Hq too large for the backward (B=%d, T=%d, Hq=%d)", B,
                 T, Hq);
-  const size_t need = polar::bwd_ws_bytes(B, T, Hq);
+  const size_t need = polar::bwd_ws_bytes(B, T, Hq, p->n_kv_heads);
   if (workspace_bytes < need)
     return fail(POLAR_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed",
                 workspace_bytes, need);
@@ -284,11 +284,12 @@ polar_status polar_attn_bwd(const polar_params *p, polar_dtype dt, int32_t B, in
   a.n_row_blocks = (T + rows - 1) / rows;
   const int keys = polar::bwd_keys_per_block();
   a.n_key_blocks = (T + keys - 1) / keys;
+  a.hsplit = (a.G % 2 == 0) ? 2 : 1;
   a.inv_log_train = inv_log_train(p);
   a.null_floor = (p->flags & POLAR_FLAG_NULL_FLOOR) ? 1 : 0;
   polar::bwd_ws_layout(a, workspace);
   const long long dq_blocks = (long long)a.n_row_blocks * a.Hkv * (a.G / a.hb) * B;
-  const long long dkv_blocks = (long long)((a.n_key_blocks + 1) / 2) * a.Hkv * B;
+  const long long dkv_blocks = (long long)((a.n_key_blocks + 1) / 2) * a.hsplit * a.Hkv * B;
   if (dq_blocks > 0x7fffffffLL || dkv_blocks > 0x7fffffffLL)
     return fail(POLAR_ERR_BAD_SHAPE, "problem too large for one launch");
   hipError_t err = polar::launch_bwd(a, (hipStream_t)stream);

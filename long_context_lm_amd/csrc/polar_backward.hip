@@ -38,6 +38,10 @@ constexpr int kD = kHeadDim;
 constexpr int kBufferFlags = 0x00020000;   // gfx9 buffer resource word 3 (raw dword access)
 constexpr int kDqWaves = 8;
 constexpr int kDkvWaves = 4;
+#ifndef POLAR_BWD_DEPTH
+#define POLAR_BWD_DEPTH 1
+#endif
+constexpr int kDkvDepth = POLAR_BWD_DEPTH;   // query tiles in flight ahead of the compute
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 using F = bf16x8;
@@ -337,7 +341,7 @@ __global__ void __launch_bounds__(64 * kWaves) polar_bwd_dq_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------------------ 3. dk / dv
-template <int kWaves>
+template <int kWaves, int kDepth>
 __global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 polar_bwd_dkv_kernel(BwdArgs a) {
   constexpr int kThreads = 64 * kWaves;
@@ -362,8 +366,13 @@ polar_bwd_dkv_kernel(BwdArgs a) {
   const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
   const int unit = xcd * (nblk >> 3) + min(xcd, nblk & 7) + local;
   const int npair = (a.n_key_blocks + 1) >> 1;
-  const int pair = unit % npair;
-  const int bg = unit / npair;
+  const int pair = (unit % (npair * a.hsplit)) / a.hsplit;
+  const int hpart = unit % a.hsplit;
+  const int bg = unit / (npair * a.hsplit);
+  // With hsplit = 2 the G query heads of the group are shared by two workgroups: the first
+  // writes dk/dv, the second a partial that a follow-up kernel adds in.
+  const int GH = a.G / a.hsplit;                    // heads walked by this workgroup
+  const int hbase = hpart * GH;
   const int g = bg % a.Hkv, b = bg / a.Hkv;
   const int nrt = (a.T + 31) / 32;
   const int rs = a.Hq * kD * 2;                     // bytes between rows of q / du
@@ -376,12 +385,20 @@ polar_bwd_dkv_kernel(BwdArgs a) {
   const int voff_p1 = voff_p0 + rs;
   const int voff_s = (tid & 31) * a.Hq * 32 + (tid >> 5) * 16;   // r0 (tid < 32) or r1
 
-  u32x4 qst, cst;
-  u32x2 qtst[2], dtst[2];
-  f32x4 sst;
-  auto stage_load = [&](int s) {
-    const int r0row = (nrt - 1 - s / a.G) * 32;
-    const int h = g * a.G + s % a.G;
+  // Staged query-side data of one step: q and c*du row chunks, q and du pair tasks, and
+  // (threads < 64) one row record.  kDepth sets are in flight.
+  struct Stage {
+    u32x4 qst, cst;
+    u32x2 qtst[2], dtst[2];
+    f32x4 sst;
+  };
+  Stage st[kDepth];
+  auto stage_load = [&](Stage &R, int s) {
+    u32x4 &qst = R.qst, &cst = R.cst;
+    u32x2 *qtst = R.qtst, *dtst = R.dtst;
+    f32x4 &sst = R.sst;
+    const int r0row = (nrt - 1 - s / GH) * 32;
+    const int h = g * a.G + hbase + s % GH;
     const size_t row0 = ((size_t)b * a.T + r0row) * a.Hq + h;
     const int nbytes = (int)(((size_t)(a.T - r0row) * a.Hq - h) * kD * 2);
     const auto qr = __builtin_amdgcn_make_buffer_rsrc(
@@ -404,8 +421,11 @@ polar_bwd_dkv_kernel(BwdArgs a) {
     }
   };
   // Rows past T: p = 0 (lse2 = +inf), zero coefficients, no arg-max key.
-  auto stage_store = [&](int buf, int s) {
-    if (tid < 64 && (nrt - 1 - s / a.G) * 32 + (tid & 31) >= a.T) {
+  auto stage_store = [&](Stage &R, int buf, int s) {
+    const u32x4 &qst = R.qst, &cst = R.cst;
+    const u32x2 *qtst = R.qtst, *dtst = R.dtst;
+    f32x4 &sst = R.sst;
+    if (tid < 64 && (nrt - 1 - s / GH) * 32 + (tid & 31) >= a.T) {
       const f32x4 pad0 = {1.f, INFINITY, 0.f, 0.f};
       const f32x4 pad1 = {0.f, 0.f, 0.f, __int_as_float(-1)};
       sst = tid < 32 ? pad0 : pad1;
@@ -460,73 +480,85 @@ polar_bwd_dkv_kernel(BwdArgs a) {
         dV[db][r] = 0.f;
       }
 
-    const int nsteps = (nrt - k0 / 32) * a.G;
-    if (nsteps > 0) {
-      stage_load(0);
-      stage_store(0, 0);
-    }
+    const int nsteps = (nrt - k0 / 32) * GH;
+    // Pipeline: step s computes from LDS buffer s&1; at its end, step s+1's staged set is
+    // stored to the other buffer and refilled with step s+1+kDepth, so every load has
+    // kDepth steps to arrive.  The step loop is unrolled by kDepth to keep set indices
+    // compile-time constants.
+#pragma unroll
+    for (int u = 0; u < kDepth; ++u)
+      if (u < nsteps) stage_load(st[u], u);
+    if (nsteps > 0) stage_store(st[0], 0, 0);
+    if (kDepth < nsteps) stage_load(st[0], kDepth);
     __syncthreads();
-    for (int s = 0; s < nsteps; ++s) {
-      const int buf = s & 1;
-      const bool more = s + 1 < nsteps;
-      if (more) stage_load(s + 1);
-      const int r0row = (nrt - 1 - s / a.G) * 32;
-      if (r0row + 31 >= kw0 && kw0 < a.T) {
-        const uint16_t *Qb = lds_at(&Qs[0][0], q_lane + buf * QBUF);
-        const uint16_t *Cb = lds_at(&Cs[0][0], q_lane + buf * QBUF);
-        const f32x16 zero = {};
-        f32x16 S, P;
+    for (int s0 = 0; s0 < nsteps; s0 += kDepth) {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          S = Bf16::mma32(*(const F *)(Qb + ks * 16), kf[ks], ks == 0 ? zero : S);
-          P = Bf16::mma32(*(const F *)(Cb + ks * 16), vf[ks], ks == 0 ? zero : P);
-        }
-        const bool diag = r0row < kw0 + 31;
-        float pv[16], dsv[16];
+      for (int u = 0; u < kDepth; ++u) {
+        const int s = s0 + u;
+        if (s >= nsteps) break;
+        const int buf = s & 1;
+        const int r0row = (nrt - 1 - s / GH) * 32;
+        if (r0row + 31 >= kw0 && kw0 < a.T) {
+          const uint16_t *Qb = lds_at(&Qs[0][0], q_lane + buf * QBUF);
+          const uint16_t *Cb = lds_at(&Cs[0][0], q_lane + buf * QBUF);
+          const f32x16 zero = {};
+          f32x16 S, P;
 #pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
-          const int ri0 = 8 * a4 + 4 * g32;
-          const f32x4 cl = *(const f32x4 *)&Sc[buf][0][ri0];
-          const f32x4 ls = *(const f32x4 *)&Sc[buf][1][ri0];
-          const f32x4 ac = *(const f32x4 *)&Sc[buf][2][ri0];
-          const f32x4 ec = *(const f32x4 *)&Sc[buf][3][ri0];
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const int r = 4 * a4 + c;
-            float p = fast_exp2(fmaf(S[r], cl[c], -ls[c]));
-            if (diag && r0row + ri0 + c < key) p = 0.f;
-            pv[r] = p;
-            dsv[r] = p * (P[r] + fmaf(ec[c], p, ac[c]));
+          for (int ks = 0; ks < 4; ++ks) {
+            S = Bf16::mma32(*(const F *)(Qb + ks * 16), kf[ks], ks == 0 ? zero : S);
+            P = Bf16::mma32(*(const F *)(Cb + ks * 16), vf[ks], ks == 0 ? zero : P);
           }
-        }
-        // Rows whose arg-max key belongs to this wave (rare): add c*dm at that key.
-        const int jl = __float_as_int(Sc[buf][5][c32]);
-        if (__ballot(jl >= kw0 && jl < kw0 + 32) != 0) {
+          const bool diag = r0row < kw0 + 31;
+          float pv[16], dsv[16];
 #pragma unroll
           for (int a4 = 0; a4 < 4; ++a4) {
             const int ri0 = 8 * a4 + 4 * g32;
-            const f32x4 jv = *(const f32x4 *)&Sc[buf][5][ri0];
-            const f32x4 dmv = *(const f32x4 *)&Sc[buf][4][ri0];
             const f32x4 cl = *(const f32x4 *)&Sc[buf][0][ri0];
+            const f32x4 ls = *(const f32x4 *)&Sc[buf][1][ri0];
+            const f32x4 ac = *(const f32x4 *)&Sc[buf][2][ri0];
+            const f32x4 ec = *(const f32x4 *)&Sc[buf][3][ri0];
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
-              if (__float_as_int(jv[c]) == key) dsv[4 * a4 + c] += dmv[c] * cl[c] * kLn2;
+            for (int c = 0; c < 4; ++c) {
+              const int r = 4 * a4 + c;
+              float p = fast_exp2(fmaf(S[r], cl[c], -ls[c]));
+              if (diag && r0row + ri0 + c < key) p = 0.f;
+              pv[r] = p;
+              dsv[r] = p * (P[r] + fmaf(ec[c], p, ac[c]));
+            }
+          }
+          // Rows whose arg-max key belongs to this wave (rare): add c*dm at that key.
+          const int jl = __float_as_int(Sc[buf][5][c32]);
+          if (__ballot(jl >= kw0 && jl < kw0 + 32) != 0) {
+#pragma unroll
+            for (int a4 = 0; a4 < 4; ++a4) {
+              const int ri0 = 8 * a4 + 4 * g32;
+              const f32x4 jv = *(const f32x4 *)&Sc[buf][5][ri0];
+              const f32x4 dmv = *(const f32x4 *)&Sc[buf][4][ri0];
+              const f32x4 cl = *(const f32x4 *)&Sc[buf][0][ri0];
+#pragma unroll
+              for (int c = 0; c < 4; ++c)
+                if (__float_as_int(jv[c]) == key) dsv[4 * a4 + c] += dmv[c] * cl[c] * kLn2;
+            }
+          }
+          const F pp0 = Bf16::pack(pv), pp1 = Bf16::pack(pv + 8);
+          const F dp0 = Bf16::pack(dsv), dp1 = Bf16::pack(dsv + 8);
+          const uint16_t *Db = lds_at(&Dt[0][0], t_lane + buf * TBUF);
+          const uint16_t *Tb = lds_at(&Qt[0][0], t_lane + buf * TBUF);
+#pragma unroll
+          for (int db = 0; db < 2; ++db) {
+            dV[db] = Bf16::mma32(*(const F *)(Db + db * 32 * TROW), pp0, dV[db]);
+            dK[db] = Bf16::mma32(*(const F *)(Tb + db * 32 * TROW), dp0, dK[db]);
+            dV[db] = Bf16::mma32(*(const F *)(Db + db * 32 * TROW + 16), pp1, dV[db]);
+            dK[db] = Bf16::mma32(*(const F *)(Tb + db * 32 * TROW + 16), dp1, dK[db]);
           }
         }
-        const F pp0 = Bf16::pack(pv), pp1 = Bf16::pack(pv + 8);
-        const F dp0 = Bf16::pack(dsv), dp1 = Bf16::pack(dsv + 8);
-        const uint16_t *Db = lds_at(&Dt[0][0], t_lane + buf * TBUF);
-        const uint16_t *Tb = lds_at(&Qt[0][0], t_lane + buf * TBUF);
-#pragma unroll
-        for (int db = 0; db < 2; ++db) {
-          dV[db] = Bf16::mma32(*(const F *)(Db + db * 32 * TROW), pp0, dV[db]);
-          dK[db] = Bf16::mma32(*(const F *)(Tb + db * 32 * TROW), dp0, dK[db]);
-          dV[db] = Bf16::mma32(*(const F *)(Db + db * 32 * TROW + 16), pp1, dV[db]);
-          dK[db] = Bf16::mma32(*(const F *)(Tb + db * 32 * TROW + 16), dp1, dK[db]);
+        if (s + 1 < nsteps) {
+          Stage &nx = st[(u + 1) % kDepth];                // constant once unrolled
+          stage_store(nx, buf ^ 1, s + 1);
+          if (s + 1 + kDepth < nsteps) stage_load(nx, s + 1 + kDepth);
         }
+        __syncthreads();
       }
-      if (more) stage_store(buf ^ 1, s + 1);
-      __syncthreads();
     }
 
     if (kvalid) {
@@ -542,10 +574,20 @@ polar_bwd_dkv_kernel(BwdArgs a) {
             kv[e] = dK[db][4 * j4 + e];
             vv[e] = dV[db][4 * j4 + e];
           }
-          *(f32x4 *)(a.dk + ob + d0) = kv;
-          *(f32x4 *)(a.dv + ob + d0) = vv;
+          *(f32x4 *)((hpart == 0 ? a.dk : a.dk_part) + ob + d0) = kv;
+          *(f32x4 *)((hpart == 0 ? a.dv : a.dv_part) + ob + d0) = vv;
         }
     }
+  }
+}
+
+// dk += dk_part, dv += dv_part (the second head half of the dk/dv kernel).
+__global__ void __launch_bounds__(256) polar_bwd_dkv_add_kernel(BwdArgs a) {
+  const size_t n4 = (size_t)a.B * a.T * a.Hkv * kD / 4;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
+    f32x4 *k = (f32x4 *)a.dk + i, *v = (f32x4 *)a.dv + i;
+    *k = *k + ((const f32x4 *)a.dk_part)[i];
+    *v = *v + ((const f32x4 *)a.dv_part)[i];
   }
 }
 
@@ -559,7 +601,25 @@ __global__ void __launch_bounds__(256) polar_bwd_param_kernel(BwdArgs a) {
   const long long lo = (long long)p * chunk;
   const long long hi = min(nr, lo + chunk);
   float dw = 0.f, dbeta = 0.f, dbias = 0.f;
-  for (long long rho = lo + sub; rho < hi; rho += 4) {
+  // Rows in a fixed order; four rows' loads are issued before their sums.
+  long long rho = lo + sub;
+  for (; rho + 12 < hi; rho += 16) {
+    f32x4 rp[4];
+    float cc[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const size_t rr = (size_t)(rho + 4 * u) * a.Hq + h;
+      rp[u] = *(const f32x4 *)(a.rp + 4 * rr);
+      cc[u] = a.c_count ? a.c_count[rr * kD + dim] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      dw = fmaf(rp[u][2], cc[u], dw);
+      dbeta += rp[u][0] + rp[u][3];
+      dbias += rp[u][1];
+    }
+  }
+  for (; rho < hi; rho += 4) {
     const size_t rr = (size_t)rho * a.Hq + h;
     const f32x4 rp = *(const f32x4 *)(a.rp + 4 * rr);
     if (a.c_count) dw = fmaf(rp[2], a.c_count[rr * kD + dim], dw);
@@ -583,7 +643,16 @@ __global__ void __launch_bounds__(128) polar_bwd_param_final_kernel(BwdArgs a) {
   const int h = blockIdx.x, tid = threadIdx.x;
   if (tid >= 66) return;
   float s = 0.f;
-  for (int p = 0; p < a.n_part; ++p) s += a.part[((size_t)h * a.n_part + p) * kPartStride + tid];
+  const float *pp = a.part + (size_t)h * a.n_part * kPartStride + tid;
+  int p = 0;
+  for (; p + 8 <= a.n_part; p += 8) {                // loads issued ahead, sums in order
+    float x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x[u] = pp[(size_t)(p + u) * kPartStride];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += x[u];
+  }
+  for (; p < a.n_part; ++p) s += pp[(size_t)p * kPartStride];
   if (tid < 64) {
     if (a.d_count_vec) a.d_count_vec[(size_t)h * kD + tid] = s;
   } else if (tid == 64) {
@@ -602,10 +671,11 @@ int n_parts(int B, int T) {
 
 }  // namespace
 
-size_t bwd_ws_bytes(int B, int T, int Hq) {
+size_t bwd_ws_bytes(int B, int T, int Hq, int Hkv) {
   const size_t nrows = (size_t)B * T * Hq;
   return 2 * align256(nrows * kD * 2) + align256(nrows * 32) + align256(nrows * 16) +
-         align256((size_t)Hq * n_parts(B, T) * kPartStride * 4);
+         align256((size_t)Hq * n_parts(B, T) * kPartStride * 4) +
+         2 * align256((size_t)B * T * Hkv * kD * 4);
 }
 
 void bwd_ws_layout(BwdArgs &a, void *ws) {
@@ -620,6 +690,10 @@ void bwd_ws_layout(BwdArgs &a, void *ws) {
   a.rp = (float *)p;
   p += align256(nrows * 16);
   a.part = (float *)p;
+  p += align256((size_t)a.Hq * n_parts(a.B, a.T) * kPartStride * 4);
+  a.dk_part = (float *)p;
+  p += align256((size_t)a.B * a.T * a.Hkv * kD * 4);
+  a.dv_part = (float *)p;
   a.n_part = n_parts(a.B, a.T);
 }
 
@@ -634,9 +708,15 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream) {
   const long long dq_blocks = (long long)a.n_row_blocks * a.Hkv * (a.G / a.hb) * a.B;
   hipLaunchKernelGGL((polar_bwd_dq_kernel<kDqWaves>), dim3((unsigned)dq_blocks),
                      dim3(64 * kDqWaves), 0, stream, a);
-  const long long dkv_blocks = (long long)((a.n_key_blocks + 1) / 2) * a.Hkv * a.B;
-  hipLaunchKernelGGL((polar_bwd_dkv_kernel<kDkvWaves>), dim3((unsigned)dkv_blocks),
+  const long long dkv_blocks =
+      (long long)((a.n_key_blocks + 1) / 2) * a.hsplit * a.Hkv * a.B;
+  hipLaunchKernelGGL((polar_bwd_dkv_kernel<kDkvWaves, kDkvDepth>), dim3((unsigned)dkv_blocks),
                      dim3(64 * kDkvWaves), 0, stream, a);
+  if (a.hsplit > 1) {
+    const long long n4 = (long long)a.B * a.T * a.Hkv * kD / 4;
+    hipLaunchKernelGGL(polar_bwd_dkv_add_kernel, dim3((unsigned)min((n4 + 255) / 256, 8192LL)),
+                       dim3(256), 0, stream, a);
+  }
   if (a.d_beta || a.d_null_bias || a.d_count_vec) {
     hipLaunchKernelGGL(polar_bwd_param_kernel, dim3(a.n_part, a.Hq), dim3(256), 0, stream, a);
     hipLaunchKernelGGL(polar_bwd_param_final_kernel, dim3(a.Hq), dim3(128), 0, stream, a);
