@@ -284,7 +284,7 @@ polar_status polar_attn_bwd(const polar_params *p, polar_dtype dt, int32_t B, in
   a.n_row_blocks = (T + rows - 1) / rows;
   const int keys = polar::bwd_keys_per_block();
   a.n_key_blocks = (T + keys - 1) / keys;
-  a.hsplit = (a.G % 2 == 0) ? 2 : 1;
+  a.hsplit = polar::bwd_head_split(a.G);
   a.inv_log_train = inv_log_train(p);
   a.null_floor = (p->flags & POLAR_FLAG_NULL_FLOOR) ? 1 : 0;
   polar::bwd_ws_layout(a, workspace);

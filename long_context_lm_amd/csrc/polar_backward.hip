@@ -42,6 +42,10 @@ constexpr int kDkvWaves = 4;
 #define POLAR_BWD_DEPTH 1
 #endif
 constexpr int kDkvDepth = POLAR_BWD_DEPTH;   // query tiles in flight ahead of the compute
+#ifndef POLAR_BWD_SPLIT
+#define POLAR_BWD_SPLIT 2
+#endif
+constexpr int kDkvSplitMax = POLAR_BWD_SPLIT;  // workgroups sharing one key block (by heads)
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 using F = bf16x8;
@@ -369,8 +373,8 @@ polar_bwd_dkv_kernel(BwdArgs a) {
   const int pair = (unit % (npair * a.hsplit)) / a.hsplit;
   const int hpart = unit % a.hsplit;
   const int bg = unit / (npair * a.hsplit);
-  // With hsplit = 2 the G query heads of the group are shared by two workgroups: the first
-  // writes dk/dv, the second a partial that a follow-up kernel adds in.
+  // With hsplit > 1 the G query heads of the group are shared by hsplit workgroups: the
+  // first writes dk/dv, the others partials that a follow-up kernel adds in, in order.
   const int GH = a.G / a.hsplit;                    // heads walked by this workgroup
   const int hbase = hpart * GH;
   const int g = bg % a.Hkv, b = bg / a.Hkv;
@@ -574,20 +578,25 @@ polar_bwd_dkv_kernel(BwdArgs a) {
             kv[e] = dK[db][4 * j4 + e];
             vv[e] = dV[db][4 * j4 + e];
           }
-          *(f32x4 *)((hpart == 0 ? a.dk : a.dk_part) + ob + d0) = kv;
-          *(f32x4 *)((hpart == 0 ? a.dv : a.dv_part) + ob + d0) = vv;
+          const size_t pofs = (size_t)(hpart - 1) * a.B * a.T * a.Hkv * kD;
+          *(f32x4 *)((hpart == 0 ? a.dk : a.dk_part + pofs) + ob + d0) = kv;
+          *(f32x4 *)((hpart == 0 ? a.dv : a.dv_part + pofs) + ob + d0) = vv;
         }
     }
   }
 }
 
-// dk += dk_part, dv += dv_part (the second head half of the dk/dv kernel).
+// dk += the partials of the other head groups of the dk/dv kernel, in a fixed order.
 __global__ void __launch_bounds__(256) polar_bwd_dkv_add_kernel(BwdArgs a) {
   const size_t n4 = (size_t)a.B * a.T * a.Hkv * kD / 4;
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
-    f32x4 *k = (f32x4 *)a.dk + i, *v = (f32x4 *)a.dv + i;
-    *k = *k + ((const f32x4 *)a.dk_part)[i];
-    *v = *v + ((const f32x4 *)a.dv_part)[i];
+    f32x4 k = ((const f32x4 *)a.dk)[i], v = ((const f32x4 *)a.dv)[i];
+    for (int p = 0; p < a.hsplit - 1; ++p) {
+      k = k + ((const f32x4 *)a.dk_part)[p * n4 + i];
+      v = v + ((const f32x4 *)a.dv_part)[p * n4 + i];
+    }
+    ((f32x4 *)a.dk)[i] = k;
+    ((f32x4 *)a.dv)[i] = v;
   }
 }
 
@@ -675,7 +684,7 @@ size_t bwd_ws_bytes(int B, int T, int Hq, int Hkv) {
   const size_t nrows = (size_t)B * T * Hq;
   return 2 * align256(nrows * kD * 2) + align256(nrows * 32) + align256(nrows * 16) +
          align256((size_t)Hq * n_parts(B, T) * kPartStride * 4) +
-         2 * align256((size_t)B * T * Hkv * kD * 4);
+         2 * align256((size_t)(kDkvSplitMax - 1) * B * T * Hkv * kD * 4);
 }
 
 void bwd_ws_layout(BwdArgs &a, void *ws) {
@@ -692,13 +701,18 @@ void bwd_ws_layout(BwdArgs &a, void *ws) {
   a.part = (float *)p;
   p += align256((size_t)a.Hq * n_parts(a.B, a.T) * kPartStride * 4);
   a.dk_part = (float *)p;
-  p += align256((size_t)a.B * a.T * a.Hkv * kD * 4);
+  p += align256((size_t)(kDkvSplitMax - 1) * a.B * a.T * a.Hkv * kD * 4);
   a.dv_part = (float *)p;
   a.n_part = n_parts(a.B, a.T);
 }
 
 int bwd_rows_per_block(int hb) { return (kDqWaves / hb) * 32; }
 int bwd_keys_per_block() { return 32 * kDkvWaves; }
+int bwd_head_split(int G) {
+  for (int s = kDkvSplitMax; s > 1; s >>= 1)
+    if (G % s == 0) return s;
+  return 1;
+}
 
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream) {
   const long long nrows = (long long)a.B * a.T * a.Hq;

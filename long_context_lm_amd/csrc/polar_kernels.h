@@ -100,11 +100,11 @@ struct BwdArgs {
   float *rows;                            // workspace: per-row r0, r1 (8 floats)
   float *rp;                              // workspace: per-row float4
   float *part;                            // workspace: [Hq][n_part][kPartStride]
-  float *dk_part, *dv_part;               // workspace: second head half of dk, dv
+  float *dk_part, *dv_part;               // workspace: dk, dv of head groups 1..hsplit-1
   int B, T, Hq, Hkv, G;
   int hb, n_row_blocks;                   // dq kernel: heads per workgroup, row blocks
   int n_key_blocks;                       // dk/dv kernel: key blocks per (b, KV head)
-  int hsplit;                             // dk/dv kernel: workgroups per key block (1 or 2)
+  int hsplit;                             // dk/dv kernel: workgroups per key block (divides G)
   int n_part;                             // parameter reduction: row chunks per head
   float inv_log_train;
   int null_floor;
@@ -115,6 +115,7 @@ size_t bwd_ws_bytes(int B, int T, int Hq, int Hkv);
 void bwd_ws_layout(BwdArgs &a, void *ws);  // sets du, cdu, rows, rp, part, dk/dv parts, n_part
 int bwd_rows_per_block(int hb);
 int bwd_keys_per_block();
+int bwd_head_split(int G);                // workgroups sharing one key block (divides G)
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream);
 
 }  // namespace polar

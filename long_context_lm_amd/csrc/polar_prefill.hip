@@ -69,10 +69,14 @@ template <> struct LdsCfg<F32> { static constexpr int kt = 64, krow = 68, vrow =
 constexpr int kModePlain = 0, kModeSave = 1, kModeVariant = 2, kModePaged = 3;
 
 // RoPE rotation angle of pair t at position pos: revolutions = frac(pos * f_t) taken
-// exactly from the 64-bit fixed-point product, then sin/cos of 2*pi*revolutions.
+// exactly from the 64-bit fixed-point product, then the hardware sine and cosine, whose
+// argument is in revolutions (the rotated values are rounded to bf16 afterwards, far
+// coarser than their error).
 __device__ __forceinline__ void rope_cs(uint64_t f, int pos, float &c, float &s) {
   const uint32_t hi = (uint32_t)(((uint64_t)(uint32_t)pos * f) >> 32);
-  sincospif(2.0f * ((float)hi * 2.3283064365386963e-10f), &s, &c);
+  const float rev = (float)hi * 2.3283064365386963e-10f;
+  s = __builtin_amdgcn_sinf(rev);
+  c = __builtin_amdgcn_cosf(rev);
 }
 
 template <class TR, int QB, int kWaves, int kMode>
