@@ -509,10 +509,14 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
   // issued a whole step earlier, so no VALU instruction waits on a recent MFMA result.
   // Tiles fully below the workgroup's first row need no mask; the diagonal tiles run one
   // at a time.  K and V use four LDS slots: tile t+3 is stored while tiles t..t+2 are live.
-  // Variant instances start at the first tile any row of the workgroup can see and run
-  // every tile through the masked path.
+  // Tiles [tf0, tf1) are seen whole by every row of the workgroup and take this pipelined
+  // path; the others are masked one at a time.  With a sliding window the loop starts at
+  // the first tile any row can see (t0) and the fully visible range starts at tf0.
   const int t0 = (kVar && a.window > 0) ? max(0, row0 - a.window + 1) / kKT : 0;
-  const int nfull = kVar ? 0 : min((pbase + row0 + 1) / kKT, ntiles);
+  const int tf1 = min((pbase + row0 + 1) / kKT, ntiles);
+  const int tf0 = (kVar && a.window > 0)
+                      ? min(tf1, (max(0, wg_last - a.window + 1) + kKT - 1) / kKT)
+                      : t0;
 
   for (int j = t0; j < t0 + 3 && j < ntiles; ++j) {
     stage_load(j);
@@ -531,11 +535,32 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
       raise_ref(qb, mx * cl2[qb]);
     }
   };
-  if (nfull > 0) {
-    score(0, Sa);
-    first_max(Sa, 0);
+  // One masked tile (window edges, diagonal, keys past the sequence).
+  auto masked_step = [&](int t) {
+    const bool stage = t + 3 < ntiles;
+    if (stage) stage_load(t + 3);
+    const int key0 = t * kKT;
+    bool live = key0 <= w_last;
+    if constexpr (kVar) live = live && (a.window == 0 || key0 + kKT > wrow0 - a.window + 1);
+    if (live) {
+      score(t % 4, Sa);
+      mask(Sa, key0);
+      first_max(Sa, key0);
+      probs(Sa, P);
+      pv_mma(t % 4, P);
+    }
+    if (stage) stage_store((t + 3) % 4, (t + 3) % 4);
+    __syncthreads();
+  };
+
+  int t = t0;
+  for (; t < tf0; ++t) masked_step(t);
+
+  if (tf1 > tf0) {
+    score(tf0 % 4, Sa);
+    first_max(Sa, tf0 * kKT);
   }
-  if (nfull > 1) score(1, Sb);
+  if (tf1 > tf0 + 1) score((tf0 + 1) % 4, Sb);
 
   auto pipe_step = [&](int t, Scores &S0, Scores &S1, Scores &S2) {
     const bool stage = t + 3 < ntiles;
@@ -543,7 +568,7 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
     score((t + 2) % 4, S2);
     probs(S0, P);
     pv_mma(t % 4, P);
-    const bool next_full = t + 1 < nfull;
+    const bool next_full = t + 1 < tf1;
     float mxs[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) mxs[qb] = tile_max(S1, qb);
@@ -560,31 +585,15 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
     __syncthreads();
   };
 
-  int t = t0;
-  while (t < nfull) {
+  while (t < tf1) {
     pipe_step(t, Sa, Sb, Sc);
-    if (++t >= nfull) break;
+    if (++t >= tf1) break;
     pipe_step(t, Sb, Sc, Sa);
-    if (++t >= nfull) break;
+    if (++t >= tf1) break;
     pipe_step(t, Sc, Sa, Sb);
     ++t;
   }
-  for (; t < ntiles; ++t) {
-    const bool stage = t + 3 < ntiles;
-    if (stage) stage_load(t + 3);
-    const int key0 = t * kKT;
-    bool live = key0 <= w_last;
-    if constexpr (kVar) live = live && (a.window == 0 || key0 + kKT > wrow0 - a.window + 1);
-    if (live) {
-      score(t % 4, Sa);
-      mask(Sa, key0);
-      first_max(Sa, key0);
-      probs(Sa, P);
-      pv_mma(t % 4, P);
-    }
-    if (stage) stage_store((t + 3) % 4, (t + 3) % 4);
-    __syncthreads();
-  }
+  for (; t < ntiles; ++t) masked_step(t);
 
   // ---- epilogue ----
   const float bias = a.null_bias ? a.null_bias[h] : 0.0f;
