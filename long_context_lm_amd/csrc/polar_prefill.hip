@@ -47,7 +47,8 @@
 #ifndef POLAR_PREFILL_KT
 #define POLAR_PREFILL_KT 64
 #endif
-// 1: probability sums on the matrix pipe (ones and Gram products); 0: fp32 adds/FMAs.
+// 1: probability sums on the matrix pipe (ones and Gram products); 0: on the vector pipe,
+// from the rounded probabilities the P.V product uses (dot2 per pair for bf16).
 #ifndef POLAR_PREFILL_MSTATS
 #define POLAR_PREFILL_MSTATS 0
 #endif
@@ -458,20 +459,12 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
         float pv[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) pv[r] = fast_exp2(fmaf(S.v[qb][kb][r], cl2[qb], negM));
-#if !POLAR_PREFILL_MSTATS
-        float s0 = 0.f, s1 = 0.f, q0 = 0.f, q1 = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          s0 += pv[r];
-          s1 += pv[r + 1];
-          q0 = fmaf(pv[r], pv[r], q0);
-          q1 = fmaf(pv[r + 1], pv[r + 1], q1);
-        }
-        Ssum[qb] += s0 + s1;
-        Qsum[qb] += q0 + q1;
-#endif
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) P.v[qb][kb][tt] = TR::pack(pv + tt * KPL);
+#if !POLAR_PREFILL_MSTATS
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) TR::stats(P.v[qb][kb][tt], Ssum[qb], Qsum[qb]);
+#endif
       }
     }
   };
