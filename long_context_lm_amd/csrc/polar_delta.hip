@@ -7,11 +7,13 @@
 // rewritten as  u = beta (v - alpha S k),  S' = alpha S + u k^T,  o = alpha S q + u (k.q),
 // so the 64 x 64 fp32 state is read once and written once where it lives in the pool.
 //
-// A 256-thread workgroup updates one (sequence, head) state at a time, NS in a row: thread
-// t owns row i = t/4 of the state and the 16 columns 16*(t%4)..+15, held in registers
-// between the read and the write, and the next state is loaded while the current one is
-// updated.  Row sums (S k, S q) and the dots (k.k, q.q, k.q) reduce over the 4 threads of
-// a row with lane shuffles in a fixed order.
+// A 256-thread workgroup updates one (sequence, head) state at a time, NS in a row, and
+// loads the next state while the current one is updated.  The state is read as 1024
+// 16-byte chunks in address order, chunk 256 j + t to thread t, so each load instruction
+// of a wave covers one contiguous kilobyte: thread t holds columns 4 (t%16)..+3 of rows
+// 16 j + t/16 (j = 0..3), in registers between the read and the write.  A row then lives
+// in one 16-lane DPP row, and the row sums (S k, S q) and the dots (k.k, q.q, k.q) reduce
+// over those 16 lanes in a fixed order that leaves the same value in all of them.
 #include "polar_kernels.h"
 
 namespace polar {
@@ -20,33 +22,34 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// Sum over the 4 lanes of a quad with DPP quad permutes (lane order fixed: (x0+x1)+(x2+x3)
-// in every lane).
-__device__ __forceinline__ float quad_sum(float x) {
+// Sum over the 16 lanes of a DPP row: quad butterflies, then the half-row and row mirrors.
+// Every lane computes ((x0+x1)+(x2+x3)) + ... in the same pairing, so all 16 lanes hold
+// the same bits.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_sum_step(float x) {
   const int xi = __float_as_int(x);
-  x += __int_as_float(__builtin_amdgcn_update_dpp(xi, xi, 0xB1, 0xF, 0xF, false));   // 1,0,3,2
-  const int yi = __float_as_int(x);
-  return x + __int_as_float(__builtin_amdgcn_update_dpp(yi, yi, 0x4E, 0xF, 0xF, false));  // 2,3,0,1
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(xi, xi, kCtrl, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x = dpp_sum_step<0xB1>(x);    // quad_perm 1,0,3,2
+  x = dpp_sum_step<0x4E>(x);    // quad_perm 2,3,0,1
+  x = dpp_sum_step<0x141>(x);   // row_half_mirror: quads 0<->1, 2<->3
+  return dpp_sum_step<0x140>(x);  // row_mirror: halves 0<->1
 }
 
-// 16 consecutive elements as floats.
-__device__ __forceinline__ void load16(const float *p, float *x) {
+// 4 consecutive elements as floats.
+__device__ __forceinline__ void load4(const float *p, float *x) {
+  const f32x4 w = *(const f32x4 *)p;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const f32x4 w = *(const f32x4 *)(p + 4 * j);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) x[4 * j + e] = w[e];
-  }
+  for (int e = 0; e < 4; ++e) x[e] = w[e];
 }
-__device__ __forceinline__ void load16(const uint16_t *p, float *x) {
+__device__ __forceinline__ void load4(const uint16_t *p, float *x) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 w = *(const u32x2 *)p;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const u32x4 w = *(const u32x4 *)(p + 8 * j);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      x[8 * j + 2 * e] = __uint_as_float(w[e] << 16);
-      x[8 * j + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
-    }
+  for (int e = 0; e < 2; ++e) {
+    x[2 * e] = __uint_as_float(w[e] << 16);
+    x[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
   }
 }
 __device__ __forceinline__ float load1(const float *p) { return *p; }
@@ -58,8 +61,9 @@ __device__ __forceinline__ float load1(const uint16_t *p) {
 // next state's slot, state row and vectors are loaded while the current one is updated.
 template <class E>
 struct DeltaLoad {
-  float s[16], q[16], k[16];
-  float v, alpha, beta;
+  f32x4 s[4];          // rows 16 j + t/16, columns 4 (t%16)..+3
+  float q[4], k[4], v[4];
+  float alpha, beta;
   int ok;
   float *S;
 };
@@ -67,54 +71,69 @@ struct DeltaLoad {
 template <class E, int NS>
 __global__ void __launch_bounds__(256) polar_delta_step_kernel(DeltaArgs a) {
   constexpr int D = kHeadDim;
-  const int t = threadIdx.x, i = t >> 2, c = t & 3;
+  const int t = threadIdx.x, r0 = t >> 4, c0 = 4 * (t & 15);
   const int units = a.B * a.H;
   auto load = [&](int unit, DeltaLoad<E> &L) {
     const int b = unit / a.H, h = unit % a.H;
     const size_t bh = (size_t)b * a.H + h;
     const int slot = a.slots[b];
     L.ok = slot >= 0 && slot < a.num_slots;
-    L.S = a.pool + ((size_t)(L.ok ? slot : 0) * a.H + h) * D * D + i * D + 16 * c;
-    if (L.ok) load16(L.S, L.s);
-    load16((const E *)a.q + bh * D + 16 * c, L.q);
-    load16((const E *)a.k + bh * D + 16 * c, L.k);
-    L.v = load1((const E *)a.v + bh * D + i);
+    L.S = a.pool + ((size_t)(L.ok ? slot : 0) * a.H + h) * D * D + 4 * t;
+    if (L.ok) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) L.s[j] = *(const f32x4 *)(L.S + 1024 * j);
+    }
+    load4((const E *)a.q + bh * D + c0, L.q);
+    load4((const E *)a.k + bh * D + c0, L.k);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) L.v[j] = load1((const E *)a.v + bh * D + 16 * j + r0);
     L.alpha = a.alpha[bh];
     L.beta = a.beta[bh];
   };
   auto update = [&](int unit, DeltaLoad<E> &L) {
     const size_t bh = (size_t)unit;                      // unit = b * H + h
+    const bool writer = (t & 15) == 0;
     if (!L.ok) {                                         // skipped sequence: zero output
-      if (c == 0) a.out[bh * D + i] = 0.f;
+      if (writer) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) a.out[bh * D + 16 * j + r0] = 0.f;
+      }
       return;
     }
-    float kk = 0.f, qq = 0.f, kq = 0.f, sk = 0.f, sq = 0.f;
+    float kk = 0.f, qq = 0.f, kq = 0.f, sk[4], sq[4];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      kk = fmaf(L.k[j], L.k[j], kk);
-      qq = fmaf(L.q[j], L.q[j], qq);
-      kq = fmaf(L.k[j], L.q[j], kq);
-      sk = fmaf(L.s[j], L.k[j], sk);
-      sq = fmaf(L.s[j], L.q[j], sq);
+    for (int e = 0; e < 4; ++e) {
+      kk = fmaf(L.k[e], L.k[e], kk);
+      qq = fmaf(L.q[e], L.q[e], qq);
+      kq = fmaf(L.k[e], L.q[e], kq);
     }
-    kk = quad_sum(kk);
-    qq = quad_sum(qq);
-    kq = quad_sum(kq);
-    sk = quad_sum(sk);
-    sq = quad_sum(sq);
-    const float rk = a.normalize ? rsqrtf(kk + 1e-12f) : 1.0f;
-    const float rq = a.normalize ? rsqrtf(qq + 1e-12f) : 1.0f;
-    const float u = L.beta * (L.v - L.alpha * sk * rk);
-    const float uk = u * rk;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const f32x4 w = {fmaf(L.alpha, L.s[4 * j], uk * L.k[4 * j]),
-                       fmaf(L.alpha, L.s[4 * j + 1], uk * L.k[4 * j + 1]),
-                       fmaf(L.alpha, L.s[4 * j + 2], uk * L.k[4 * j + 2]),
-                       fmaf(L.alpha, L.s[4 * j + 3], uk * L.k[4 * j + 3])};
-      *(f32x4 *)(L.S + 4 * j) = w;
+      sk[j] = 0.f;
+      sq[j] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sk[j] = fmaf(L.s[j][e], L.k[e], sk[j]);
+        sq[j] = fmaf(L.s[j][e], L.q[e], sq[j]);
+      }
+      sk[j] = row16_sum(sk[j]);
+      sq[j] = row16_sum(sq[j]);
     }
-    if (c == 0) a.out[bh * D + i] = L.alpha * sq * rq + u * (kq * rk * rq);
+    kk = row16_sum(kk);
+    qq = row16_sum(qq);
+    kq = row16_sum(kq);
+    const float rk = a.normalize ? rsqrtf(kk + 1e-12f) : 1.0f;
+    const float rq = a.normalize ? rsqrtf(qq + 1e-12f) : 1.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float u = L.beta * (L.v[j] - L.alpha * sk[j] * rk);
+      const float uk = u * rk;
+      f32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = fmaf(L.alpha, L.s[j][e], uk * L.k[e]);
+      *(f32x4 *)(L.S + 1024 * j) = w;
+      if (writer) a.out[bh * D + 16 * j + r0] = L.alpha * sq[j] * rq + u * (kq * rk * rq);
+    }
   };
   const int u0 = blockIdx.x * NS;
   DeltaLoad<E> L[2];
