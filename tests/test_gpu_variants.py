@@ -62,3 +62,15 @@ def test_variant_full_size_sampled(gpu_lib):
     heads = np.array([0, 5, 10, 15])
     want = oracle_prefill(p, rows=rows, heads=heads, window=4096, rope_theta=10000.0)
     check(p, select(got, rows=rows, heads=heads), want, "C4 W=4096 rope", heads=heads)
+
+
+def test_variant_full_size_rope_softmax_sampled(gpu_lib):
+    """T = 64K with RoPE on load and the plain softmax output, no window (the variant
+    workload of the benchmark), sampled rows."""
+    print("[case] variant C4 W=0 theta=10000 sampled", flush=True)
+    p = synth.prefill_inputs("c4")
+    got = run(p, window=0, rope_theta=10000.0)
+    rows = np.array([0, 1, 2, 63, 64, 2047, 2048, 40000, 65535])
+    heads = np.array([0, 3, 8, 15])
+    want = oracle_prefill(p, rows=rows, heads=heads, window=0, rope_theta=10000.0)
+    check(p, select(got, rows=rows, heads=heads), want, "C4 W=0 rope", heads=heads)
