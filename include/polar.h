@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define POLAR_ABI_VERSION 1
+#define POLAR_ABI_VERSION 2   /* 2: polar_variant gained the key-rotation workspace */
 
 #if defined(__GNUC__)
 #define POLAR_API __attribute__((visibility("default")))
@@ -121,12 +121,27 @@ POLAR_API polar_status polar_attn_fwd(const polar_params *p, polar_dtype dt, int
  *               0 = no rotation.
  *   attn        optional device float32 [B,T,Hq,d], 16-byte aligned: the plain softmax
  *               attention output u = sum_j p_j v_j.  NULL = not written.
+ *   workspace   optional device buffer, 16-byte aligned, of workspace_bytes >=
+ *               polar_variant_workspace_bytes(): with rope_theta > 0 the keys are rotated
+ *               once into it, before the attention kernel, instead of in every workgroup
+ *               that stages them.  The results are bit-identical either way.  NULL (or
+ *               rope_theta == 0) = not used; a buffer that is too small is an error.  The
+ *               caller owns it; its contents are scratch.
  */
 typedef struct {
   int32_t window;
   float rope_theta;
   float *attn;
+  void *workspace;
+  size_t workspace_bytes;
 } polar_variant;
+
+/*
+ * Bytes of the key-rotation workspace of polar_attn_fwd_variant: B*T*Hkv*d elements of
+ * dtype `dt` (0 on invalid arguments).
+ */
+POLAR_API size_t polar_variant_workspace_bytes(const polar_params *p, polar_dtype dt, int32_t B,
+                                     int32_t T);
 
 /*
  * polar_attn_fwd with the variant modes above.  Same arguments, outputs and conventions

@@ -5,9 +5,9 @@ The computation lives in libpolar.so (HIP kernels for gfx950 behind the C ABI of
 include/polar.h).  ``polar`` holds the torch-facing wrappers; ``_lib`` the raw binding.
 """
 from .polar import (attn_fwd, attn_decode_paged, decode_workspace_bytes,  # noqa: F401
-                    attn_fwd_train, attn_bwd, bwd_workspace_bytes, attn_fwd_variant, kv_append,
-                    attn_prefill_paged, delta_step)
+                    attn_fwd_train, attn_bwd, bwd_workspace_bytes, attn_fwd_variant,
+                    variant_workspace_bytes, kv_append, attn_prefill_paged, delta_step)
 
 __all__ = ["attn_fwd", "attn_decode_paged", "decode_workspace_bytes", "attn_fwd_train",
-           "attn_bwd", "bwd_workspace_bytes", "attn_fwd_variant", "kv_append",
-           "attn_prefill_paged", "delta_step"]
+           "attn_bwd", "bwd_workspace_bytes", "attn_fwd_variant", "variant_workspace_bytes",
+           "kv_append", "attn_prefill_paged", "delta_step"]

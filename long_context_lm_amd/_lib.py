@@ -30,7 +30,8 @@ POLAR_DELTA_NORMALIZE_QK = 1
 
 EXPORTS = ("polar_attn_fwd", "polar_decode_workspace_bytes", "polar_attn_decode_paged",
            "polar_attn_fwd_train", "polar_bwd_workspace_bytes", "polar_attn_bwd",
-           "polar_attn_fwd_variant", "polar_kv_append", "polar_attn_prefill_paged",
+           "polar_attn_fwd_variant", "polar_variant_workspace_bytes", "polar_kv_append",
+           "polar_attn_prefill_paged",
            "polar_delta_step",
            "polar_status_str", "polar_last_error", "polar_abi_version")
 
@@ -55,7 +56,8 @@ class polar_delta_params(ctypes.Structure):
 
 class polar_variant(ctypes.Structure):
     _fields_ = [("window", ctypes.c_int32), ("rope_theta", ctypes.c_float),
-                ("attn", ctypes.c_void_p)]
+                ("attn", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t)]
 
 
 class polar_saved(ctypes.Structure):
@@ -114,6 +116,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.polar_attn_fwd_variant.restype = I32
     lib.polar_attn_fwd_variant.argtypes = [P(polar_params), P(polar_variant), I32, I32, I32, VP,
                                            VP, VP, P(polar_outputs), VP]
+    lib.polar_variant_workspace_bytes.restype = SZ
+    lib.polar_variant_workspace_bytes.argtypes = [P(polar_params), I32, I32, I32]
     lib.polar_kv_append.restype = I32
     lib.polar_kv_append.argtypes = [P(polar_params), I32, I32, I32, VP, VP, VP, VP, I32, I32, VP,
                                     I32, VP, I32, VP]
@@ -194,6 +198,10 @@ def polar_delta_step(params, dtype, B, state_pool, num_slots, slots, q, k, v, al
                      stream) -> int:
     return load().polar_delta_step(ctypes.byref(params), dtype, B, state_pool, num_slots, slots,
                                    q, k, v, alpha, beta, out, stream)
+
+
+def polar_variant_workspace_bytes(params, dtype, B, T) -> int:
+    return load().polar_variant_workspace_bytes(ctypes.byref(params), dtype, B, T)
 
 
 def polar_bwd_workspace_bytes(params, B, T) -> int:

@@ -86,6 +86,8 @@ polar_status prefill(const polar_params *p, polar_dtype dt, int32_t B, int32_t T
       return fail(POLAR_ERR_BAD_SHAPE, "rope_theta must be 0 or a finite value > 1");
     if (var->attn && !aligned16(var->attn))
       return fail(POLAR_ERR_MISALIGNED, "variant attn output must be 16-byte aligned");
+    if (var->workspace && !aligned16(var->workspace))
+      return fail(POLAR_ERR_MISALIGNED, "variant workspace must be 16-byte aligned");
   }
   if (B < 0 || T < 0) return fail(POLAR_ERR_BAD_SHAPE, "B (%d) and T (%d) must be >= 0", B, T);
   if (B == 0 || T == 0) return POLAR_OK;
@@ -125,6 +127,16 @@ polar_status prefill(const polar_params *p, polar_dtype dt, int32_t B, int32_t T
   a.window = var ? var->window : 0;
   a.rope = (var && var->rope_theta > 0.f) ? 1 : 0;
   a.variant = (a.attn || a.window > 0 || a.rope) ? 1 : 0;
+  a.k_rotated = 0;
+  // Keys rotated once into the caller's workspace instead of in every staging workgroup.
+  void *k_rot = nullptr;
+  if (a.rope && var->workspace) {
+    const size_t need = (size_t)B * T * p->n_kv_heads * polar::kHeadDim * (size_t)elt;
+    if (var->workspace_bytes < need)
+      return fail(POLAR_ERR_WORKSPACE_TOO_SMALL, "variant workspace has %zu bytes, needs %zu",
+                  var->workspace_bytes, need);
+    k_rot = var->workspace;
+  }
   a.paged = paged ? 1 : 0;
   a.page_table = paged ? paged->page_table : nullptr;
   a.start_pos = paged ? paged->start_pos : nullptr;
@@ -154,7 +166,14 @@ polar_status prefill(const polar_params *p, polar_dtype dt, int32_t B, int32_t T
   const long long blocks = (long long)a.n_row_blocks * a.Hkv * (a.G / a.hb) * B;
   if (blocks > 0x7fffffffLL)
     return fail(POLAR_ERR_BAD_SHAPE, "problem too large for one launch (%lld workgroups)", blocks);
-  hipError_t err = polar::launch_prefill((int)dt, a, (hipStream_t)stream);
+  hipError_t err = hipSuccess;
+  if (k_rot) {
+    err = polar::launch_rope_keys((int)dt, a, k_rot, (hipStream_t)stream);
+    if (err != hipSuccess) return fail(POLAR_ERR_HIP, "key rotation launch: %s", hipGetErrorString(err));
+    a.k = k_rot;
+    a.k_rotated = 1;
+  }
+  err = polar::launch_prefill((int)dt, a, (hipStream_t)stream);
   if (err != hipSuccess) return fail(POLAR_ERR_HIP, "prefill launch: %s", hipGetErrorString(err));
   return POLAR_OK;
 }
@@ -175,6 +194,14 @@ polar_status polar_attn_fwd(const polar_params *p, polar_dtype dt, int32_t B, in
                             const void *q, const void *k, const void *v,
                             const polar_outputs *out, void *stream) {
   return prefill(p, dt, B, T, q, k, v, out, nullptr, nullptr, stream);
+}
+
+size_t polar_variant_workspace_bytes(const polar_params *p, polar_dtype dt, int32_t B,
+                                     int32_t T) {
+  if (!p || B < 0 || T < 0 || p->n_kv_heads < 1 ||
+      (dt != POLAR_DTYPE_BF16 && dt != POLAR_DTYPE_F32))
+    return 0;
+  return (size_t)B * T * p->n_kv_heads * polar::kHeadDim * (dt == POLAR_DTYPE_BF16 ? 2 : 4);
 }
 
 polar_status polar_attn_fwd_variant(const polar_params *p, const polar_variant *var,

@@ -21,6 +21,7 @@ struct PrefillArgs {
   int variant;                            // 1: launch the variant instance
   int window;                             // W >= 1: row i sees keys i-W+1..i; 0: all
   int rope;                               // 1: rotate q and k by RoPE on load
+  int k_rotated;                          // 1: k is already rotated (rotate q only)
   uint64_t rope_f[kHeadDim / 2];          // revolutions per position of pair t, 2^-64 units
   int B, T, Hq, Hkv, G;                   // G = Hq / Hkv
   int hb;                                 // query heads per workgroup (divides G, <= 4)
@@ -39,6 +40,9 @@ struct PrefillArgs {
 int prefill_heads_per_block(int G);
 int prefill_rows_per_block(int dtype, int hb);
 hipError_t launch_prefill(int dtype, const PrefillArgs &a, hipStream_t stream);
+// Rotates the keys a.k [B,T,Hkv,d] by RoPE at positions 0..T-1 into k_out (same layout),
+// with exactly the arithmetic the prefill's staging applies.
+hipError_t launch_rope_keys(int dtype, const PrefillArgs &a, void *k_out, hipStream_t stream);
 
 struct DecodeArgs {
   const void *q;                          // [B,Hq,d]

@@ -80,6 +80,15 @@ __device__ __forceinline__ void rope_cs(uint64_t f, int pos, float &c, float &s)
   c = __builtin_amdgcn_cosf(rev);
 }
 
+// The rotated pair, with the contraction spelled out so that every place that rotates a
+// key rounds the same way: (x0 c - x1 s, x0 s + x1 c).
+__device__ __forceinline__ float rot_re(float x0, float x1, float c, float s) {
+  return fmaf(x0, c, -(x1 * s));
+}
+__device__ __forceinline__ float rot_im(float x0, float x1, float c, float s) {
+  return fmaf(x0, s, x1 * c);
+}
+
 template <class TR, int QB, int kWaves, int kMode>
 __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs a) {
   constexpr bool kSave = kMode == kModeSave;
@@ -162,8 +171,8 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
               float c, sn;
               rope_cs(a.rope_f[ks * 8 + g32 * 4 + m], row, c, sn);
               const float x0 = (float)qf[qb][ks][2 * m], x1 = (float)qf[qb][ks][2 * m + 1];
-              qf[qb][ks][2 * m] = (__bf16)(x0 * c - x1 * sn);
-              qf[qb][ks][2 * m + 1] = (__bf16)(x0 * sn + x1 * c);
+              qf[qb][ks][2 * m] = (__bf16)rot_re(x0, x1, c, sn);
+              qf[qb][ks][2 * m + 1] = (__bf16)rot_im(x0, x1, c, sn);
             }
           } else {
             // fp32: lanes l and l^32 hold the two elements of pair ks.
@@ -270,7 +279,7 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
       const int ch = tid + kThreads * j;
       const int key = ch / CPR, part = ch % CPR;
       if constexpr (kVar) {
-        if (a.rope) {
+        if (a.rope && !a.k_rotated) {
           // Rotate the staged chunk: pairs (2t, 2t+1) of key position staged_key0 + key.
           const int pos = staged_key0 + key;
 #pragma unroll
@@ -280,14 +289,14 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
               rope_cs(a.rope_f[part * 4 + m], pos, c, sn);
               x0 = __uint_as_float(kst[j][m] << 16);
               x1 = __uint_as_float(kst[j][m] & 0xFFFF0000u);
-              const bf16x2 r = {(__bf16)(x0 * c - x1 * sn), (__bf16)(x0 * sn + x1 * c)};
+              const bf16x2 r = {(__bf16)rot_re(x0, x1, c, sn), (__bf16)rot_im(x0, x1, c, sn)};
               kst[j][m] = __builtin_bit_cast(uint32_t, r);
             } else {
               rope_cs(a.rope_f[part * 2 + m], pos, c, sn);
               x0 = __uint_as_float(kst[j][2 * m]);
               x1 = __uint_as_float(kst[j][2 * m + 1]);
-              kst[j][2 * m] = __float_as_uint(x0 * c - x1 * sn);
-              kst[j][2 * m + 1] = __float_as_uint(x0 * sn + x1 * c);
+              kst[j][2 * m] = __float_as_uint(rot_re(x0, x1, c, sn));
+              kst[j][2 * m + 1] = __float_as_uint(rot_im(x0, x1, c, sn));
             }
           }
         }
@@ -684,6 +693,37 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
   }
 }
 
+// Key rotation ahead of the variant prefill: thread per pair of dimensions of one key
+// row, with the staging's arithmetic (rope_cs, fp32 products, one rounding to the storage
+// type), so the attention kernel sees the same rotated keys either way.
+template <class E>
+__global__ void __launch_bounds__(256) polar_rope_keys_kernel(PrefillArgs a, E *k_out) {
+  constexpr int kPairs = kD / 2;
+  const long long n = (long long)a.B * a.T * a.Hkv * kPairs;
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n;
+       i += (long long)gridDim.x * 256) {
+    const int t = (int)(i % kPairs);
+    const long long row = i / kPairs;                  // (b * T + pos) * Hkv + g
+    const int pos = (int)((row / a.Hkv) % a.T);
+    const E *src = (const E *)a.k + row * kD + 2 * t;
+    float c, sn;
+    rope_cs(a.rope_f[t], pos, c, sn);
+    float x0, x1;
+    if constexpr (sizeof(E) == 2) {
+      const uint32_t w = *(const uint32_t *)src;
+      x0 = __uint_as_float(w << 16);
+      x1 = __uint_as_float(w & 0xFFFF0000u);
+      const bf16x2 r = {(__bf16)rot_re(x0, x1, c, sn), (__bf16)rot_im(x0, x1, c, sn)};
+      *(bf16x2 *)(k_out + row * kD + 2 * t) = r;
+    } else {
+      x0 = src[0];
+      x1 = src[1];
+      k_out[row * kD + 2 * t] = rot_re(x0, x1, c, sn);
+      k_out[row * kD + 2 * t + 1] = rot_im(x0, x1, c, sn);
+    }
+  }
+}
+
 constexpr int kQbBf16 = POLAR_PREFILL_QB;
 constexpr int kQbF32 = 1;
 constexpr int kWavesBf16 = POLAR_PREFILL_WAVES;
@@ -701,6 +741,20 @@ int prefill_rows_per_block(int dtype, int hb) {
   const int qb = dtype == 1 ? kQbBf16 : kQbF32;
   const int waves = dtype == 1 ? kWavesBf16 : kWavesF32;
   return (waves / hb) * 32 * qb;
+}
+
+hipError_t launch_rope_keys(int dtype, const PrefillArgs &a, void *k_out, hipStream_t stream) {
+  const long long n = (long long)a.B * a.T * a.Hkv * (kD / 2);
+  if (n <= 0) return hipSuccess;
+  const long long need = (n + 255) / 256;
+  const unsigned blocks = (unsigned)(need < 65536 ? need : 65536);
+  if (dtype == 1)
+    hipLaunchKernelGGL((polar_rope_keys_kernel<uint16_t>), dim3(blocks), dim3(256), 0, stream, a,
+                       (uint16_t *)k_out);
+  else
+    hipLaunchKernelGGL((polar_rope_keys_kernel<float>), dim3(blocks), dim3(256), 0, stream, a,
+                       (float *)k_out);
+  return hipGetLastError();
 }
 
 hipError_t launch_prefill(int dtype, const PrefillArgs &a, hipStream_t stream) {

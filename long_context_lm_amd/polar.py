@@ -108,20 +108,38 @@ def attn_fwd_variant(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, window: 
                      rope_theta: float = 0.0, want_attn: bool = True, beta=None,
                      null_bias=None, count_vec=None, train_len: int = 2048,
                      flags: int = _lib.POLAR_FLAG_LENGTH_TEMP | _lib.POLAR_FLAG_NULL_FLOOR,
+                     rotate_keys_once: bool = True, workspace: Optional[torch.Tensor] = None,
                      stream=None) -> dict:
     """Prefill with the variant modes: sliding ``window``, RoPE on load (``rope_theta``) and
-    the plain softmax output ("attn", when ``want_attn``)."""
+    the plain softmax output ("attn", when ``want_attn``).
+
+    With RoPE and ``rotate_keys_once``, the keys are rotated once into ``workspace`` (a
+    uint8 device tensor of at least variant_workspace_bytes(...) bytes, allocated here when
+    None) before the attention kernel; otherwise every workgroup rotates the keys it
+    stages.  Both give bit-identical results."""
     prm, keep, (B, T, Hq, Hkv, d) = _prefill_args(q, k, v, beta, null_bias, count_vec,
                                                   train_len, flags)
     dev = q.device
     out, cout = _outputs((B, T), Hq, d, dev, keep[2] is not None, True, True)
     out["attn"] = (torch.empty(B, T, Hq, d, device=dev, dtype=torch.float32)
                    if want_attn else None)
-    var = _lib.polar_variant(window, rope_theta, _ptr(out["attn"]))
+    ws_ptr, ws_bytes = None, 0
+    if rope_theta > 0 and rotate_keys_once:
+        need = _lib.polar_variant_workspace_bytes(prm, _DT[q.dtype], B, T)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    var = _lib.polar_variant(window, rope_theta, _ptr(out["attn"]), ws_ptr, ws_bytes)
     s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
     _lib.check(_lib.polar_attn_fwd_variant(prm, var, _DT[q.dtype], B, T, q.data_ptr(),
                                            k.data_ptr(), v.data_ptr(), cout, s))
     return out
+
+
+def variant_workspace_bytes(Hq: int, Hkv: int, B: int, T: int, dtype=torch.bfloat16,
+                            d: int = 64) -> int:
+    prm = _lib.polar_params(Hq, Hkv, d, 2048, 0, None, None, None)
+    return _lib.polar_variant_workspace_bytes(prm, _DT[dtype], B, T)
 
 
 def bwd_workspace_bytes(Hq: int, Hkv: int, B: int, T: int, d: int = 64) -> int:

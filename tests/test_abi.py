@@ -23,7 +23,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(_lib.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert _lib.polar_abi_version() == 1
+    assert _lib.polar_abi_version() == 2
 
 
 def test_status_strings():
@@ -227,9 +227,10 @@ def test_fwd_train_validation():
 
 
 # ------------------------------------------------------------------ variant modes
-def var_fwd(window=0, theta=0.0, attn=None, **kw):
-    return _lib.polar_attn_fwd_variant(params(), _lib.polar_variant(window, theta, attn), 1,
-                                       kw.get("B", 1), kw.get("T", 8), A, A, A, outs(), None)
+def var_fwd(window=0, theta=0.0, attn=None, ws=None, ws_bytes=0, dt=1, **kw):
+    return _lib.polar_attn_fwd_variant(params(),
+                                       _lib.polar_variant(window, theta, attn, ws, ws_bytes),
+                                       dt, kw.get("B", 1), kw.get("T", 8), A, A, A, outs(), None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -239,10 +240,23 @@ def var_fwd(window=0, theta=0.0, attn=None, **kw):
     (dict(theta=float("inf")), _lib.POLAR_ERR_BAD_SHAPE),
     (dict(theta=float("nan")), _lib.POLAR_ERR_BAD_SHAPE),
     (dict(attn=A + 4), _lib.POLAR_ERR_MISALIGNED),
+    (dict(theta=10000.0, ws=A + 8, ws_bytes=1 << 20), _lib.POLAR_ERR_MISALIGNED),
+    # 1 x 8 keys x 4 KV heads x 64 dims x 2 bytes = 4096 bytes needed (8192 for fp32)
+    (dict(theta=10000.0, ws=A, ws_bytes=4095), _lib.POLAR_ERR_WORKSPACE_TOO_SMALL),
+    (dict(theta=10000.0, ws=A, ws_bytes=8191, dt=0), _lib.POLAR_ERR_WORKSPACE_TOO_SMALL),
 ])
 def test_variant_validation_errors(kw, code):
     assert var_fwd(**kw) == code
     assert _lib.polar_last_error() != ""
+
+
+def test_variant_workspace_bytes():
+    # B * T * Hkv * d * element size; the workspace is only read with rope_theta > 0
+    assert _lib.polar_variant_workspace_bytes(params(), 1, 3, 100) == 3 * 100 * 4 * 64 * 2
+    assert _lib.polar_variant_workspace_bytes(params(), 0, 3, 100) == 3 * 100 * 4 * 64 * 4
+    assert _lib.polar_variant_workspace_bytes(params(), 1, 0, 100) == 0
+    assert _lib.polar_variant_workspace_bytes(params(), 7, 3, 100) == 0
+    assert _lib.load().polar_variant_workspace_bytes(None, 1, 3, 100) == 0
 
 
 def test_variant_empty_calls():

@@ -45,6 +45,20 @@ def test_variant_parity(gpu_lib, cfg, B, T, Hq, Hkv, window, theta):
     check(p, got, want, f"{cfg} W={window} theta={theta}")
 
 
+@pytest.mark.parametrize("cfg,T,window,attn", [("c2", 333, 0, True), ("c2", 200, 64, False),
+                                              ("c1", 150, 37, True)])
+def test_keys_rotated_once_equal_keys_rotated_in_staging(gpu_lib, cfg, T, window, attn):
+    """The workspace path (keys rotated by their own kernel before the prefill) and the
+    in-staging rotation use the same arithmetic, so every output is bit-identical."""
+    print(f"[case] rotate once vs in staging {cfg} T={T} W={window}", flush=True)
+    p = synth.prefill_inputs(cfg, B=2, T=T, Hq=8, Hkv=2, train_len=64)
+    a = run(p, window=window, rope_theta=10000.0, want_attn=attn, rotate_keys_once=True)
+    b = run(p, window=window, rope_theta=10000.0, want_attn=attn, rotate_keys_once=False)
+    for n in ("dir", "count", "n_eff", "gate", "lse", "attn"):
+        if a.get(n) is not None:
+            assert torch.equal(a[n], b[n]), n
+
+
 def test_variant_without_modes_equals_plain_forward(gpu_lib):
     p = synth.prefill_inputs("c2", B=1, T=200, Hq=8, Hkv=2, train_len=64)
     a = run(p, want_attn=False)
