@@ -217,6 +217,46 @@ def measure_variants(dev, q, k, v, pkw, pre, steps: int, warmup: int):
     return res
 
 
+def measure_decode_b1(dev, steps: int, warmup: int):
+    """The other reading of the 16 single-token queries: one sequence whose 16 query heads
+    decode against a 262,144-token cache (4 KV heads, 268 MB of K and V)."""
+    import torch
+    import synth
+    from long_context_lm_amd import attn_decode_paged, decode_workspace_bytes
+    d = synth.decode_inputs("c5", B=1)
+
+    def to_dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    qd, kc, vc = to_dev(d.q), to_dev(d.k_pool), to_dev(d.v_pool)
+    table = torch.from_numpy(d.page_table).to(dev)
+    lens = torch.from_numpy(d.seq_lens).to(dev)
+    kw = dict(beta=torch.from_numpy(d.beta).to(dev), null_bias=torch.from_numpy(d.null_bias).to(dev),
+              count_vec=torch.from_numpy(d.count_vec).to(dev), train_len=d.train_len,
+              flags=d.flags)
+    ws = torch.empty(decode_workspace_bytes(d.Hq, d.Hkv, d.B, d.max_seq_len), dtype=torch.uint8,
+                     device=dev)
+    f = lambda: attn_decode_paged(qd, kc, vc, table, lens, d.max_seq_len, workspace=ws, **kw)
+    for _ in range(warmup):
+        f()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for e in ev:
+        e[0].record()
+        f()
+        e[1].record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    byt = decode_bytes(d.B, d.max_seq_len, d.Hq, d.Hkv, d.d, d.page_size, d.page_table.shape[1])
+    gbs = byt / (ms * 1e-3) / 1e9
+    print(f"[bench] decode B=1: {ms:.3f} ms ({gbs:.1f} GB/s)", file=sys.stderr, flush=True)
+    return {"workload": "paged decode B=1 L=262144 Hq=16 Hkv=4 d=64 page=64 shuffled table "
+                        "(one token's 16 heads)",
+            "value": round(gbs, 1), "unit": "GB/s", "ms": round(ms, 4), "bytes": byt,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}}
+
+
 def measure_paged(dev, pre, steps: int, warmup: int):
     """The last 4096-token chunk of the T=64K sequence over a shuffled page pool: KV append
     of the chunk, then its chunked prefill over the 61440 cached tokens and itself."""
@@ -473,6 +513,8 @@ def main():
                                        min(args.warmup, 2))
     rec["paged"] = measure_paged(dev, pre, max(1, args.steps // 2), min(args.warmup, 2))
     del q, k, v, qd, kc, vc, table, lens, ws
+    torch.cuda.empty_cache()
+    rec["decode_b1"] = measure_decode_b1(dev, args.steps, min(args.warmup, 2))
     torch.cuda.empty_cache()
     rec["backward"] = measure_backward(dev, max(1, args.steps // 2), args.warmup,
                                        not args.no_cpu_baseline)

@@ -13,8 +13,9 @@
 //   * online max / sum / sum-of-squares with a lazily raised reference, as in prefill;
 //   * the V page is read once, transposed through LDS, and O^T += V^T P^T on MFMA.
 // Each split writes (reference, max score, S, Q, u[64]) per query head to the workspace.
-// Combine kernel: one wave per (b, query head) merges the splits with factors 2^(M_s-R)
-// (squared for Q) and applies the direction / count epilogue with n = seq_len.
+// Combine kernel: one workgroup per (b, query head) merges the splits with factors
+// 2^(M_s-R) (squared for Q), each wave a contiguous share of them, and applies the
+// direction / count epilogue with n = seq_len.
 #include "polar_kernels.h"
 #include "polar_mfma.h"
 
@@ -26,6 +27,10 @@ constexpr int kP = kPageSize;
 constexpr int kEntry = 68;        // floats per (b, head, split) partial
 constexpr float kLazyTheta = 8.0f;
 constexpr int kTargetWaves = 4096;
+#ifndef POLAR_DECODE_COMBINE_WAVES
+#define POLAR_DECODE_COMBINE_WAVES 8
+#endif
+constexpr int kCombineWaves = POLAR_DECODE_COMBINE_WAVES;   // waves per (b, head) merge
 
 template <class TR> struct DecCfg;
 template <> struct DecCfg<Bf16> { static constexpr int vrow = 72; };
@@ -233,46 +238,89 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-// One wave per (sequence, query head).  Lanes own splits for the scalar merge; the value
-// merge walks the splits 64 at a time with each split's weight read from a lane register.
-__global__ void __launch_bounds__(256) polar_decode_combine_kernel(DecodeArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (pair >= a.B * a.Hq) return;
+// One workgroup of kCombineWaves waves per (sequence, query head).  All threads find the
+// reference R = max of the splits' references (and the row maximum); then wave w merges a
+// contiguous share of the splits: lanes own splits for the scalar weights 2^(M_s - R),
+// and the value merge walks them 64 at a time, each split's weight read from a lane
+// register, into four independent accumulators.  The waves' partial sums are added in a
+// fixed order, so the result does not depend on timing.
+__global__ void __launch_bounds__(64 * kCombineWaves) polar_decode_combine_kernel(DecodeArgs a) {
+  constexpr int NW = kCombineWaves;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int pair = blockIdx.x;
   const int b = pair / a.Hq, h = pair % a.Hq;
-  const float *e = a.ws + (size_t)pair * a.n_split * kEntry;
+  const int n = a.n_split;
+  const float *e = a.ws + (size_t)pair * n * kEntry;
+  __shared__ float red[NW][2];
+  __shared__ float part[NW][2 + kD];
   float R = -INFINITY, smax = -INFINITY;
-  for (int s = lane; s < a.n_split; s += 64) {
+  for (int s = tid; s < n; s += 64 * NW) {
     R = fmaxf(R, e[s * kEntry + 0]);
     smax = fmaxf(smax, e[s * kEntry + 1]);
   }
   R = wave_max(R);
   smax = wave_max(smax);
-  float S = 0.f, Q = 0.f, u = 0.f;
-  for (int s0 = 0; s0 < a.n_split; s0 += 64) {
+  if (lane == 0) {
+    red[wave][0] = R;
+    red[wave][1] = smax;
+  }
+  __syncthreads();
+  R = red[0][0];
+  smax = red[0][1];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) {
+    R = fmaxf(R, red[i][0]);
+    smax = fmaxf(smax, red[i][1]);
+  }
+
+  const int per = (n + NW - 1) / NW;
+  const int s_begin = min(n, wave * per), s_end = min(n, s_begin + per);
+  float S = 0.f, Q = 0.f, u0 = 0.f, u1 = 0.f, u2 = 0.f, u3 = 0.f;
+  for (int s0 = s_begin; s0 < s_end; s0 += 64) {
     const int s = s0 + lane;
     float w = 0.f;
-    if (s < a.n_split) {
+    if (s < s_end) {
       const float Ms = e[s * kEntry + 0];
       w = Ms == -INFINITY ? 0.f : fast_exp2(Ms - R);
       S = fmaf(e[s * kEntry + 2], w, S);
       Q = fmaf(e[s * kEntry + 3], w * w, Q);
     }
-    const int cnt = min(64, a.n_split - s0);
+    const int cnt = min(64, s_end - s0);
     const float *us = e + (size_t)s0 * kEntry + 4 + lane;
     int j = 0;
-    for (; j + 4 <= cnt; j += 4) {
-      const float u0 = us[(j + 0) * kEntry], u1 = us[(j + 1) * kEntry];
-      const float u2 = us[(j + 2) * kEntry], u3 = us[(j + 3) * kEntry];
-      u = fmaf(u0, __shfl(w, j + 0), u);
-      u = fmaf(u1, __shfl(w, j + 1), u);
-      u = fmaf(u2, __shfl(w, j + 2), u);
-      u = fmaf(u3, __shfl(w, j + 3), u);
+    for (; j + 8 <= cnt; j += 8) {
+      float x[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = us[(j + i) * kEntry];
+      u0 = fmaf(x[0], __shfl(w, j + 0), u0);
+      u1 = fmaf(x[1], __shfl(w, j + 1), u1);
+      u2 = fmaf(x[2], __shfl(w, j + 2), u2);
+      u3 = fmaf(x[3], __shfl(w, j + 3), u3);
+      u0 = fmaf(x[4], __shfl(w, j + 4), u0);
+      u1 = fmaf(x[5], __shfl(w, j + 5), u1);
+      u2 = fmaf(x[6], __shfl(w, j + 6), u2);
+      u3 = fmaf(x[7], __shfl(w, j + 7), u3);
     }
-    for (; j < cnt; ++j) u = fmaf(us[j * kEntry], __shfl(w, j), u);
+    for (; j < cnt; ++j) u0 = fmaf(us[j * kEntry], __shfl(w, j), u0);
   }
   S = wave_sum(S);
   Q = wave_sum(Q);
+  part[wave][2 + lane] = (u0 + u1) + (u2 + u3);
+  if (lane == 0) {
+    part[wave][0] = S;
+    part[wave][1] = Q;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  S = part[0][0];
+  Q = part[0][1];
+  float u = part[0][2 + lane];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) {
+    S += part[i][0];
+    Q += part[i][1];
+    u += part[i][2 + lane];
+  }
   const int L = min(max(a.seq_lens[b], 1), a.max_seq_len);
   const float beta = a.beta ? a.beta[h] : 8.0f;
   const float tau =
@@ -329,7 +377,8 @@ hipError_t launch_decode(int dtype, const DecodeArgs &a, hipStream_t stream) {
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int pairs = a.B * a.Hq;
-  hipLaunchKernelGGL(polar_decode_combine_kernel, dim3((pairs + 3) / 4), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(polar_decode_combine_kernel, dim3(pairs), dim3(64 * kCombineWaves), 0, stream,
+                     a);
   return hipGetLastError();
 }
 

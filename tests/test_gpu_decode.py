@@ -107,3 +107,13 @@ def test_c5_full_size_sampled_sequences(gpu_lib):
     assert torch.isfinite(got["n_eff"]).all()
     # every (b, h) has its planted needle: the gate fires
     assert (got["gate"] > 0.5).all()
+
+
+def test_one_sequence_full_length(gpu_lib):
+    """The other reading of the 16 single-token queries: B = 1, all 16 heads of one token
+    against a 262,144-token cache (the split grid then comes from one sequence alone)."""
+    print("[case] decode B=1 L=262144", flush=True)
+    d = synth.decode_inputs("c5", B=1)
+    got = gpu_decode(d)
+    assert_close(got, oracle_decode(d), d.count_vec, d.dtype, label="decode B=1 L=262144")
+    assert (got["gate"] > 0.5).all()
