@@ -693,34 +693,41 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
   }
 }
 
-// Key rotation ahead of the variant prefill: thread per pair of dimensions of one key
-// row, with the staging's arithmetic (rope_cs, fp32 products, one rounding to the storage
-// type), so the attention kernel sees the same rotated keys either way.
+// Key rotation ahead of the variant prefill: one thread per 16-byte chunk of a key row (4
+// pairs for bf16, 2 for fp32), with the staging's arithmetic (rope_cs, the same explicit
+// FMAs, one rounding to the storage type), so the attention kernel sees the same rotated
+// keys either way.
 template <class E>
 __global__ void __launch_bounds__(256) polar_rope_keys_kernel(PrefillArgs a, E *k_out) {
-  constexpr int kPairs = kD / 2;
-  const long long n = (long long)a.B * a.T * a.Hkv * kPairs;
+  constexpr int kVec = 16 / (int)sizeof(E);            // elements per chunk
+  constexpr int kChunks = kD / kVec;                   // chunks per key row
+  const long long n = (long long)a.B * a.T * a.Hkv * kChunks;
   for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n;
        i += (long long)gridDim.x * 256) {
-    const int t = (int)(i % kPairs);
-    const long long row = i / kPairs;                  // (b * T + pos) * Hkv + g
+    const int part = (int)(i % kChunks);
+    const long long row = i / kChunks;                 // (b * T + pos) * Hkv + g
     const int pos = (int)((row / a.Hkv) % a.T);
-    const E *src = (const E *)a.k + row * kD + 2 * t;
-    float c, sn;
-    rope_cs(a.rope_f[t], pos, c, sn);
-    float x0, x1;
+    u32x4 w = *(const u32x4 *)((const E *)a.k + row * kD + part * kVec);
     if constexpr (sizeof(E) == 2) {
-      const uint32_t w = *(const uint32_t *)src;
-      x0 = __uint_as_float(w << 16);
-      x1 = __uint_as_float(w & 0xFFFF0000u);
-      const bf16x2 r = {(__bf16)rot_re(x0, x1, c, sn), (__bf16)rot_im(x0, x1, c, sn)};
-      *(bf16x2 *)(k_out + row * kD + 2 * t) = r;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        float c, sn;
+        rope_cs(a.rope_f[part * 4 + m], pos, c, sn);
+        const float x0 = __uint_as_float(w[m] << 16), x1 = __uint_as_float(w[m] & 0xFFFF0000u);
+        const bf16x2 r = {(__bf16)rot_re(x0, x1, c, sn), (__bf16)rot_im(x0, x1, c, sn)};
+        w[m] = __builtin_bit_cast(uint32_t, r);
+      }
     } else {
-      x0 = src[0];
-      x1 = src[1];
-      k_out[row * kD + 2 * t] = rot_re(x0, x1, c, sn);
-      k_out[row * kD + 2 * t + 1] = rot_im(x0, x1, c, sn);
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        float c, sn;
+        rope_cs(a.rope_f[part * 2 + m], pos, c, sn);
+        const float x0 = __uint_as_float(w[2 * m]), x1 = __uint_as_float(w[2 * m + 1]);
+        w[2 * m] = __float_as_uint(rot_re(x0, x1, c, sn));
+        w[2 * m + 1] = __float_as_uint(rot_im(x0, x1, c, sn));
+      }
     }
+    *(u32x4 *)(k_out + row * kD + part * kVec) = w;
   }
 }
 
@@ -744,7 +751,7 @@ int prefill_rows_per_block(int dtype, int hb) {
 }
 
 hipError_t launch_rope_keys(int dtype, const PrefillArgs &a, void *k_out, hipStream_t stream) {
-  const long long n = (long long)a.B * a.T * a.Hkv * (kD / 2);
+  const long long n = (long long)a.B * a.T * a.Hkv * (kD / (dtype == 1 ? 8 : 4));
   if (n <= 0) return hipSuccess;
   const long long need = (n + 255) / 256;
   const unsigned blocks = (unsigned)(need < 65536 ? need : 65536);
