@@ -380,6 +380,9 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
 #endif
     if constexpr (kPaged) {
       if (!tok[slot]) {                               // a page with an invalid id
+        // The empty volatile statement keeps this rare path a branch: if-converted, it
+        // costs one select per score of every tile.
+        asm volatile("");
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -425,6 +428,7 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S.v[qb][kb][r]);
       if (mx > lbest[qb]) {
+        asm volatile("");     // a branch, not selects: lanes rarely improve after a few tiles
         int key = 0;
 #pragma unroll
         for (int kb = NKB - 1; kb >= 0; --kb)
