@@ -9,12 +9,15 @@
 // Work decomposition (one workgroup = kWaves waves):
 //  * a workgroup owns `hb` query heads that share one KV head (GQA) and a block of rows;
 //    each wave owns 32*QB consecutive rows of one of those heads;
-//  * K and V tiles of 64 keys are staged global -> registers -> LDS, double buffered, so
-//    every K/V byte brought on chip serves all `hb` heads and all rows of the block;
+//  * K and V tiles of 64 keys are staged into LDS through a four-slot ring, so every K/V
+//    byte brought on chip serves all `hb` heads and all rows of the block.  bf16 tiles go
+//    global -> LDS directly (buffer loads with the LDS destination), row-major with a
+//    16-byte chunk swizzle, and V^T fragments come from the transposing LDS read; fp32
+//    tiles, and bf16 keys that still need RoPE, pass through registers (V transposed);
 //  * S^T = K Q^T runs on MFMA with K from LDS and Q resident in registers.  The 32x32
 //    output puts one query per lane (column) and 16 keys per lane, so the row statistics
 //    need one cross-half exchange per tile and the probabilities are already laid out as
-//    the B operand of O^T = V^T P^T, whose V^T operand is read from a transposed LDS tile;
+//    the B operand of O^T = V^T P^T;
 //  * online statistics per row, in log2 units x = beta*tau*log2(e)*<q,k>:
 //      running reference M (raised lazily when the tile maximum exceeds it by > 8),
 //      S = sum 2^(x-M), Q = sum 2^(2(x-M)), u = sum 2^(x-M) v, and the exact row maximum.
@@ -49,6 +52,10 @@
 #endif
 // 1: probability sums on the matrix pipe (ones and Gram products); 0: on the vector pipe,
 // from the rounded probabilities the P.V product uses (dot2 per pair for bf16).
+// Direct (bf16) tiles: tile t + DEPTH is loaded while step t runs (DEPTH + 1 LDS slots).
+#ifndef POLAR_PREFILL_DEPTH
+#define POLAR_PREFILL_DEPTH 3
+#endif
 #ifndef POLAR_PREFILL_MSTATS
 #define POLAR_PREFILL_MSTATS 0
 #endif
@@ -68,6 +75,9 @@ template <> struct LdsCfg<Bf16> {
 template <> struct LdsCfg<F32> { static constexpr int kt = 64, krow = 68, vrow = 65; };
 
 constexpr int kModePlain = 0, kModeSave = 1, kModeVariant = 2, kModePaged = 3;
+// Variant whose keys still need RoPE (no rotated copy): they are rotated while staged
+// through registers, so this mode keeps the register staging path.
+constexpr int kModeVariantRot = 4;
 
 // RoPE rotation angle of pair t at position pos: revolutions = frac(pos * f_t) taken
 // exactly from the 64-bit fixed-point product, then the hardware sine and cosine, whose
@@ -92,7 +102,7 @@ __device__ __forceinline__ float rot_im(float x0, float x1, float c, float s) {
 template <class TR, int QB, int kWaves, int kMode>
 __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs a) {
   constexpr bool kSave = kMode == kModeSave;
-  constexpr bool kVar = kMode == kModeVariant;
+  constexpr bool kVar = kMode == kModeVariant || kMode == kModeVariantRot;
   constexpr bool kPaged = kMode == kModePaged;
   static_assert(!kPaged || LdsCfg<TR>::kt == kPageSize, "a key tile is one page");
   constexpr int kThreads = 64 * kWaves;
@@ -104,8 +114,23 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
   constexpr int KROW = LdsCfg<TR>::krow, VROW = LdsCfg<TR>::vrow;
   constexpr int VEC = TR::vec;                       // elements per 16-byte chunk
   constexpr int CPR = kD / VEC;                      // chunks per key row
-  __shared__ __attribute__((aligned(16))) E Ks[4][kKT * KROW];
-  __shared__ __attribute__((aligned(16))) E Vs[4][kD * VROW];
+  // bf16 tiles go global -> LDS directly (buffer_load ... lds), unpadded, with the 16-byte
+  // chunks of key row k stored in slot order chunk ^ (k & 7) so that fragment reads spread
+  // over the banks; K fragments are read as rows, V^T fragments with the transposing
+  // ds_read_b64_tr_b16.  Other instances stage through registers into padded tiles (V
+  // transposed on the way).
+  constexpr bool kDirect = KPL == 8 && kMode != kModeVariantRot && kKT == 64 && kThreads == 512;
+  static_assert(!(kDirect && POLAR_PREFILL_MSTATS), "direct tiles take the vector statistics");
+  constexpr int kSlotBytes = kDirect ? 2 * kKT * kD * (int)sizeof(E)
+                                     : (kKT * KROW + kD * VROW) * (int)sizeof(E);
+  // Tile t + kDepth is loaded during step t; the ring holds tiles t .. t + kDepth.  Direct
+  // loads cost no registers, so they run further ahead than the register staging.
+  constexpr int kDepth = kDirect ? POLAR_PREFILL_DEPTH : 3;
+  constexpr int kSlots = kDepth + 1;
+  static_assert(kDepth >= 3 && 2 * (kDepth - 3) < 16, "depth 3..10");
+  __shared__ __attribute__((aligned(16))) char smem[kSlots * kSlotBytes];
+  auto Ks = reinterpret_cast<E (*)[kKT * KROW]>(smem);
+  auto Vs = reinterpret_cast<E (*)[kD * VROW]>(smem + 4 * kKT * KROW * sizeof(E));
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g32 = lane >> 5, c32 = lane & 31;
@@ -230,7 +255,9 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
   u32x4 kst[NK];
   vchunk_t vst[NV][VKEYS];
   int staged_key0 = 0;                               // variant: position of the staged tile
-  int tok[4] = {1, 1, 1, 1};                         // paged: slot holds a valid page
+  int tok[kSlots];                                   // paged: slot holds a valid page
+#pragma unroll
+  for (int i = 0; i < kSlots; ++i) tok[i] = 1;
   auto stage_load = [&](int t) {
     const int key0 = t * kKT;
     staged_key0 = key0;
@@ -239,15 +266,33 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
     int base = (int)((size_t)key0 * kv_row_bytes), rstride = (int)kv_row_bytes;
     if constexpr (kPaged) {
       const int npg = min(a.stride, (pbase + a.T + kPageSize - 1) / kPageSize);
-      const int page = t < npg ? a.page_table[(size_t)b * a.stride + t] : -1;
+      // A scalar load (the index is uniform): it does not count against vmcnt, which the
+      // direct tiles' wait relies on.
+      const int tu = __builtin_amdgcn_readfirstlane(t);
+      const int page =
+          tu < npg ? a.page_table[(size_t)__builtin_amdgcn_readfirstlane(b) * a.stride + tu] : -1;
       const bool pok = page >= 0 && page < a.num_pages;
-      tok[t & 3] = pok;
+      tok[t % kSlots] = pok;
       const size_t pe = ((size_t)(pok ? page : 0) * a.Hkv + g) * kPageSize * kD;
       const int nb = pok ? kPageSize * kD * (int)sizeof(E) : 0;
       rk = __builtin_amdgcn_make_buffer_rsrc((void *)((const E *)a.k + pe), 0, nb, kBufferFlags);
       rv = __builtin_amdgcn_make_buffer_rsrc((void *)((const E *)a.v + pe), 0, nb, kBufferFlags);
       base = 0;
       rstride = kD * (int)sizeof(E);
+    }
+    if constexpr (kDirect) {
+      // Wave w moves keys 8w..8w+7 of K and of V: lane l takes key 8w + l/8 and the chunk
+      // that belongs in slot l%8 of that row, and the hardware writes lane l's 16 bytes at
+      // the wave's LDS base + 16 l.
+      const int key = 8 * wave + (lane >> 3);
+      const int off = base + key * rstride + (((lane & 7) ^ (key & 7)) << 4);
+      char *dst = smem + (t % kSlots) * kSlotBytes + wave * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void *)dst,
+                                               16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rv, (__attribute__((address_space(3))) void *)(dst + kKT * kD * sizeof(E)), 16, off, 0,
+          0, 0);
+      return;
     }
 #pragma unroll
     for (int j = 0; j < NK; ++j) {
@@ -274,6 +319,14 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
     }
   };
   auto stage_store = [&](int slot, int vslot) {
+    if constexpr (kDirect) {
+      // The tiles go straight to LDS.  Wait until this wave's loads of the tile needed next
+      // have landed: every call issues two loads (K and V) per tile, so at most the
+      // 2 (kDepth - 3) of the tiles after it may still be in flight.  The caller's barrier
+      // then publishes the tile.
+      __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * (kDepth - 3)));   // vmcnt(2 (kDepth - 3))
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < NK; ++j) {
       const int ch = tid + kThreads * j;
@@ -333,6 +386,25 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
   const uint32_t k_lane = (uint32_t)((c32 * KROW + g32 * KPL) * sizeof(E));
   const uint32_t v_lane = (uint32_t)((c32 * VROW + g32 * KPL) * sizeof(E));
   constexpr uint32_t KSLOT = kKT * KROW * sizeof(E), VSLOT = kD * VROW * sizeof(E);
+  // Direct tiles: byte offsets of this lane's fragments inside a slot.  K fragment (kb, ks):
+  // key kb*32 + c32, chunk 2 ks + g32.  V^T fragment (kb, tt, db), half h: lane i of 16-lane
+  // group G reads 4 dims of key kb*32 + 16 tt + 8 h + 4 (G/2) + i/4 and, transposed, holds
+  // dim 32 db + (lane % 32) of keys ... + 4 (lane / 32) + 0..3, the slot order of P.
+  uint32_t kofs[NKS], vofs[2];
+  {
+    const int sw = c32 & 7;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      kofs[ks] = (uint32_t)(c32 * 128 + (((2 * ks + g32) ^ sw) << 4));
+    const int G4 = lane >> 4, i = lane & 15;
+    const int krow = 4 * (G4 >> 1) + (i >> 2);
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+      const int chunk = 4 * db + 2 * (G4 & 1) + ((i & 3) >> 1);
+      vofs[db] = (uint32_t)(kKT * kD * sizeof(E) + krow * 128 + ((chunk ^ (krow & 7)) << 4) +
+                            (i & 1) * 8);
+    }
+  }
   auto lds_at = [](const E *base, uint32_t off) {
     asm volatile("" : "+v"(off));
     return reinterpret_cast<const E *>(reinterpret_cast<const char *>(base) + off);
@@ -346,8 +418,22 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
   // its predecessor's result); with POLAR_PREFILL_SPLIT each key block accumulates even
   // and odd contraction steps separately and adds the halves afterwards.
   auto score = [&](int slot, Scores &S) {
-    const E *Kt = lds_at(&Ks[0][0], k_lane + slot * KSLOT);
     const f32x16 zero = {};
+    if constexpr (kDirect) {
+      const char *sb = smem + slot * kSlotBytes;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const char *kp = reinterpret_cast<const char *>(lds_at((const E *)sb, kofs[ks]));
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          const F ka = *reinterpret_cast<const F *>(kp + kb * 32 * 128);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            S.v[qb][kb] = TR::mma32(ka, qf[qb][ks], ks == 0 ? zero : S.v[qb][kb]);
+        }
+      }
+    } else {
+    const E *Kt = lds_at(&Ks[0][0], k_lane + slot * KSLOT);
 #if POLAR_PREFILL_SPLIT
     f32x16 h2[QB][NKB];
 #pragma unroll
@@ -378,6 +464,7 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
           S.v[qb][kb] = TR::mma32(ka, qf[qb][ks], ks == 0 ? zero : S.v[qb][kb]);
       }
 #endif
+    }
     if constexpr (kPaged) {
       if (!tok[slot]) {                               // a page with an invalid id
         // The empty volatile statement keeps this rare path a branch: if-converted, it
@@ -483,6 +570,28 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
   };
   // O^T += V^T P^T
   auto pv_mma = [&](int slot, const Probs &P) {
+    if constexpr (kDirect) {
+      typedef short s16x4 __attribute__((ext_vector_type(4)));
+      const char *sb = smem + slot * kSlotBytes;
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        const char *vp = reinterpret_cast<const char *>(lds_at((const E *)sb, vofs[db]));
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int tt = 0; tt < NT; ++tt) {
+            const int r0 = (kb * 32 + 16 * tt) * 128;
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4 *)(vp + r0));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4 *)(vp + r0 + 8 * 128));
+            const F va = __builtin_bit_cast(F, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) o[qb][db] = TR::mma32(va, P.v[qb][kb][tt], o[qb][db]);
+          }
+      }
+      return;
+    }
     const E *Vt = lds_at(&Vs[0][0], v_lane + slot * VSLOT);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
@@ -524,9 +633,16 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
                       ? min(tf1, (max(0, wg_last - a.window + 1) + kKT - 1) / kKT)
                       : t0;
 
-  for (int j = t0; j < t0 + 3 && j < ntiles; ++j) {
-    stage_load(j);
-    stage_store(j % 4, j % 4);
+  if constexpr (kDirect) {
+    // Every step issues one tile's loads, past the sequence end too (they read zeros), so
+    // the count of loads in flight after any tile is fixed.
+    for (int j = t0; j < t0 + kDepth; ++j) stage_load(j);
+    stage_store(0, 0);
+  } else {
+    for (int j = t0; j < t0 + 3 && j < ntiles; ++j) {
+      stage_load(j);
+      stage_store(j % 4, j % 4);
+    }
   }
   __syncthreads();
 
@@ -543,19 +659,19 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
   };
   // One masked tile (window edges, diagonal, keys past the sequence).
   auto masked_step = [&](int t) {
-    const bool stage = t + 3 < ntiles;
-    if (stage) stage_load(t + 3);
+    const bool stage = kDirect || t + 3 < ntiles;
+    if (stage) stage_load(t + kDepth);
     const int key0 = t * kKT;
     bool live = key0 <= w_last;
     if constexpr (kVar) live = live && (a.window == 0 || key0 + kKT > wrow0 - a.window + 1);
     if (live) {
-      score(t % 4, Sa);
+      score(t % kSlots, Sa);
       mask(Sa, key0);
       first_max(Sa, key0);
       probs(Sa, P);
-      pv_mma(t % 4, P);
+      pv_mma(t % kSlots, P);
     }
-    if (stage) stage_store((t + 3) % 4, (t + 3) % 4);
+    if (stage) stage_store((t + 3) % kSlots, (t + 3) % kSlots);
     __syncthreads();
   };
 
@@ -563,17 +679,17 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
   for (; t < tf0; ++t) masked_step(t);
 
   if (tf1 > tf0) {
-    score(tf0 % 4, Sa);
+    score(tf0 % kSlots, Sa);
     first_max(Sa, tf0 * kKT);
   }
-  if (tf1 > tf0 + 1) score((tf0 + 1) % 4, Sb);
+  if (tf1 > tf0 + 1) score((tf0 + 1) % kSlots, Sb);
 
   auto pipe_step = [&](int t, Scores &S0, Scores &S1, Scores &S2) {
-    const bool stage = t + 3 < ntiles;
-    stage_load(t + 3);       // unconditional: loads past the sequence return zeros
-    score((t + 2) % 4, S2);
+    const bool stage = kDirect || t + 3 < ntiles;
+    stage_load(t + kDepth);  // unconditional: loads past the sequence return zeros
+    score((t + 2) % kSlots, S2);
     probs(S0, P);
-    pv_mma(t % 4, P);
+    pv_mma(t % kSlots, P);
     const bool next_full = t + 1 < tf1;
     float mxs[QB];
 #pragma unroll
@@ -587,7 +703,7 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
       smax[qb] = next_full ? fmaxf(smax[qb], mxs[qb]) : smax[qb];
       raise_ref(qb, next_full ? mxs[qb] * cl2[qb] : -INFINITY);
     }
-    if (stage) stage_store((t + 3) % 4, (t + 3) % 4);
+    if (stage) stage_store((t + 3) % kSlots, (t + 3) % kSlots);
     __syncthreads();
   };
 
@@ -775,7 +891,8 @@ hipError_t launch_prefill(int dtype, const PrefillArgs &a, hipStream_t stream) {
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   dim3 grid((unsigned)blocks);
   const int mode = a.paged ? kModePaged
-                 : a.variant ? kModeVariant : (a.u_norm != nullptr ? kModeSave : kModePlain);
+                 : a.variant ? ((a.rope && !a.k_rotated) ? kModeVariantRot : kModeVariant)
+                 : (a.u_norm != nullptr ? kModeSave : kModePlain);
   const dim3 bb(64 * kWavesBf16), bf(64 * kWavesF32);
   if (dtype == 1) {
     if (mode == kModePlain)
@@ -787,6 +904,9 @@ hipError_t launch_prefill(int dtype, const PrefillArgs &a, hipStream_t stream) {
     else if (mode == kModeVariant)
       hipLaunchKernelGGL((polar_prefill_kernel<Bf16, kQbBf16, kWavesBf16, kModeVariant>), grid,
                          bb, 0, stream, a);
+    else if (mode == kModeVariantRot)
+      hipLaunchKernelGGL((polar_prefill_kernel<Bf16, kQbBf16, kWavesBf16, kModeVariantRot>),
+                         grid, bb, 0, stream, a);
     else
       hipLaunchKernelGGL((polar_prefill_kernel<Bf16, kQbBf16, kWavesBf16, kModePaged>), grid,
                          bb, 0, stream, a);
@@ -797,7 +917,7 @@ hipError_t launch_prefill(int dtype, const PrefillArgs &a, hipStream_t stream) {
     else if (mode == kModeSave)
       hipLaunchKernelGGL((polar_prefill_kernel<F32, kQbF32, kWavesF32, kModeSave>), grid, bf, 0,
                          stream, a);
-    else if (mode == kModeVariant)
+    else if (mode == kModeVariant || mode == kModeVariantRot)   // fp32 always stages K itself
       hipLaunchKernelGGL((polar_prefill_kernel<F32, kQbF32, kWavesF32, kModeVariant>), grid, bf,
                          0, stream, a);
     else
