@@ -60,14 +60,6 @@ float inv_log_train(const polar_params *p) {
   return (p->flags & POLAR_FLAG_LENGTH_TEMP) ? (float)(1.0 / log((double)p->train_len)) : 0.f;
 }
 
-}  // namespace
-
-extern "C" {
-
-}  // extern "C"
-
-namespace {
-
 struct PagedSrc {
   const int32_t *page_table, *start_pos;
   int stride, num_pages, max_seq_len;
