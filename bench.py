@@ -39,10 +39,17 @@ PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
 
 
 # Sources each timed kernel is built from; a counter record stays valid while these are unchanged.
+_PREFILL_SRC = ["polar_prefill.hip", "polar_mfma.h", "polar_kernels.h"]
+_DECODE_SRC = ["polar_decode.hip", "polar_mfma.h", "polar_kernels.h"]
 KERNEL_SOURCES = {
-    "prefill": ["polar_prefill.hip", "polar_mfma.h", "polar_kernels.h"],
-    "decode": ["polar_decode.hip", "polar_mfma.h", "polar_kernels.h"],
+    "prefill": _PREFILL_SRC,
+    "decode": _DECODE_SRC,
+    "decode_b1": _DECODE_SRC,
     "backward": ["polar_backward.hip", "polar_mfma.h", "polar_kernels.h"],
+    "variant": _PREFILL_SRC,            # key rotation + variant prefill, full causal range
+    "variant_window": _PREFILL_SRC,     # key rotation + variant prefill, 4096-key window
+    "paged": _PREFILL_SRC,
+    "append": ["polar_paged.hip", "polar_kernels.h"],
     "memory_step": ["polar_delta.hip", "polar_kernels.h"],
 }
 
@@ -208,7 +215,9 @@ def measure_variants(dev, q, k, v, pkw, pre, steps: int, warmup: int):
                      "ms": round(ms, 4), "value": round(tf, 2), "unit": "TFLOP/s",
                      "roofline": {"bound": "mfma", "achieved": round(tf, 2),
                                   "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                                  "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None}}
+                                  "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                                  "traffic": traffic_record("variant_window" if var["window"]
+                                                            else "variant")}}
         print(f"[bench] variant {name}: {ms:.3f} ms ({tf:.1f} TFLOP/s)", file=sys.stderr,
               flush=True)
     res["workload"] = ("prefill variants at B=1 T=65536 Hq=16 Hkv=4 d=64 bf16: flops over the "
@@ -254,7 +263,8 @@ def measure_decode_b1(dev, steps: int, warmup: int):
                         "(one token's 16 heads)",
             "value": round(gbs, 1), "unit": "GB/s", "ms": round(ms, 4), "bytes": byt,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}}
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": traffic_record("decode_b1")}}
 
 
 def measure_paged(dev, pre, steps: int, warmup: int):
@@ -301,11 +311,12 @@ def measure_paged(dev, pre, steps: int, warmup: int):
             "value": round(tf, 2), "unit": "TFLOP/s", "prefill_ms": round(p_ms, 4),
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
-                         "traffic": None},
+                         "traffic": traffic_record("paged")},
             "append": {"us": round(a_ms * 1e3, 2), "value": round(gbs, 1), "unit": "GB/s",
                        "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
                                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                    "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}}}
+                                    "frac": round(gbs / PEAK_HBM_GBS, 4),
+                                    "traffic": traffic_record("append")}}}
 
 
 def _delta_setup(dev):

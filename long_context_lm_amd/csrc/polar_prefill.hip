@@ -570,6 +570,26 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
   };
   // O^T += V^T P^T
   auto pv_mma = [&](int slot, const Probs &P) {
+    if constexpr (kDirect && !kPaged) {
+      // One asm block per 32-dimension half (see tr_read_tile).  The paged instance keeps
+      // the builtin below: with the block's full LDS wait it was 4% slower, as the wait
+      // also covers the page-id load issued at the start of the step.
+      static_assert(NKB == 2 && NT == 2, "a direct tile is two 32-key blocks of two halves");
+      const char *sb = smem + slot * kSlotBytes;
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        F va[4];
+        tr_read_tile(lds_addr(sb) + vofs[db], va);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+              o[qb][db] = TR::mma32(va[2 * kb + tt], P.v[qb][kb][tt], o[qb][db]);
+      }
+      return;
+    }
     if constexpr (kDirect) {
       typedef short s16x4 __attribute__((ext_vector_type(4)));
       const char *sb = smem + slot * kSlotBytes;
