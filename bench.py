@@ -93,15 +93,25 @@ def traffic_record(kind: str):
     return r["fetch_bytes"] * rec["fetch_factor"] + r["write_bytes"] * rec["write_factor"]
 
 
+# Oracle timings run after every GPU leg (each leg queues its own), so that seconds of CPU
+# work never sit between a leg's warmup and its timed calls.
+CPU_JOBS = []
+
+
+def blas_threads() -> int:
+    """Threads the oracle's NumPy BLAS runs with."""
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max(i["num_threads"] for i in threadpool_info()))
+    except Exception:  # pragma: no cover
+        return int(os.cpu_count() or 1)
+
+
 def cpu_baseline(pre, dec):
     """The CPU oracle, as it stands, on a bounded sample of the same two workloads."""
     import oracle
     import synth
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max(i["num_threads"] for i in threadpool_info())
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count()
+    cores = blas_threads()
     rows = np.linspace(0, pre.T - 1, 3072).astype(np.int64)
     t0 = time.perf_counter()
     oracle.polar_prefill(pre.as_f32("q"), pre.as_f32("k"), pre.as_f32("v"), pre.beta,
@@ -169,16 +179,18 @@ def measure_backward(dev, steps: int, warmup: int, with_cpu: bool):
     print(f"[bench] backward mean {b_ms:.3f} ms ({tf:.1f} TFLOP/s), training forward "
           f"{f_ms:.3f} ms", file=sys.stderr, flush=True)
     if with_cpu:
-        import oracle
-        t0 = time.perf_counter()
-        oracle.polar_prefill_grad(p.as_f32("q"), p.as_f32("k"), p.as_f32("v"), cot_np, p.beta,
-                                  p.null_bias, p.count_vec, p.train_len, p.flags)
-        t = time.perf_counter() - t0
-        rec["cpu_baseline"] = {"value": round(backward_flops(p.B, p.T, p.Hq, p.d) / t / 1e12, 5),
-                               "unit": "TFLOP/s", "cores": int(torch.get_num_threads()),
-                               "kind": "oracle",
-                               "sample": f"float64 autograd backward of the whole workload, "
-                                         f"all 8 sequences ({t:.1f} s)"}
+        def job():
+            import oracle
+            t0 = time.perf_counter()
+            oracle.polar_prefill_grad(p.as_f32("q"), p.as_f32("k"), p.as_f32("v"), cot_np,
+                                      p.beta, p.null_bias, p.count_vec, p.train_len, p.flags)
+            t = time.perf_counter() - t0
+            rec["cpu_baseline"] = {
+                "value": round(backward_flops(p.B, p.T, p.Hq, p.d) / t / 1e12, 5),
+                "unit": "TFLOP/s", "cores": int(torch.get_num_threads()), "kind": "oracle",
+                "sample": f"float64 autograd backward of the whole workload, all 8 sequences "
+                          f"({t:.1f} s)"}
+        CPU_JOBS.append(job)
     return rec
 
 
@@ -189,9 +201,11 @@ def visible_pairs(T: int, window: int) -> float:
     return window * (window + 1) / 2.0 + float(T - window) * window
 
 
-def measure_variants(dev, q, k, v, pkw, pre, steps: int, warmup: int):
+def measure_variants(dev, q, k, v, pkw, pre, steps: int, warmup: int, with_cpu: bool = False):
     """The variant modes on the T=64K workload: RoPE + softmax output over the full causal
-    range, and RoPE with a 4096-key sliding window."""
+    range, and RoPE with a 4096-key sliding window.  With ``with_cpu``, the oracle's variant
+    prefill is timed beside each on a bounded sample of rows (RoPE of the whole q and k
+    included, as the oracle does it)."""
     import torch
     from long_context_lm_amd import attn_fwd_variant, variant_workspace_bytes
     res = {}
@@ -220,6 +234,24 @@ def measure_variants(dev, q, k, v, pkw, pre, steps: int, warmup: int):
                                                             else "variant")}}
         print(f"[bench] variant {name}: {ms:.3f} ms ({tf:.1f} TFLOP/s)", file=sys.stderr,
               flush=True)
+        if with_cpu:
+            def job(r=res[name], window=var["window"], theta=var["rope_theta"]):
+                import oracle
+                n_rows = 1024
+                rows = np.linspace(0, pre.T - 1, n_rows).astype(np.int64)
+                t0 = time.perf_counter()
+                oracle.polar_prefill(pre.as_f32("q"), pre.as_f32("k"), pre.as_f32("v"),
+                                     pre.beta, pre.null_bias, pre.count_vec, pre.train_len,
+                                     pre.flags, rows=rows, window=window, rope_theta=theta)
+                dt = time.perf_counter() - t0
+                vis = np.minimum(rows + 1, window) if window else rows + 1
+                fl = 4.0 * pre.d * pre.Hq * float(vis.sum())
+                r["cpu_baseline"] = {
+                    "value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": blas_threads(),
+                    "kind": "oracle",
+                    "sample": f"{n_rows} rows evenly spaced of T=65536, all 16 heads, RoPE of "
+                              f"the whole q and k included ({dt:.1f} s)"}
+            CPU_JOBS.append(job)
     res["workload"] = ("prefill variants at B=1 T=65536 Hq=16 Hkv=4 d=64 bf16: flops over the "
                        "visible pairs of each mode; the time includes rotating the keys once "
                        "into the caller's workspace")
@@ -267,9 +299,10 @@ def measure_decode_b1(dev, steps: int, warmup: int):
                          "traffic": traffic_record("decode_b1")}}
 
 
-def measure_paged(dev, pre, steps: int, warmup: int):
+def measure_paged(dev, pre, steps: int, warmup: int, with_cpu: bool = False):
     """The last 4096-token chunk of the T=64K sequence over a shuffled page pool: KV append
-    of the chunk, then its chunked prefill over the 61440 cached tokens and itself."""
+    of the chunk, then its chunked prefill over the 61440 cached tokens and itself.  With
+    ``with_cpu``, the oracle's chunked prefill is timed on the chunk's first 512 rows."""
     import torch
     import synth
     from long_context_lm_amd import attn_prefill_paged, kv_append
@@ -306,17 +339,38 @@ def measure_paged(dev, pre, steps: int, warmup: int):
     gbs = a_bytes / (a_ms * 1e-3) / 1e9
     print(f"[bench] paged: append {a_ms * 1e3:.1f} us ({gbs:.0f} GB/s), chunked prefill "
           f"{p_ms:.3f} ms ({tf:.1f} TFLOP/s)", file=sys.stderr, flush=True)
-    return {"workload": "last 4096-token chunk of the B=1 T=65536 Hq=16 Hkv=4 d=64 bf16 sequence "
-                        "(61440 tokens cached in shuffled 64-token pages)",
-            "value": round(tf, 2), "unit": "TFLOP/s", "prefill_ms": round(p_ms, 4),
-            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
-                         "traffic": traffic_record("paged")},
-            "append": {"us": round(a_ms * 1e3, 2), "value": round(gbs, 1), "unit": "GB/s",
-                       "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
-                                    "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                    "frac": round(gbs / PEAK_HBM_GBS, 4),
-                                    "traffic": traffic_record("append")}}}
+    rec = {"workload": "last 4096-token chunk of the B=1 T=65536 Hq=16 Hkv=4 d=64 bf16 sequence "
+                       "(61440 tokens cached in shuffled 64-token pages)",
+           "cpu_baseline": None,
+           "value": round(tf, 2), "unit": "TFLOP/s", "prefill_ms": round(p_ms, 4),
+           "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                        "traffic": traffic_record("paged")},
+           "append": {"us": round(a_ms * 1e3, 2), "value": round(gbs, 1), "unit": "GB/s",
+                      "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
+                                   "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                   "frac": round(gbs / PEAK_HBM_GBS, 4),
+                                   "traffic": traffic_record("append")}}}
+    if with_cpu:
+        def job():
+            import oracle
+            n_rows = 512
+            # the chunk's own keys are appended first (untimed), as on the GPU
+            kp, vp = oracle.kv_append(ci.k_pool, ci.v_pool, ci.page_table, ci.start_pos,
+                                      ci.chunk("k"), ci.chunk("v"), ci.page_size, ci.max_seq_len)
+            t0 = time.perf_counter()
+            oracle.polar_prefill_paged(synth.bf16_bits_to_f32(ci.chunk("q"))[:, :n_rows], kp, vp,
+                                       ci.page_table, ci.start_pos, ci.page_size, pre.beta,
+                                       pre.null_bias, pre.count_vec, pre.train_len, pre.flags,
+                                       to_f64=lambda a: synth.bf16_bits_to_f32(a).astype(np.float64))
+            dt = time.perf_counter() - t0
+            fl = 4.0 * pre.d * pre.Hq * float(np.sum(start + np.arange(n_rows) + 1.0))
+            rec["cpu_baseline"] = {"value": fl / dt / 1e12, "unit": "TFLOP/s",
+                                   "cores": blas_threads(), "kind": "oracle",
+                                   "sample": f"first {n_rows} rows of the chunk, all 16 heads "
+                                             f"({dt:.1f} s)"}
+        CPU_JOBS.append(job)
+    return rec
 
 
 def _delta_setup(dev):
@@ -382,14 +436,16 @@ def measure_memory_step(dev, steps: int, warmup: int, with_cpu: bool = False):
                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                         "traffic": traffic_record("memory_step")}}
     if with_cpu:
-        import oracle
-        t0 = time.perf_counter()
-        oracle.delta_step_pool(d.pool, d.slots, d.as_f32("q"), d.as_f32("k"), d.as_f32("v"),
-                               d.alpha, d.beta)
-        t = time.perf_counter() - t0
-        rec["cpu_baseline"] = {"value": round(algo / t / 1e9, 3), "unit": "GB/s", "cores": 1,
-                               "kind": "oracle",
-                               "sample": f"float64 step of all 256 x 16 states ({t:.1f} s)"}
+        def job():
+            import oracle
+            t0 = time.perf_counter()
+            oracle.delta_step_pool(d.pool, d.slots, d.as_f32("q"), d.as_f32("k"),
+                                   d.as_f32("v"), d.alpha, d.beta)
+            t = time.perf_counter() - t0
+            rec["cpu_baseline"] = {"value": round(algo / t / 1e9, 3), "unit": "GB/s",
+                                   "cores": 1, "kind": "oracle",
+                                   "sample": f"float64 step of all 256 x 16 states ({t:.1f} s)"}
+        CPU_JOBS.append(job)
     return rec
 
 
@@ -521,8 +577,9 @@ def main():
                                 "traffic": tr_dec}},
     }
     rec["variants"] = measure_variants(dev, q, k, v, pkw, pre, max(1, args.steps // 4),
-                                       min(args.warmup, 2))
-    rec["paged"] = measure_paged(dev, pre, max(1, args.steps // 2), min(args.warmup, 2))
+                                       min(args.warmup, 2), not args.no_cpu_baseline)
+    rec["paged"] = measure_paged(dev, pre, max(1, args.steps // 2), min(args.warmup, 2),
+                                 not args.no_cpu_baseline)
     del q, k, v, qd, kc, vc, table, lens, ws
     torch.cuda.empty_cache()
     rec["decode_b1"] = measure_decode_b1(dev, args.steps, min(args.warmup, 2))
@@ -532,8 +589,10 @@ def main():
     rec["memory_step"] = measure_memory_step(dev, args.steps, args.warmup,
                                              not args.no_cpu_baseline)
     if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        print("[bench] timing the CPU oracle on bounded samples", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(pre, dec)
+        for job in CPU_JOBS:
+            job()
     else:
         rec["cpu_baseline"] = None
     print(json.dumps(rec), flush=True)
