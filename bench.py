@@ -258,7 +258,7 @@ def measure_variants(dev, q, k, v, pkw, pre, steps: int, warmup: int, with_cpu: 
     return res
 
 
-def measure_decode_b1(dev, steps: int, warmup: int):
+def measure_decode_b1(dev, steps: int, warmup: int, with_cpu: bool = False):
     """The other reading of the 16 single-token queries: one sequence whose 16 query heads
     decode against a 262,144-token cache (4 KV heads, 268 MB of K and V)."""
     import torch
@@ -291,12 +291,27 @@ def measure_decode_b1(dev, steps: int, warmup: int):
     byt = decode_bytes(d.B, d.max_seq_len, d.Hq, d.Hkv, d.d, d.page_size, d.page_table.shape[1])
     gbs = byt / (ms * 1e-3) / 1e9
     print(f"[bench] decode B=1: {ms:.3f} ms ({gbs:.1f} GB/s)", file=sys.stderr, flush=True)
-    return {"workload": "paged decode B=1 L=262144 Hq=16 Hkv=4 d=64 page=64 shuffled table "
-                        "(one token's 16 heads)",
-            "value": round(gbs, 1), "unit": "GB/s", "ms": round(ms, 4), "bytes": byt,
-            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                         "traffic": traffic_record("decode_b1")}}
+    rec = {"workload": "paged decode B=1 L=262144 Hq=16 Hkv=4 d=64 page=64 shuffled table "
+                       "(one token's 16 heads)",
+           "value": round(gbs, 1), "unit": "GB/s", "ms": round(ms, 4), "bytes": byt,
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                        "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                        "traffic": traffic_record("decode_b1")},
+           "cpu_baseline": None}
+    if with_cpu:
+        def job():
+            import oracle
+            t0 = time.perf_counter()
+            oracle.polar_decode_paged(synth.bf16_bits_to_f32(d.q), d.k_pool, d.v_pool,
+                                      d.page_table, d.seq_lens, d.page_size, d.beta,
+                                      d.null_bias, d.count_vec, d.train_len, d.flags,
+                                      to_f64=lambda a: synth.bf16_bits_to_f32(a).astype(np.float64))
+            t = time.perf_counter() - t0
+            rec["cpu_baseline"] = {"value": byt / t / 1e9, "unit": "GB/s", "cores": blas_threads(),
+                                   "kind": "oracle",
+                                   "sample": f"the whole workload ({t:.1f} s)"}
+        CPU_JOBS.append(job)
+    return rec
 
 
 def measure_paged(dev, pre, steps: int, warmup: int, with_cpu: bool = False):
@@ -582,7 +597,8 @@ def main():
                                  not args.no_cpu_baseline)
     del q, k, v, qd, kc, vc, table, lens, ws
     torch.cuda.empty_cache()
-    rec["decode_b1"] = measure_decode_b1(dev, args.steps, min(args.warmup, 2))
+    rec["decode_b1"] = measure_decode_b1(dev, args.steps, min(args.warmup, 2),
+                                         not args.no_cpu_baseline)
     torch.cuda.empty_cache()
     rec["backward"] = measure_backward(dev, max(1, args.steps // 2), args.warmup,
                                        not args.no_cpu_baseline)
