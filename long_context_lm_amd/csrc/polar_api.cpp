@@ -119,7 +119,6 @@ polar_status prefill(const polar_params *p, polar_dtype dt, int32_t B, int32_t T
   a.window = var ? var->window : 0;
   a.rope = (var && var->rope_theta > 0.f) ? 1 : 0;
   a.variant = (a.attn || a.window > 0 || a.rope) ? 1 : 0;
-  a.k_rotated = 0;
   // Keys rotated once into the caller's workspace instead of in every staging workgroup.
   void *k_rot = nullptr;
   if (a.rope && var->workspace) {
@@ -151,8 +150,10 @@ polar_status prefill(const polar_params *p, polar_dtype dt, int32_t B, int32_t T
   a.Hkv = p->n_kv_heads;
   a.G = a.Hq / a.Hkv;
   a.hb = polar::prefill_heads_per_block(a.G);
-  const int rows = polar::prefill_rows_per_block((int)dt, a.hb);
-  a.n_row_blocks = (T + rows - 1) / rows;
+  a.k_rotated = k_rot ? 1 : 0;          // the keys are rotated into k_rot before the launch
+  const polar::PrefillShape shape = polar::prefill_shape((int)dt, a);
+  a.waves = shape.waves;
+  a.n_row_blocks = (T + shape.rows - 1) / shape.rows;
   a.inv_log_train = inv_log_train(p);
   a.null_floor = (p->flags & POLAR_FLAG_NULL_FLOOR) ? 1 : 0;
   const long long blocks = (long long)a.n_row_blocks * a.Hkv * (a.G / a.hb) * B;
@@ -163,7 +164,6 @@ polar_status prefill(const polar_params *p, polar_dtype dt, int32_t B, int32_t T
     err = polar::launch_rope_keys((int)dt, a, k_rot, (hipStream_t)stream);
     if (err != hipSuccess) return fail(POLAR_ERR_HIP, "key rotation launch: %s", hipGetErrorString(err));
     a.k = k_rot;
-    a.k_rotated = 1;
   }
   err = polar::launch_prefill((int)dt, a, (hipStream_t)stream);
   if (err != hipSuccess) return fail(POLAR_ERR_HIP, "prefill launch: %s", hipGetErrorString(err));

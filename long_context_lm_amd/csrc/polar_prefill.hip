@@ -52,9 +52,11 @@
 #endif
 // 1: probability sums on the matrix pipe (ones and Gram products); 0: on the vector pipe,
 // from the rounded probabilities the P.V product uses (dot2 per pair for bf16).
-// Direct (bf16) tiles: tile t + DEPTH is loaded while step t runs (DEPTH + 1 LDS slots).
+// Direct (bf16) tiles: tile t + DEPTH is loaded while step t runs (DEPTH + 1 LDS slots;
+// DEPTH 0: one more than the distance the scores run ahead, the least that keeps each
+// tile's loads a whole step ahead of their use).
 #ifndef POLAR_PREFILL_DEPTH
-#define POLAR_PREFILL_DEPTH 3
+#define POLAR_PREFILL_DEPTH 0
 #endif
 #ifndef POLAR_PREFILL_MSTATS
 #define POLAR_PREFILL_MSTATS 0
@@ -119,15 +121,21 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
   // over the banks; K fragments are read as rows, V^T fragments with the transposing
   // ds_read_b64_tr_b16.  Other instances stage through registers into padded tiles (V
   // transposed on the way).
-  constexpr bool kDirect = KPL == 8 && kMode != kModeVariantRot && kKT == 64 && kThreads == 512;
+  constexpr bool kDirect =
+      KPL == 8 && kMode != kModeVariantRot && kKT == 64 && (kWaves == 8 || kWaves == 12);
   static_assert(!(kDirect && POLAR_PREFILL_MSTATS), "direct tiles take the vector statistics");
   constexpr int kSlotBytes = kDirect ? 2 * kKT * kD * (int)sizeof(E)
                                      : (kKT * KROW + kD * VROW) * (int)sizeof(E);
   // Tile t + kDepth is loaded during step t; the ring holds tiles t .. t + kDepth.  Direct
   // loads cost no registers, so they run further ahead than the register staging.
-  constexpr int kDepth = kDirect ? POLAR_PREFILL_DEPTH : 3;
+  // Scores run two tiles ahead of their probabilities, or one with 12-wave workgroups:
+  // that frees a 32-register score buffer, so three waves fit on each SIMD.
+  constexpr int kAhead = (kDirect && kWaves == 12) ? 1 : 2;
+  constexpr int kDepth =
+      kDirect ? (POLAR_PREFILL_DEPTH > 0 ? POLAR_PREFILL_DEPTH : kAhead + 1) : 3;
   constexpr int kSlots = kDepth + 1;
-  static_assert(kDepth >= 3 && 2 * (kDepth - 3) < 16, "depth 3..10");
+  static_assert(kAhead == 1 || kAhead == 2, "scores one or two tiles ahead");
+  static_assert(kDepth >= kAhead + 1 && 2 * (kDepth - kAhead - 1) < 16, "loads in flight < 16");
   __shared__ __attribute__((aligned(16))) char smem[kSlots * kSlotBytes];
   auto Ks = reinterpret_cast<E (*)[kKT * KROW]>(smem);
   auto Vs = reinterpret_cast<E (*)[kD * VROW]>(smem + 4 * kKT * KROW * sizeof(E));
@@ -281,9 +289,12 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
       rstride = kD * (int)sizeof(E);
     }
     if constexpr (kDirect) {
-      // Wave w moves keys 8w..8w+7 of K and of V: lane l takes key 8w + l/8 and the chunk
-      // that belongs in slot l%8 of that row, and the hardware writes lane l's 16 bytes at
-      // the wave's LDS base + 16 l.
+      // Wave w < 8 moves keys 8w..8w+7 of K and of V: lane l takes key 8w + l/8 and the
+      // chunk that belongs in slot l%8 of that row, and the hardware writes lane l's 16
+      // bytes at the wave's LDS base + 16 l.  Further waves only compute.
+      if constexpr (kWaves > 8) {
+        if (wave >= 8) return;
+      }
       const int key = 8 * wave + (lane >> 3);
       const int off = base + key * rstride + (((lane & 7) ^ (key & 7)) << 4);
       char *dst = smem + (t % kSlots) * kSlotBytes + wave * 1024;
@@ -321,10 +332,10 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
   auto stage_store = [&](int slot, int vslot) {
     if constexpr (kDirect) {
       // The tiles go straight to LDS.  Wait until this wave's loads of the tile needed next
-      // have landed: every call issues two loads (K and V) per tile, so at most the
-      // 2 (kDepth - 3) of the tiles after it may still be in flight.  The caller's barrier
-      // then publishes the tile.
-      __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * (kDepth - 3)));   // vmcnt(2 (kDepth - 3))
+      // (t + 1 + kAhead after step t) have landed: every call issues two loads (K and V)
+      // per tile, so those of the kDepth - kAhead - 1 tiles after it may still be in
+      // flight.  The caller's barrier then publishes the tile.
+      __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * (kDepth - kAhead - 1)));
       return;
     }
 #pragma unroll
@@ -702,7 +713,31 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
     score(tf0 % kSlots, Sa);
     first_max(Sa, tf0 * kKT);
   }
-  if (tf1 > tf0 + 1) score((tf0 + 1) % kSlots, Sb);
+  if (kAhead == 2 && tf1 > tf0 + 1) score((tf0 + 1) % kSlots, Sb);
+
+  // Scores one tile ahead: step t issues tile t+1's scores, then tile t's probabilities and
+  // P.V product (which cover the score MFMAs' latency), then tile t+1's maximum.
+  auto pipe_step1 = [&](int t, Scores &S0, Scores &S1) {
+    stage_load(t + kDepth);  // unconditional: loads past the sequence return zeros
+    score((t + 1) % kSlots, S1);
+    probs(S0, P);
+    pv_mma(t % kSlots, P);
+    const bool next_full = t + 1 < tf1;
+    float mxs[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) mxs[qb] = tile_max(S1, qb);
+    if (next_full) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) track(S1, qb, (t + 1) * kKT);
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      smax[qb] = next_full ? fmaxf(smax[qb], mxs[qb]) : smax[qb];
+      raise_ref(qb, next_full ? mxs[qb] * cl2[qb] : -INFINITY);
+    }
+    stage_store(0, 0);
+    __syncthreads();
+  };
 
   auto pipe_step = [&](int t, Scores &S0, Scores &S1, Scores &S2) {
     const bool stage = kDirect || t + 3 < ntiles;
@@ -727,13 +762,22 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
     __syncthreads();
   };
 
-  while (t < tf1) {
-    pipe_step(t, Sa, Sb, Sc);
-    if (++t >= tf1) break;
-    pipe_step(t, Sb, Sc, Sa);
-    if (++t >= tf1) break;
-    pipe_step(t, Sc, Sa, Sb);
-    ++t;
+  if constexpr (kAhead == 1) {
+    while (t < tf1) {
+      pipe_step1(t, Sa, Sb);
+      if (++t >= tf1) break;
+      pipe_step1(t, Sb, Sa);
+      ++t;
+    }
+  } else {
+    while (t < tf1) {
+      pipe_step(t, Sa, Sb, Sc);
+      if (++t >= tf1) break;
+      pipe_step(t, Sb, Sc, Sa);
+      if (++t >= tf1) break;
+      pipe_step(t, Sc, Sa, Sb);
+      ++t;
+    }
   }
   for (; t < ntiles; ++t) masked_step(t);
 
@@ -874,7 +918,11 @@ __global__ void __launch_bounds__(256) polar_rope_keys_kernel(PrefillArgs a, E *
 constexpr int kQbBf16 = POLAR_PREFILL_QB;
 constexpr int kQbF32 = 1;
 constexpr int kWavesBf16 = POLAR_PREFILL_WAVES;
+constexpr int kWavesBf16Wide = 12;   // plain and variant launches with many row blocks
 constexpr int kWavesF32 = 4;
+// The wide instances pay off once the grid holds about four workgroups per CU (256 CUs):
+// with fewer, 96-row blocks leave CUs idle.
+constexpr long long kWideMinWorkgroups = 1024;
 
 }  // namespace
 
@@ -884,10 +932,17 @@ int prefill_heads_per_block(int G) {
   return 1;
 }
 
-int prefill_rows_per_block(int dtype, int hb) {
-  const int qb = dtype == 1 ? kQbBf16 : kQbF32;
-  const int waves = dtype == 1 ? kWavesBf16 : kWavesF32;
-  return (waves / hb) * 32 * qb;
+PrefillShape prefill_shape(int dtype, const PrefillArgs &a) {
+  if (dtype != 1) return {kWavesF32, (kWavesF32 / a.hb) * 32 * kQbF32};
+  const int narrow = (kWavesBf16 / a.hb) * 32 * kQbBf16;
+  // Plain and variant launches whose keys are already rotated (direct tiles) may go wide.
+  const bool direct_mode = !a.paged && a.u_norm == nullptr && !(a.rope && !a.k_rotated);
+  if (kQbBf16 == 1 && direct_mode) {
+    const int wide = (kWavesBf16Wide / a.hb) * 32;
+    const long long wgs = (long long)((a.T + wide - 1) / wide) * a.Hkv * (a.G / a.hb) * a.B;
+    if (wgs >= kWideMinWorkgroups) return {kWavesBf16Wide, wide};
+  }
+  return {kWavesBf16, narrow};
 }
 
 hipError_t launch_rope_keys(int dtype, const PrefillArgs &a, void *k_out, hipStream_t stream) {
@@ -914,7 +969,18 @@ hipError_t launch_prefill(int dtype, const PrefillArgs &a, hipStream_t stream) {
                  : a.variant ? ((a.rope && !a.k_rotated) ? kModeVariantRot : kModeVariant)
                  : (a.u_norm != nullptr ? kModeSave : kModePlain);
   const dim3 bb(64 * kWavesBf16), bf(64 * kWavesF32);
-  if (dtype == 1) {
+  if (dtype == 1 && a.waves == kWavesBf16Wide) {
+    const dim3 bw(64 * kWavesBf16Wide);
+    if (mode == kModePlain)
+      hipLaunchKernelGGL((polar_prefill_kernel<Bf16, 1, kWavesBf16Wide, kModePlain>), grid, bw, 0,
+                         stream, a);
+    else if (mode == kModeVariant)
+      hipLaunchKernelGGL((polar_prefill_kernel<Bf16, 1, kWavesBf16Wide, kModeVariant>), grid, bw,
+                         0, stream, a);
+    else
+      return hipErrorInvalidConfiguration;   // prefill_shape never picks it for other modes
+  } else if (dtype == 1) {
+    if (a.waves != kWavesBf16) return hipErrorInvalidConfiguration;
     if (mode == kModePlain)
       hipLaunchKernelGGL((polar_prefill_kernel<Bf16, kQbBf16, kWavesBf16, kModePlain>), grid, bb,
                          0, stream, a);
@@ -931,6 +997,7 @@ hipError_t launch_prefill(int dtype, const PrefillArgs &a, hipStream_t stream) {
       hipLaunchKernelGGL((polar_prefill_kernel<Bf16, kQbBf16, kWavesBf16, kModePaged>), grid,
                          bb, 0, stream, a);
   } else {
+    if (a.waves != kWavesF32) return hipErrorInvalidConfiguration;
     if (mode == kModePlain)
       hipLaunchKernelGGL((polar_prefill_kernel<F32, kQbF32, kWavesF32, kModePlain>), grid, bf, 0,
                          stream, a);

@@ -4,6 +4,8 @@ Element-wise on every output at sizes the oracle finishes in seconds (several ro
 several 64-key tiles, ragged tails), and on sampled rows at the full workload sizes in the
 launch configuration the benchmark uses.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -154,3 +156,26 @@ def test_c4_full_size_sampled_rows(gpu_lib):
     # the planted needles dominate the last row: gate near 1, small n_eff
     for (_, h, _, i) in p.needles:
         assert got["gate"][0, i, h].item() > 0.9
+
+
+def _first_sequence(p):
+    return dataclasses.replace(p, B=1, q=p.q[:1], k=p.k[:1], v=p.v[:1],
+                               needles=[n for n in p.needles if n[0] == 0])
+
+
+def test_wide_workgroups_ragged_rows_and_equal_to_narrow(gpu_lib):
+    """B=4, T=8000, 16/4 heads: enough row blocks for the 12-wave instance (96-row blocks,
+    the last one ragged).  Sampled rows against the oracle, and every output bit-identical
+    to the 8-wave instance, which a one-sequence launch of the same inputs uses (the
+    per-row arithmetic is the same)."""
+    print("[case] prefill wide B=4 T=8000", flush=True)
+    p = synth.prefill_inputs("c2", B=4, T=8000)
+    got = gpu_prefill(p)
+    rows = np.array([0, 1, 63, 64, 95, 96, 191, 192, 4000, 7967, 7968, 7999])
+    batches = np.array([0, 3])
+    want = oracle_prefill(p, rows=rows, batches=batches)
+    assert_close(select(got, batches=batches, rows=rows), want, p.count_vec, p.dtype,
+                 label="wide B=4 T=8000")
+    one = gpu_prefill(_first_sequence(p))
+    for key in ("dir", "count", "n_eff", "gate", "lse"):
+        assert torch.equal(got[key][:1], one[key]), key

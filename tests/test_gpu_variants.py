@@ -1,6 +1,8 @@
 """GPU parity of the variant modes (sliding window, RoPE on load, plain softmax output)
 against the float64 oracle, through the C ABI.  Tolerances as in tests/parity.py; the
 plain softmax output uses the direction metric scaled by |attn|."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -88,3 +90,21 @@ def test_variant_full_size_rope_softmax_sampled(gpu_lib):
     heads = np.array([0, 3, 8, 15])
     want = oracle_prefill(p, rows=rows, heads=heads, window=0, rope_theta=10000.0)
     check(p, select(got, rows=rows, heads=heads), want, "C4 W=0 rope", heads=heads)
+
+
+def test_wide_variant_ragged_rows_and_equal_to_narrow(gpu_lib):
+    """Window 1000 with RoPE at B=4, T=8000: the 12-wave variant instance (keys rotated once
+    into the workspace), sampled rows against the oracle, and bit-identical to the 8-wave
+    instance of a one-sequence launch."""
+    print("[case] variant wide B=4 T=8000 W=1000 theta=10000", flush=True)
+    p = synth.prefill_inputs("c2", B=4, T=8000)
+    var = dict(window=1000, rope_theta=10000.0)
+    got = run(p, **var)
+    rows = np.array([0, 1, 95, 96, 999, 1000, 1001, 5000, 7968, 7999])
+    batches = np.array([0, 3])
+    want = oracle_prefill(p, rows=rows, batches=batches, **var)
+    check(p, select(got, batches=batches, rows=rows), want, "wide W=1000 rope")
+    one = run(dataclasses.replace(p, B=1, q=p.q[:1], k=p.k[:1], v=p.v[:1],
+                                  needles=[n for n in p.needles if n[0] == 0]), **var)
+    for key in ("dir", "count", "n_eff", "gate", "lse", "attn"):
+        assert torch.equal(got[key][:1], one[key]), key
