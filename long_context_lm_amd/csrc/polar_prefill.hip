@@ -6,11 +6,13 @@
 // scores never exist in memory.  The arithmetic per row is section 2.1's direction and
 // magnitude channels (definitions in include/polar.h).
 //
-// Work decomposition (one workgroup = kWaves waves):
+// Work decomposition (one workgroup = kWaves waves: 8, or 12 for plain and variant
+// launches with many row blocks, as prefill_shape picks):
 //  * a workgroup owns `hb` query heads that share one KV head (GQA) and a block of rows;
 //    each wave owns 32*QB consecutive rows of one of those heads;
-//  * K and V tiles of 64 keys are staged into LDS through a four-slot ring, so every K/V
-//    byte brought on chip serves all `hb` heads and all rows of the block.  bf16 tiles go
+//  * K and V tiles of 64 keys are staged into LDS through a ring of three or four slots,
+//    so every K/V byte brought on chip serves all `hb` heads and all rows of the block.
+//    bf16 tiles go
 //    global -> LDS directly (buffer loads with the LDS destination), row-major with a
 //    16-byte chunk swizzle, and V^T fragments come from the transposing LDS read; fp32
 //    tiles, and bf16 keys that still need RoPE, pass through registers (V transposed);
@@ -27,9 +29,10 @@
 //  * training instances (kMode == kModeSave) also keep, per lane, the first key attaining
 //    the lane's running maximum score and write |u| and that key (the row's arg-max) for
 //    the backward pass;
-//  * variant instances (kMode == kModeVariant) add a sliding window, RoPE applied to q at
-//    load and to each K tile while it is staged into LDS, and the plain softmax output;
-//    every tile goes through the masked path;
+//  * variant instances add a sliding window, RoPE and the plain softmax output: q is
+//    rotated as it is loaded, and K either arrives rotated (kModeVariant, rotated once by
+//    polar_rope_keys_kernel) or is rotated while each tile is staged through registers
+//    (kModeVariantRot); tiles that every row sees whole take the pipelined path;
 //  * paged instances (kMode == kModePaged) serve chunked prefill over a paged KV cache: the
 //    rows are C new tokens at positions start_pos[b].., and a 64-key tile is one page,
 //    read through the page table (pages with invalid ids are masked out).
@@ -650,11 +653,14 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
   // ---- software-pipelined key loop ----
   // On gfx950 a wave waiting to issue an MFMA also holds back VALU issue of the other wave
   // on its SIMD, so matrix and vector work overlap inside each wave's own instruction
-  // stream.  Step t issues the scores of tile t+2 (MFMA) beside tile t's probabilities
-  // (VALU), then tile t's P.V product beside the maximum of tile t+1, whose scores were
-  // issued a whole step earlier, so no VALU instruction waits on a recent MFMA result.
-  // Tiles fully below the workgroup's first row need no mask; the diagonal tiles run one
-  // at a time.  K and V use four LDS slots: tile t+3 is stored while tiles t..t+2 are live.
+  // stream.  With scores two tiles ahead (8-wave instances), step t issues the scores of
+  // tile t+2 (MFMA) beside tile t's probabilities (VALU), then tile t's P.V product beside
+  // the maximum of tile t+1, whose scores were issued a whole step earlier, so no VALU
+  // instruction waits on a recent MFMA result; K and V use four LDS slots (tile t+3 is
+  // stored while tiles t..t+2 are live).  With scores one tile ahead (12-wave instances),
+  // step t issues tile t+1's scores, then tile t's probabilities and P.V product, which
+  // cover their latency, then tile t+1's maximum; three slots.  Tiles fully below the
+  // workgroup's first row need no mask; the diagonal tiles run one at a time.
   // Tiles [tf0, tf1) are seen whole by every row of the workgroup and take this pipelined
   // path; the others are masked one at a time.  With a sliding window the loop starts at
   // the first tile any row can see (t0) and the fully visible range starts at tf0.
