@@ -28,7 +28,7 @@ constexpr int kEntry = 68;        // floats per (b, head, split) partial
 constexpr float kLazyTheta = 8.0f;
 constexpr int kTargetWaves = 4096;
 #ifndef POLAR_DECODE_COMBINE_WAVES
-#define POLAR_DECODE_COMBINE_WAVES 8
+#define POLAR_DECODE_COMBINE_WAVES 16
 #endif
 constexpr int kCombineWaves = POLAR_DECODE_COMBINE_WAVES;   // waves per (b, head) merge
 
