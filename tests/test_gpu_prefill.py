@@ -179,3 +179,18 @@ def test_wide_workgroups_ragged_rows_and_equal_to_narrow(gpu_lib):
     one = gpu_prefill(_first_sequence(p))
     for key in ("dir", "count", "n_eff", "gate", "lse"):
         assert torch.equal(got[key][:1], one[key]), key
+
+
+def test_wide_workgroups_short_rows_large_batch(gpu_lib):
+    """B=300, T=50: 1200 workgroups choose the 12-wave instance, whose 96-row block then
+    holds 50 valid rows (waves 8-11 see none).  All rows of two sequences against the oracle,
+    and the first sequence bit-identical to its own (8-wave) launch."""
+    print("[case] prefill wide B=300 T=50", flush=True)
+    p = synth.prefill_inputs("c2", B=300, T=50)
+    got = gpu_prefill(p)
+    batches = np.array([0, 299])
+    want = oracle_prefill(p, batches=batches)
+    assert_close(select(got, batches=batches), want, p.count_vec, p.dtype, label="wide B=300 T=50")
+    one = gpu_prefill(_first_sequence(p))
+    for key in ("dir", "count", "n_eff", "gate", "lse"):
+        assert torch.equal(got[key][:1], one[key]), key
