@@ -1,6 +1,6 @@
 """CPU oracle for Polar Attention (test infrastructure only).
 
-Only the tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py``
+Only the tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` legs of ``bench.py``
 may import this package.  The product path (``long_context_lm_amd``) never does.
 """
 from .polar_oracle import (length_temperature, null_floor, polar_prefill, polar_decode_paged,

@@ -1,7 +1,7 @@
 """Plain float64 CPU oracle of the Polar Attention forward (prefill and paged decode).
 
 TEST INFRASTRUCTURE: imported only by tests/, ``__graft_entry__.smoke()`` and the
-``cpu_baseline`` leg of bench.py.  It shares no code with the HIP path.
+``cpu_baseline`` legs of bench.py.  It shares no code with the HIP path.
 
 What it computes follows the "ATMA: Length-Invariant Language Modeling via Polar Attention
 and Gated-Delta Compression Memory" technical summary (gist.science), section 2.1
