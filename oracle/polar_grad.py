@@ -1,6 +1,6 @@
 """Float64 reverse-mode oracle of the causal Polar Attention prefill (the backward pass).
 
-TEST INFRASTRUCTURE: imported only by tests/ and bench.py's ``cpu_baseline`` leg.  It
+TEST INFRASTRUCTURE: imported only by tests/, ``__graft_entry__.smoke()`` and bench.py's ``cpu_baseline`` legs.  It
 shares no code with the HIP path.
 
 The forward is written out again with torch CPU tensors in float64 (the definitions of
