@@ -1,7 +1,7 @@
 """Float64 CPU oracle of the gated-delta memory step (the recurrent memory stream).
 
-TEST INFRASTRUCTURE: imported only by tests/, ``__graft_entry__.smoke()`` and bench.py's ``cpu_baseline`` legs.  It shares
-no code with the HIP path.
+TEST INFRASTRUCTURE: imported only by tests/, ``__graft_entry__.smoke()`` and bench.py's
+``cpu_baseline`` legs.  It shares no code with the HIP path.
 
 The "ATMA: Length-Invariant Language Modeling via Polar Attention and Gated-Delta
 Compression Memory" technical summary (gist.science) adds to Polar Attention a third,

@@ -1,7 +1,7 @@
 """Float64 reverse-mode oracle of the causal Polar Attention prefill (the backward pass).
 
-TEST INFRASTRUCTURE: imported only by tests/, ``__graft_entry__.smoke()`` and bench.py's ``cpu_baseline`` legs.  It
-shares no code with the HIP path.
+TEST INFRASTRUCTURE: imported only by tests/, ``__graft_entry__.smoke()`` and bench.py's
+``cpu_baseline`` legs.  It shares no code with the HIP path.
 
 The forward is written out again with torch CPU tensors in float64 (the definitions of
 the "ATMA: Length-Invariant Language Modeling via Polar Attention and Gated-Delta
