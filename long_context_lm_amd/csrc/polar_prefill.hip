@@ -6,11 +6,11 @@
 // scores never exist in memory.  The arithmetic per row is section 2.1's direction and
 // magnitude channels (definitions in include/polar.h).
 //
-// Work decomposition (one workgroup = kWaves waves: 8, or 12 for plain and variant
+// Work decomposition (one workgroup = kWaves waves: 8, or 16 for plain and variant
 // launches with many row blocks, as prefill_shape picks):
 //  * a workgroup owns `hb` query heads that share one KV head (GQA) and a block of rows;
 //    each wave owns 32*QB consecutive rows of one of those heads;
-//  * K and V tiles of 64 keys are staged into LDS through a ring of three or four slots,
+//  * K and V tiles of 64 keys are staged into LDS through a ring of two or four slots,
 //    so every K/V byte brought on chip serves all `hb` heads and all rows of the block.
 //    bf16 tiles go
 //    global -> LDS directly (buffer loads with the LDS destination), row-major with a
@@ -125,19 +125,22 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
   // ds_read_b64_tr_b16.  Other instances stage through registers into padded tiles (V
   // transposed on the way).
   constexpr bool kDirect =
-      KPL == 8 && kMode != kModeVariantRot && kKT == 64 && (kWaves == 8 || kWaves == 12);
+      KPL == 8 && kMode != kModeVariantRot && kKT == 64 &&
+      (kWaves == 8 || kWaves == 16);
   static_assert(!(kDirect && POLAR_PREFILL_MSTATS), "direct tiles take the vector statistics");
   constexpr int kSlotBytes = kDirect ? 2 * kKT * kD * (int)sizeof(E)
                                      : (kKT * KROW + kD * VROW) * (int)sizeof(E);
   // Tile t + kDepth is loaded during step t; the ring holds tiles t .. t + kDepth.  Direct
   // loads cost no registers, so they run further ahead than the register staging.
-  // Scores run two tiles ahead of their probabilities, or one with 12-wave workgroups:
-  // that frees a 32-register score buffer, so three waves fit on each SIMD.
-  constexpr int kAhead = (kDirect && kWaves == 12) ? 1 : 2;
+  // Scores run two tiles ahead of their probabilities in 8-wave workgroups.  16-wave
+  // workgroups use each tile's scores in the step that issues them: with one score buffer
+  // instead of three the kernel fits 128 registers, four waves share each SIMD, and the
+  // other waves cover the score MFMAs' latency.
+  constexpr int kAhead = (kDirect && kWaves == 16) ? 0 : 2;
   constexpr int kDepth =
       kDirect ? (POLAR_PREFILL_DEPTH > 0 ? POLAR_PREFILL_DEPTH : kAhead + 1) : 3;
   constexpr int kSlots = kDepth + 1;
-  static_assert(kAhead == 1 || kAhead == 2, "scores one or two tiles ahead");
+  static_assert(kAhead == 0 || kAhead == 2, "scores in the same step or two tiles ahead");
   static_assert(kDepth >= kAhead + 1 && 2 * (kDepth - kAhead - 1) < 16, "loads in flight < 16");
   __shared__ __attribute__((aligned(16))) char smem[kSlots * kSlotBytes];
   auto Ks = reinterpret_cast<E (*)[kKT * KROW]>(smem);
@@ -657,10 +660,10 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
   // tile t+2 (MFMA) beside tile t's probabilities (VALU), then tile t's P.V product beside
   // the maximum of tile t+1, whose scores were issued a whole step earlier, so no VALU
   // instruction waits on a recent MFMA result; K and V use four LDS slots (tile t+3 is
-  // stored while tiles t..t+2 are live).  With scores one tile ahead (12-wave instances),
-  // step t issues tile t+1's scores, then tile t's probabilities and P.V product, which
-  // cover their latency, then tile t+1's maximum; three slots.  Tiles fully below the
-  // workgroup's first row need no mask; the diagonal tiles run one at a time.
+  // stored while tiles t..t+2 are live).  16-wave instances take each tile whole in one
+  // step (scores, maximum, probabilities, P.V) and leave the overlap to the other waves
+  // of the SIMD; two slots.  Tiles fully below the workgroup's first row need no mask;
+  // the diagonal tiles run one at a time.
   // Tiles [tf0, tf1) are seen whole by every row of the workgroup and take this pipelined
   // path; the others are masked one at a time.  With a sliding window the loop starts at
   // the first tile any row can see (t0) and the fully visible range starts at tf0.
@@ -715,35 +718,11 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
   int t = t0;
   for (; t < tf0; ++t) masked_step(t);
 
-  if (tf1 > tf0) {
+  if (kAhead > 0 && tf1 > tf0) {
     score(tf0 % kSlots, Sa);
     first_max(Sa, tf0 * kKT);
   }
   if (kAhead == 2 && tf1 > tf0 + 1) score((tf0 + 1) % kSlots, Sb);
-
-  // Scores one tile ahead: step t issues tile t+1's scores, then tile t's probabilities and
-  // P.V product (which cover the score MFMAs' latency), then tile t+1's maximum.
-  auto pipe_step1 = [&](int t, Scores &S0, Scores &S1) {
-    stage_load(t + kDepth);  // unconditional: loads past the sequence return zeros
-    score((t + 1) % kSlots, S1);
-    probs(S0, P);
-    pv_mma(t % kSlots, P);
-    const bool next_full = t + 1 < tf1;
-    float mxs[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) mxs[qb] = tile_max(S1, qb);
-    if (next_full) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) track(S1, qb, (t + 1) * kKT);
-    }
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      smax[qb] = next_full ? fmaxf(smax[qb], mxs[qb]) : smax[qb];
-      raise_ref(qb, next_full ? mxs[qb] * cl2[qb] : -INFINITY);
-    }
-    stage_store(0, 0);
-    __syncthreads();
-  };
 
   auto pipe_step = [&](int t, Scores &S0, Scores &S1, Scores &S2) {
     const bool stage = kDirect || t + 3 < ntiles;
@@ -768,12 +747,17 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
     __syncthreads();
   };
 
-  if constexpr (kAhead == 1) {
-    while (t < tf1) {
-      pipe_step1(t, Sa, Sb);
-      if (++t >= tf1) break;
-      pipe_step1(t, Sb, Sa);
-      ++t;
+  if constexpr (kAhead == 0) {
+    // Each tile's scores, maximum, probabilities and P.V in one step; the other waves of
+    // the SIMD cover the score MFMAs' latency.
+    for (; t < tf1; ++t) {
+      stage_load(t + kDepth);
+      score(t % kSlots, Sa);
+      first_max(Sa, t * kKT);
+      probs(Sa, P);
+      pv_mma(t % kSlots, P);
+      stage_store(0, 0);
+      __syncthreads();
     }
   } else {
     while (t < tf1) {
@@ -924,11 +908,11 @@ __global__ void __launch_bounds__(256) polar_rope_keys_kernel(PrefillArgs a, E *
 constexpr int kQbBf16 = POLAR_PREFILL_QB;
 constexpr int kQbF32 = 1;
 constexpr int kWavesBf16 = POLAR_PREFILL_WAVES;
-constexpr int kWavesBf16Wide = 12;   // plain and variant launches with many row blocks
+constexpr int kWavesBf16Wide = 16;   // plain and variant launches with many row blocks
 constexpr int kWavesF32 = 4;
-// The wide instances pay off once the grid holds about four workgroups per CU (256 CUs):
-// with fewer, 96-row blocks leave CUs idle.
-constexpr long long kWideMinWorkgroups = 1024;
+// The wide instances pay off once the grid holds two workgroups per CU (256 CUs): with
+// fewer, 128-row blocks leave CUs idle.
+constexpr long long kWideMinWorkgroups = 512;
 
 }  // namespace
 
