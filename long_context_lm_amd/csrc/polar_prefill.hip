@@ -6,7 +6,7 @@
 // scores never exist in memory.  The arithmetic per row is section 2.1's direction and
 // magnitude channels (definitions in include/polar.h).
 //
-// Work decomposition (one workgroup = kWaves waves: 8, or 16 for plain and variant
+// Work decomposition (one workgroup = kWaves waves: 8, or 16 for plain, variant and paged
 // launches with many row blocks, as prefill_shape picks):
 //  * a workgroup owns `hb` query heads that share one KV head (GQA) and a block of rows;
 //    each wave owns 32*QB consecutive rows of one of those heads;
@@ -908,7 +908,7 @@ __global__ void __launch_bounds__(256) polar_rope_keys_kernel(PrefillArgs a, E *
 constexpr int kQbBf16 = POLAR_PREFILL_QB;
 constexpr int kQbF32 = 1;
 constexpr int kWavesBf16 = POLAR_PREFILL_WAVES;
-constexpr int kWavesBf16Wide = 16;   // plain and variant launches with many row blocks
+constexpr int kWavesBf16Wide = 16;   // launches with many row blocks (not the training one)
 constexpr int kWavesF32 = 4;
 // The wide instances pay off once the grid holds two workgroups per CU (256 CUs): with
 // fewer, 128-row blocks leave CUs idle.
@@ -925,8 +925,9 @@ int prefill_heads_per_block(int G) {
 PrefillShape prefill_shape(int dtype, const PrefillArgs &a) {
   if (dtype != 1) return {kWavesF32, (kWavesF32 / a.hb) * 32 * kQbF32};
   const int narrow = (kWavesBf16 / a.hb) * 32 * kQbBf16;
-  // Plain and variant launches whose keys are already rotated (direct tiles) may go wide.
-  const bool direct_mode = !a.paged && a.u_norm == nullptr && !(a.rope && !a.k_rotated);
+  // Plain, variant and paged launches whose keys are already rotated (direct tiles) may go
+  // wide; the training forward stays narrow (16 waves spill its arg-max tracking).
+  const bool direct_mode = a.u_norm == nullptr && !(a.rope && !a.k_rotated);
   if (kQbBf16 == 1 && direct_mode) {
     const int wide = (kWavesBf16Wide / a.hb) * 32;
     const long long wgs = (long long)((a.T + wide - 1) / wide) * a.Hkv * (a.G / a.hb) * a.B;
@@ -967,6 +968,9 @@ hipError_t launch_prefill(int dtype, const PrefillArgs &a, hipStream_t stream) {
     else if (mode == kModeVariant)
       hipLaunchKernelGGL((polar_prefill_kernel<Bf16, 1, kWavesBf16Wide, kModeVariant>), grid, bw,
                          0, stream, a);
+    else if (mode == kModePaged)
+      hipLaunchKernelGGL((polar_prefill_kernel<Bf16, 1, kWavesBf16Wide, kModePaged>), grid, bw, 0,
+                         stream, a);
     else
       return hipErrorInvalidConfiguration;   // prefill_shape never picks it for other modes
   } else if (dtype == 1) {
