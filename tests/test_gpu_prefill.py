@@ -164,14 +164,14 @@ def _first_sequence(p):
 
 
 def test_wide_workgroups_ragged_rows_and_equal_to_narrow(gpu_lib):
-    """B=4, T=8000, 16/4 heads: enough row blocks for the 12-wave instance (96-row blocks,
+    """B=4, T=8000, 16/4 heads: enough row blocks for the 16-wave instance (128-row blocks,
     the last one ragged).  Sampled rows against the oracle, and every output bit-identical
     to the 8-wave instance, which a one-sequence launch of the same inputs uses (the
     per-row arithmetic is the same)."""
     print("[case] prefill wide B=4 T=8000", flush=True)
     p = synth.prefill_inputs("c2", B=4, T=8000)
     got = gpu_prefill(p)
-    rows = np.array([0, 1, 63, 64, 95, 96, 191, 192, 4000, 7967, 7968, 7999])
+    rows = np.array([0, 1, 63, 64, 127, 128, 255, 256, 4000, 7935, 7936, 7999])
     batches = np.array([0, 3])
     want = oracle_prefill(p, rows=rows, batches=batches)
     assert_close(select(got, batches=batches, rows=rows), want, p.count_vec, p.dtype,
@@ -182,8 +182,8 @@ def test_wide_workgroups_ragged_rows_and_equal_to_narrow(gpu_lib):
 
 
 def test_wide_workgroups_short_rows_large_batch(gpu_lib):
-    """B=300, T=50: 1200 workgroups choose the 12-wave instance, whose 96-row block then
-    holds 50 valid rows (waves 8-11 see none).  All rows of two sequences against the oracle,
+    """B=300, T=50: 1200 workgroups choose the 16-wave instance, whose 128-row block then
+    holds 50 valid rows (the waves of rows 64-127 see none).  All rows of two sequences against the oracle,
     and the first sequence bit-identical to its own (8-wave) launch."""
     print("[case] prefill wide B=300 T=50", flush=True)
     p = synth.prefill_inputs("c2", B=300, T=50)
@@ -191,6 +191,24 @@ def test_wide_workgroups_short_rows_large_batch(gpu_lib):
     batches = np.array([0, 299])
     want = oracle_prefill(p, batches=batches)
     assert_close(select(got, batches=batches), want, p.count_vec, p.dtype, label="wide B=300 T=50")
+    one = gpu_prefill(_first_sequence(p))
+    for key in ("dir", "count", "n_eff", "gate", "lse"):
+        assert torch.equal(got[key][:1], one[key]), key
+
+
+@pytest.mark.parametrize("B,T,Hq,Hkv", [(128, 600, 4, 4), (64, 600, 8, 4)])
+def test_wide_workgroups_fewer_heads_per_block(gpu_lib, B, T, Hq, Hkv):
+    """GQA groups of 1 and 2 heads: the 16-wave instance then owns 512- or 256-row blocks
+    (more masked diagonal tiles per workgroup).  Sampled rows of two sequences against the
+    oracle, and the first sequence bit-identical to its own (8-wave) launch."""
+    print(f"[case] prefill wide B={B} T={T} Hq={Hq} Hkv={Hkv}", flush=True)
+    p = synth.prefill_inputs("c2", B=B, T=T, Hq=Hq, Hkv=Hkv)
+    got = gpu_prefill(p)
+    rows = np.array([0, 1, 63, 64, 255, 256, 511, 512, T - 1])
+    batches = np.array([0, B - 1])
+    want = oracle_prefill(p, rows=rows, batches=batches)
+    assert_close(select(got, batches=batches, rows=rows), want, p.count_vec, p.dtype,
+                 label=f"wide Hq={Hq} Hkv={Hkv}")
     one = gpu_prefill(_first_sequence(p))
     for key in ("dir", "count", "n_eff", "gate", "lse"):
         assert torch.equal(got[key][:1], one[key]), key

@@ -93,14 +93,14 @@ def test_variant_full_size_rope_softmax_sampled(gpu_lib):
 
 
 def test_wide_variant_ragged_rows_and_equal_to_narrow(gpu_lib):
-    """Window 1000 with RoPE at B=4, T=8000: the 12-wave variant instance (keys rotated once
+    """Window 1000 with RoPE at B=4, T=8000: the 16-wave variant instance (keys rotated once
     into the workspace), sampled rows against the oracle, and bit-identical to the 8-wave
     instance of a one-sequence launch."""
     print("[case] variant wide B=4 T=8000 W=1000 theta=10000", flush=True)
     p = synth.prefill_inputs("c2", B=4, T=8000)
     var = dict(window=1000, rope_theta=10000.0)
     got = run(p, **var)
-    rows = np.array([0, 1, 95, 96, 999, 1000, 1001, 5000, 7968, 7999])
+    rows = np.array([0, 1, 127, 128, 999, 1000, 1001, 5000, 7936, 7999])
     batches = np.array([0, 3])
     want = oracle_prefill(p, rows=rows, batches=batches, **var)
     check(p, select(got, batches=batches, rows=rows), want, "wide W=1000 rope")
