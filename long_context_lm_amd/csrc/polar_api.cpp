@@ -152,7 +152,7 @@ polar_status prefill(const polar_params *p, polar_dtype dt, int32_t B, int32_t T
   a.hb = polar::prefill_heads_per_block(a.G);
   a.k_rotated = k_rot ? 1 : 0;          // the keys are rotated into k_rot before the launch
   const polar::PrefillShape shape = polar::prefill_shape((int)dt, a);
-  a.waves = shape.waves;
+  a.lean = shape.lean;
   a.n_row_blocks = (T + shape.rows - 1) / shape.rows;
   a.inv_log_train = inv_log_train(p);
   a.null_floor = (p->flags & POLAR_FLAG_NULL_FLOOR) ? 1 : 0;

@@ -25,7 +25,7 @@ struct PrefillArgs {
   uint64_t rope_f[kHeadDim / 2];          // revolutions per position of pair t, 2^-64 units
   int B, T, Hq, Hkv, G;                   // G = Hq / Hkv
   int hb;                                 // query heads per workgroup (divides G, <= 4)
-  int waves;                              // waves per workgroup of the instance (prefill_shape)
+  int lean;                               // 1: the lean instance (prefill_shape)
   int n_row_blocks;                       // ceil(T / rows per workgroup)
   float inv_log_train;                    // 1/ln(train_len) with the length temperature, else 0
   int null_floor;                         // 1: add the extreme-value term to the floor
@@ -39,10 +39,10 @@ struct PrefillArgs {
 
 // dtype: 0 = f32, 1 = bf16 (same numbering as polar_dtype).
 int prefill_heads_per_block(int G);
-// Waves and rows per workgroup of the prefill instance that runs a.  Reads dtype and
+// Whether the lean prefill instance runs a, and its rows per workgroup.  Reads dtype and
 // a.B, a.T, a.Hkv, a.G, a.hb, a.paged, a.variant, a.rope, a.k_rotated, a.u_norm.
 struct PrefillShape {
-  int waves, rows;
+  int lean, rows;
 };
 PrefillShape prefill_shape(int dtype, const PrefillArgs &a);
 hipError_t launch_prefill(int dtype, const PrefillArgs &a, hipStream_t stream);

@@ -6,8 +6,7 @@
 // scores never exist in memory.  The arithmetic per row is section 2.1's direction and
 // magnitude channels (definitions in include/polar.h).
 //
-// Work decomposition (one workgroup = kWaves waves: 8, or 16 for plain, variant and paged
-// launches with many row blocks, as prefill_shape picks):
+// Work decomposition (one workgroup = kWaves waves: 8 for bf16, 4 for fp32):
 //  * a workgroup owns `hb` query heads that share one KV head (GQA) and a block of rows;
 //    each wave owns 32*QB consecutive rows of one of those heads;
 //  * K and V tiles of 64 keys are staged into LDS through a ring of two or four slots,
@@ -104,7 +103,8 @@ __device__ __forceinline__ float rot_im(float x0, float x1, float c, float s) {
   return fmaf(x0, s, x1 * c);
 }
 
-template <class TR, int QB, int kWaves, int kMode>
+// kLean: each tile's scores are used in the step that issues them (see kAhead below).
+template <class TR, int QB, int kWaves, int kMode, bool kLean>
 __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs a) {
   constexpr bool kSave = kMode == kModeSave;
   constexpr bool kVar = kMode == kModeVariant || kMode == kModeVariantRot;
@@ -125,18 +125,19 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
   // ds_read_b64_tr_b16.  Other instances stage through registers into padded tiles (V
   // transposed on the way).
   constexpr bool kDirect =
-      KPL == 8 && kMode != kModeVariantRot && kKT == 64 &&
-      (kWaves == 8 || kWaves == 16);
+      KPL == 8 && kMode != kModeVariantRot && kKT == 64 && kWaves == 8;
   static_assert(!(kDirect && POLAR_PREFILL_MSTATS), "direct tiles take the vector statistics");
   constexpr int kSlotBytes = kDirect ? 2 * kKT * kD * (int)sizeof(E)
                                      : (kKT * KROW + kD * VROW) * (int)sizeof(E);
   // Tile t + kDepth is loaded during step t; the ring holds tiles t .. t + kDepth.  Direct
   // loads cost no registers, so they run further ahead than the register staging.
-  // Scores run two tiles ahead of their probabilities in 8-wave workgroups.  16-wave
-  // workgroups use each tile's scores in the step that issues them: with one score buffer
-  // instead of three the kernel fits 128 registers, four waves share each SIMD, and the
-  // other waves cover the score MFMAs' latency.
-  constexpr int kAhead = (kDirect && kWaves == 16) ? 0 : 2;
+  // Scores run two tiles ahead of their probabilities, so that no vector instruction waits
+  // on a recent MFMA result.  Lean instances use each tile's scores in the step that issues
+  // them: with one score buffer instead of three they fit 128 registers, two workgroups
+  // share each CU (four waves per SIMD), and the other workgroup's waves, whose barriers
+  // fall elsewhere, cover the score MFMAs' latency.
+  static_assert(!kLean || (kDirect && !kSave), "lean instances: direct tiles, no arg-max");
+  constexpr int kAhead = kLean ? 0 : 2;
   constexpr int kDepth =
       kDirect ? (POLAR_PREFILL_DEPTH > 0 ? POLAR_PREFILL_DEPTH : kAhead + 1) : 3;
   constexpr int kSlots = kDepth + 1;
@@ -295,12 +296,9 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
       rstride = kD * (int)sizeof(E);
     }
     if constexpr (kDirect) {
-      // Wave w < 8 moves keys 8w..8w+7 of K and of V: lane l takes key 8w + l/8 and the
-      // chunk that belongs in slot l%8 of that row, and the hardware writes lane l's 16
-      // bytes at the wave's LDS base + 16 l.  Further waves only compute.
-      if constexpr (kWaves > 8) {
-        if (wave >= 8) return;
-      }
+      // Wave w moves keys 8w..8w+7 of K and of V: lane l takes key 8w + l/8 and the chunk
+      // that belongs in slot l%8 of that row, and the hardware writes lane l's 16 bytes at
+      // the wave's LDS base + 16 l.
       const int key = 8 * wave + (lane >> 3);
       const int off = base + key * rstride + (((lane & 7) ^ (key & 7)) << 4);
       char *dst = smem + (t % kSlots) * kSlotBytes + wave * 1024;
@@ -660,9 +658,9 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
   // tile t+2 (MFMA) beside tile t's probabilities (VALU), then tile t's P.V product beside
   // the maximum of tile t+1, whose scores were issued a whole step earlier, so no VALU
   // instruction waits on a recent MFMA result; K and V use four LDS slots (tile t+3 is
-  // stored while tiles t..t+2 are live).  16-wave instances take each tile whole in one
-  // step (scores, maximum, probabilities, P.V) and leave the overlap to the other waves
-  // of the SIMD; two slots.  Tiles fully below the workgroup's first row need no mask;
+  // stored while tiles t..t+2 are live).  Lean instances take each tile whole in one step
+  // (scores, maximum, probabilities, P.V) and leave the overlap to the other workgroup on
+  // the CU; two slots.  Tiles fully below the workgroup's first row need no mask;
   // the diagonal tiles run one at a time.
   // Tiles [tf0, tf1) are seen whole by every row of the workgroup and take this pipelined
   // path; the others are masked one at a time.  With a sliding window the loop starts at
@@ -748,8 +746,8 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
   };
 
   if constexpr (kAhead == 0) {
-    // Each tile's scores, maximum, probabilities and P.V in one step; the other waves of
-    // the SIMD cover the score MFMAs' latency.
+    // Each tile's scores, maximum, probabilities and P.V in one step; the waves of the
+    // other workgroup on the CU cover the score MFMAs' latency.
     for (; t < tf1; ++t) {
       stage_load(t + kDepth);
       score(t % kSlots, Sa);
@@ -908,11 +906,11 @@ __global__ void __launch_bounds__(256) polar_rope_keys_kernel(PrefillArgs a, E *
 constexpr int kQbBf16 = POLAR_PREFILL_QB;
 constexpr int kQbF32 = 1;
 constexpr int kWavesBf16 = POLAR_PREFILL_WAVES;
-constexpr int kWavesBf16Wide = 16;   // launches with many row blocks (not the training one)
 constexpr int kWavesF32 = 4;
-// The wide instances pay off once the grid holds two workgroups per CU (256 CUs): with
-// fewer, 128-row blocks leave CUs idle.
-constexpr long long kWideMinWorkgroups = 512;
+// The lean instances pay off once the grid holds two workgroups per CU (256 CUs); with one
+// per CU the pipelined instances keep their two waves per SIMD busier.
+constexpr long long kLeanMinWorkgroups = 512;
+constexpr bool kHaveLean = kWavesBf16 == 8 && kQbBf16 == 1;
 
 }  // namespace
 
@@ -923,17 +921,14 @@ int prefill_heads_per_block(int G) {
 }
 
 PrefillShape prefill_shape(int dtype, const PrefillArgs &a) {
-  if (dtype != 1) return {kWavesF32, (kWavesF32 / a.hb) * 32 * kQbF32};
-  const int narrow = (kWavesBf16 / a.hb) * 32 * kQbBf16;
-  // Plain, variant and paged launches whose keys are already rotated (direct tiles) may go
-  // wide; the training forward stays narrow (16 waves spill its arg-max tracking).
+  if (dtype != 1) return {0, (kWavesF32 / a.hb) * 32 * kQbF32};
+  const int rows = (kWavesBf16 / a.hb) * 32 * kQbBf16;
+  // Plain, variant and paged launches whose keys are already rotated (direct tiles) may be
+  // lean; the training forward keeps the pipelined instance (its arg-max tracking needs
+  // 138 registers without the pipeline, too many for two workgroups per CU).
   const bool direct_mode = a.u_norm == nullptr && !(a.rope && !a.k_rotated);
-  if (kQbBf16 == 1 && direct_mode) {
-    const int wide = (kWavesBf16Wide / a.hb) * 32;
-    const long long wgs = (long long)((a.T + wide - 1) / wide) * a.Hkv * (a.G / a.hb) * a.B;
-    if (wgs >= kWideMinWorkgroups) return {kWavesBf16Wide, wide};
-  }
-  return {kWavesBf16, narrow};
+  const long long wgs = (long long)((a.T + rows - 1) / rows) * a.Hkv * (a.G / a.hb) * a.B;
+  return {(kHaveLean && direct_mode && wgs >= kLeanMinWorkgroups) ? 1 : 0, rows};
 }
 
 hipError_t launch_rope_keys(int dtype, const PrefillArgs &a, void *k_out, hipStream_t stream) {
@@ -960,50 +955,53 @@ hipError_t launch_prefill(int dtype, const PrefillArgs &a, hipStream_t stream) {
                  : a.variant ? ((a.rope && !a.k_rotated) ? kModeVariantRot : kModeVariant)
                  : (a.u_norm != nullptr ? kModeSave : kModePlain);
   const dim3 bb(64 * kWavesBf16), bf(64 * kWavesF32);
-  if (dtype == 1 && a.waves == kWavesBf16Wide) {
-    const dim3 bw(64 * kWavesBf16Wide);
-    if (mode == kModePlain)
-      hipLaunchKernelGGL((polar_prefill_kernel<Bf16, 1, kWavesBf16Wide, kModePlain>), grid, bw, 0,
-                         stream, a);
-    else if (mode == kModeVariant)
-      hipLaunchKernelGGL((polar_prefill_kernel<Bf16, 1, kWavesBf16Wide, kModeVariant>), grid, bw,
-                         0, stream, a);
-    else if (mode == kModePaged)
-      hipLaunchKernelGGL((polar_prefill_kernel<Bf16, 1, kWavesBf16Wide, kModePaged>), grid, bw, 0,
-                         stream, a);
-    else
-      return hipErrorInvalidConfiguration;   // prefill_shape never picks it for other modes
+  if (dtype == 1 && a.lean) {
+    if constexpr (kHaveLean) {
+      if (mode == kModePlain)
+        hipLaunchKernelGGL((polar_prefill_kernel<Bf16, 1, kWavesBf16, kModePlain, true>), grid,
+                           bb, 0, stream, a);
+      else if (mode == kModeVariant)
+        hipLaunchKernelGGL((polar_prefill_kernel<Bf16, 1, kWavesBf16, kModeVariant, true>), grid,
+                           bb, 0, stream, a);
+      else if (mode == kModePaged)
+        hipLaunchKernelGGL((polar_prefill_kernel<Bf16, 1, kWavesBf16, kModePaged, true>), grid,
+                           bb, 0, stream, a);
+      else
+        return hipErrorInvalidConfiguration;   // prefill_shape never picks it for other modes
+    } else {
+      return hipErrorInvalidConfiguration;
+    }
   } else if (dtype == 1) {
-    if (a.waves != kWavesBf16) return hipErrorInvalidConfiguration;
     if (mode == kModePlain)
-      hipLaunchKernelGGL((polar_prefill_kernel<Bf16, kQbBf16, kWavesBf16, kModePlain>), grid, bb,
-                         0, stream, a);
-    else if (mode == kModeSave)
-      hipLaunchKernelGGL((polar_prefill_kernel<Bf16, kQbBf16, kWavesBf16, kModeSave>), grid, bb,
-                         0, stream, a);
-    else if (mode == kModeVariant)
-      hipLaunchKernelGGL((polar_prefill_kernel<Bf16, kQbBf16, kWavesBf16, kModeVariant>), grid,
-                         bb, 0, stream, a);
-    else if (mode == kModeVariantRot)
-      hipLaunchKernelGGL((polar_prefill_kernel<Bf16, kQbBf16, kWavesBf16, kModeVariantRot>),
+      hipLaunchKernelGGL((polar_prefill_kernel<Bf16, kQbBf16, kWavesBf16, kModePlain, false>),
                          grid, bb, 0, stream, a);
-    else
-      hipLaunchKernelGGL((polar_prefill_kernel<Bf16, kQbBf16, kWavesBf16, kModePaged>), grid,
-                         bb, 0, stream, a);
-  } else {
-    if (a.waves != kWavesF32) return hipErrorInvalidConfiguration;
-    if (mode == kModePlain)
-      hipLaunchKernelGGL((polar_prefill_kernel<F32, kQbF32, kWavesF32, kModePlain>), grid, bf, 0,
-                         stream, a);
     else if (mode == kModeSave)
-      hipLaunchKernelGGL((polar_prefill_kernel<F32, kQbF32, kWavesF32, kModeSave>), grid, bf, 0,
-                         stream, a);
-    else if (mode == kModeVariant || mode == kModeVariantRot)   // fp32 always stages K itself
-      hipLaunchKernelGGL((polar_prefill_kernel<F32, kQbF32, kWavesF32, kModeVariant>), grid, bf,
-                         0, stream, a);
+      hipLaunchKernelGGL((polar_prefill_kernel<Bf16, kQbBf16, kWavesBf16, kModeSave, false>),
+                         grid, bb, 0, stream, a);
+    else if (mode == kModeVariant)
+      hipLaunchKernelGGL((polar_prefill_kernel<Bf16, kQbBf16, kWavesBf16, kModeVariant, false>),
+                         grid, bb, 0, stream, a);
+    else if (mode == kModeVariantRot)
+      hipLaunchKernelGGL(
+          (polar_prefill_kernel<Bf16, kQbBf16, kWavesBf16, kModeVariantRot, false>), grid, bb, 0,
+          stream, a);
     else
-      hipLaunchKernelGGL((polar_prefill_kernel<F32, kQbF32, kWavesF32, kModePaged>), grid, bf, 0,
-                         stream, a);
+      hipLaunchKernelGGL((polar_prefill_kernel<Bf16, kQbBf16, kWavesBf16, kModePaged, false>),
+                         grid, bb, 0, stream, a);
+  } else {
+    if (a.lean) return hipErrorInvalidConfiguration;
+    if (mode == kModePlain)
+      hipLaunchKernelGGL((polar_prefill_kernel<F32, kQbF32, kWavesF32, kModePlain, false>), grid,
+                         bf, 0, stream, a);
+    else if (mode == kModeSave)
+      hipLaunchKernelGGL((polar_prefill_kernel<F32, kQbF32, kWavesF32, kModeSave, false>), grid,
+                         bf, 0, stream, a);
+    else if (mode == kModeVariant || mode == kModeVariantRot)   // fp32 always stages K itself
+      hipLaunchKernelGGL((polar_prefill_kernel<F32, kQbF32, kWavesF32, kModeVariant, false>),
+                         grid, bf, 0, stream, a);
+    else
+      hipLaunchKernelGGL((polar_prefill_kernel<F32, kQbF32, kWavesF32, kModePaged, false>), grid,
+                         bf, 0, stream, a);
   }
   return hipGetLastError();
 }

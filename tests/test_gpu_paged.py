@@ -104,11 +104,12 @@ def test_last_chunk_of_64k_sequence_sampled(gpu_lib):
     assert_close(select(out, rows=rows), full, p.count_vec, "bf16", label="C4 last chunk")
 
 
-def test_wide_paged_chunks_equal_narrow(gpu_lib):
-    """Four 4096-token chunks (16/4 heads): 512 workgroups choose the 16-wave instance.
+def test_lean_paged_chunks_equal_pipelined(gpu_lib):
+    """Four 4096-token chunks (16/4 heads): 1024 workgroups choose the lean instance.
     The first 256 rows of two sequences against the oracle, and every output bit-identical
-    to one-sequence launches on the same pools (128 workgroups each: the 8-wave instance)."""
-    print("[case] paged wide B=4 C=4096", flush=True)
+    to one-sequence launches on the same pools (256 workgroups each: the pipelined
+    instance)."""
+    print("[case] paged lean B=4 C=4096", flush=True)
     ci = synth.chunk_inputs("c2", B=4, C=4096, starts=(0, 1000, 2500, 3000))
     kc, vc, out = _append_and_run(ci)
     p = ci.full
@@ -124,7 +125,7 @@ def test_wide_paged_chunks_equal_narrow(gpu_lib):
             ci.start_pos[b:b + 1], ci.page_size, p.beta, p.null_bias, p.count_vec, p.train_len,
             p.flags, to_f64=_f)
         got = {n: out[n][b:b + 1, :256] for n in ("dir", "count", "n_eff", "gate", "lse")}
-        assert_close(got, want, p.count_vec, dt, label=f"wide paged b={b}")
+        assert_close(got, want, p.count_vec, dt, label=f"lean paged b={b}")
     for b in range(4):
         one = attn_prefill_paged(q[b:b + 1], kc, vc, table[b:b + 1], start[b:b + 1],
                                  ci.max_seq_len, beta=p.beta, null_bias=p.null_bias,

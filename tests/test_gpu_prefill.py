@@ -163,52 +163,52 @@ def _first_sequence(p):
                                needles=[n for n in p.needles if n[0] == 0])
 
 
-def test_wide_workgroups_ragged_rows_and_equal_to_narrow(gpu_lib):
-    """B=4, T=8000, 16/4 heads: enough row blocks for the 16-wave instance (128-row blocks,
-    the last one ragged).  Sampled rows against the oracle, and every output bit-identical
-    to the 8-wave instance, which a one-sequence launch of the same inputs uses (the
-    per-row arithmetic is the same)."""
-    print("[case] prefill wide B=4 T=8000", flush=True)
+def test_lean_ragged_rows_and_equal_to_pipelined(gpu_lib):
+    """B=4, T=8000, 16/4 heads: 2000 workgroups of 64 rows (the last one ragged) choose the
+    lean instance.  Sampled rows against the oracle, and every output bit-identical to the
+    pipelined instance, which a one-sequence launch of the same inputs uses (500 workgroups;
+    the per-row arithmetic is the same)."""
+    print("[case] prefill lean B=4 T=8000", flush=True)
     p = synth.prefill_inputs("c2", B=4, T=8000)
     got = gpu_prefill(p)
     rows = np.array([0, 1, 63, 64, 127, 128, 255, 256, 4000, 7935, 7936, 7999])
     batches = np.array([0, 3])
     want = oracle_prefill(p, rows=rows, batches=batches)
     assert_close(select(got, batches=batches, rows=rows), want, p.count_vec, p.dtype,
-                 label="wide B=4 T=8000")
+                 label="lean B=4 T=8000")
     one = gpu_prefill(_first_sequence(p))
     for key in ("dir", "count", "n_eff", "gate", "lse"):
         assert torch.equal(got[key][:1], one[key]), key
 
 
-def test_wide_workgroups_short_rows_large_batch(gpu_lib):
-    """B=300, T=50: 1200 workgroups choose the 16-wave instance, whose 128-row block then
-    holds 50 valid rows (the waves of rows 64-127 see none).  All rows of two sequences against the oracle,
-    and the first sequence bit-identical to its own (8-wave) launch."""
-    print("[case] prefill wide B=300 T=50", flush=True)
+def test_lean_short_rows_large_batch(gpu_lib):
+    """B=300, T=50: 1200 workgroups choose the lean instance, whose 64-row block then holds
+    50 valid rows (the waves of rows 32-63 see 18).  All rows of two sequences against the
+    oracle, and the first sequence bit-identical to its own (pipelined) launch."""
+    print("[case] prefill lean B=300 T=50", flush=True)
     p = synth.prefill_inputs("c2", B=300, T=50)
     got = gpu_prefill(p)
     batches = np.array([0, 299])
     want = oracle_prefill(p, batches=batches)
-    assert_close(select(got, batches=batches), want, p.count_vec, p.dtype, label="wide B=300 T=50")
+    assert_close(select(got, batches=batches), want, p.count_vec, p.dtype, label="lean B=300 T=50")
     one = gpu_prefill(_first_sequence(p))
     for key in ("dir", "count", "n_eff", "gate", "lse"):
         assert torch.equal(got[key][:1], one[key]), key
 
 
 @pytest.mark.parametrize("B,T,Hq,Hkv", [(128, 600, 4, 4), (64, 600, 8, 4)])
-def test_wide_workgroups_fewer_heads_per_block(gpu_lib, B, T, Hq, Hkv):
-    """GQA groups of 1 and 2 heads: the 16-wave instance then owns 512- or 256-row blocks
+def test_lean_fewer_heads_per_block(gpu_lib, B, T, Hq, Hkv):
+    """GQA groups of 1 and 2 heads: the lean instance then owns 256- or 128-row blocks
     (more masked diagonal tiles per workgroup).  Sampled rows of two sequences against the
-    oracle, and the first sequence bit-identical to its own (8-wave) launch."""
-    print(f"[case] prefill wide B={B} T={T} Hq={Hq} Hkv={Hkv}", flush=True)
+    oracle, and the first sequence bit-identical to its own (pipelined) launch."""
+    print(f"[case] prefill lean B={B} T={T} Hq={Hq} Hkv={Hkv}", flush=True)
     p = synth.prefill_inputs("c2", B=B, T=T, Hq=Hq, Hkv=Hkv)
     got = gpu_prefill(p)
     rows = np.array([0, 1, 63, 64, 255, 256, 511, 512, T - 1])
     batches = np.array([0, B - 1])
     want = oracle_prefill(p, rows=rows, batches=batches)
     assert_close(select(got, batches=batches, rows=rows), want, p.count_vec, p.dtype,
-                 label=f"wide Hq={Hq} Hkv={Hkv}")
+                 label=f"lean Hq={Hq} Hkv={Hkv}")
     one = gpu_prefill(_first_sequence(p))
     for key in ("dir", "count", "n_eff", "gate", "lse"):
         assert torch.equal(got[key][:1], one[key]), key

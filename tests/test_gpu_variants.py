@@ -92,18 +92,18 @@ def test_variant_full_size_rope_softmax_sampled(gpu_lib):
     check(p, select(got, rows=rows, heads=heads), want, "C4 W=0 rope", heads=heads)
 
 
-def test_wide_variant_ragged_rows_and_equal_to_narrow(gpu_lib):
-    """Window 1000 with RoPE at B=4, T=8000: the 16-wave variant instance (keys rotated once
-    into the workspace), sampled rows against the oracle, and bit-identical to the 8-wave
-    instance of a one-sequence launch."""
-    print("[case] variant wide B=4 T=8000 W=1000 theta=10000", flush=True)
+def test_lean_variant_ragged_rows_and_equal_to_pipelined(gpu_lib):
+    """Window 1000 with RoPE at B=4, T=8000: the lean variant instance (keys rotated once
+    into the workspace), sampled rows against the oracle, and bit-identical to the
+    pipelined instance of a one-sequence launch."""
+    print("[case] variant lean B=4 T=8000 W=1000 theta=10000", flush=True)
     p = synth.prefill_inputs("c2", B=4, T=8000)
     var = dict(window=1000, rope_theta=10000.0)
     got = run(p, **var)
     rows = np.array([0, 1, 127, 128, 999, 1000, 1001, 5000, 7936, 7999])
     batches = np.array([0, 3])
     want = oracle_prefill(p, rows=rows, batches=batches, **var)
-    check(p, select(got, batches=batches, rows=rows), want, "wide W=1000 rope")
+    check(p, select(got, batches=batches, rows=rows), want, "lean W=1000 rope")
     one = run(dataclasses.replace(p, B=1, q=p.q[:1], k=p.k[:1], v=p.v[:1],
                                   needles=[n for n in p.needles if n[0] == 0]), **var)
     for key in ("dir", "count", "n_eff", "gate", "lse", "attn"):
