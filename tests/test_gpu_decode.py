@@ -117,3 +117,39 @@ def test_one_sequence_full_length(gpu_lib):
     got = gpu_decode(d)
     assert_close(got, oracle_decode(d), d.count_vec, d.dtype, label="decode B=1 L=262144")
     assert (got["gate"] > 0.5).all()
+
+
+def test_decode_invalid_page_ids_mask_their_keys(gpu_lib):
+    """Pages with ids outside [0, num_pages) (-1, and one past the pool) have their keys
+    masked out, while n = seq_len still drives tau and the floor.  Expected values: the
+    oracle's row function over the sequence's keys with that page's 64 keys removed, with
+    lo = -64 so that the key count stays seq_len."""
+    import dataclasses
+    import oracle
+    d = synth.decode_inputs("c5", B=3, seq_lens=[3000, 1500, 700])
+    good = d.page_table.copy()
+    bad = good.copy()
+    dropped = {0: (5, -1), 1: (0, d.num_pages), 2: (8, -3)}   # sequence: (logical page, bad id)
+    for b, (pg, bid) in dropped.items():
+        assert (pg + 1) * d.page_size <= d.seq_lens[b] - 1     # not the page of the query
+        bad[b, pg] = bid
+    got = gpu_decode(dataclasses.replace(d, page_table=bad))
+    conv = lambda a: synth.bf16_bits_to_f32(a).astype(np.float64)
+    G = d.Hq // d.Hkv
+    want = {k: np.zeros((d.B, d.Hq) + ((64,) if k in ("dir", "count") else ()))
+            for k in ("dir", "count", "n_eff", "gate", "lse")}
+    for b, (pg, _) in dropped.items():
+        L = int(d.seq_lens[b])
+        keep = np.ones(L, bool)
+        keep[pg * d.page_size:(pg + 1) * d.page_size] = False
+        for g in range(d.Hkv):
+            K = conv(oracle.gather_pages(d.k_pool, good[b], g, L, d.page_size))[keep]
+            V = conv(oracle.gather_pages(d.v_pool, good[b], g, L, d.page_size))[keep]
+            for h in range(g * G, (g + 1) * G):
+                res = oracle.polar_oracle._polar_rows(
+                    conv(d.q[b, h])[None], K, V, np.array([L - d.page_size]), d.beta[h],
+                    d.null_bias[h], d.count_vec[h], d.train_len, d.flags,
+                    lo=np.array([-d.page_size]))
+                for k in want:
+                    want[k][b, h] = res[k][0]
+    assert_close(got, want, d.count_vec, d.dtype, label="decode invalid pages")

@@ -133,3 +133,57 @@ def test_lean_paged_chunks_equal_pipelined(gpu_lib):
         torch.cuda.synchronize()
         for n in ("dir", "count", "n_eff", "gate", "lse"):
             assert torch.equal(out[n][b:b + 1], one[n]), (b, n)
+
+
+def test_lean_paged_invalid_page_ids_mask_their_keys(gpu_lib):
+    """Pages of the cached prefix with ids outside [0, num_pages) (-1, and one past the
+    pool) have their keys masked out, while n = pos + 1 still drives tau and the floor.
+    Expected values: the oracle's row function over the sequence's keys with that page's
+    64 keys removed, with lo = -64 so that the row's key count stays pos + 1.  Lean
+    instance (1024 workgroups), and bit-identical to one-sequence (pipelined) launches."""
+    print("[case] paged lean invalid page ids B=4 C=4096", flush=True)
+    ci = synth.chunk_inputs("c2", B=4, C=4096, starts=(0, 1000, 2500, 3000))
+    kc, vc, _ = _append_and_run(ci)
+    p, dt = ci.full, ci.full.dtype
+    kp, vp = oracle.kv_append(ci.k_pool, ci.v_pool, ci.page_table, ci.start_pos, ci.chunk("k"),
+                              ci.chunk("v"), ci.page_size, ci.max_seq_len)
+    num_pages = kp.shape[0]
+    bad = ci.page_table.copy()
+    dropped = {1: (3, -1), 3: (10, num_pages)}      # sequence: (logical page, bad id)
+    for b, (pg, bid) in dropped.items():
+        assert (pg + 1) * 64 <= ci.start_pos[b]      # a page of the prefix
+        bad[b, pg] = bid
+    q = to_dev(ci.chunk("q"), dt)
+    table = torch.from_numpy(bad).cuda()
+    start = torch.from_numpy(ci.start_pos).cuda()
+    kw = dict(beta=p.beta, null_bias=p.null_bias, count_vec=p.count_vec, train_len=p.train_len,
+              flags=p.flags)
+    out = attn_prefill_paged(q, kc, vc, table, start, ci.max_seq_len, **kw)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 63, 64, 2000, 4095])
+    G = p.Hq // p.Hkv
+    qf = _f(ci.chunk("q"))
+    for b, (pg, _) in dropped.items():
+        L = int(ci.start_pos[b]) + ci.C
+        pos = int(ci.start_pos[b]) + rows
+        keep = np.ones(L, bool)
+        keep[pg * 64:(pg + 1) * 64] = False
+        want = {k: np.zeros((1, len(rows), p.Hq) + ((64,) if k in ("dir", "count") else ()))
+                for k in ("dir", "count", "n_eff", "gate", "lse")}
+        for g in range(p.Hkv):
+            K = _f(oracle.gather_pages(kp, ci.page_table[b], g, L, ci.page_size))[keep]
+            V = _f(oracle.gather_pages(vp, ci.page_table[b], g, L, ci.page_size))[keep]
+            for h in range(g * G, (g + 1) * G):
+                res = oracle.polar_oracle._polar_rows(qf[b, rows, h], K, V, pos + 1 - 64, p.beta[h],
+                                         p.null_bias[h], p.count_vec[h], p.train_len, p.flags,
+                                         lo=np.full(len(rows), -64))
+                for k in want:
+                    want[k][0, :, h] = res[k]
+        got = {n: out[n][b:b + 1, rows] for n in want}
+        assert_close(got, want, p.count_vec, dt, label=f"invalid page b={b}")
+    for b in range(4):
+        one = attn_prefill_paged(q[b:b + 1], kc, vc, table[b:b + 1], start[b:b + 1],
+                                 ci.max_seq_len, **kw)
+        torch.cuda.synchronize()
+        for n in ("dir", "count", "n_eff", "gate", "lse"):
+            assert torch.equal(out[n][b:b + 1], one[n]), (b, n)
