@@ -107,10 +107,6 @@ struct Bf16 {
     u32x4 z = {0u, 0u, 0u, 0u};
     return __builtin_bit_cast(frag_t, z);
   }
-  __device__ static __forceinline__ frag_t ones() {
-    const u32x4 o = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
-    return __builtin_bit_cast(frag_t, o);
-  }
   // Round kpl probabilities to bf16 (nearest-even) for the P.V product.
   __device__ static __forceinline__ frag_t pack(const float *x) {
     frag_t r;
@@ -147,7 +143,6 @@ struct F32 {
   }
   __device__ static __forceinline__ frag_t load(const elem_t *p) { return *p; }
   __device__ static __forceinline__ frag_t zero() { return 0.0f; }
-  __device__ static __forceinline__ frag_t ones() { return 1.0f; }
   __device__ static __forceinline__ frag_t pack(const float *x) { return x[0]; }
   __device__ static __forceinline__ void stats(frag_t f, float &S, float &Q) {
     S += f;

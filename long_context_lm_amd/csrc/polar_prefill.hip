@@ -49,26 +49,18 @@
 #ifndef POLAR_PREFILL_SPLIT
 #define POLAR_PREFILL_SPLIT 0
 #endif
-#ifndef POLAR_PREFILL_KT
-#define POLAR_PREFILL_KT 64
-#endif
-// 1: probability sums on the matrix pipe (ones and Gram products); 0: on the vector pipe,
-// from the rounded probabilities the P.V product uses (dot2 per pair for bf16).
 // Direct (bf16) tiles: tile t + DEPTH is loaded while step t runs (DEPTH + 1 LDS slots;
 // DEPTH 0: one more than the distance the scores run ahead, the least that keeps each
 // tile's loads a whole step ahead of their use).
 #ifndef POLAR_PREFILL_DEPTH
 #define POLAR_PREFILL_DEPTH 0
 #endif
-#ifndef POLAR_PREFILL_MSTATS
-#define POLAR_PREFILL_MSTATS 0
-#endif
 
 namespace polar {
 namespace {
 
 constexpr int kD = kHeadDim;
-constexpr int kKTBf16 = POLAR_PREFILL_KT;   // keys per tile (bf16 instances)
+constexpr int kKTBf16 = 64;   // keys per tile (bf16 instances): one page of the paged cache
 constexpr float kLazyTheta = 8.0f;
 constexpr int kBufferFlags = 0x00020000;   // gfx9 buffer resource word 3 (raw dword access)
 
@@ -126,7 +118,6 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
   // transposed on the way).
   constexpr bool kDirect =
       KPL == 8 && kMode != kModeVariantRot && kKT == 64 && kWaves == 8;
-  static_assert(!(kDirect && POLAR_PREFILL_MSTATS), "direct tiles take the vector statistics");
   constexpr int kSlotBytes = kDirect ? 2 * kKT * kD * (int)sizeof(E)
                                      : (kKT * KROW + kD * VROW) * (int)sizeof(E);
   // Tile t + kDepth is loaded during step t; the ring holds tiles t .. t + kDepth.  Direct
@@ -227,10 +218,6 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
   }
 
   f32x16 o[QB][2];
-  // Statistics on the matrix pipe: sacc = 1 * P^T (every row holds sum p of the lane's
-  // query), qacc = P P^T (its diagonal holds sum p^2).  Both use the rounded P of the P.V
-  // product.
-  f32x16 sacc[QB], qacc[QB];
   float Mref[QB], smax[QB], Ssum[QB], Qsum[QB];
   float lbest[QB];                          // kSave: this lane's best score so far
   int lkey[QB];                             // kSave: first key attaining it
@@ -240,11 +227,6 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
     for (int db = 0; db < 2; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[qb][db][r] = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      sacc[qb][r] = 0.f;
-      qacc[qb][r] = 0.f;
-    }
     Mref[qb] = -INFINITY;
     smax[qb] = -INFINITY;
     lbest[qb] = -INFINITY;
@@ -550,13 +532,6 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
       const float alpha2 = alpha * alpha;
       Ssum[qb] *= alpha;
       Qsum[qb] *= alpha2;
-#if POLAR_PREFILL_MSTATS
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        sacc[qb][r] *= alpha;
-        qacc[qb][r] *= alpha2;
-      }
-#endif
 #pragma unroll
       for (int db = 0; db < 2; ++db)
 #pragma unroll
@@ -576,10 +551,8 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
         for (int r = 0; r < 16; ++r) pv[r] = fast_exp2(fmaf(S.v[qb][kb][r], cl2[qb], negM));
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) P.v[qb][kb][tt] = TR::pack(pv + tt * KPL);
-#if !POLAR_PREFILL_MSTATS
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) TR::stats(P.v[qb][kb][tt], Ssum[qb], Qsum[qb]);
-#endif
       }
     }
   };
@@ -638,17 +611,6 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) o[qb][db] = TR::mma32(va, P.v[qb][kb][tt], o[qb][db]);
         }
-#if POLAR_PREFILL_MSTATS
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int tt = 0; tt < NT; ++tt)
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          sacc[qb] = TR::mma32(TR::ones(), P.v[qb][kb][tt], sacc[qb]);
-          qacc[qb] = TR::mma32(P.v[qb][kb][tt], P.v[qb][kb][tt], qacc[qb]);
-        }
-#endif
   };
 
   // ---- software-pipelined key loop ----
@@ -774,20 +736,8 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int row = wrow0 + qb * 32 + c32;
-    // Every register of sacc holds this lane's row sum.  The diagonal of qacc: row c32 of
-    // column c32 sits in the wave half g = (c32/4)%2, register 4*(c32/8) + c32%4.
-#if POLAR_PREFILL_MSTATS
-    const float St = sacc[qb][0];
-    const int rdiag = 4 * (c32 >> 3) + (c32 & 3);
-    float dq = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) dq = (r == rdiag) ? qacc[qb][r] : dq;
-    const float dq_other = half_other(dq);
-    const float Qt = (g32 == ((c32 >> 2) & 1)) ? dq : dq_other;
-#else
     const float St = half_sum(Ssum[qb]);
     const float Qt = half_sum(Qsum[qb]);
-#endif
     float nrm = 0.f;
 #pragma unroll
     for (int db = 0; db < 2; ++db)
