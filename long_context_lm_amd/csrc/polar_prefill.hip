@@ -95,9 +95,13 @@ __device__ __forceinline__ float rot_im(float x0, float x1, float c, float s) {
   return fmaf(x0, s, x1 * c);
 }
 
-// kLean: each tile's scores are used in the step that issues them (see kAhead below).
+// kLean: each tile's scores are used in the step that issues them (see kAhead below).  The
+// lean training instance is held to 128 registers (four waves per SIMD): its arg-max
+// tracking would take 138, and the spills (outside the key loop's vector work) cost less
+// than the occupancy.
 template <class TR, int QB, int kWaves, int kMode, bool kLean>
-__global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs a) {
+__global__ void __launch_bounds__(64 * kWaves, (kLean && kMode == kModeSave) ? 4 : 1)
+    polar_prefill_kernel(PrefillArgs a) {
   constexpr bool kSave = kMode == kModeSave;
   constexpr bool kVar = kMode == kModeVariant || kMode == kModeVariantRot;
   constexpr bool kPaged = kMode == kModePaged;
@@ -127,7 +131,7 @@ __global__ void __launch_bounds__(64 * kWaves) polar_prefill_kernel(PrefillArgs 
   // them: with one score buffer instead of three they fit 128 registers, two workgroups
   // share each CU (four waves per SIMD), and the other workgroup's waves, whose barriers
   // fall elsewhere, cover the score MFMAs' latency.
-  static_assert(!kLean || (kDirect && !kSave), "lean instances: direct tiles, no arg-max");
+  static_assert(!kLean || kDirect, "lean instances stage direct tiles");
   constexpr int kAhead = kLean ? 0 : 2;
   constexpr int kDepth =
       kDirect ? (POLAR_PREFILL_DEPTH > 0 ? POLAR_PREFILL_DEPTH : kAhead + 1) : 3;
@@ -873,10 +877,8 @@ int prefill_heads_per_block(int G) {
 PrefillShape prefill_shape(int dtype, const PrefillArgs &a) {
   if (dtype != 1) return {0, (kWavesF32 / a.hb) * 32 * kQbF32};
   const int rows = (kWavesBf16 / a.hb) * 32 * kQbBf16;
-  // Plain, variant and paged launches whose keys are already rotated (direct tiles) may be
-  // lean; the training forward keeps the pipelined instance (its arg-max tracking needs
-  // 138 registers without the pipeline, too many for two workgroups per CU).
-  const bool direct_mode = a.u_norm == nullptr && !(a.rope && !a.k_rotated);
+  // Launches whose keys are already rotated (direct tiles) may be lean.
+  const bool direct_mode = !(a.rope && !a.k_rotated);
   const long long wgs = (long long)((a.T + rows - 1) / rows) * a.Hkv * (a.G / a.hb) * a.B;
   return {(kHaveLean && direct_mode && wgs >= kLeanMinWorkgroups) ? 1 : 0, rows};
 }
@@ -915,6 +917,9 @@ hipError_t launch_prefill(int dtype, const PrefillArgs &a, hipStream_t stream) {
                            bb, 0, stream, a);
       else if (mode == kModePaged)
         hipLaunchKernelGGL((polar_prefill_kernel<Bf16, 1, kWavesBf16, kModePaged, true>), grid,
+                           bb, 0, stream, a);
+      else if (mode == kModeSave)
+        hipLaunchKernelGGL((polar_prefill_kernel<Bf16, 1, kWavesBf16, kModeSave, true>), grid,
                            bb, 0, stream, a);
       else
         return hipErrorInvalidConfiguration;   // prefill_shape never picks it for other modes

@@ -128,3 +128,23 @@ def test_backward_full_c2_sampled(gpu_lib):
         want = oracle_backward(p, cot, batches=[b])
         sel = {n: got[n][b:b + 1] for n in ("dq", "dk", "dv")}
         assert_grads_close(sel, want, keys=("dq", "dk", "dv"), label=f"C2 batch {b}")
+
+
+def test_lean_forward_train_equals_pipelined_and_plain(gpu_lib):
+    """B=8, T=2048, 16/4 heads: 1024 workgroups choose the lean training instance (held to
+    128 registers).  Every output and residual bit-identical to one-sequence launches
+    (128 workgroups: the pipelined instance), and the outputs to the plain forward."""
+    print("[case] fwd_train lean B=8 T=2048 16/4", flush=True)
+    import dataclasses
+    p = synth.prefill_inputs("c2")
+    _, tr = gpu_forward_train(p)
+    plain = gpu_prefill(p)
+    keys = ("dir", "count", "n_eff", "gate", "lse")
+    for n in keys:
+        assert torch.equal(tr[n], plain[n]), n
+    for b in (0, 5):
+        one = dataclasses.replace(p, B=1, q=p.q[b:b + 1], k=p.k[b:b + 1], v=p.v[b:b + 1],
+                                  needles=[x for x in p.needles if x[0] == b])
+        _, t1 = gpu_forward_train(one)
+        for n in keys + ("u_norm", "arg_max"):
+            assert torch.equal(tr[n][b:b + 1], t1[n]), (b, n)
