@@ -130,19 +130,21 @@ def test_backward_full_c2_sampled(gpu_lib):
         assert_grads_close(sel, want, keys=("dq", "dk", "dv"), label=f"C2 batch {b}")
 
 
-def test_lean_forward_train_equals_pipelined_and_plain(gpu_lib):
-    """B=8, T=2048, 16/4 heads: 1024 workgroups choose the lean training instance (held to
-    128 registers).  Every output and residual bit-identical to one-sequence launches
-    (128 workgroups: the pipelined instance), and the outputs to the plain forward."""
-    print("[case] fwd_train lean B=8 T=2048 16/4", flush=True)
+@pytest.mark.parametrize("B,T,Hq,Hkv", [(8, 2048, 16, 4), (128, 600, 4, 4), (64, 600, 8, 4)])
+def test_lean_forward_train_equals_pipelined_and_plain(gpu_lib, B, T, Hq, Hkv):
+    """At least 512 workgroups choose the lean training instance (held to 128 registers):
+    1024 at B=8, T=2048, 16/4 heads; 1536 and 1280 with one and two heads per block (256-
+    and 128-row blocks).  Every output and residual bit-identical to one-sequence launches
+    (the pipelined instance), and the outputs to the plain forward."""
+    print(f"[case] fwd_train lean B={B} T={T} {Hq}/{Hkv}", flush=True)
     import dataclasses
-    p = synth.prefill_inputs("c2")
+    p = synth.prefill_inputs("c2", B=B, T=T, Hq=Hq, Hkv=Hkv)
     _, tr = gpu_forward_train(p)
     plain = gpu_prefill(p)
     keys = ("dir", "count", "n_eff", "gate", "lse")
     for n in keys:
         assert torch.equal(tr[n], plain[n]), n
-    for b in (0, 5):
+    for b in (0, B - 3):
         one = dataclasses.replace(p, B=1, q=p.q[b:b + 1], k=p.k[b:b + 1], v=p.v[b:b + 1],
                                   needles=[x for x in p.needles if x[0] == b])
         _, t1 = gpu_forward_train(one)
