@@ -49,9 +49,10 @@
 #ifndef POLAR_PREFILL_SPLIT
 #define POLAR_PREFILL_SPLIT 0
 #endif
-// Direct (bf16) tiles: tile t + DEPTH is loaded while step t runs (DEPTH + 1 LDS slots;
-// DEPTH 0: one more than the distance the scores run ahead, the least that keeps each
-// tile's loads a whole step ahead of their use).
+// Direct (bf16) tiles: tile t + DEPTH is loaded while step t runs (DEPTH + 1 LDS slots).
+// An instance never goes below one more than the distance its scores run ahead, the least
+// that keeps each tile's loads a whole step ahead of their use (the default, 0, asks for
+// exactly that).
 #ifndef POLAR_PREFILL_DEPTH
 #define POLAR_PREFILL_DEPTH 0
 #endif
@@ -134,7 +135,7 @@ __global__ void __launch_bounds__(64 * kWaves, (kLean && kMode == kModeSave) ? 4
   static_assert(!kLean || kDirect, "lean instances stage direct tiles");
   constexpr int kAhead = kLean ? 0 : 2;
   constexpr int kDepth =
-      kDirect ? (POLAR_PREFILL_DEPTH > 0 ? POLAR_PREFILL_DEPTH : kAhead + 1) : 3;
+      kDirect ? (POLAR_PREFILL_DEPTH > kAhead + 1 ? POLAR_PREFILL_DEPTH : kAhead + 1) : 3;
   constexpr int kSlots = kDepth + 1;
   static_assert(kAhead == 0 || kAhead == 2, "scores in the same step or two tiles ahead");
   static_assert(kDepth >= kAhead + 1 && 2 * (kDepth - kAhead - 1) < 16, "loads in flight < 16");
