@@ -25,7 +25,7 @@ struct PrefillArgs {
   uint64_t rope_f[kHeadDim / 2];          // revolutions per position of pair t, 2^-64 units
   int B, T, Hq, Hkv, G;                   // G = Hq / Hkv
   int hb;                                 // query heads per workgroup (divides G, <= 4)
-  int lean;                               // 1: the lean instance (prefill_shape)
+  int lean;                               // 1: lean instance, 2: paged split (prefill_shape)
   int n_row_blocks;                       // ceil(T / rows per workgroup)
   float inv_log_train;                    // 1/ln(train_len) with the length temperature, else 0
   int null_floor;                         // 1: add the extreme-value term to the floor
@@ -39,8 +39,8 @@ struct PrefillArgs {
 
 // dtype: 0 = f32, 1 = bf16 (same numbering as polar_dtype).
 int prefill_heads_per_block(int G);
-// Whether the lean prefill instance runs a, and its rows per workgroup.  Reads dtype and
-// a.B, a.T, a.Hkv, a.G, a.hb, a.paged, a.variant, a.rope, a.k_rotated, a.u_norm.
+// Which prefill instance runs a (0 pipelined, 1 lean, 2 paged split) and its rows per
+// workgroup.  Reads dtype and a.B, a.T, a.Hkv, a.G, a.hb, a.paged, a.rope, a.k_rotated.
 struct PrefillShape {
   int lean, rows;
 };

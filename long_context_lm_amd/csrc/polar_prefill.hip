@@ -6,7 +6,8 @@
 // scores never exist in memory.  The arithmetic per row is section 2.1's direction and
 // magnitude channels (definitions in include/polar.h).
 //
-// Work decomposition (one workgroup = kWaves waves: 8 for bf16, 4 for fp32):
+// Work decomposition (one workgroup = kWaves waves: 8 for bf16, or 16 for the paged split
+// instance; 4 for fp32):
 //  * a workgroup owns `hb` query heads that share one KV head (GQA) and a block of rows;
 //    each wave owns 32*QB consecutive rows of one of those heads;
 //  * K and V tiles of 64 keys are staged into LDS through a ring of two or four slots,
@@ -121,8 +122,14 @@ __global__ void __launch_bounds__(64 * kWaves, (kLean && kMode == kModeSave) ? 4
   // over the banks; K fragments are read as rows, V^T fragments with the transposing
   // ds_read_b64_tr_b16.  Other instances stage through registers into padded tiles (V
   // transposed on the way).
+  // Split instance (paged, lean, 16 waves): waves w and w + 8 own the same rows and head;
+  // the first eight take the first half of the fully visible tiles, the other eight the
+  // rest, and the halves merge through LDS at the end.
+  constexpr bool kSplit = kPaged && kLean && kWaves == 16;
+  constexpr int kRowWaves = kSplit ? 8 : kWaves;     // waves that own distinct rows
   constexpr bool kDirect =
-      KPL == 8 && kMode != kModeVariantRot && kKT == 64 && kWaves == 8;
+      KPL == 8 && kMode != kModeVariantRot && kKT == 64 && (kWaves == 8 || kSplit);
+  static_assert(!kSplit || QB == 1, "split instance: one query block per wave");
   constexpr int kSlotBytes = kDirect ? 2 * kKT * kD * (int)sizeof(E)
                                      : (kKT * KROW + kD * VROW) * (int)sizeof(E);
   // Tile t + kDepth is loaded during step t; the ring holds tiles t .. t + kDepth.  Direct
@@ -139,11 +146,18 @@ __global__ void __launch_bounds__(64 * kWaves, (kLean && kMode == kModeSave) ? 4
   constexpr int kSlots = kDepth + 1;
   static_assert(kAhead == 0 || kAhead == 2, "scores in the same step or two tiles ahead");
   static_assert(kDepth >= kAhead + 1 && 2 * (kDepth - kAhead - 1) < 16, "loads in flight < 16");
-  __shared__ __attribute__((aligned(16))) char smem[kSlots * kSlotBytes];
+  constexpr int kXchBytes = 8 * 36 * 64 * (int)sizeof(float);   // split merge: 36 values/lane
+  constexpr int kRingBytes = kSlots * kSlotBytes;
+  constexpr int kSmemBytes = kSplit ? (2 * kRingBytes > kXchBytes ? 2 * kRingBytes : kXchBytes)
+                                    : kRingBytes;
+  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
   auto Ks = reinterpret_cast<E (*)[kKT * KROW]>(smem);
   auto Vs = reinterpret_cast<E (*)[kD * VROW]>(smem + 4 * kKT * KROW * sizeof(E));
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int grp = kSplit ? (wave >> 3) : 0;          // split instance: key-range half
+  const int wv = kSplit ? (wave & 7) : wave;         // row-owning wave index
+  char *const gsmem = smem + grp * kRingBytes;       // this half's ring
   const int g32 = lane >> 5, c32 = lane & 31;
 
   // Heaviest row blocks first; consecutive blocks cycle over (KV head, batch).
@@ -155,10 +169,10 @@ __global__ void __launch_bounds__(64 * kWaves, (kLean && kMode == kModeSave) ? 4
   const int y = id % NY;
   const int rb = a.n_row_blocks - 1 - id / NY;
   const int g = y / n_hc, hc = y % n_hc;
-  const int h = g * a.G + hc * a.hb + (wave % a.hb);
-  const int WR = (kWaves / a.hb) * 32 * QB;
+  const int h = g * a.G + hc * a.hb + (wv % a.hb);
+  const int WR = (kRowWaves / a.hb) * 32 * QB;
   const int row0 = rb * WR;
-  const int wrow0 = row0 + (wave / a.hb) * 32 * QB;
+  const int wrow0 = row0 + (wv / a.hb) * 32 * QB;
   // Row r of this sequence sits at position pbase + r (pbase = 0 outside paged instances).
   const int pbase = kPaged ? min(max(a.start_pos[b], 0), a.max_seq_len - a.T) : 0;
   const int wg_last = min(row0 + WR, a.T) - 1;
@@ -286,9 +300,9 @@ __global__ void __launch_bounds__(64 * kWaves, (kLean && kMode == kModeSave) ? 4
       // Wave w moves keys 8w..8w+7 of K and of V: lane l takes key 8w + l/8 and the chunk
       // that belongs in slot l%8 of that row, and the hardware writes lane l's 16 bytes at
       // the wave's LDS base + 16 l.
-      const int key = 8 * wave + (lane >> 3);
+      const int key = 8 * wv + (lane >> 3);
       const int off = base + key * rstride + (((lane & 7) ^ (key & 7)) << 4);
-      char *dst = smem + (t % kSlots) * kSlotBytes + wave * 1024;
+      char *dst = gsmem + (t % kSlots) * kSlotBytes + wv * 1024;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void *)dst,
                                                16, off, 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -422,7 +436,7 @@ __global__ void __launch_bounds__(64 * kWaves, (kLean && kMode == kModeSave) ? 4
   auto score = [&](int slot, Scores &S) {
     const f32x16 zero = {};
     if constexpr (kDirect) {
-      const char *sb = smem + slot * kSlotBytes;
+      const char *sb = gsmem + slot * kSlotBytes;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         const char *kp = reinterpret_cast<const char *>(lds_at((const E *)sb, kofs[ks]));
@@ -568,7 +582,7 @@ __global__ void __launch_bounds__(64 * kWaves, (kLean && kMode == kModeSave) ? 4
       // the builtin below: with the block's full LDS wait it was 4% slower, as the wait
       // also covers the page-id load issued at the start of the step.
       static_assert(NKB == 2 && NT == 2, "a direct tile is two 32-key blocks of two halves");
-      const char *sb = smem + slot * kSlotBytes;
+      const char *sb = gsmem + slot * kSlotBytes;
 #pragma unroll
       for (int db = 0; db < 2; ++db) {
         F va[4];
@@ -585,7 +599,7 @@ __global__ void __launch_bounds__(64 * kWaves, (kLean && kMode == kModeSave) ? 4
     }
     if constexpr (kDirect) {
       typedef short s16x4 __attribute__((ext_vector_type(4)));
-      const char *sb = smem + slot * kSlotBytes;
+      const char *sb = gsmem + slot * kSlotBytes;
 #pragma unroll
       for (int db = 0; db < 2; ++db) {
         const char *vp = reinterpret_cast<const char *>(lds_at((const E *)sb, vofs[db]));
@@ -638,10 +652,13 @@ __global__ void __launch_bounds__(64 * kWaves, (kLean && kMode == kModeSave) ? 4
                       ? min(tf1, (max(0, wg_last - a.window + 1) + kKT - 1) / kKT)
                       : t0;
 
+  // Split instance: the first half owns tiles [t0, tm), the second [tm, ntiles).
+  const int tm = kSplit ? tf1 / 2 : t0;
+  const int tb = (kSplit && grp) ? tm : t0;
   if constexpr (kDirect) {
     // Every step issues one tile's loads, past the sequence end too (they read zeros), so
     // the count of loads in flight after any tile is fixed.
-    for (int j = t0; j < t0 + kDepth; ++j) stage_load(j);
+    for (int j = tb; j < tb + kDepth; ++j) stage_load(j);
     stage_store(0, 0);
   } else {
     for (int j = t0; j < t0 + 3 && j < ntiles; ++j) {
@@ -712,7 +729,30 @@ __global__ void __launch_bounds__(64 * kWaves, (kLean && kMode == kModeSave) ? 4
     __syncthreads();
   };
 
-  if constexpr (kAhead == 0) {
+  if constexpr (kSplit) {
+    // Both halves take the same number of barrier steps (WG-uniform); a half past its last
+    // tile only waits.
+    const int te = grp ? ntiles : tm;
+    const int nsteps = max(tm - t0, ntiles - tm);
+    for (int s = 0; s < nsteps; ++s) {
+      const int tt = tb + s;
+      if (tt < te) {
+        stage_load(tt + kDepth);
+        const int key0 = tt * kKT;
+        const bool full = tt < tf1;
+        if (full || key0 <= w_last) {
+          score(tt % kSlots, Sa);
+          if (!full) mask(Sa, key0);
+          first_max(Sa, key0);
+          probs(Sa, P);
+          pv_mma(tt % kSlots, P);
+        }
+      }
+      stage_store(0, 0);
+      __syncthreads();
+    }
+    t = ntiles;
+  } else if constexpr (kAhead == 0) {
     // Each tile's scores, maximum, probabilities and P.V in one step; the waves of the
     // other workgroup on the CU cover the score MFMAs' latency.
     for (; t < tf1; ++t) {
@@ -735,6 +775,37 @@ __global__ void __launch_bounds__(64 * kWaves, (kLean && kMode == kModeSave) ? 4
     }
   }
   for (; t < ntiles; ++t) masked_step(t);
+
+  if constexpr (kSplit) {
+    // Merge the halves: the second writes (u, M, max, S, Q) per lane, the first rescales
+    // both to the larger reference and adds.  Every tile load has landed and been read
+    // before the last step's barrier, so the rings' LDS is free.
+    float *x = reinterpret_cast<float *>(smem) + wv * 36 * 64 + lane;
+    if (grp) {
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[(db * 16 + r) * 64] = o[0][db][r];
+      x[32 * 64] = Mref[0];
+      x[33 * 64] = smax[0];
+      x[34 * 64] = Ssum[0];
+      x[35 * 64] = Qsum[0];
+    }
+    __syncthreads();
+    if (grp) return;
+    const float M1 = x[32 * 64], M0 = Mref[0];
+    const float M = fmaxf(M0, M1);
+    const float a0 = M0 == -INFINITY ? 0.f : fast_exp2(M0 - M);
+    const float a1 = M1 == -INFINITY ? 0.f : fast_exp2(M1 - M);
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[0][db][r] = o[0][db][r] * a0 + x[(db * 16 + r) * 64] * a1;
+    smax[0] = fmaxf(smax[0], x[33 * 64]);
+    Ssum[0] = Ssum[0] * a0 + x[34 * 64] * a1;
+    Qsum[0] = Qsum[0] * (a0 * a0) + x[35 * 64] * (a1 * a1);
+    Mref[0] = M;
+  }
 
   // ---- epilogue ----
   const float bias = a.null_bias ? a.null_bias[h] : 0.0f;
@@ -881,7 +952,11 @@ PrefillShape prefill_shape(int dtype, const PrefillArgs &a) {
   // Launches whose keys are already rotated (direct tiles) may be lean.
   const bool direct_mode = !(a.rope && !a.k_rotated);
   const long long wgs = (long long)((a.T + rows - 1) / rows) * a.Hkv * (a.G / a.hb) * a.B;
-  return {(kHaveLean && direct_mode && wgs >= kLeanMinWorkgroups) ? 1 : 0, rows};
+  if (kHaveLean && direct_mode && wgs >= kLeanMinWorkgroups) return {1, rows};
+  // Paged launches with fewer workgroups split each row block's keys over two halves of a
+  // 16-wave workgroup: four waves per SIMD instead of two.
+  if (kHaveLean && a.paged) return {2, rows};
+  return {0, rows};
 }
 
 hipError_t launch_rope_keys(int dtype, const PrefillArgs &a, void *k_out, hipStream_t stream) {
@@ -908,7 +983,13 @@ hipError_t launch_prefill(int dtype, const PrefillArgs &a, hipStream_t stream) {
                  : a.variant ? ((a.rope && !a.k_rotated) ? kModeVariantRot : kModeVariant)
                  : (a.u_norm != nullptr ? kModeSave : kModePlain);
   const dim3 bb(64 * kWavesBf16), bf(64 * kWavesF32);
-  if (dtype == 1 && a.lean) {
+  if (dtype == 1 && a.lean == 2) {
+    if constexpr (kHaveLean) {
+      if (mode != kModePaged) return hipErrorInvalidConfiguration;
+      hipLaunchKernelGGL((polar_prefill_kernel<Bf16, 1, 16, kModePaged, true>), grid,
+                         dim3(1024), 0, stream, a);
+    }
+  } else if (dtype == 1 && a.lean) {
     if constexpr (kHaveLean) {
       if (mode == kModePlain)
         hipLaunchKernelGGL((polar_prefill_kernel<Bf16, 1, kWavesBf16, kModePlain, true>), grid,
