@@ -13,7 +13,13 @@ the timed steps, the backward pass is timed on its own at the 2K training shape 
 reported in ``backward`` (TFLOP/s over the five products of the gradient, 2.5x the
 forward count).
 
+Besides the headline pair, the JSON line carries one object per further leg, each with its
+own roofline and, unless ``--no-cpu-baseline``, the oracle timed beside it: the forward at
+the 2K training shape and at 16K (``prefill_c2``, ``prefill_c3``), the variant modes, the
+paged chunk, the one-sequence decode, the backward and the memory step.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                       [--legs all|LEG,LEG...]  (a subset of the extra legs, for profiling)
        python bench.py --copy-probe BYTES   (plain device copy, for counter calibration)
        python bench.py --memory-step-probe fused|ref --steps K
                                             (one form of the memory step, for counters)
@@ -43,6 +49,8 @@ _PREFILL_SRC = ["polar_prefill.hip", "polar_mfma.h", "polar_kernels.h"]
 _DECODE_SRC = ["polar_decode.hip", "polar_mfma.h", "polar_kernels.h"]
 KERNEL_SOURCES = {
     "prefill": _PREFILL_SRC,
+    "prefill_c2": _PREFILL_SRC,
+    "prefill_c3": _PREFILL_SRC,
     "decode": _DECODE_SRC,
     "decode_b1": _DECODE_SRC,
     "backward": ["polar_backward.hip", "polar_mfma.h", "polar_kernels.h"],
@@ -98,6 +106,19 @@ def traffic_record(kind: str):
 CPU_JOBS = []
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (the oracle's machine)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def blas_threads() -> int:
     """Threads the oracle's NumPy BLAS runs with."""
     try:
@@ -129,11 +150,67 @@ def cpu_baseline(pre, dec):
     dbytes = decode_bytes(len(batches), dec.max_seq_len, dec.Hq, dec.Hkv, dec.d, dec.page_size,
                           dec.page_table.shape[1])
     return {"value": flops / t_pre / 1e12, "unit": "TFLOP/s", "cores": int(cores),
-            "kind": "oracle",
+            "kind": "oracle", "cpu": cpu_model(),
             "sample": f"prefill rows {len(rows)} evenly spaced of T=65536, all 16 heads "
                       f"({t_pre:.1f} s)",
             "decode": {"value": dbytes / t_dec / 1e9, "unit": "GB/s",
                        "sample": f"decode, all {len(batches)} sequences ({t_dec:.1f} s)"}}
+
+
+def measure_prefill_cfg(dev, name: str, steps: int, warmup: int, with_cpu: bool):
+    """The causal forward on another of the pages' shapes: "c2" (B=8, T=2048, the training
+    length, 5% planted near-copy keys) or "c3" (B=1, T=16384, 8x the training length, one
+    needle per head), with the oracle timed on all of C2 or on 1024 rows of C3."""
+    import torch
+    import synth
+    from long_context_lm_amd import attn_fwd
+    p = synth.prefill_inputs(name)
+
+    def to_dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = to_dev(p.q), to_dev(p.k), to_dev(p.v)
+    kw = dict(beta=torch.from_numpy(p.beta).to(dev), null_bias=torch.from_numpy(p.null_bias).to(dev),
+              count_vec=torch.from_numpy(p.count_vec).to(dev), train_len=p.train_len, flags=p.flags)
+    for _ in range(warmup):
+        attn_fwd(q, k, v, **kw)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for e in ev:
+        e[0].record()
+        attn_fwd(q, k, v, **kw)
+        e[1].record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    F = prefill_flops(p.B, p.T, p.Hq, p.d)
+    tf = F / (ms * 1e-3) / 1e12
+    print(f"[bench] prefill {name} B={p.B} T={p.T}: {ms:.4f} ms ({tf:.1f} TFLOP/s)",
+          file=sys.stderr, flush=True)
+    rec = {"workload": f"prefill B={p.B} T={p.T} Hq=16 Hkv=4 d=64 causal bf16 "
+                       + ("(2K training length, 5% planted near-copy keys)" if name == "c2"
+                          else "(16K, 8x train length, one needle per head)"),
+           "value": round(tf, 2), "unit": "TFLOP/s", "ms": round(ms, 4),
+           "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                        "traffic": traffic_record("prefill_" + name)},
+           "cpu_baseline": None}
+    if with_cpu:
+        def job():
+            import oracle
+            rows = None if name == "c2" else np.linspace(0, p.T - 1, 1024).astype(np.int64)
+            t0 = time.perf_counter()
+            oracle.polar_prefill(p.as_f32("q"), p.as_f32("k"), p.as_f32("v"), p.beta,
+                                 p.null_bias, p.count_vec, p.train_len, p.flags, rows=rows)
+            t = time.perf_counter() - t0
+            r = np.arange(p.T) if rows is None else rows
+            fl = 4.0 * p.d * p.B * p.Hq * float((r + 1).sum())
+            rec["cpu_baseline"] = {
+                "value": fl / t / 1e12, "unit": "TFLOP/s", "cores": blas_threads(),
+                "kind": "oracle", "cpu": cpu_model(),
+                "sample": ("the whole workload, all 8 sequences" if rows is None else
+                           "1024 rows evenly spaced of T=16384, all 16 heads") + f" ({t:.1f} s)"}
+        CPU_JOBS.append(job)
+    return rec
 
 
 def measure_backward(dev, steps: int, warmup: int, with_cpu: bool):
@@ -187,7 +264,7 @@ def measure_backward(dev, steps: int, warmup: int, with_cpu: bool):
             t = time.perf_counter() - t0
             rec["cpu_baseline"] = {
                 "value": round(backward_flops(p.B, p.T, p.Hq, p.d) / t / 1e12, 5),
-                "unit": "TFLOP/s", "cores": int(torch.get_num_threads()), "kind": "oracle",
+                "unit": "TFLOP/s", "cores": int(torch.get_num_threads()), "kind": "oracle", "cpu": cpu_model(),
                 "sample": f"float64 autograd backward of the whole workload, all 8 sequences "
                           f"({t:.1f} s)"}
         CPU_JOBS.append(job)
@@ -242,13 +319,14 @@ def measure_variants(dev, q, k, v, pkw, pre, steps: int, warmup: int, with_cpu: 
                 t0 = time.perf_counter()
                 oracle.polar_prefill(pre.as_f32("q"), pre.as_f32("k"), pre.as_f32("v"),
                                      pre.beta, pre.null_bias, pre.count_vec, pre.train_len,
-                                     pre.flags, rows=rows, window=window, rope_theta=theta)
+                                     pre.flags, rows=rows, window=window, rope_theta=theta,
+                                     rope_bf16=True)
                 dt = time.perf_counter() - t0
                 vis = np.minimum(rows + 1, window) if window else rows + 1
                 fl = 4.0 * pre.d * pre.Hq * float(vis.sum())
                 r["cpu_baseline"] = {
                     "value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": blas_threads(),
-                    "kind": "oracle",
+                    "kind": "oracle", "cpu": cpu_model(),
                     "sample": f"{n_rows} rows evenly spaced of T=65536, all 16 heads, RoPE of "
                               f"the whole q and k included ({dt:.1f} s)"}
             CPU_JOBS.append(job)
@@ -308,7 +386,7 @@ def measure_decode_b1(dev, steps: int, warmup: int, with_cpu: bool = False):
                                       to_f64=lambda a: synth.bf16_bits_to_f32(a).astype(np.float64))
             t = time.perf_counter() - t0
             rec["cpu_baseline"] = {"value": byt / t / 1e9, "unit": "GB/s", "cores": blas_threads(),
-                                   "kind": "oracle",
+                                   "kind": "oracle", "cpu": cpu_model(),
                                    "sample": f"the whole workload ({t:.1f} s)"}
         CPU_JOBS.append(job)
     return rec
@@ -381,7 +459,7 @@ def measure_paged(dev, pre, steps: int, warmup: int, with_cpu: bool = False):
             dt = time.perf_counter() - t0
             fl = 4.0 * pre.d * pre.Hq * float(np.sum(start + np.arange(n_rows) + 1.0))
             rec["cpu_baseline"] = {"value": fl / dt / 1e12, "unit": "TFLOP/s",
-                                   "cores": blas_threads(), "kind": "oracle",
+                                   "cores": blas_threads(), "kind": "oracle", "cpu": cpu_model(),
                                    "sample": f"first {n_rows} rows of the chunk, all 16 heads "
                                              f"({dt:.1f} s)"}
         CPU_JOBS.append(job)
@@ -458,7 +536,7 @@ def measure_memory_step(dev, steps: int, warmup: int, with_cpu: bool = False):
                                    d.as_f32("v"), d.alpha, d.beta)
             t = time.perf_counter() - t0
             rec["cpu_baseline"] = {"value": round(algo / t / 1e9, 3), "unit": "GB/s",
-                                   "cores": 1, "kind": "oracle",
+                                   "cores": 1, "kind": "oracle", "cpu": cpu_model(),
                                    "sample": f"float64 step of all 256 x 16 states ({t:.1f} s)"}
         CPU_JOBS.append(job)
     return rec
@@ -489,12 +567,18 @@ def copy_probe(nbytes: int):
     print(json.dumps({"copy_probe_bytes": nbytes}))
 
 
+EXTRA_LEGS = ("c2", "c3", "variants", "paged", "decode_b1", "backward", "memory_step")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--legs", default="all",
+                    help="comma list of extra legs to run beside the headline pair: "
+                         + ",".join(EXTRA_LEGS))
     ap.add_argument("--copy-probe", type=int, default=0)
     ap.add_argument("--memory-step-probe", choices=("fused", "ref"), default=None)
     args = ap.parse_args()
@@ -591,19 +675,30 @@ def main():
                                 "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                                 "traffic": tr_dec}},
     }
-    rec["variants"] = measure_variants(dev, q, k, v, pkw, pre, max(1, args.steps // 4),
-                                       min(args.warmup, 2), not args.no_cpu_baseline)
-    rec["paged"] = measure_paged(dev, pre, max(1, args.steps // 2), min(args.warmup, 2),
-                                 not args.no_cpu_baseline)
+    legs = EXTRA_LEGS if args.legs == "all" else tuple(x for x in args.legs.split(",") if x)
+    unknown = [x for x in legs if x not in EXTRA_LEGS]
+    if unknown:
+        print(f"unknown legs {unknown}; choose from {EXTRA_LEGS}", file=sys.stderr)
+        sys.exit(2)
+    cpu = not args.no_cpu_baseline
+    if "variants" in legs:
+        rec["variants"] = measure_variants(dev, q, k, v, pkw, pre, max(1, args.steps // 4),
+                                           min(args.warmup, 2), cpu)
+    if "paged" in legs:
+        rec["paged"] = measure_paged(dev, pre, max(1, args.steps // 2), min(args.warmup, 2), cpu)
     del q, k, v, qd, kc, vc, table, lens, ws
     torch.cuda.empty_cache()
-    rec["decode_b1"] = measure_decode_b1(dev, args.steps, min(args.warmup, 2),
-                                         not args.no_cpu_baseline)
+    for name in ("c2", "c3"):
+        if name in legs:
+            rec["prefill_" + name] = measure_prefill_cfg(dev, name, args.steps, args.warmup, cpu)
     torch.cuda.empty_cache()
-    rec["backward"] = measure_backward(dev, max(1, args.steps // 2), args.warmup,
-                                       not args.no_cpu_baseline)
-    rec["memory_step"] = measure_memory_step(dev, args.steps, args.warmup,
-                                             not args.no_cpu_baseline)
+    if "decode_b1" in legs:
+        rec["decode_b1"] = measure_decode_b1(dev, args.steps, min(args.warmup, 2), cpu)
+        torch.cuda.empty_cache()
+    if "backward" in legs:
+        rec["backward"] = measure_backward(dev, max(1, args.steps // 2), args.warmup, cpu)
+    if "memory_step" in legs:
+        rec["memory_step"] = measure_memory_step(dev, args.steps, args.warmup, cpu)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on bounded samples", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(pre, dec)

@@ -1,5 +1,6 @@
 /*
- * libpolar — Polar Attention forward for AMD Instinct MI355X (gfx950).  C ABI, version 1.
+ * libpolar — Polar Attention forward for AMD Instinct MI355X (gfx950).  C ABI, version 3
+ * (POLAR_ABI_VERSION below; polar_abi_version() reports the loaded library's).
  *
  * The operation is the attention mixing step of the ATMA hybrid decoder as described in
  * "ATMA: Length-Invariant Language Modeling via Polar Attention and Gated-Delta
@@ -45,7 +46,10 @@
 extern "C" {
 #endif
 
-#define POLAR_ABI_VERSION 2   /* 2: polar_variant gained the key-rotation workspace */
+/* 2: polar_variant gained the key-rotation workspace.
+ * 3: polar_decode_workspace_bytes lost its page_size argument (the only page size is 64 and
+ *    the workspace never depended on it). */
+#define POLAR_ABI_VERSION 3
 
 #if defined(__GNUC__)
 #define POLAR_API __attribute__((visibility("default")))
@@ -76,7 +80,7 @@ enum {
 typedef struct {
   int32_t n_q_heads;                /* Hq >= 1                                            */
   int32_t n_kv_heads;               /* Hkv >= 1, Hq % Hkv == 0                             */
-  int32_t head_dim;                 /* d; must be 64 in version 1                          */
+  int32_t head_dim;                 /* d; must be 64 (only size)                         */
   int32_t train_len;                /* T_train; must be >= 2 when LENGTH_TEMP is set       */
   uint32_t flags;                   /* POLAR_FLAG_* bits                                   */
   const float *beta;                /* device [Hq] logit scale beta_h; NULL -> sqrt(d)     */
@@ -154,10 +158,12 @@ POLAR_API polar_status polar_attn_fwd_variant(const polar_params *p, const polar
 
 /*
  * Workspace bytes polar_attn_decode_paged needs for this batch size and length bound
- * (0 on invalid arguments).  The value depends only on the arguments.
+ * (0 on invalid arguments: p NULL, B < 1, max_seq_len < 1, bad head counts).  The value
+ * depends only on the arguments; it holds the split-KV partials (M, max, S, Q, u[d]) of
+ * every (sequence, query head, key split).
  */
-POLAR_API size_t polar_decode_workspace_bytes(const polar_params *p, int32_t B, int32_t max_seq_len,
-                                    int32_t page_size);
+POLAR_API size_t polar_decode_workspace_bytes(const polar_params *p, int32_t B,
+                                              int32_t max_seq_len);
 
 /*
  * One-token GQA-grouped decode over a paged KV cache (section 2.2: the decode kernel reads
@@ -178,7 +184,7 @@ POLAR_API size_t polar_decode_workspace_bytes(const polar_params *p, int32_t B, 
  *                    page_table_stride >= ceil(max_seq_len / page_size).
  *   workspace        device scratch of >= polar_decode_workspace_bytes(...) bytes,
  *                    16-byte aligned; its contents on entry are ignored.
- *   page_size must be 64 in version 1.
+ *   page_size must be 64 in this version.
  */
 POLAR_API polar_status polar_attn_decode_paged(const polar_params *p, polar_dtype dt, int32_t B,
                                      const void *q, const void *k_cache, const void *v_cache,
@@ -243,7 +249,7 @@ POLAR_API polar_status polar_attn_fwd_train(const polar_params *p, polar_dtype d
 POLAR_API size_t polar_bwd_workspace_bytes(const polar_params *p, int32_t B, int32_t T);
 
 /*
- * Backward pass of the causal prefill.  bf16 inputs only in version 1
+ * Backward pass of the causal prefill.  bf16 inputs only in this version
  * (POLAR_ERR_UNSUPPORTED for float32).
  *   p, dt, B, T, q, k, v  exactly as passed to polar_attn_fwd_train.
  *   fwd                   its outputs: dir, n_eff, gate and lse are read (count unused).
@@ -266,17 +272,20 @@ POLAR_API polar_status polar_attn_bwd(const polar_params *p, polar_dtype dt, int
  * keys and values are written into cache pages, then the new tokens attend the paged
  * prefix).  Pools, page table and page_size are as for polar_attn_decode_paged.
  *   start_pos   device int32 [B]: position of the chunk's first token in its sequence
- *               (the number of tokens already cached).  Values are clamped to
- *               [0, max_seq_len - C].
- *   max_seq_len host bound: start_pos[b] + C <= max_seq_len;
+ *               (the number of tokens already cached).  Both calls clamp each value to
+ *               [0, max_seq_len - C] the same way (a device value cannot be checked before
+ *               the launch), so a chunk appended and then attended with the same
+ *               arguments always lands at, and reads from, the same positions.
+ *   max_seq_len host bound, >= C: start_pos[b] + C <= max_seq_len;
  *               page_table_stride >= ceil(max_seq_len / page_size).
  * --------------------------------------------------------------------------------- */
 
 /*
  * Writes k_new, v_new [B,C,Hkv,d] (dtype `dt`, 16-byte aligned) into the pools: token t of
- * sequence b goes to position start_pos[b] + t, page page_table[b, pos / page_size], slot
- * pos % page_size.  Tokens whose page id lies outside [0, num_pages) are dropped.  The
- * pools are the only memory written.  Only n_kv_heads and head_dim of `p` are used.
+ * sequence b goes to position pos = s + t with s = start_pos[b] clamped to
+ * [0, max_seq_len - C], page page_table[b, pos / page_size], slot pos % page_size.  Tokens
+ * whose page id lies outside [0, num_pages) are dropped.  The pools are the only memory
+ * written.  Only n_kv_heads and head_dim of `p` are used.
  */
 POLAR_API polar_status polar_kv_append(const polar_params *p, polar_dtype dt, int32_t B, int32_t C,
                              const void *k_new, const void *v_new, void *k_cache,
@@ -286,10 +295,11 @@ POLAR_API polar_status polar_kv_append(const polar_params *p, polar_dtype dt, in
 
 /*
  * Chunked causal prefill over the paged cache: q [B,C,Hq,d] are the queries of C new
- * tokens per sequence; row t (position pos = start_pos[b] + t) attends keys 0..pos of its
+ * tokens per sequence; row t (position pos = s + t, s = start_pos[b] clamped to
+ * [0, max_seq_len - C]) attends keys 0..pos of its
  * sequence, read from the pools through the page table (append the chunk's own keys and
  * values first).  n = pos + 1 drives tau and the floor, so the rows equal causal prefill
- * rows start_pos[b]..start_pos[b]+C-1 of the whole sequence.  Keys on pages with ids
+ * rows s..s+C-1 of the whole sequence.  Keys on pages with ids
  * outside [0, num_pages) are masked out.  Outputs as for polar_attn_fwd with T = C.
  */
 POLAR_API polar_status polar_attn_prefill_paged(const polar_params *p, polar_dtype dt, int32_t B,
@@ -313,8 +323,8 @@ enum { POLAR_DELTA_NORMALIZE_QK = 1u };
 
 typedef struct {
   int32_t n_heads;                  /* H >= 1                                              */
-  int32_t key_dim;                  /* d_k; must be 64 in version 1                        */
-  int32_t value_dim;                /* d_v; must be 64 in version 1                        */
+  int32_t key_dim;                  /* d_k; must be 64 (only size)                       */
+  int32_t value_dim;                /* d_v; must be 64 (only size)                       */
   uint32_t flags;                   /* POLAR_DELTA_* bits                                  */
 } polar_delta_params;
 

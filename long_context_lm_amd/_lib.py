@@ -100,7 +100,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.polar_attn_fwd.argtypes = [P(polar_params), I32, I32, I32, VP, VP, VP, P(polar_outputs),
                                    VP]
     lib.polar_decode_workspace_bytes.restype = SZ
-    lib.polar_decode_workspace_bytes.argtypes = [P(polar_params), I32, I32, I32]
+    lib.polar_decode_workspace_bytes.argtypes = [P(polar_params), I32, I32]
     lib.polar_attn_decode_paged.restype = I32
     lib.polar_attn_decode_paged.argtypes = [P(polar_params), I32, I32, VP, VP, VP, I32, I32, VP,
                                             I32, VP, I32, VP, SZ, P(polar_outputs), VP]
@@ -156,8 +156,8 @@ def polar_attn_fwd(params, dtype, B, T, q, k, v, outputs, stream) -> int:
                                  ctypes.byref(outputs), stream)
 
 
-def polar_decode_workspace_bytes(params, B, max_seq_len, page_size) -> int:
-    return load().polar_decode_workspace_bytes(ctypes.byref(params), B, max_seq_len, page_size)
+def polar_decode_workspace_bytes(params, B, max_seq_len) -> int:
+    return load().polar_decode_workspace_bytes(ctypes.byref(params), B, max_seq_len)
 
 
 def polar_attn_decode_paged(params, dtype, B, q, k_cache, v_cache, num_pages, page_size,

@@ -316,9 +316,8 @@ polar_status polar_attn_bwd(const polar_params *p, polar_dtype dt, int32_t B, in
   return POLAR_OK;
 }
 
-size_t polar_decode_workspace_bytes(const polar_params *p, int32_t B, int32_t max_seq_len,
-                                    int32_t page_size) {
-  if (!p || B < 1 || max_seq_len < 1 || page_size != polar::kPageSize || p->n_kv_heads < 1 ||
+size_t polar_decode_workspace_bytes(const polar_params *p, int32_t B, int32_t max_seq_len) {
+  if (!p || B < 1 || max_seq_len < 1 || p->n_kv_heads < 1 ||
       p->n_q_heads < 1 || p->n_q_heads % p->n_kv_heads != 0)
     return 0;
   return polar::decode_ws_bytes(B, p->n_q_heads, p->n_kv_heads, max_seq_len);

@@ -38,14 +38,8 @@ constexpr int kD = kHeadDim;
 constexpr int kBufferFlags = 0x00020000;   // gfx9 buffer resource word 3 (raw dword access)
 constexpr int kDqWaves = 8;
 constexpr int kDkvWaves = 4;
-#ifndef POLAR_BWD_DEPTH
-#define POLAR_BWD_DEPTH 1
-#endif
-constexpr int kDkvDepth = POLAR_BWD_DEPTH;   // query tiles in flight ahead of the compute
-#ifndef POLAR_BWD_SPLIT
-#define POLAR_BWD_SPLIT 2
-#endif
-constexpr int kDkvSplitMax = POLAR_BWD_SPLIT;  // workgroups sharing one key block (by heads)
+constexpr int kDkvDepth = 1;      // query tiles in flight ahead of the compute
+constexpr int kDkvSplitMax = 2;   // workgroups sharing one key block (by heads)
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 using F = bf16x8;

@@ -33,10 +33,7 @@ constexpr int kTargetWaves = 4096;
 // were 1% slower).
 constexpr int kMinWaves = 2048;
 constexpr int kMinPagesPerSplit = 8;
-#ifndef POLAR_DECODE_COMBINE_WAVES
-#define POLAR_DECODE_COMBINE_WAVES 16
-#endif
-constexpr int kCombineWaves = POLAR_DECODE_COMBINE_WAVES;   // waves per (b, head) merge
+constexpr int kCombineWaves = 16;   // waves per (b, head) merge
 
 template <class TR> struct DecCfg;
 template <> struct DecCfg<Bf16> { static constexpr int vrow = 72; };

@@ -149,12 +149,8 @@ __global__ void __launch_bounds__(256) polar_delta_step_kernel(DeltaArgs a) {
 
 }  // namespace
 
-#ifndef POLAR_DELTA_NS
-#define POLAR_DELTA_NS 4
-#endif
-
 hipError_t launch_delta_step(int dtype, const DeltaArgs &a, hipStream_t stream) {
-  constexpr int NS = POLAR_DELTA_NS;
+  constexpr int NS = 4;   // states per workgroup
   const long long units = (long long)a.B * a.H;
   if (units <= 0) return hipSuccess;
   const dim3 grid((unsigned)((units + NS - 1) / NS));

@@ -56,27 +56,28 @@ __device__ __forceinline__ int vpos32(int k32) {
 
 // The four bf16 A-operand fragments of a 64-key tile stored as swizzled key rows in LDS,
 // read transposed with ds_read_b64_tr_b16: fragment j (key block j/2, half j%2) is the pair
-// of 8-byte reads at rows 16 j and 16 j + 8 (row pitch 128 bytes) from lane address addr.
+// of 8-byte reads at rows 16 j (from lane address lo) and 16 j + 8 (from hi; the two
+// addresses differ where the swizzle of the row differs), row pitch 128 bytes.
 // The reads are issued in one asm block that waits for them before it ends.  Through the
 // builtin, the compiler cannot tell these reads from the tiles still being written by
 // buffer_load ... lds and first waits for every load in flight, including the tile fetched
 // ahead in the same step; the tile read here was published by an earlier barrier.
-// (Outputs are early-clobber: none may take the address register while reads are pending.)
-__device__ __forceinline__ void tr_read_tile(uint32_t addr, bf16x8 f[4]) {
+// (Outputs are early-clobber: none may take an address register while reads are pending.)
+__device__ __forceinline__ void tr_read_tile(uint32_t lo, uint32_t hi, bf16x8 f[4]) {
   typedef short s16x4 __attribute__((ext_vector_type(4)));
   s16x4 r0, r1, r2, r3, r4, r5, r6, r7;
   asm volatile(
       "ds_read_b64_tr_b16 %0, %8\n\t"
-      "ds_read_b64_tr_b16 %1, %8 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %1, %9\n\t"
       "ds_read_b64_tr_b16 %2, %8 offset:2048\n\t"
-      "ds_read_b64_tr_b16 %3, %8 offset:3072\n\t"
+      "ds_read_b64_tr_b16 %3, %9 offset:2048\n\t"
       "ds_read_b64_tr_b16 %4, %8 offset:4096\n\t"
-      "ds_read_b64_tr_b16 %5, %8 offset:5120\n\t"
+      "ds_read_b64_tr_b16 %5, %9 offset:4096\n\t"
       "ds_read_b64_tr_b16 %6, %8 offset:6144\n\t"
-      "ds_read_b64_tr_b16 %7, %8 offset:7168\n\t"
+      "ds_read_b64_tr_b16 %7, %9 offset:6144\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
-      : "v"(addr));
+      : "v"(lo), "v"(hi));
   f[0] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
   f[1] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(r2, r3, 0, 1, 2, 3, 4, 5, 6, 7));
   f[2] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(r4, r5, 0, 1, 2, 3, 4, 5, 6, 7));

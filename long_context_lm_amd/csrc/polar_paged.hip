@@ -2,8 +2,9 @@
 //
 // The decode kernel of the ATMA technical summary (gist.science), section 2.2, reads keys
 // and values from paged cache blocks; this is the write side.  Token t of sequence b lands
-// at logical position start_pos[b] + t: page page_table[b, pos / 64], slot pos % 64, for
-// every KV head (page-major pools [num_pages, Hkv, 64, d]).  Pure data movement: one
+// at logical position s + t, with s = start_pos[b] clamped to [0, max_seq_len - C] exactly
+// as the chunked prefill clamps it: page page_table[b, pos / 64], slot pos % 64, for every
+// KV head (page-major pools [num_pages, Hkv, 64, d]).  Pure data movement: one
 // 16-byte chunk per thread and grid-stride loop, coalesced on both sides (a (page, head)
 // block is 64 contiguous rows).
 #include "polar_kernels.h"
@@ -24,8 +25,7 @@ __global__ void __launch_bounds__(256) polar_kv_append_kernel(AppendArgs a) {
     r /= a.Hkv;
     const int t = (int)(r % a.C);
     const int b = (int)(r / a.C);
-    const int pos = max(a.start_pos[b], 0) + t;
-    if (pos >= a.max_seq_len) continue;
+    const int pos = min(max(a.start_pos[b], 0), a.max_seq_len - a.C) + t;
     const int page = a.page_table[(size_t)b * a.stride + pos / kPageSize];
     if (page < 0 || page >= a.num_pages) continue;
     const size_t src = (((size_t)b * a.C + t) * a.Hkv + g) * a.row_bytes + part * 16;

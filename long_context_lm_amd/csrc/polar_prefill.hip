@@ -39,32 +39,27 @@
 #include "polar_kernels.h"
 #include "polar_mfma.h"
 
-// Launch shape (build-time tuning knobs): query blocks of 32 rows per wave, waves per
-// workgroup.
-#ifndef POLAR_PREFILL_QB
-#define POLAR_PREFILL_QB 1
-#endif
-#ifndef POLAR_PREFILL_WAVES
-#define POLAR_PREFILL_WAVES 8
-#endif
-#ifndef POLAR_PREFILL_SPLIT
-#define POLAR_PREFILL_SPLIT 0
-#endif
-// Direct (bf16) tiles: tile t + DEPTH is loaded while step t runs (DEPTH + 1 LDS slots).
-// An instance never goes below one more than the distance its scores run ahead, the least
-// that keeps each tile's loads a whole step ahead of their use (the default, 0, asks for
-// exactly that).
-#ifndef POLAR_PREFILL_DEPTH
-#define POLAR_PREFILL_DEPTH 0
-#endif
-
 namespace polar {
 namespace {
 
 constexpr int kD = kHeadDim;
 constexpr int kKTBf16 = 64;   // keys per tile (bf16 instances): one page of the paged cache
 constexpr float kLazyTheta = 8.0f;
+// The running reference before any visible key: finite, so that -M needs no select, and so
+// low that the first visible tile always raises it (the rescale factor is then 0).
+constexpr float kNoRef = -3.0e38f;
 constexpr int kBufferFlags = 0x00020000;   // gfx9 buffer resource word 3 (raw dword access)
+
+// Direct (bf16) tiles hold 16-byte chunk c of key row r at slot c ^ tile_swz(r) of the
+// row's 128 bytes.  The LDS serves 256 bytes (64 four-byte banks) per cycle:
+//  * a K fragment read (ds_read_b128) covers one chunk of 16 consecutive rows per cycle,
+//    and the 8 rows of each parity get 8 distinct slots, so the 16 lanes hit 16 distinct
+//    16-byte bank groups;
+//  * a V^T fragment read (ds_read_b64_tr_b16) covers 4 chunks of 4 consecutive rows per
+//    32 lanes; rows two apart differ in bit 2 of the swizzle, so their chunk sets land in
+//    different halves of the row's bank groups.
+// Rows r and r + 8 (r & 8 == 0) differ by slot bit 1: tile_swz(r + 8) == tile_swz(r) ^ 2.
+__device__ __forceinline__ int tile_swz(int r) { return ((r >> 2) & 3) | ((r & 2) << 1); }
 
 template <class TR> struct LdsCfg;
 template <> struct LdsCfg<Bf16> {
@@ -97,12 +92,12 @@ __device__ __forceinline__ float rot_im(float x0, float x1, float c, float s) {
   return fmaf(x0, s, x1 * c);
 }
 
-// kLean: each tile's scores are used in the step that issues them (see kAhead below).  The
-// lean training instance is held to 128 registers (four waves per SIMD): its arg-max
-// tracking would take 138, and the spills (outside the key loop's vector work) cost less
-// than the occupancy.
+// kLean: each tile's scores are used in the step that issues them (see kAhead below).  Lean
+// instances are held to 128 registers (four waves per SIMD); the training instance, whose
+// arg-max tracking needs a few more, spills 7 outside the key loop's vector work, which
+// costs less than the occupancy.
 template <class TR, int QB, int kWaves, int kMode, bool kLean>
-__global__ void __launch_bounds__(64 * kWaves, (kLean && kMode == kModeSave) ? 4 : 1)
+__global__ void __launch_bounds__(64 * kWaves, kLean ? 4 : 1)
     polar_prefill_kernel(PrefillArgs a) {
   constexpr bool kSave = kMode == kModeSave;
   constexpr bool kVar = kMode == kModeVariant || kMode == kModeVariantRot;
@@ -141,16 +136,18 @@ __global__ void __launch_bounds__(64 * kWaves, (kLean && kMode == kModeSave) ? 4
   // fall elsewhere, cover the score MFMAs' latency.
   static_assert(!kLean || kDirect, "lean instances stage direct tiles");
   constexpr int kAhead = kLean ? 0 : 2;
-  constexpr int kDepth =
-      kDirect ? (POLAR_PREFILL_DEPTH > kAhead + 1 ? POLAR_PREFILL_DEPTH : kAhead + 1) : 3;
+  constexpr int kDepth = kDirect ? kAhead + 1 : 3;
   constexpr int kSlots = kDepth + 1;
   static_assert(kAhead == 0 || kAhead == 2, "scores in the same step or two tiles ahead");
   static_assert(kDepth >= kAhead + 1 && 2 * (kDepth - kAhead - 1) < 16, "loads in flight < 16");
+  // The split merge reuses the rings' LDS after the last barrier: no tile load may still be
+  // in flight then, which holds when each step waits for all of its loads (one tile ahead).
+  static_assert(!kSplit || kDepth == 1, "split instance loads one tile ahead");
   constexpr int kXchBytes = 8 * 36 * 64 * (int)sizeof(float);   // split merge: 36 values/lane
   constexpr int kRingBytes = kSlots * kSlotBytes;
   constexpr int kSmemBytes = kSplit ? (2 * kRingBytes > kXchBytes ? 2 * kRingBytes : kXchBytes)
                                     : kRingBytes;
-  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
+  __shared__ __attribute__((aligned(128))) char smem[kSmemBytes];
   auto Ks = reinterpret_cast<E (*)[kKT * KROW]>(smem);
   auto Vs = reinterpret_cast<E (*)[kD * VROW]>(smem + 4 * kKT * KROW * sizeof(E));
 
@@ -184,10 +181,9 @@ __global__ void __launch_bounds__(64 * kWaves, (kLean && kMode == kModeSave) ? 4
   const size_t kv_row_bytes = (size_t)a.Hkv * kD * sizeof(E);
   const size_t kv_base = ((size_t)b * a.T * a.Hkv + g) * kD;
   const int kv_bytes = (int)(((size_t)a.T * a.Hkv - g) * kD * sizeof(E));
-  const auto krsrc = __builtin_amdgcn_make_buffer_rsrc((void *)((const E *)a.k + kv_base), 0,
-                                                       kv_bytes, kBufferFlags);
-  const auto vrsrc = __builtin_amdgcn_make_buffer_rsrc((void *)((const E *)a.v + kv_base), 0,
-                                                       kv_bytes, kBufferFlags);
+  const E *const kbase = (const E *)a.k + kv_base, *const vbase = (const E *)a.v + kv_base;
+  const auto krsrc = __builtin_amdgcn_make_buffer_rsrc((void *)kbase, 0, kv_bytes, kBufferFlags);
+  const auto vrsrc = __builtin_amdgcn_make_buffer_rsrc((void *)vbase, 0, kv_bytes, kBufferFlags);
 
   // Per-row logit scales: natural units and log2 units.
   const float beta = a.beta ? a.beta[h] : 8.0f;
@@ -246,7 +242,7 @@ __global__ void __launch_bounds__(64 * kWaves, (kLean && kMode == kModeSave) ? 4
     for (int db = 0; db < 2; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[qb][db][r] = 0.f;
-    Mref[qb] = -INFINITY;
+    Mref[qb] = kNoRef;
     smax[qb] = -INFINITY;
     lbest[qb] = -INFINITY;
     lkey[qb] = 0;
@@ -271,6 +267,8 @@ __global__ void __launch_bounds__(64 * kWaves, (kLean && kMode == kModeSave) ? 4
   u32x4 kst[NK];
   vchunk_t vst[NV][VKEYS];
   int staged_key0 = 0;                               // variant: position of the staged tile
+  // This wave's part of a direct tile in LDS (uniform: one scalar register).
+  const uint32_t wave_lds = __builtin_amdgcn_readfirstlane(lds_addr(gsmem) + wv * 1024);
   int tok[kSlots];                                   // paged: slot holds a valid page
 #pragma unroll
   for (int i = 0; i < kSlots; ++i) tok[i] = 1;
@@ -299,15 +297,24 @@ __global__ void __launch_bounds__(64 * kWaves, (kLean && kMode == kModeSave) ? 4
     if constexpr (kDirect) {
       // Wave w moves keys 8w..8w+7 of K and of V: lane l takes key 8w + l/8 and the chunk
       // that belongs in slot l%8 of that row, and the hardware writes lane l's 16 bytes at
-      // the wave's LDS base + 16 l.
+      // the wave's LDS base + 16 l.  The lane's offset inside a tile is fixed: the tile's
+      // start moves the (scalar) buffer resource instead, whose size still ends at the
+      // sequence's last key, so keys past it read zeros.  The LDS destination is uniform.
+      if constexpr (!kPaged) {
+        const int toff = key0 * (int)kv_row_bytes;
+        const int rem = max(kv_bytes - toff, 0);
+        rk = __builtin_amdgcn_make_buffer_rsrc((void *)((const char *)kbase + toff), 0, rem,
+                                               kBufferFlags);
+        rv = __builtin_amdgcn_make_buffer_rsrc((void *)((const char *)vbase + toff), 0, rem,
+                                               kBufferFlags);
+      }
       const int key = 8 * wv + (lane >> 3);
-      const int off = base + key * rstride + (((lane & 7) ^ (key & 7)) << 4);
-      char *dst = gsmem + (t % kSlots) * kSlotBytes + wv * 1024;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void *)dst,
-                                               16, off, 0, 0, 0);
+      const int loff = key * rstride + (((lane & 7) ^ tile_swz(key)) << 4);
+      const uint32_t dst = wave_lds + (uint32_t)((t % kSlots) * kSlotBytes);
+      using lds_void = __attribute__((address_space(3))) void *;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void)(uintptr_t)dst, 16, loff, 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rv, (__attribute__((address_space(3))) void *)(dst + kKT * kD * sizeof(E)), 16, off, 0,
-          0, 0);
+          rv, (lds_void)(uintptr_t)(dst + kKT * kD * sizeof(E)), 16, loff, 0, 0, 0);
       return;
     }
 #pragma unroll
@@ -405,19 +412,23 @@ __global__ void __launch_bounds__(64 * kWaves, (kLean && kMode == kModeSave) ? 4
   // Direct tiles: byte offsets of this lane's fragments inside a slot.  K fragment (kb, ks):
   // key kb*32 + c32, chunk 2 ks + g32.  V^T fragment (kb, tt, db), half h: lane i of 16-lane
   // group G reads 4 dims of key kb*32 + 16 tt + 8 h + 4 (G/2) + i/4 and, transposed, holds
-  // dim 32 db + (lane % 32) of keys ... + 4 (lane / 32) + 0..3, the slot order of P.
-  uint32_t kofs[NKS], vofs[2];
+  // dim 32 db + (lane % 32) of keys ... + 4 (lane / 32) + 0..3, the slot order of P.  The
+  // swizzle of a row depends on its index mod 16, so one offset serves every kb and tt;
+  // the h = 1 rows (8 further on) have slot bit 1 flipped: address bit 5 (slot and ring
+  // bases are multiples of 128 bytes, the LDS array starts at address 0).
+  // The K offsets of the four chunk pairs differ only in slot bits 1 and 2: chunk 2 ks + g32
+  // sits at kofs0 ^ (32 ks).
+  static_assert(kSlotBytes % 128 == 0 && kRingBytes % 128 == 0, "row-aligned slots");
+  uint32_t kofs0, vofs[2];
   {
-    const int sw = c32 & 7;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-      kofs[ks] = (uint32_t)(c32 * 128 + (((2 * ks + g32) ^ sw) << 4));
+    const int sw = tile_swz(c32);
+    kofs0 = (uint32_t)(c32 * 128 + ((g32 ^ sw) << 4));
     const int G4 = lane >> 4, i = lane & 15;
     const int krow = 4 * (G4 >> 1) + (i >> 2);
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
       const int chunk = 4 * db + 2 * (G4 & 1) + ((i & 3) >> 1);
-      vofs[db] = (uint32_t)(kKT * kD * sizeof(E) + krow * 128 + ((chunk ^ (krow & 7)) << 4) +
+      vofs[db] = (uint32_t)(kKT * kD * sizeof(E) + krow * 128 + ((chunk ^ tile_swz(krow)) << 4) +
                             (i & 1) * 8);
     }
   }
@@ -425,24 +436,43 @@ __global__ void __launch_bounds__(64 * kWaves, (kLean && kMode == kModeSave) ? 4
     asm volatile("" : "+v"(off));
     return reinterpret_cast<const E *>(reinterpret_cast<const char *>(base) + off);
   };
+  // K fragment row addresses of the four chunk pairs, (kofs0 ^ 32 ks) + slot base, each
+  // formed by one instruction in the step that uses it (no per-slot addresses are held
+  // across the loop; the kb offset stays an immediate of the reads).  The slot base is a
+  // multiple of 128, so ks = 2, 3 flip bit 6 of the ks = 0, 1 addresses (inline operands
+  // only: 96 would be a literal).
+  using lds_frag = const __attribute__((address_space(3))) F *;
+  auto k_addrs = [&](const char *sb, lds_frag (&kp)[4]) {
+    uint32_t a0, a1, a2, a3;
+    const uint32_t base = lds_addr(sb);
+    asm volatile("v_add_u32 %0, %1, %2" : "=v"(a0) : "s"(base), "v"(kofs0));
+    asm volatile("v_xad_u32 %0, %1, 32, %2" : "=v"(a1) : "v"(kofs0), "s"(base));
+    asm volatile("v_xor_b32 %0, 64, %1" : "=v"(a2) : "v"(a0));
+    asm volatile("v_xor_b32 %0, 64, %1" : "=v"(a3) : "v"(a1));
+    kp[0] = (lds_frag)(uintptr_t)a0;
+    kp[1] = (lds_frag)(uintptr_t)a1;
+    kp[2] = (lds_frag)(uintptr_t)a2;
+    kp[3] = (lds_frag)(uintptr_t)a3;
+  };
 
   // ---- per-tile building blocks ----
   struct Scores { f32x16 v[QB][NKB]; };
   struct Probs { F v[QB][NKB][NT]; };
   // S^T = K Q^T for the two 32-key blocks of a tile.
   // Independent accumulation chains are issued round-robin (a dependent MFMA waits for
-  // its predecessor's result); with POLAR_PREFILL_SPLIT each key block accumulates even
-  // and odd contraction steps separately and adds the halves afterwards.
+  // its predecessor's result).
   auto score = [&](int slot, Scores &S) {
     const f32x16 zero = {};
     if constexpr (kDirect) {
-      const char *sb = gsmem + slot * kSlotBytes;
+      static_assert(NKS == 4, "a direct key row is four chunk pairs");
+      lds_frag kpa[4];
+      k_addrs(gsmem + slot * kSlotBytes, kpa);
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const char *kp = reinterpret_cast<const char *>(lds_at((const E *)sb, kofs[ks]));
+        const lds_frag kp = kpa[ks];
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
-          const F ka = *reinterpret_cast<const F *>(kp + kb * 32 * 128);
+          const F ka = kp[kb * 32 * 128 / (int)sizeof(F)];
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb)
             S.v[qb][kb] = TR::mma32(ka, qf[qb][ks], ks == 0 ? zero : S.v[qb][kb]);
@@ -450,26 +480,6 @@ __global__ void __launch_bounds__(64 * kWaves, (kLean && kMode == kModeSave) ? 4
       }
     } else {
     const E *Kt = lds_at(&Ks[0][0], k_lane + slot * KSLOT);
-#if POLAR_PREFILL_SPLIT
-    f32x16 h2[QB][NKB];
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const F ka = TR::load(Kt + kb * 32 * KROW + ks * KSTEP);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          if (ks & 1)
-            h2[qb][kb] = TR::mma32(ka, qf[qb][ks], ks == 1 ? zero : h2[qb][kb]);
-          else
-            S.v[qb][kb] = TR::mma32(ka, qf[qb][ks], ks == 0 ? zero : S.v[qb][kb]);
-        }
-      }
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) S.v[qb][kb] += h2[qb][kb];
-#else
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
@@ -479,7 +489,6 @@ __global__ void __launch_bounds__(64 * kWaves, (kLean && kMode == kModeSave) ? 4
         for (int qb = 0; qb < QB; ++qb)
           S.v[qb][kb] = TR::mma32(ka, qf[qb][ks], ks == 0 ? zero : S.v[qb][kb]);
       }
-#endif
     }
     if constexpr (kPaged) {
       if (!tok[slot]) {                               // a page with an invalid id
@@ -562,7 +571,7 @@ __global__ void __launch_bounds__(64 * kWaves, (kLean && kMode == kModeSave) ? 4
   auto probs = [&](const Scores &S, Probs &P) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      const float negM = Mref[qb] == -INFINITY ? 0.f : -Mref[qb];
+      const float negM = -Mref[qb];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         float pv[16];
@@ -586,7 +595,8 @@ __global__ void __launch_bounds__(64 * kWaves, (kLean && kMode == kModeSave) ? 4
 #pragma unroll
       for (int db = 0; db < 2; ++db) {
         F va[4];
-        tr_read_tile(lds_addr(sb) + vofs[db], va);
+        const uint32_t lo = lds_addr(sb) + vofs[db];
+        tr_read_tile(lo, (lo ^ 32u) + 8 * 128, va);
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -599,20 +609,21 @@ __global__ void __launch_bounds__(64 * kWaves, (kLean && kMode == kModeSave) ? 4
     }
     if constexpr (kDirect) {
       typedef short s16x4 __attribute__((ext_vector_type(4)));
-      const char *sb = gsmem + slot * kSlotBytes;
+      using lds_v4 = __attribute__((address_space(3))) s16x4 *;
+      const uint32_t sbase = lds_addr(gsmem + slot * kSlotBytes);
 #pragma unroll
       for (int db = 0; db < 2; ++db) {
-        const char *vp = reinterpret_cast<const char *>(lds_at((const E *)sb, vofs[db]));
+        uint32_t lo = sbase + vofs[db];
+        asm volatile("" : "+v"(lo));
+        const uint32_t hi = (lo ^ 32u) + 8 * 128;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int tt = 0; tt < NT; ++tt) {
-            const int r0 = (kb * 32 + 16 * tt) * 128;
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4 *)(vp + r0));
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4 *)(vp + r0 + 8 * 128));
-            const F va = __builtin_bit_cast(F, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            const uint32_t r0 = (kb * 32 + 16 * tt) * 128;
+            const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4)(uintptr_t)(lo + r0));
+            const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4)(uintptr_t)(hi + r0));
+            const F va = __builtin_bit_cast(F, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) o[qb][db] = TR::mma32(va, P.v[qb][kb][tt], o[qb][db]);
           }
@@ -795,8 +806,8 @@ __global__ void __launch_bounds__(64 * kWaves, (kLean && kMode == kModeSave) ? 4
     if (grp) return;
     const float M1 = x[32 * 64], M0 = Mref[0];
     const float M = fmaxf(M0, M1);
-    const float a0 = M0 == -INFINITY ? 0.f : fast_exp2(M0 - M);
-    const float a1 = M1 == -INFINITY ? 0.f : fast_exp2(M1 - M);
+    const float a0 = fast_exp2(M0 - M);
+    const float a1 = fast_exp2(M1 - M);
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
@@ -929,14 +940,13 @@ __global__ void __launch_bounds__(256) polar_rope_keys_kernel(PrefillArgs a, E *
   }
 }
 
-constexpr int kQbBf16 = POLAR_PREFILL_QB;
+constexpr int kQbBf16 = 1;
 constexpr int kQbF32 = 1;
-constexpr int kWavesBf16 = POLAR_PREFILL_WAVES;
+constexpr int kWavesBf16 = 8;
 constexpr int kWavesF32 = 4;
 // The lean instances pay off once the grid holds two workgroups per CU (256 CUs); with one
 // per CU the pipelined instances keep their two waves per SIMD busier.
 constexpr long long kLeanMinWorkgroups = 512;
-constexpr bool kHaveLean = kWavesBf16 == 8 && kQbBf16 == 1;
 
 }  // namespace
 
@@ -952,10 +962,10 @@ PrefillShape prefill_shape(int dtype, const PrefillArgs &a) {
   // Launches whose keys are already rotated (direct tiles) may be lean.
   const bool direct_mode = !(a.rope && !a.k_rotated);
   const long long wgs = (long long)((a.T + rows - 1) / rows) * a.Hkv * (a.G / a.hb) * a.B;
-  if (kHaveLean && direct_mode && wgs >= kLeanMinWorkgroups) return {1, rows};
+  if (direct_mode && wgs >= kLeanMinWorkgroups) return {1, rows};
   // Paged launches with fewer workgroups split each row block's keys over two halves of a
   // 16-wave workgroup: four waves per SIMD instead of two.
-  if (kHaveLean && a.paged) return {2, rows};
+  if (a.paged) return {2, rows};
   return {0, rows};
 }
 
@@ -984,30 +994,24 @@ hipError_t launch_prefill(int dtype, const PrefillArgs &a, hipStream_t stream) {
                  : (a.u_norm != nullptr ? kModeSave : kModePlain);
   const dim3 bb(64 * kWavesBf16), bf(64 * kWavesF32);
   if (dtype == 1 && a.lean == 2) {
-    if constexpr (kHaveLean) {
-      if (mode != kModePaged) return hipErrorInvalidConfiguration;
-      hipLaunchKernelGGL((polar_prefill_kernel<Bf16, 1, 16, kModePaged, true>), grid,
-                         dim3(1024), 0, stream, a);
-    }
+    if (mode != kModePaged) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((polar_prefill_kernel<Bf16, 1, 16, kModePaged, true>), grid,
+                       dim3(1024), 0, stream, a);
   } else if (dtype == 1 && a.lean) {
-    if constexpr (kHaveLean) {
-      if (mode == kModePlain)
-        hipLaunchKernelGGL((polar_prefill_kernel<Bf16, 1, kWavesBf16, kModePlain, true>), grid,
-                           bb, 0, stream, a);
-      else if (mode == kModeVariant)
-        hipLaunchKernelGGL((polar_prefill_kernel<Bf16, 1, kWavesBf16, kModeVariant, true>), grid,
-                           bb, 0, stream, a);
-      else if (mode == kModePaged)
-        hipLaunchKernelGGL((polar_prefill_kernel<Bf16, 1, kWavesBf16, kModePaged, true>), grid,
-                           bb, 0, stream, a);
-      else if (mode == kModeSave)
-        hipLaunchKernelGGL((polar_prefill_kernel<Bf16, 1, kWavesBf16, kModeSave, true>), grid,
-                           bb, 0, stream, a);
-      else
-        return hipErrorInvalidConfiguration;   // prefill_shape never picks it for other modes
-    } else {
-      return hipErrorInvalidConfiguration;
-    }
+    if (mode == kModePlain)
+      hipLaunchKernelGGL((polar_prefill_kernel<Bf16, 1, kWavesBf16, kModePlain, true>), grid,
+                         bb, 0, stream, a);
+    else if (mode == kModeVariant)
+      hipLaunchKernelGGL((polar_prefill_kernel<Bf16, 1, kWavesBf16, kModeVariant, true>), grid,
+                         bb, 0, stream, a);
+    else if (mode == kModePaged)
+      hipLaunchKernelGGL((polar_prefill_kernel<Bf16, 1, kWavesBf16, kModePaged, true>), grid,
+                         bb, 0, stream, a);
+    else if (mode == kModeSave)
+      hipLaunchKernelGGL((polar_prefill_kernel<Bf16, 1, kWavesBf16, kModeSave, true>), grid,
+                         bb, 0, stream, a);
+    else
+      return hipErrorInvalidConfiguration;   // prefill_shape never picks it for other modes
   } else if (dtype == 1) {
     if (mode == kModePlain)
       hipLaunchKernelGGL((polar_prefill_kernel<Bf16, kQbBf16, kWavesBf16, kModePlain, false>),

@@ -23,10 +23,20 @@ def _params(Hq, Hkv, d, beta, null_bias, count_vec, train_len, flags):
                              _ptr(count_vec))
 
 
-def _device_f32(x, device):
+def _device_f32(x, device, numel=None, name="parameter"):
+    """A per-head parameter as a contiguous float32 tensor on ``device`` (copied there if
+    needed), holding exactly ``numel`` values: the kernels index it by head."""
     if x is None:
         return None
-    return torch.as_tensor(x, dtype=torch.float32, device=device).contiguous()
+    t = torch.as_tensor(x, dtype=torch.float32, device=device).contiguous()
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} must hold {numel} values (got {t.numel()})")
+    return t
+
+
+def _head_params(beta, null_bias, count_vec, Hq, d, dev):
+    return (_device_f32(beta, dev, Hq, "beta"), _device_f32(null_bias, dev, Hq, "null_bias"),
+            _device_f32(count_vec, dev, Hq * d, "count_vec"))
 
 
 def _check_input(t: torch.Tensor, name: str) -> None:
@@ -36,6 +46,23 @@ def _check_input(t: torch.Tensor, name: str) -> None:
         raise ValueError(f"{name} has dtype {t.dtype}; bfloat16 or float32 expected")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def _check_aux(t, name: str, device, dtype, shape=None) -> None:
+    """A tensor the kernels read or write beside q, k and v (tables, positions, slots, saved
+    residuals, workspaces): it must sit on the inputs' GPU, since the library takes a bare
+    device pointer, and be contiguous, since the only row strides the C calls know are the
+    ones their arguments state."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if t.device != torch.device(device):
+        raise ValueError(f"{name} must be on {device} (got {t.device})")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
 
 
 def _outputs(lead, Hq, d, device, want_count, want_gate, want_lse):
@@ -62,8 +89,7 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta=None, null_
     if k.shape != (B, T, Hkv, d) or v.shape != k.shape or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("k and v must be [B,T,Hkv,d] with q's dtype")
     dev = q.device
-    beta, null_bias, count_vec = (_device_f32(beta, dev), _device_f32(null_bias, dev),
-                                  _device_f32(count_vec, dev))
+    beta, null_bias, count_vec = _head_params(beta, null_bias, count_vec, Hq, d, dev)
     prm = _params(Hq, Hkv, d, beta, null_bias, count_vec, train_len, flags)
     out, cout = _outputs((B, T), Hq, d, dev, count_vec is not None, want_gate, want_lse)
     s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
@@ -80,8 +106,7 @@ def _prefill_args(q, k, v, beta, null_bias, count_vec, train_len, flags):
     if k.shape != (B, T, Hkv, d) or v.shape != k.shape or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("k and v must be [B,T,Hkv,d] with q's dtype")
     dev = q.device
-    beta, null_bias, count_vec = (_device_f32(beta, dev), _device_f32(null_bias, dev),
-                                  _device_f32(count_vec, dev))
+    beta, null_bias, count_vec = _head_params(beta, null_bias, count_vec, Hq, d, dev)
     prm = _params(Hq, Hkv, d, beta, null_bias, count_vec, train_len, flags)
     return prm, (beta, null_bias, count_vec), (B, T, Hq, Hkv, d)
 
@@ -128,6 +153,7 @@ def attn_fwd_variant(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, window: 
         need = _lib.polar_variant_workspace_bytes(prm, _DT[q.dtype], B, T)
         if workspace is None:
             workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        _check_aux(workspace, "workspace", dev, None)
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     var = _lib.polar_variant(window, rope_theta, _ptr(out["attn"]), ws_ptr, ws_bytes)
     s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
@@ -162,11 +188,19 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, fwd: dict, cot: 
     prm, keep, (B, T, Hq, Hkv, d) = _prefill_args(q, k, v, beta, null_bias, count_vec,
                                                   train_len, flags)
     dev = q.device
+    f32t = torch.float32
+    for name, dt, shp in (("dir", f32t, (B, T, Hq, d)), ("n_eff", f32t, (B, T, Hq)),
+                          ("gate", f32t, (B, T, Hq)), ("lse", f32t, (B, T, Hq)),
+                          ("u_norm", f32t, (B, T, Hq)), ("arg_max", torch.int32, (B, T, Hq))):
+        _check_aux(fwd.get(name), f"fwd[{name!r}]", dev, dt, shp)
     cts = {}
     for name in ("dir", "count", "n_eff", "gate", "lse"):
         c = cot.get(name)
         cts[name] = None if c is None else torch.as_tensor(
             c, dtype=torch.float32, device=dev).contiguous()
+        if c is not None:
+            want = (B, T, Hq, d) if name in ("dir", "count") else (B, T, Hq)
+            _check_aux(cts[name], f"cot[{name!r}]", dev, f32t, want)
     f32 = dict(device=dev, dtype=torch.float32)
     g = dict(dq=torch.empty(B, T, Hq, d, **f32), dk=torch.empty(B, T, Hkv, d, **f32),
              dv=torch.empty(B, T, Hkv, d, **f32))
@@ -176,6 +210,7 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, fwd: dict, cot: 
     need = _lib.polar_bwd_workspace_bytes(prm, B, T)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _check_aux(workspace, "workspace", dev, None)
     fo = _lib.polar_outputs(_ptr(fwd["dir"]), None, _ptr(fwd["n_eff"]), _ptr(fwd["gate"]),
                             _ptr(fwd["lse"]))
     sv = _lib.polar_saved(_ptr(fwd["u_norm"]), _ptr(fwd["arg_max"]))
@@ -189,10 +224,9 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, fwd: dict, cot: 
     return g
 
 
-def decode_workspace_bytes(Hq: int, Hkv: int, B: int, max_seq_len: int, page_size: int = 64,
-                           d: int = 64) -> int:
+def decode_workspace_bytes(Hq: int, Hkv: int, B: int, max_seq_len: int, d: int = 64) -> int:
     prm = _lib.polar_params(Hq, Hkv, d, 2048, 0, None, None, None)
-    return _lib.polar_decode_workspace_bytes(prm, B, max_seq_len, page_size)
+    return _lib.polar_decode_workspace_bytes(prm, B, max_seq_len)
 
 
 def attn_decode_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
@@ -208,17 +242,19 @@ def attn_decode_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
     num_pages, Hkv, page, d2 = k_cache.shape
     if d2 != d or v_cache.shape != k_cache.shape:
         raise ValueError("caches must be [num_pages,Hkv,page,d] matching q")
-    if page_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
-        raise ValueError("page_table and seq_lens must be int32")
-    if page_table.dim() != 2 or page_table.shape[0] != B or seq_lens.shape != (B,):
-        raise ValueError("page_table must be [B,stride] and seq_lens [B]")
     dev = q.device
-    beta, null_bias, count_vec = (_device_f32(beta, dev), _device_f32(null_bias, dev),
-                                  _device_f32(count_vec, dev))
+    if page_table.dim() != 2 or page_table.shape[0] != B:
+        raise ValueError("page_table must be [B,stride]")
+    _check_aux(page_table, "page_table", dev, torch.int32)
+    _check_aux(seq_lens, "seq_lens", dev, torch.int32, (B,))
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        _check_aux(t, n, dev, q.dtype)
+    beta, null_bias, count_vec = _head_params(beta, null_bias, count_vec, Hq, d, dev)
     prm = _params(Hq, Hkv, d, beta, null_bias, count_vec, train_len, flags)
-    need = _lib.polar_decode_workspace_bytes(prm, B, max_seq_len, page)
+    need = _lib.polar_decode_workspace_bytes(prm, B, max_seq_len)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _check_aux(workspace, "workspace", dev, None)
     out, cout = _outputs((B,), Hq, d, dev, count_vec is not None, want_gate, want_lse)
     s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
     _lib.check(_lib.polar_attn_decode_paged(
@@ -228,16 +264,17 @@ def attn_decode_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
     return out
 
 
-def _paged_args(k_cache, v_cache, page_table, start_pos, B):
+def _paged_args(k_cache, v_cache, page_table, start_pos, B, dev):
     for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache")):
         _check_input(t, n)
+        _check_aux(t, n, dev, None)
     num_pages, Hkv, page, d = k_cache.shape
     if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
         raise ValueError("caches must match")
-    if page_table.dtype != torch.int32 or start_pos.dtype != torch.int32:
-        raise ValueError("page_table and start_pos must be int32")
-    if page_table.dim() != 2 or page_table.shape[0] != B or start_pos.shape != (B,):
-        raise ValueError("page_table must be [B,stride] and start_pos [B]")
+    if page_table.dim() != 2 or page_table.shape[0] != B:
+        raise ValueError("page_table must be [B,stride]")
+    _check_aux(page_table, "page_table", dev, torch.int32)
+    _check_aux(start_pos, "start_pos", dev, torch.int32, (B,))
     return num_pages, Hkv, page, d
 
 
@@ -248,7 +285,8 @@ def kv_append(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor,
     for t, n in ((k_new, "k_new"), (v_new, "v_new")):
         _check_input(t, n)
     B, C, Hkv, d = k_new.shape
-    num_pages, Hkv2, page, d2 = _paged_args(k_cache, v_cache, page_table, start_pos, B)
+    num_pages, Hkv2, page, d2 = _paged_args(k_cache, v_cache, page_table, start_pos, B,
+                                            k_new.device)
     if (Hkv2, d2) != (Hkv, d) or v_new.shape != k_new.shape or k_new.dtype != k_cache.dtype:
         raise ValueError("k_new/v_new must be [B,C,Hkv,d] matching the pools")
     prm = _lib.polar_params(Hkv, Hkv, d, 2048, 0, None, None, None)
@@ -268,12 +306,11 @@ def attn_prefill_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Te
     start_pos[b] + t; its keys come from the pools (append the chunk first)."""
     _check_input(q, "q")
     B, C, Hq, d = q.shape
-    num_pages, Hkv, page, d2 = _paged_args(k_cache, v_cache, page_table, start_pos, B)
+    num_pages, Hkv, page, d2 = _paged_args(k_cache, v_cache, page_table, start_pos, B, q.device)
     if d2 != d or k_cache.dtype != q.dtype:
         raise ValueError("caches must match q's head_dim and dtype")
     dev = q.device
-    beta, null_bias, count_vec = (_device_f32(beta, dev), _device_f32(null_bias, dev),
-                                  _device_f32(count_vec, dev))
+    beta, null_bias, count_vec = _head_params(beta, null_bias, count_vec, Hq, d, dev)
     prm = _params(Hq, Hkv, d, beta, null_bias, count_vec, train_len, flags)
     out, cout = _outputs((B, C), Hq, d, dev, count_vec is not None, want_gate, want_lse)
     s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
@@ -291,17 +328,19 @@ def delta_step(state_pool: torch.Tensor, slots: torch.Tensor, q: torch.Tensor, k
     state_pool[slots[b]] for every sequence b and returns o [B,H,d_v] (float32)."""
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _check_input(t, n)
-    if state_pool.dtype != torch.float32 or not state_pool.is_contiguous():
-        raise ValueError("state_pool must be a contiguous float32 tensor")
+    dev = q.device
+    _check_aux(state_pool, "state_pool", dev, torch.float32)
+    if state_pool.dim() != 4:
+        raise ValueError("state_pool must be [num_slots,H,d_v,d_k]")
     num_slots, H, dv, dk = state_pool.shape
     B = q.shape[0]
     if q.shape != (B, H, dk) or k.shape != q.shape or v.shape != (B, H, dv):
         raise ValueError("q, k must be [B,H,d_k] and v [B,H,d_v] matching the pool")
-    if slots.dtype != torch.int32 or slots.shape != (B,):
-        raise ValueError("slots must be int32 [B]")
-    dev = q.device
+    _check_aux(slots, "slots", dev, torch.int32, (B,))
     alpha = torch.as_tensor(alpha, dtype=torch.float32, device=dev).contiguous()
     beta = torch.as_tensor(beta, dtype=torch.float32, device=dev).contiguous()
+    _check_aux(alpha, "alpha", dev, torch.float32, (B, H))
+    _check_aux(beta, "beta", dev, torch.float32, (B, H))
     out = torch.empty(B, H, dv, device=dev, dtype=torch.float32)
     prm = _lib.polar_delta_params(H, dk, dv, _lib.POLAR_DELTA_NORMALIZE_QK if normalize_qk else 0)
     s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream

@@ -39,6 +39,7 @@ import math
 from typing import Optional
 
 import numpy as np
+import torch
 from scipy.special import expit
 
 FLAG_LENGTH_TEMP = 1
@@ -126,6 +127,15 @@ def rope(x: np.ndarray, theta: float, positions: Optional[np.ndarray] = None) ->
     return out
 
 
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """float64 values rounded to bfloat16 (torch's conversion: nearest, ties to even) and
+    widened back to float64.  Values are first narrowed to float32, which is exact for
+    the rounding to bfloat16 except in a double-rounding tie far below these tensors'
+    scale."""
+    t = torch.from_numpy(np.ascontiguousarray(x, np.float64)).to(torch.float32)
+    return t.to(torch.bfloat16).to(torch.float64).numpy()
+
+
 def _params(Hq, d, beta, null_bias, count_vec):
     beta = np.full(Hq, math.sqrt(d)) if beta is None else np.asarray(beta, np.float64)
     null_bias = np.zeros(Hq) if null_bias is None else np.asarray(null_bias, np.float64)
@@ -138,12 +148,15 @@ def polar_prefill(q, k, v, beta=None, null_bias=None, count_vec=None, train_len:
                   flags: int = FLAG_LENGTH_TEMP | FLAG_NULL_FLOOR,
                   rows: Optional[np.ndarray] = None, heads: Optional[np.ndarray] = None,
                   batches: Optional[np.ndarray] = None, max_elems: int = 1 << 24,
-                  window: int = 0, rope_theta: float = 0.0) -> dict:
+                  window: int = 0, rope_theta: float = 0.0, rope_bf16: bool = False) -> dict:
     """Causal Polar Attention prefill.
 
     Variants: ``window`` W >= 1 restricts row i to keys max(0, i-W+1)..i (so it sees
     n = min(i+1, W) keys); ``rope_theta`` > 0 rotates q and k by RoPE at their positions
     before the scores.  ``attn`` is the plain softmax attention output sum_j p_j v_j.
+    ``rope_bf16``: the model works in bfloat16, so the rotated q and k it attends with are
+    bfloat16 values: the exact rotation is rounded to bfloat16 (nearest, ties to even)
+    before the scores.
 
     q [B,T,Hq,d], k and v [B,T,Hkv,d] (any float dtype; computed in float64).
     Row i of head h sees keys 0..i of KV head h // (Hq // Hkv).
@@ -154,6 +167,8 @@ def polar_prefill(q, k, v, beta=None, null_bias=None, count_vec=None, train_len:
     """
     if rope_theta > 0:
         q, k = rope(q, rope_theta), rope(k, rope_theta)
+        if rope_bf16:
+            q, k = round_bf16(q), round_bf16(k)
     q = np.asarray(q)
     B, T, Hq, d = q.shape
     Hkv = k.shape[2]
@@ -237,23 +252,34 @@ def polar_decode_paged(q, k_pool, v_pool, page_table, seq_lens, page_size: int, 
     return out
 
 
+def chunk_start(start_pos, C: int, max_seq_len: Optional[int]) -> np.ndarray:
+    """Position of each chunk's first token.  The library's own rule (the pages say nothing
+    of out-of-range starts): a start is clamped to [0, max_seq_len - C], so that the chunk
+    fits the sequence bound and append and chunked prefill agree on where it lies."""
+    s = np.asarray(start_pos, np.int64)
+    if max_seq_len is None:
+        return s
+    assert max_seq_len >= C, "the sequence bound must hold the chunk"
+    return np.minimum(np.maximum(s, 0), max_seq_len - C)
+
+
 def kv_append(k_pool: np.ndarray, v_pool: np.ndarray, page_table: np.ndarray,
               start_pos: np.ndarray, k_new: np.ndarray, v_new: np.ndarray, page_size: int,
               max_seq_len: int):
     """Write a chunk of new keys and values into the paged pools (returns new pools).
 
-    Token t of sequence b goes to logical position start_pos[b] + t, i.e. physical page
-    page_table[b, pos // page_size], slot pos % page_size, for every KV head.  Tokens whose
-    position reaches max_seq_len or whose page id is outside the pool are dropped.
+    Token t of sequence b goes to logical position s + t (s = start_pos[b] clamped by
+    ``chunk_start``), i.e. physical page page_table[b, pos // page_size], slot
+    pos % page_size, for every KV head.  Tokens whose page id is outside the pool are
+    dropped.
     """
     k_pool, v_pool = k_pool.copy(), v_pool.copy()
     B, C = k_new.shape[:2]
     num_pages = k_pool.shape[0]
+    starts = chunk_start(start_pos, C, max_seq_len)
     for b in range(B):
         for t in range(C):
-            pos = int(start_pos[b]) + t
-            if pos >= max_seq_len:
-                continue
+            pos = int(starts[b]) + t
             page = int(page_table[b, pos // page_size])
             if not 0 <= page < num_pages:
                 continue
@@ -265,14 +291,17 @@ def kv_append(k_pool: np.ndarray, v_pool: np.ndarray, page_table: np.ndarray,
 def polar_prefill_paged(q, k_pool, v_pool, page_table, start_pos, page_size: int, beta=None,
                         null_bias=None, count_vec=None, train_len: int = 2048,
                         flags: int = FLAG_LENGTH_TEMP | FLAG_NULL_FLOOR,
-                        to_f64=lambda a: np.asarray(a, np.float64)) -> dict:
+                        to_f64=lambda a: np.asarray(a, np.float64),
+                        max_seq_len: Optional[int] = None) -> dict:
     """Chunked prefill over a paged cache: row t of sequence b is the token at position
-    start_pos[b] + t and attends the logical keys 0..start_pos[b] + t (the cached prefix
-    and the chunk up to itself), gathered through the page table.
+    s + t (s = start_pos[b], clamped by ``chunk_start`` when ``max_seq_len`` is given) and
+    attends the logical keys 0..s + t (the cached prefix and the chunk up to itself),
+    gathered through the page table.
     q [B,C,Hq,d]; returns float64 dir, count [B,C,Hq,d] and n_eff, gate, lse [B,C,Hq].
     """
     q = np.asarray(q, np.float64)
     B, C, Hq, d = q.shape
+    start_pos = chunk_start(start_pos, C, max_seq_len)
     Hkv = k_pool.shape[1]
     G = Hq // Hkv
     beta, null_bias, count_vec = _params(Hq, d, beta, null_bias, count_vec)

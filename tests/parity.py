@@ -6,6 +6,12 @@ Error metrics, per output, maximum over rows (b, i, h):
   dir    |x^ - x|_2 / |x|_2                 (|x| = 1)
   count  |x^ - x|_2 / |w_h|_2               (count -> 0 as n_eff -> 1, so the bound of
                                              the tanh map is the natural scale)
+  count_rel |x^ - x|_2 / |x|_2              over rows with tanh(ln n_eff) >= 1/2 (n_eff >=
+                                             sqrt 3): the relative error of the count
+                                             output itself.  Below that floor the tanh map
+                                             multiplies the relative n_eff error by
+                                             (1 - th^2) / th > 3/2, and count -> 0, so
+                                             those rows are judged by the |w_h| metric
   gate   |x^ - x|                           (in [0, 1])
   lse    |x^ - x| / max(1, |x|)
 Thresholds: 1e-4 for float32 inputs, 2e-2 for bfloat16 inputs with fp32 accumulation.
@@ -18,6 +24,7 @@ import synth
 from long_context_lm_amd import attn_decode_paged, attn_fwd
 
 TOL = {"f32": 1e-4, "bf16": 2e-2}
+COUNT_REL_FLOOR = 0.5       # tanh(ln n_eff) at or above which count is judged relatively
 
 
 def to_dev(a: np.ndarray, dtype: str, dev="cuda") -> torch.Tensor:
@@ -39,7 +46,7 @@ def oracle_prefill(p: synth.PrefillInputs, rows=None, heads=None, batches=None, 
     return oracle.polar_prefill(p.as_f32("q"), p.as_f32("k"), p.as_f32("v"), p.beta,
                                 p.null_bias, p.count_vec, p.train_len, p.flags, rows=rows,
                                 heads=heads, batches=batches, window=window,
-                                rope_theta=rope_theta)
+                                rope_theta=rope_theta, rope_bf16=p.dtype == "bf16")
 
 
 def gpu_decode(d: synth.DecodeInputs, **kw) -> dict:
@@ -79,7 +86,11 @@ def errors(got: dict, want: dict, count_vec: np.ndarray, heads=None) -> dict:
     e["dir"] = float(np.max(np.linalg.norm(g["dir"] - want["dir"], axis=-1) /
                             np.where(dn > 0, dn, 1.0)))
     if g.get("count") is not None:
-        e["count"] = float(np.max(np.linalg.norm(g["count"] - want["count"], axis=-1) / wn))
+        dc = np.linalg.norm(g["count"] - want["count"], axis=-1)
+        e["count"] = float(np.max(dc / wn))
+        cn = np.linalg.norm(want["count"], axis=-1)
+        rel_rows = (np.tanh(np.log(want["n_eff"])) >= COUNT_REL_FLOOR) & (cn > 0)
+        e["count_rel"] = float(np.max(dc[rel_rows] / cn[rel_rows])) if rel_rows.any() else 0.0
     if g.get("gate") is not None:
         e["gate"] = float(np.max(np.abs(g["gate"] - want["gate"])))
     if g.get("lse") is not None:

@@ -23,7 +23,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(_lib.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert _lib.polar_abi_version() == 2
+    assert _lib.polar_abi_version() == 3
 
 
 def test_status_strings():
@@ -96,19 +96,18 @@ def dec(p=None, dt=1, B=2, q=A, kc=A, vc=A, num_pages=10, page=64, table=A, stri
     p = params() if p is None else p
     o = outs() if o is None else o
     if ws_bytes is None:
-        ws_bytes = _lib.polar_decode_workspace_bytes(p, B, max_len, page)
+        ws_bytes = _lib.polar_decode_workspace_bytes(p, B, max(max_len, 1))
     return _lib.polar_attn_decode_paged(p, dt, B, q, kc, vc, num_pages, page, table, stride,
                                         lens, max_len, ws, ws_bytes, o, None)
 
 
 def test_workspace_bytes():
     p = params()
-    n = _lib.polar_decode_workspace_bytes(p, 16, 262144, 64)
+    n = _lib.polar_decode_workspace_bytes(p, 16, 262144)
     assert n > 0 and n % 16 == 0
-    assert _lib.polar_decode_workspace_bytes(p, 16, 262144, 32) == 0
-    assert _lib.polar_decode_workspace_bytes(p, 16, 0, 64) == 0
-    assert _lib.polar_decode_workspace_bytes(params(n_q_heads=5), 16, 100, 64) == 0
-    assert _lib.polar_decode_workspace_bytes(p, 0, 100, 64) == 0
+    assert _lib.polar_decode_workspace_bytes(p, 16, 0) == 0
+    assert _lib.polar_decode_workspace_bytes(params(n_q_heads=5), 16, 100) == 0
+    assert _lib.polar_decode_workspace_bytes(p, 0, 100) == 0
 
 
 @pytest.mark.parametrize("kw,code", [

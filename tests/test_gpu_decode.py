@@ -96,14 +96,14 @@ def test_workspace_reuse_and_determinism(gpu_lib):
         assert torch.equal(a[key], b[key]), key
 
 
-def test_c5_full_size_sampled_sequences(gpu_lib):
+def test_c5_full_size_all_sequences(gpu_lib):
+    """The 256K workload at full size (16 sequences x 262,144 keys): every sequence and
+    head against the oracle."""
+    print("[case] decode C5 B=16 L=262144", flush=True)
     d = synth.decode_inputs("c5")
     got = gpu_decode(d)
-    batches = np.array([0, 9, 15])
-    want = oracle_decode(d, batches=batches)
-    sel = {k: (None if v is None else v[torch.as_tensor(batches, device=v.device)])
-           for k, v in got.items()}
-    assert_close(sel, want, d.count_vec, d.dtype, label="c5 full B=16 L=262144")
+    want = oracle_decode(d)
+    assert_close(got, want, d.count_vec, d.dtype, label="c5 full B=16 L=262144")
     assert torch.isfinite(got["n_eff"]).all()
     # every (b, h) has its planted needle: the gate fires
     assert (got["gate"] > 0.5).all()

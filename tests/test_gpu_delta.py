@@ -1,7 +1,8 @@
 """GPU parity of the in-place gated-delta memory step against the float64 oracle, through
-the C ABI.  fp32 state arithmetic: the bound is 1e-5 of the largest state / output entry
-per step (64-term fp32 dot products) and 1e-4 after 32 chained steps; slots the batch does
-not name must stay bit-identical."""
+the C ABI.  fp32 state arithmetic, judged per state and per output vector: the relative
+Frobenius error of every (slot, head) state and the relative error of every (sequence, head)
+output, at most 1e-5 after one step (64-term fp32 dot products) and 1e-4 after 32 chained
+steps; slots the batch does not name must stay bit-identical."""
 import numpy as np
 import pytest
 import torch
@@ -21,7 +22,13 @@ def _dev(d):
 
 
 def _err(got, want):
-    return float(np.max(np.abs(got - want))) / float(np.max(np.abs(want)))
+    """Largest relative error of one state (last two axes) or output vector (last axis),
+    so that an error in a small-norm state is not hidden by a large one elsewhere."""
+    got, want = np.asarray(got, np.float64), np.asarray(want, np.float64)
+    axes = (-2, -1) if want.ndim >= 4 else (-1,)
+    num = np.sqrt(np.sum((got - want) ** 2, axis=axes))
+    den = np.sqrt(np.sum(want ** 2, axis=axes))
+    return float(np.max(num / np.maximum(den, 1e-30)))
 
 
 # (bf16, 256, 16, 1024) is the benchmark's step; (f32, 7, 3, 9) leaves a workgroup with a
@@ -74,5 +81,7 @@ def test_delta_step_invalid_slot_and_no_normalisation(gpu_lib):
     want_pool, want_out = oracle.delta_step_pool(d.pool, d.slots, d.q, d.k, d.v, d.alpha, d.beta,
                                                  normalize=False)
     assert float(out[2].abs().max()) == 0.0
-    assert _err(pool.cpu().numpy().astype(np.float64), want_pool) <= 1e-5
-    assert _err(out.cpu().numpy().astype(np.float64), want_out) <= 1e-5
+    used = np.array([s for s in d.slots if s >= 0])
+    assert _err(pool.cpu().numpy()[used], want_pool[used]) <= 1e-5
+    live = np.arange(4) != 2
+    assert _err(out.cpu().numpy()[live], want_out[live]) <= 1e-5

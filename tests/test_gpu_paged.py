@@ -56,6 +56,7 @@ def _bits(t):
     (2, 100, (37, 64), 8, 2),        # ragged chunk, unaligned starts
     (1, 1, (500,), 4, 1),            # one token (the decode case)
     (3, 64, (0, 1, 130), 4, 4),      # no GQA
+    (2, 200, (0, 300), 8, 4),        # two heads per block (128-row blocks), split instance
 ])
 def test_append_bit_exact_and_chunked_prefill_parity(gpu_lib, B, C, starts, Hq, Hkv):
     print(f"[case] paged B={B} C={C} starts={starts} {Hq}/{Hkv}", flush=True)
@@ -79,6 +80,34 @@ def test_append_drops_tokens_on_invalid_pages(gpu_lib):
     kp, _ = oracle.kv_append(ci.k_pool, ci.v_pool, ci.page_table, ci.start_pos, ci.chunk("k"),
                              ci.chunk("v"), ci.page_size, ci.max_seq_len)
     np.testing.assert_array_equal(_bits(kc), kp)
+
+
+def test_out_of_range_starts_are_clamped_alike(gpu_lib):
+    """start_pos outside [0, max_seq_len - C] (here -7 and 999, with max_seq_len 264 and
+    C = 64): the append kernel and the chunked prefill both clamp it, so the pools match
+    the oracle's (which clamps the same way) bit for bit and the rows match its chunked
+    prefill at the clamped starts."""
+    print("[case] paged clamped starts", flush=True)
+    ci = synth.chunk_inputs("c2", B=2, C=64, starts=(0, 200), Hq=8, Hkv=2, train_len=64)
+    wild = np.array([-7, 999], np.int32)
+    kc, vc, table, _ = _setup(ci)
+    start = torch.from_numpy(wild).cuda()
+    kv_append(to_dev(ci.chunk("k"), "bf16"), to_dev(ci.chunk("v"), "bf16"), kc, vc, table, start,
+              ci.max_seq_len)
+    p = ci.full
+    out = attn_prefill_paged(to_dev(ci.chunk("q"), "bf16"), kc, vc, table, start, ci.max_seq_len,
+                             beta=p.beta, null_bias=p.null_bias, count_vec=p.count_vec,
+                             train_len=p.train_len, flags=p.flags)
+    torch.cuda.synchronize()
+    kp, vp = oracle.kv_append(ci.k_pool, ci.v_pool, ci.page_table, wild, ci.chunk("k"),
+                              ci.chunk("v"), ci.page_size, ci.max_seq_len)
+    np.testing.assert_array_equal(_bits(kc), kp)
+    np.testing.assert_array_equal(_bits(vc), vp)
+    want = oracle.polar_prefill_paged(_f(ci.chunk("q")), kp, vp, ci.page_table, wild,
+                                      ci.page_size, p.beta, p.null_bias, p.count_vec,
+                                      p.train_len, p.flags, to_f64=_f,
+                                      max_seq_len=ci.max_seq_len)
+    assert_close(out, want, p.count_vec, "bf16", label="clamped starts")
 
 
 def test_chunked_prefill_float32(gpu_lib):
@@ -107,8 +136,8 @@ def test_last_chunk_of_64k_sequence_sampled(gpu_lib):
 def test_lean_and_split_paged_chunks(gpu_lib):
     """Four 4096-token chunks (16/4 heads): 1024 workgroups choose the lean instance; a
     one-sequence launch (256 workgroups) the split instance, whose two 8-wave halves take
-    the two halves of the key range and merge.  The first 256 rows of two sequences
-    against the oracle from both, and every row of the two within the bf16 bound of each
+    the two halves of the key range and merge.  Every row of two of the chunks against the
+    oracle, from both instances, and the two instances within the bf16 bound of each
     other."""
     print("[case] paged lean and split B=4 C=4096", flush=True)
     ci = synth.chunk_inputs("c2", B=4, C=4096, starts=(0, 1000, 2500, 3000))
@@ -122,17 +151,16 @@ def test_lean_and_split_paged_chunks(gpu_lib):
                               ci.chunk("v"), ci.page_size, ci.max_seq_len)
     for b in (0, 3):
         want = oracle.polar_prefill_paged(
-            _f(ci.chunk("q")[b:b + 1, :256]), kp, vp, ci.page_table[b:b + 1],
+            _f(ci.chunk("q")[b:b + 1]), kp, vp, ci.page_table[b:b + 1],
             ci.start_pos[b:b + 1], ci.page_size, p.beta, p.null_bias, p.count_vec, p.train_len,
             p.flags, to_f64=_f)
-        got = {n: out[n][b:b + 1, :256] for n in ("dir", "count", "n_eff", "gate", "lse")}
+        got = {n: out[n][b:b + 1] for n in ("dir", "count", "n_eff", "gate", "lse")}
         assert_close(got, want, p.count_vec, dt, label=f"lean paged b={b}")
         one = attn_prefill_paged(q[b:b + 1], kc, vc, table[b:b + 1], start[b:b + 1],
                                  ci.max_seq_len, beta=p.beta, null_bias=p.null_bias,
                                  count_vec=p.count_vec, train_len=p.train_len, flags=p.flags)
         torch.cuda.synchronize()
-        got1 = {n: one[n][:, :256] for n in ("dir", "count", "n_eff", "gate", "lse")}
-        assert_close(got1, want, p.count_vec, dt, label=f"split paged b={b}")
+        assert_close(one, want, p.count_vec, dt, label=f"split paged b={b}")
         lean_all = {n: host(out[n][b:b + 1]) for n in ("dir", "count", "n_eff", "gate", "lse")}
         assert_close(one, lean_all, p.count_vec, dt, label=f"split vs lean b={b}")
 

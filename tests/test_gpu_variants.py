@@ -47,6 +47,20 @@ def test_variant_parity(gpu_lib, cfg, B, T, Hq, Hkv, window, theta):
     check(p, got, want, f"{cfg} W={window} theta={theta}")
 
 
+@pytest.mark.parametrize("beta,T,window", [(16.0, 2048, 0), (24.0, 700, 0), (16.0, 3000, 1000)])
+def test_rope_at_sharper_beta(gpu_lib, beta, T, window):
+    """RoPE with sharper logits than the default beta = 8 (near one-hot rows dominate).  The
+    kernel rounds the rotated q and k to bfloat16, as a bfloat16 model holds them, and so
+    does the oracle; what is left is the rounding of P and the hardware sine and cosine,
+    so the errors do not grow with beta."""
+    print(f"[case] rope beta={beta} T={T} W={window}", flush=True)
+    p = synth.prefill_inputs("c2", B=1, T=T, Hq=8, Hkv=2, train_len=2048)
+    p = dataclasses.replace(p, beta=np.full(p.Hq, beta, np.float32))
+    got = run(p, window=window, rope_theta=10000.0)
+    want = oracle_prefill(p, window=window, rope_theta=10000.0)
+    check(p, got, want, f"rope beta={beta} T={T} W={window}")
+
+
 @pytest.mark.parametrize("cfg,T,window,attn", [("c2", 333, 0, True), ("c2", 200, 64, False),
                                               ("c1", 150, 37, True)])
 def test_keys_rotated_once_equal_keys_rotated_in_staging(gpu_lib, cfg, T, window, attn):

@@ -5,7 +5,9 @@
   nothing);
 * a chunk of one token equals paged decode of that sequence;
 * appending into pages and gathering back returns the contiguous keys and values exactly;
-  dropped tokens (past max_seq_len, invalid pages) leave the pool unchanged.
+  dropped tokens (invalid pages) leave the pool unchanged;
+* a start outside [0, max_seq_len - C] behaves exactly like the nearest start inside it, in
+  the append and in the chunked prefill alike.
 """
 import numpy as np
 
@@ -67,7 +69,30 @@ def test_append_drops_out_of_range_tokens():
     kp, vp = oracle.kv_append(ci.k_pool, ci.v_pool, table, ci.start_pos, ci.chunk("k"),
                               ci.chunk("v"), ci.page_size, ci.max_seq_len)
     np.testing.assert_array_equal(kp, ci.k_pool)
-    kp2, _ = oracle.kv_append(ci.k_pool, ci.v_pool, ci.page_table, ci.start_pos, ci.chunk("k"),
-                              ci.chunk("v"), ci.page_size, max_seq_len=32)
-    changed = np.any(kp2 != ci.k_pool, axis=(1, 3))      # [pages, slots]
-    assert changed.sum() <= 32                              # only positions < 32 written
+
+
+def test_chunk_start_clamp_closed_form():
+    np.testing.assert_array_equal(oracle.chunk_start([-3, 0, 5, 90, 91, 999], 10, 100),
+                                  [0, 0, 5, 90, 90, 90])
+    np.testing.assert_array_equal(oracle.chunk_start([-3, 999], 10, None), [-3, 999])
+
+
+def test_out_of_range_starts_act_like_the_clamped_start():
+    """Appending and attending with starts (-7, 999) over max_seq_len = 264, C = 64 is the
+    same as with the clamped starts (0, 200): the same pool and the same rows."""
+    ci = synth.chunk_inputs("c2", B=2, C=64, starts=(0, 200), Hq=4, Hkv=2, train_len=16)
+    assert ci.max_seq_len == 264
+    wild = np.array([-7, 999], np.int32)
+    args = (ci.chunk("k"), ci.chunk("v"), ci.page_size, ci.max_seq_len)
+    kp, vp = oracle.kv_append(ci.k_pool, ci.v_pool, ci.page_table, ci.start_pos, *args)
+    kw, vw = oracle.kv_append(ci.k_pool, ci.v_pool, ci.page_table, wild, *args)
+    np.testing.assert_array_equal(kw, kp)
+    np.testing.assert_array_equal(vw, vp)
+    p = ci.full
+    common = (ci.page_size, p.beta, p.null_bias, p.count_vec, p.train_len, p.flags)
+    want = oracle.polar_prefill_paged(_f(ci.chunk("q")), kp, vp, ci.page_table, ci.start_pos,
+                                      *common, to_f64=_f)
+    got = oracle.polar_prefill_paged(_f(ci.chunk("q")), kp, vp, ci.page_table, wild, *common,
+                                     to_f64=_f, max_seq_len=ci.max_seq_len)
+    for n in ("dir", "count", "n_eff", "gate", "lse"):
+        np.testing.assert_array_equal(got[n], want[n])

@@ -5,7 +5,9 @@
 * a windowed row equals the last causal row of the sliced sequence it sees;
 * window 1 has closed forms; a window of at least T changes nothing;
 * RoPE preserves norms, makes scores depend on position differences only, is the identity
-  at position 0, and rotates one pair by pos * theta**(-2t/d).
+  at position 0, and rotates one pair by pos * theta**(-2t/d);
+* the bfloat16 rounding of rotated q and k is nearest-even, and leaves bfloat16 values
+  (position 0) unchanged.
 """
 import math
 
@@ -14,6 +16,7 @@ import pytest
 import torch
 
 import oracle
+import synth
 
 OUTS = ("dir", "count", "n_eff", "gate", "lse", "attn")
 
@@ -109,3 +112,29 @@ def test_rope_pair_rotation_closed_form():
         np.testing.assert_allclose(r[0, p_i, 0, :2], [math.cos(pos), math.sin(pos)], atol=1e-15)
         a1 = pos * 100.0 ** (-2 * 1 / 4)              # theta^(-2t/d) with t = 1, d = 4
         np.testing.assert_allclose(r[0, p_i, 0, 2:], [math.cos(a1), math.sin(a1)], atol=1e-15)
+
+
+def test_round_bf16_nearest_even_closed_forms():
+    """bfloat16 keeps 8 significant bits: halfway cases go to the even neighbour."""
+    r = oracle.polar_oracle.round_bf16
+    x = np.array([1.0, 1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, 1 + 2.0 ** -7, 1 + 2.0 ** -8 + 2.0 ** -20,
+                  -3.0, 2.0 ** -100])
+    want = np.array([1.0, 1.0, 1 + 2.0 ** -6, 1 + 2.0 ** -7, 1 + 2.0 ** -7, -3.0, 2.0 ** -100])
+    np.testing.assert_array_equal(r(x), want)
+
+
+def test_rope_bf16_rounding_keeps_bf16_values_at_position_zero():
+    """At position 0 the rotation is the identity, so rounding bf16 inputs changes nothing:
+    a one-token prefill with RoPE in bfloat16 equals the plain prefill, while a
+    non-bfloat16 input shows the rounding."""
+    p = synth.prefill_inputs("c2", B=1, T=1, Hq=4, Hkv=2, train_len=16)
+    args = (p.as_f32("q"), p.as_f32("k"), p.as_f32("v"), p.beta, p.null_bias, p.count_vec,
+            p.train_len, p.flags)
+    a = oracle.polar_prefill(*args, rope_theta=10000.0, rope_bf16=True)
+    b = oracle.polar_prefill(*args)
+    for n in ("dir", "count", "n_eff", "gate", "lse"):
+        np.testing.assert_array_equal(a[n], b[n])
+    q = p.as_f32("q").astype(np.float64) * (1 + 2.0 ** -12)   # off the bf16 grid
+    c = oracle.polar_prefill(q, *args[1:], rope_theta=10000.0, rope_bf16=True)
+    d = oracle.polar_prefill(q, *args[1:], rope_theta=10000.0)
+    assert np.any(c["lse"] != d["lse"])
