@@ -194,6 +194,34 @@ POLAR_API polar_status polar_attn_decode_paged(const polar_params *p, polar_dtyp
                                      void *workspace, size_t workspace_bytes,
                                      const polar_outputs *out, void *stream);
 
+/*
+ * polar_attn_decode_paged for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same arguments,
+ * results and conventions as polar_attn_decode_paged, without the workspace: the split
+ * partials live in a static device array of the library, POLAR_NOALLOC_SCRATCH_BYTES
+ * bytes per GPU, held from the library's first use on that GPU until the process ends.
+ * Nothing on this call path allocates (no hipMalloc, hipFree or allocating library call).
+ *   - The scratch is looked up on the current device (hipGetDevice) on its first call
+ *     there; `stream` must belong to the current device.
+ *   - A decode needing more than POLAR_NOALLOC_SCRATCH_BYTES of partials
+ *     (polar_decode_workspace_bytes) returns POLAR_ERR_WORKSPACE_TOO_SMALL and launches
+ *     nothing.
+ *   - Every call on one GPU shares that GPU's scratch: calls that overlap on one GPU (on
+ *     different streams or threads without ordering between them) race and give
+ *     unspecified results.  Calls ordered on one stream are safe; the scratch keeps the
+ *     last call's partials, which the next call overwrites before it reads them.
+ */
+#define POLAR_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+POLAR_API polar_status polar_attn_decode_paged_noalloc(const polar_params *p, polar_dtype dt,
+                                                       int32_t B, const void *q,
+                                                       const void *k_cache, const void *v_cache,
+                                                       int32_t num_pages, int32_t page_size,
+                                                       const int32_t *page_table,
+                                                       int32_t page_table_stride,
+                                                       const int32_t *seq_lens,
+                                                       int32_t max_seq_len,
+                                                       const polar_outputs *out, void *stream);
+
 /* ---------------------------------------------------------------------------------
  * Training: forward with residuals, and the backward pass of the causal prefill.
  *

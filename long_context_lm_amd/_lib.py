@@ -29,6 +29,7 @@ POLAR_FLAG_NULL_FLOOR = 2
 POLAR_DELTA_NORMALIZE_QK = 1
 
 EXPORTS = ("polar_attn_fwd", "polar_decode_workspace_bytes", "polar_attn_decode_paged",
+           "polar_attn_decode_paged_noalloc",
            "polar_attn_fwd_train", "polar_bwd_workspace_bytes", "polar_attn_bwd",
            "polar_attn_fwd_variant", "polar_variant_workspace_bytes", "polar_kv_append",
            "polar_attn_prefill_paged",
@@ -104,6 +105,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.polar_attn_decode_paged.restype = I32
     lib.polar_attn_decode_paged.argtypes = [P(polar_params), I32, I32, VP, VP, VP, I32, I32, VP,
                                             I32, VP, I32, VP, SZ, P(polar_outputs), VP]
+    lib.polar_attn_decode_paged_noalloc.restype = I32
+    lib.polar_attn_decode_paged_noalloc.argtypes = [P(polar_params), I32, I32, VP, VP, VP, I32,
+                                                    I32, VP, I32, VP, I32, P(polar_outputs), VP]
     lib.polar_attn_fwd_train.restype = I32
     lib.polar_attn_fwd_train.argtypes = [P(polar_params), I32, I32, I32, VP, VP, VP,
                                          P(polar_outputs), P(polar_saved), VP]
@@ -167,6 +171,18 @@ def polar_attn_decode_paged(params, dtype, B, q, k_cache, v_cache, num_pages, pa
                                           num_pages, page_size, page_table, page_table_stride,
                                           seq_lens, max_seq_len, workspace, workspace_bytes,
                                           ctypes.byref(outputs), stream)
+
+
+POLAR_NOALLOC_SCRATCH_BYTES = 16 << 20    # include/polar.h
+
+
+def polar_attn_decode_paged_noalloc(params, dtype, B, q, k_cache, v_cache, num_pages,
+                                    page_size, page_table, page_table_stride, seq_lens,
+                                    max_seq_len, outputs, stream) -> int:
+    return load().polar_attn_decode_paged_noalloc(ctypes.byref(params), dtype, B, q, k_cache,
+                                                  v_cache, num_pages, page_size, page_table,
+                                                  page_table_stride, seq_lens, max_seq_len,
+                                                  ctypes.byref(outputs), stream)
 
 
 def polar_attn_fwd_train(params, dtype, B, T, q, k, v, outputs, saved, stream) -> int:

@@ -323,13 +323,18 @@ size_t polar_decode_workspace_bytes(const polar_params *p, int32_t B, int32_t ma
   return polar::decode_ws_bytes(B, p->n_q_heads, p->n_kv_heads, max_seq_len);
 }
 
-polar_status polar_attn_decode_paged(const polar_params *p, polar_dtype dt, int32_t B,
-                                     const void *q, const void *k_cache, const void *v_cache,
-                                     int32_t num_pages, int32_t page_size,
-                                     const int32_t *page_table, int32_t page_table_stride,
-                                     const int32_t *seq_lens, int32_t max_seq_len,
-                                     void *workspace, size_t workspace_bytes,
-                                     const polar_outputs *out, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// The paged decode; with no_alloc the split partials go to the library's static scratch
+// (workspace and workspace_bytes are ignored) instead of the caller's workspace.
+polar_status decode(const polar_params *p, polar_dtype dt, int32_t B, const void *q,
+                    const void *k_cache, const void *v_cache, int32_t num_pages,
+                    int32_t page_size, const int32_t *page_table, int32_t page_table_stride,
+                    const int32_t *seq_lens, int32_t max_seq_len, void *workspace,
+                    size_t workspace_bytes, const polar_outputs *out, void *stream,
+                    bool no_alloc) {
   polar_status st = check_params(p, dt, out);
   if (st != POLAR_OK) return st;
   if (B < 0) return fail(POLAR_ERR_BAD_SHAPE, "B (%d) must be >= 0", B);
@@ -339,9 +344,11 @@ polar_status polar_attn_decode_paged(const polar_params *p, polar_dtype dt, int3
   if (B == 0) return POLAR_OK;
   st = check_outputs(p, out);
   if (st != POLAR_OK) return st;
-  if (!q || !k_cache || !v_cache || !page_table || !seq_lens || !workspace)
+  if (!q || !k_cache || !v_cache || !page_table || !seq_lens || (!no_alloc && !workspace))
     return fail(POLAR_ERR_NULL_POINTER,
-                "q, k_cache, v_cache, page_table, seq_lens and workspace must be non-NULL");
+                no_alloc ? "q, k_cache, v_cache, page_table and seq_lens must be non-NULL"
+                         : "q, k_cache, v_cache, page_table, seq_lens and workspace must be "
+                           "non-NULL");
   if (num_pages < 1) return fail(POLAR_ERR_BAD_SHAPE, "num_pages (%d) must be >= 1", num_pages);
   if (max_seq_len < 1)
     return fail(POLAR_ERR_BAD_SHAPE, "max_seq_len (%d) must be >= 1", max_seq_len);
@@ -349,10 +356,16 @@ polar_status polar_attn_decode_paged(const polar_params *p, polar_dtype dt, int3
   if (page_table_stride < need_pages)
     return fail(POLAR_ERR_BAD_SHAPE, "page_table_stride (%d) < ceil(max_seq_len/page_size) (%d)",
                 page_table_stride, need_pages);
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(workspace))
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      (!no_alloc && !aligned16(workspace)))
     return fail(POLAR_ERR_MISALIGNED, "q, caches and workspace must be 16-byte aligned");
   const size_t need = polar::decode_ws_bytes(B, p->n_q_heads, p->n_kv_heads, max_seq_len);
-  if (workspace_bytes < need)
+  if (no_alloc && need > polar::kNoAllocScratchBytes)
+    return fail(POLAR_ERR_WORKSPACE_TOO_SMALL,
+                "this decode needs %zu bytes of split partials; the static scratch of the "
+                "allocation-free entry point holds %zu (use polar_attn_decode_paged with a "
+                "workspace)", need, polar::kNoAllocScratchBytes);
+  if (!no_alloc && workspace_bytes < need)
     return fail(POLAR_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed",
                 workspace_bytes, need);
 
@@ -361,6 +374,12 @@ polar_status polar_attn_decode_paged(const polar_params *p, polar_dtype dt, int3
   if ((long long)p->n_kv_heads * grid.n_hchunk > 65535 || B > 65535)
     return fail(POLAR_ERR_BAD_SHAPE, "grid too large (B=%d, Hkv*chunks=%lld)", B,
                 (long long)p->n_kv_heads * grid.n_hchunk);
+  if (no_alloc) {
+    // Every argument has been checked; now the scratch's address on this device.
+    const hipError_t e = polar::noalloc_scratch(&workspace);
+    if (e != hipSuccess)
+      return fail(POLAR_ERR_HIP, "scratch lookup: %s", hipGetErrorString(e));
+  }
   polar::DecodeArgs a;
   a.q = q;
   a.k_cache = k_cache;
@@ -391,6 +410,33 @@ polar_status polar_attn_decode_paged(const polar_params *p, polar_dtype dt, int3
   hipError_t err = polar::launch_decode((int)dt, a, (hipStream_t)stream);
   if (err != hipSuccess) return fail(POLAR_ERR_HIP, "decode launch: %s", hipGetErrorString(err));
   return POLAR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+polar_status polar_attn_decode_paged(const polar_params *p, polar_dtype dt, int32_t B,
+                                     const void *q, const void *k_cache, const void *v_cache,
+                                     int32_t num_pages, int32_t page_size,
+                                     const int32_t *page_table, int32_t page_table_stride,
+                                     const int32_t *seq_lens, int32_t max_seq_len,
+                                     void *workspace, size_t workspace_bytes,
+                                     const polar_outputs *out, void *stream) {
+  return decode(p, dt, B, q, k_cache, v_cache, num_pages, page_size, page_table,
+                page_table_stride, seq_lens, max_seq_len, workspace, workspace_bytes, out,
+                stream, false);
+}
+
+polar_status polar_attn_decode_paged_noalloc(const polar_params *p, polar_dtype dt, int32_t B,
+                                             const void *q, const void *k_cache,
+                                             const void *v_cache, int32_t num_pages,
+                                             int32_t page_size, const int32_t *page_table,
+                                             int32_t page_table_stride, const int32_t *seq_lens,
+                                             int32_t max_seq_len, const polar_outputs *out,
+                                             void *stream) {
+  return decode(p, dt, B, q, k_cache, v_cache, num_pages, page_size, page_table,
+                page_table_stride, seq_lens, max_seq_len, nullptr, 0, out, stream, true);
 }
 
 polar_status polar_kv_append(const polar_params *p, polar_dtype dt, int32_t B, int32_t C,

@@ -16,6 +16,8 @@
 // Combine kernel: one workgroup per (b, query head) merges the splits with factors
 // 2^(M_s-R) (squared for Q), each wave a contiguous share of them, and applies the
 // direction / count epilogue with n = seq_len.
+#include <mutex>
+
 #include "polar_kernels.h"
 #include "polar_mfma.h"
 
@@ -365,6 +367,32 @@ DecodeGrid decode_grid(int B, int Hq, int Hkv, int max_seq_len) {
   d.pages_per_split = (int)((npages + ns - 1) / ns);
   d.n_split = (npages + d.pages_per_split - 1) / d.pages_per_split;
   return d;
+}
+
+// Scratch of the allocation-free decode entry point: the split partials live in this
+// device array instead of a caller workspace.  Each GPU the library runs on holds its own
+// copy until the process ends; every call on that GPU shares it.  Host code never passes
+// the array's name to a kernel (on the host it is only a stand-in): the device address is
+// looked up once per device with hipGetSymbolAddress and kept.
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+
+hipError_t noalloc_scratch(void **ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void *per_device[kMaxDevices];
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!per_device[dev]) {
+    void *p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));   // with dev current
+    if (err != hipSuccess) return err;
+    per_device[dev] = p;
+  }
+  *ptr = per_device[dev];
+  return hipSuccess;
 }
 
 size_t decode_ws_bytes(int B, int Hq, int Hkv, int max_seq_len) {

@@ -70,6 +70,10 @@ struct DecodeGrid {
 DecodeGrid decode_grid(int B, int Hq, int Hkv, int max_seq_len);
 size_t decode_ws_bytes(int B, int Hq, int Hkv, int max_seq_len);
 hipError_t launch_decode(int dtype, const DecodeArgs &a, hipStream_t stream);
+// The allocation-free decode's static scratch: its size, and its device address on the
+// current device (looked up on the first call on each device).
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+hipError_t noalloc_scratch(void **ptr);
 
 // Writes a chunk of new keys/values into the page pools.
 struct AppendArgs {

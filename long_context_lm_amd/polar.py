@@ -234,8 +234,12 @@ def attn_decode_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
                       beta=None, null_bias=None, count_vec=None, train_len: int = 2048,
                       flags: int = _lib.POLAR_FLAG_LENGTH_TEMP | _lib.POLAR_FLAG_NULL_FLOOR,
                       workspace: Optional[torch.Tensor] = None, want_gate: bool = True,
-                      want_lse: bool = True, stream=None) -> dict:
-    """GQA paged decode.  q [B,Hq,d]; caches [num_pages,Hkv,page,d]; table [B,stride] int32."""
+                      want_lse: bool = True, no_alloc: bool = False, stream=None) -> dict:
+    """GQA paged decode.  q [B,Hq,d]; caches [num_pages,Hkv,page,d]; table [B,stride] int32.
+
+    With ``no_alloc`` the call goes to polar_attn_decode_paged_noalloc, whose split partials
+    live in the library's static scratch: no workspace is passed (``workspace`` must be
+    None) and the C call allocates nothing; the outputs are still allocated here."""
     for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
         _check_input(t, n)
     B, Hq, d = q.shape
@@ -251,12 +255,21 @@ def attn_decode_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
         _check_aux(t, n, dev, q.dtype)
     beta, null_bias, count_vec = _head_params(beta, null_bias, count_vec, Hq, d, dev)
     prm = _params(Hq, Hkv, d, beta, null_bias, count_vec, train_len, flags)
-    need = _lib.polar_decode_workspace_bytes(prm, B, max_seq_len)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
-    _check_aux(workspace, "workspace", dev, None)
+    if no_alloc and workspace is not None:
+        raise ValueError("the allocation-free decode takes no workspace")
+    if not no_alloc:
+        need = _lib.polar_decode_workspace_bytes(prm, B, max_seq_len)
+        if workspace is None:
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        _check_aux(workspace, "workspace", dev, None)
     out, cout = _outputs((B,), Hq, d, dev, count_vec is not None, want_gate, want_lse)
     s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+    if no_alloc:
+        _lib.check(_lib.polar_attn_decode_paged_noalloc(
+            prm, _DT[q.dtype], B, q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+            num_pages, page, page_table.data_ptr(), page_table.shape[1], seq_lens.data_ptr(),
+            max_seq_len, cout, s))
+        return out
     _lib.check(_lib.polar_attn_decode_paged(
         prm, _DT[q.dtype], B, q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), num_pages,
         page, page_table.data_ptr(), page_table.shape[1], seq_lens.data_ptr(), max_seq_len,

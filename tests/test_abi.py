@@ -346,3 +346,35 @@ def test_delta_step_empty_and_null_params():
     lib = _lib.load()
     assert lib.polar_delta_step(None, 1, 1, A, 1, A, A, A, A, A, A, A, None) == \
         _lib.POLAR_ERR_NULL_POINTER
+
+
+def dec_noalloc(p=None, dt=1, B=2, q=A, kc=A, vc=A, num_pages=10, page=64, table=A, stride=4,
+                lens=A, max_len=256, o=None):
+    p = params() if p is None else p
+    o = outs() if o is None else o
+    return _lib.polar_attn_decode_paged_noalloc(p, dt, B, q, kc, vc, num_pages, page, table,
+                                                stride, lens, max_len, o, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(page=32), _lib.POLAR_ERR_UNSUPPORTED),
+    (dict(B=-1), _lib.POLAR_ERR_BAD_SHAPE),
+    (dict(q=None), _lib.POLAR_ERR_NULL_POINTER),
+    (dict(table=None), _lib.POLAR_ERR_NULL_POINTER),
+    (dict(stride=3), _lib.POLAR_ERR_BAD_SHAPE),
+    (dict(kc=A + 8), _lib.POLAR_ERR_MISALIGNED),
+    # 4096 sequences of 256K keys need 17.8 MB of split partials: more than the scratch
+    (dict(B=4096, max_len=262144, stride=4096, num_pages=1 << 20), _lib.POLAR_ERR_WORKSPACE_TOO_SMALL),
+])
+def test_noalloc_decode_validation(kw, code):
+    """The allocation-free decode validates like the workspace one, and refuses a decode
+    whose partials exceed its static scratch, all before any HIP call."""
+    assert dec_noalloc(**kw) == code
+    if code == _lib.POLAR_ERR_WORKSPACE_TOO_SMALL:
+        assert "static scratch" in _lib.polar_last_error()
+        p = params()
+        assert _lib.polar_decode_workspace_bytes(p, 4096, 262144) > _lib.POLAR_NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_decode_empty_batch_launches_nothing():
+    assert dec_noalloc(B=0, q=None, kc=None, vc=None, table=None, lens=None) == _lib.POLAR_OK
