@@ -16,6 +16,9 @@ rule; the reading taken is the published gated delta rule, one token per step:
 
 with per-(sequence, head) gate alpha and write strength beta.  Written out literally
 (identity matrix, outer products), in float64.
+
+The memory stream over a sequence (``delta_sequence_pool``) applies that step token after
+token, in order, reading every output o_t and leaving the last state in the pool.
 """
 from __future__ import annotations
 
@@ -57,4 +60,26 @@ def delta_step_pool(pool: np.ndarray, slots, q, k, v, alpha, beta, normalize: bo
         if not 0 <= s < pool.shape[0]:
             continue
         pool[s], out[b] = delta_step(pool[s], q[b], k[b], v[b], alpha[b], beta[b], normalize)
+    return pool, out
+
+
+def delta_sequence_pool(pool: np.ndarray, slots, q, k, v, alpha, beta, normalize: bool = True):
+    """The memory stream over T tokens for B sequences whose states sit in a pool
+    [num_slots, H, d_v, d_k]: for t = 0..T-1 in order, S <- step(S, q_t, k_t, v_t, alpha_t,
+    beta_t) and o_t = S q_t.  q, k [B,T,H,d_k]; v [B,T,H,d_v]; alpha, beta [B,T,H].
+    Returns (pool with the final states, o [B,T,H,d_v]) in float64; sequences whose slot
+    lies outside the pool are skipped (zero outputs)."""
+    pool = np.array(pool, np.float64)
+    q, k, v = (np.asarray(a) for a in (q, k, v))
+    B, T, H = q.shape[:3]
+    out = np.zeros((B, T, H, v.shape[-1]))
+    for b in range(B):
+        s = int(slots[b])
+        if not 0 <= s < pool.shape[0]:
+            continue
+        S = pool[s]
+        for t in range(T):
+            S, out[b, t] = delta_step(S, q[b, t], k[b, t], v[b, t], alpha[b, t], beta[b, t],
+                                      normalize)
+        pool[s] = S
     return pool, out
