@@ -1,5 +1,5 @@
 /*
- * libpolar — Polar Attention forward for AMD Instinct MI355X (gfx950).  C ABI, version 3
+ * libpolar — Polar Attention forward for AMD Instinct MI355X (gfx950).  C ABI, version 4
  * (POLAR_ABI_VERSION below; polar_abi_version() reports the loaded library's).
  *
  * The operation is the attention mixing step of the ATMA hybrid decoder as described in
@@ -48,8 +48,9 @@ extern "C" {
 
 /* 2: polar_variant gained the key-rotation workspace.
  * 3: polar_decode_workspace_bytes lost its page_size argument (the only page size is 64 and
- *    the workspace never depended on it). */
-#define POLAR_ABI_VERSION 3
+ *    the workspace never depended on it).
+ * 4: polar_delta_sequence (the memory stream over T tokens) added; nothing else changed. */
+#define POLAR_ABI_VERSION 4
 
 #if defined(__GNUC__)
 #define POLAR_API __attribute__((visibility("default")))
@@ -371,6 +372,28 @@ POLAR_API polar_status polar_delta_step(const polar_delta_params *p, polar_dtype
                               float *state_pool, int32_t num_slots, const int32_t *slots,
                               const void *q, const void *k, const void *v, const float *alpha,
                               const float *beta, float *out, void *stream);
+
+/*
+ * The memory stream over a sequence: for t = 0..T-1 in order, the step above on token t of
+ * each of the B sequences, o_t = S_t q_t for every token (the recurrent channel of section
+ * 2.1 run over a prompt or a training sequence, its state updated in place as in section
+ * 2.2).  The result equals T chained polar_delta_step calls up to fp32 rounding order.
+ *   state_pool  as for the step: slot slots[b] holds sequence b's state on entry and its
+ *               state after token T-1 on return.  Slots outside [0, num_slots) are
+ *               skipped (outputs zero, no state touched); two sequences naming the same
+ *               slot race.
+ *   q, k        [B,T,H,d_k] and v [B,T,H,d_v], dtype `dt`, row-major, 16-byte aligned.
+ *   alpha, beta device float32 [B,T,H].
+ *   out         device float32 [B,T,H,d_v], 16-byte aligned: o_t.
+ * T = 0 or B = 0 is a no-op.  Errors: POLAR_ERR_NULL_POINTER, POLAR_ERR_BAD_SHAPE (T < 0,
+ * B*T*H beyond 2^56), POLAR_ERR_MISALIGNED, POLAR_ERR_UNSUPPORTED as for the step.
+ */
+POLAR_API polar_status polar_delta_sequence(const polar_delta_params *p, polar_dtype dt,
+                                            int32_t B, int32_t T, float *state_pool,
+                                            int32_t num_slots, const int32_t *slots,
+                                            const void *q, const void *k, const void *v,
+                                            const float *alpha, const float *beta, float *out,
+                                            void *stream);
 
 /* Static description of a status code. */
 POLAR_API const char *polar_status_str(polar_status s);

@@ -33,7 +33,7 @@ EXPORTS = ("polar_attn_fwd", "polar_decode_workspace_bytes", "polar_attn_decode_
            "polar_attn_fwd_train", "polar_bwd_workspace_bytes", "polar_attn_bwd",
            "polar_attn_fwd_variant", "polar_variant_workspace_bytes", "polar_kv_append",
            "polar_attn_prefill_paged",
-           "polar_delta_step",
+           "polar_delta_step", "polar_delta_sequence",
            "polar_status_str", "polar_last_error", "polar_abi_version")
 
 
@@ -131,6 +131,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.polar_delta_step.restype = I32
     lib.polar_delta_step.argtypes = [P(polar_delta_params), I32, I32, VP, I32, VP, VP, VP, VP, VP,
                                      VP, VP, VP]
+    lib.polar_delta_sequence.restype = I32
+    lib.polar_delta_sequence.argtypes = [P(polar_delta_params), I32, I32, I32, VP, I32, VP, VP, VP,
+                                         VP, VP, VP, VP, VP]
     lib.polar_status_str.restype = ctypes.c_char_p
     lib.polar_status_str.argtypes = [I32]
     lib.polar_last_error.restype = ctypes.c_char_p
@@ -214,6 +217,12 @@ def polar_delta_step(params, dtype, B, state_pool, num_slots, slots, q, k, v, al
                      stream) -> int:
     return load().polar_delta_step(ctypes.byref(params), dtype, B, state_pool, num_slots, slots,
                                    q, k, v, alpha, beta, out, stream)
+
+
+def polar_delta_sequence(params, dtype, B, T, state_pool, num_slots, slots, q, k, v, alpha, beta,
+                         out, stream) -> int:
+    return load().polar_delta_sequence(ctypes.byref(params), dtype, B, T, state_pool, num_slots,
+                                       slots, q, k, v, alpha, beta, out, stream)
 
 
 def polar_variant_workspace_bytes(params, dtype, B, T) -> int:

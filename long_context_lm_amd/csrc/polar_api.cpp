@@ -510,10 +510,9 @@ polar_status polar_attn_prefill_paged(const polar_params *p, polar_dtype dt, int
   return prefill(p, dt, B, C, q, k_cache, v_cache, out, nullptr, nullptr, stream, &src);
 }
 
-polar_status polar_delta_step(const polar_delta_params *p, polar_dtype dt, int32_t B,
-                              float *state_pool, int32_t num_slots, const int32_t *slots,
-                              const void *q, const void *k, const void *v, const float *alpha,
-                              const float *beta, float *out, void *stream) {
+namespace {
+// Checks shared by the step and the sequence entry points.
+polar_status delta_params_ok(const polar_delta_params *p, polar_dtype dt) {
   if (!p) return fail(POLAR_ERR_NULL_POINTER, "params is NULL");
   if (dt != POLAR_DTYPE_F32 && dt != POLAR_DTYPE_BF16)
     return fail(POLAR_ERR_UNSUPPORTED, "unknown dtype %d", (int)dt);
@@ -522,6 +521,15 @@ polar_status polar_delta_step(const polar_delta_params *p, polar_dtype dt, int32
     return fail(POLAR_ERR_UNSUPPORTED, "key_dim and value_dim must be %d", polar::kHeadDim);
   if (p->flags & ~(uint32_t)POLAR_DELTA_NORMALIZE_QK)
     return fail(POLAR_ERR_UNSUPPORTED, "unknown flag bits 0x%x", p->flags);
+  return POLAR_OK;
+}
+}  // namespace
+
+polar_status polar_delta_step(const polar_delta_params *p, polar_dtype dt, int32_t B,
+                              float *state_pool, int32_t num_slots, const int32_t *slots,
+                              const void *q, const void *k, const void *v, const float *alpha,
+                              const float *beta, float *out, void *stream) {
+  if (polar_status st = delta_params_ok(p, dt)) return st;
   if (B < 0) return fail(POLAR_ERR_BAD_SHAPE, "B (%d) must be >= 0", B);
   if (B == 0) return POLAR_OK;
   if (!state_pool || !slots || !q || !k || !v || !alpha || !beta || !out)
@@ -546,6 +554,44 @@ polar_status polar_delta_step(const polar_delta_params *p, polar_dtype dt, int32
   a.normalize = (p->flags & POLAR_DELTA_NORMALIZE_QK) ? 1 : 0;
   hipError_t err = polar::launch_delta_step((int)dt, a, (hipStream_t)stream);
   if (err != hipSuccess) return fail(POLAR_ERR_HIP, "delta step launch: %s", hipGetErrorString(err));
+  return POLAR_OK;
+}
+
+polar_status polar_delta_sequence(const polar_delta_params *p, polar_dtype dt, int32_t B,
+                                  int32_t T, float *state_pool, int32_t num_slots,
+                                  const int32_t *slots, const void *q, const void *k,
+                                  const void *v, const float *alpha, const float *beta,
+                                  float *out, void *stream) {
+  if (polar_status st = delta_params_ok(p, dt)) return st;
+  if (B < 0 || T < 0) return fail(POLAR_ERR_BAD_SHAPE, "B (%d) and T (%d) must be >= 0", B, T);
+  if (B == 0 || T == 0) return POLAR_OK;
+  if (!state_pool || !slots || !q || !k || !v || !alpha || !beta || !out)
+    return fail(POLAR_ERR_NULL_POINTER, "all tensors must be non-NULL");
+  if (num_slots < 1) return fail(POLAR_ERR_BAD_SHAPE, "num_slots (%d) must be >= 1", num_slots);
+  if (2LL * B * p->n_heads > 0x7fffffffLL)
+    return fail(POLAR_ERR_BAD_SHAPE, "B*H too large for one launch");
+  if ((long long)B * T * p->n_heads > (1LL << 56))
+    return fail(POLAR_ERR_BAD_SHAPE, "B*T*H too large");
+  if (!aligned16(state_pool) || !aligned16(q) || !aligned16(k) || !aligned16(v) ||
+      !aligned16(out))
+    return fail(POLAR_ERR_MISALIGNED, "state_pool, q, k, v and out must be 16-byte aligned");
+  polar::DeltaSeqArgs a;
+  a.pool = state_pool;
+  a.slots = slots;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.alpha = alpha;
+  a.beta = beta;
+  a.out = out;
+  a.B = B;
+  a.T = T;
+  a.H = p->n_heads;
+  a.num_slots = num_slots;
+  a.normalize = (p->flags & POLAR_DELTA_NORMALIZE_QK) ? 1 : 0;
+  hipError_t err = polar::launch_delta_sequence((int)dt, a, (hipStream_t)stream);
+  if (err != hipSuccess)
+    return fail(POLAR_ERR_HIP, "delta sequence launch: %s", hipGetErrorString(err));
   return POLAR_OK;
 }
 

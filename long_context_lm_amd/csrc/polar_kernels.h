@@ -95,6 +95,16 @@ struct DeltaArgs {
   int B, H, num_slots, normalize;
 };
 hipError_t launch_delta_step(int dtype, const DeltaArgs &a, hipStream_t stream);
+// The memory stream over T tokens per sequence (states [num_slots,H,d,d] fp32, in place).
+struct DeltaSeqArgs {
+  float *pool;
+  const int32_t *slots;                   // [B]
+  const void *q, *k, *v;                  // [B,T,H,d]
+  const float *alpha, *beta;              // [B,T,H]
+  float *out;                             // [B,T,H,d]
+  int B, T, H, num_slots, normalize;
+};
+hipError_t launch_delta_sequence(int dtype, const DeltaSeqArgs &a, hipStream_t stream);
 
 // Backward pass of the causal prefill (bf16 inputs).  Per-row quantities (float4 each;
 // r0 and r1 of a row are adjacent in `rows`):

@@ -349,6 +349,8 @@ def delta_step(state_pool: torch.Tensor, slots: torch.Tensor, q: torch.Tensor, k
     B = q.shape[0]
     if q.shape != (B, H, dk) or k.shape != q.shape or v.shape != (B, H, dv):
         raise ValueError("q, k must be [B,H,d_k] and v [B,H,d_v] matching the pool")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k and v must share one dtype")
     _check_aux(slots, "slots", dev, torch.int32, (B,))
     alpha = torch.as_tensor(alpha, dtype=torch.float32, device=dev).contiguous()
     beta = torch.as_tensor(beta, dtype=torch.float32, device=dev).contiguous()
@@ -360,4 +362,39 @@ def delta_step(state_pool: torch.Tensor, slots: torch.Tensor, q: torch.Tensor, k
     _lib.check(_lib.polar_delta_step(prm, _DT[q.dtype], B, state_pool.data_ptr(), num_slots,
                                      slots.data_ptr(), q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                      alpha.data_ptr(), beta.data_ptr(), out.data_ptr(), s))
+    return out
+
+
+def delta_sequence(state_pool: torch.Tensor, slots: torch.Tensor, q: torch.Tensor,
+                   k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor, beta: torch.Tensor,
+                   normalize_qk: bool = True, stream=None) -> torch.Tensor:
+    """The memory stream over T tokens (see polar_delta_sequence): runs the gated-delta step
+    for t = 0..T-1 on state_pool[slots[b]] in place and returns o [B,T,H,d_v] (float32).
+    q, k [B,T,H,d_k]; v [B,T,H,d_v]; alpha, beta [B,T,H]."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check_input(t, n)
+    dev = q.device
+    _check_aux(state_pool, "state_pool", dev, torch.float32)
+    if state_pool.dim() != 4:
+        raise ValueError("state_pool must be [num_slots,H,d_v,d_k]")
+    num_slots, H, dv, dk = state_pool.shape
+    if q.dim() != 4:
+        raise ValueError("q must be [B,T,H,d_k]")
+    B, T = q.shape[:2]
+    if q.shape != (B, T, H, dk) or k.shape != q.shape or v.shape != (B, T, H, dv):
+        raise ValueError("q, k must be [B,T,H,d_k] and v [B,T,H,d_v] matching the pool")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k and v must share one dtype")
+    _check_aux(slots, "slots", dev, torch.int32, (B,))
+    alpha = torch.as_tensor(alpha, dtype=torch.float32, device=dev).contiguous()
+    beta = torch.as_tensor(beta, dtype=torch.float32, device=dev).contiguous()
+    _check_aux(alpha, "alpha", dev, torch.float32, (B, T, H))
+    _check_aux(beta, "beta", dev, torch.float32, (B, T, H))
+    out = torch.empty(B, T, H, dv, device=dev, dtype=torch.float32)
+    prm = _lib.polar_delta_params(H, dk, dv, _lib.POLAR_DELTA_NORMALIZE_QK if normalize_qk else 0)
+    s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+    _lib.check(_lib.polar_delta_sequence(prm, _DT[q.dtype], B, T, state_pool.data_ptr(),
+                                         num_slots, slots.data_ptr(), q.data_ptr(), k.data_ptr(),
+                                         v.data_ptr(), alpha.data_ptr(), beta.data_ptr(),
+                                         out.data_ptr(), s))
     return out

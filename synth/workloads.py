@@ -409,3 +409,30 @@ def delta_inputs(B: int = 256, H: int = 16, num_slots: int = 1024, d_k: int = 64
     if dtype == "bf16":
         q, k, v = round_bf16(q), round_bf16(k), round_bf16(v)
     return DeltaInputs(dtype=dtype, pool=pool, slots=slots, q=q, k=k, v=v, alpha=alpha, beta=beta)
+
+
+@dataclasses.dataclass
+class DeltaSeqInputs(DeltaInputs):
+    """The memory stream over T tokens for B sequences: q, k [B,T,H,d_k], v [B,T,H,d_v],
+    alpha, beta [B,T,H]; pool and slots as for one step."""
+
+
+def delta_seq_inputs(B: int = 32, T: int = 2048, H: int = 16, num_slots: int = 64,
+                     d_k: int = 64, d_v: int = 64, dtype: str = "bf16", seed: int = 4101,
+                     alpha_range=(0.9, 1.0)) -> DeltaSeqInputs:
+    """A prompt or training sequence through the recurrent memory: the step's
+    distributions (states N(0, 1/d_k), q, k, v N(0, 1), beta ~ U(0, 1)) drawn per token,
+    gates alpha ~ U(alpha_range) per (token, head), B distinct slots."""
+    s = np.random.SeedSequence(seed).spawn(6)
+    pool = (_normal(s[0], (num_slots, H, d_v, d_k)) / np.float32(np.sqrt(d_k))).astype(np.float32)
+    q = _normal(s[1], (B, T, H, d_k))
+    k = _normal(s[2], (B, T, H, d_k))
+    v = _normal(s[3], (B, T, H, d_v))
+    g = np.random.Generator(np.random.PCG64(s[4]))
+    alpha = g.uniform(alpha_range[0], alpha_range[1], (B, T, H)).astype(np.float32)
+    beta = g.uniform(0.0, 1.0, (B, T, H)).astype(np.float32)
+    slots = np.random.Generator(np.random.PCG64(s[5])).permutation(num_slots)[:B].astype(np.int32)
+    if dtype == "bf16":
+        q, k, v = round_bf16(q), round_bf16(k), round_bf16(v)
+    return DeltaSeqInputs(dtype=dtype, pool=pool, slots=slots, q=q, k=k, v=v, alpha=alpha,
+                          beta=beta)

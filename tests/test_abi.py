@@ -23,7 +23,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(_lib.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert _lib.polar_abi_version() == 3
+    assert _lib.polar_abi_version() == 4
 
 
 def test_status_strings():
@@ -345,6 +345,43 @@ def test_delta_step_empty_and_null_params():
     assert dstep(B=0, pool=None, slots=None, q=None) == _lib.POLAR_OK
     lib = _lib.load()
     assert lib.polar_delta_step(None, 1, 1, A, 1, A, A, A, A, A, A, A, None) == \
+        _lib.POLAR_ERR_NULL_POINTER
+
+
+def dseq(H=4, dk=64, dv=64, flags=1, dt=1, B=3, T=100, pool=A, num_slots=8, slots=A, q=A, k=A,
+         v=A, al=A, be=A, out=A):
+    prm = _lib.polar_delta_params(H, dk, dv, flags)
+    return _lib.polar_delta_sequence(prm, dt, B, T, pool, num_slots, slots, q, k, v, al, be, out,
+                                     None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dk=32), _lib.POLAR_ERR_UNSUPPORTED),
+    (dict(dv=128), _lib.POLAR_ERR_UNSUPPORTED),
+    (dict(flags=2), _lib.POLAR_ERR_UNSUPPORTED),
+    (dict(dt=3), _lib.POLAR_ERR_UNSUPPORTED),
+    (dict(H=0), _lib.POLAR_ERR_BAD_SHAPE),
+    (dict(B=-1), _lib.POLAR_ERR_BAD_SHAPE),
+    (dict(T=-1), _lib.POLAR_ERR_BAD_SHAPE),
+    (dict(num_slots=0), _lib.POLAR_ERR_BAD_SHAPE),
+    (dict(B=1 << 30, H=4), _lib.POLAR_ERR_BAD_SHAPE),
+    (dict(slots=None), _lib.POLAR_ERR_NULL_POINTER),
+    (dict(k=None), _lib.POLAR_ERR_NULL_POINTER),
+    (dict(al=None), _lib.POLAR_ERR_NULL_POINTER),
+    (dict(pool=A + 4), _lib.POLAR_ERR_MISALIGNED),
+    (dict(v=A + 8), _lib.POLAR_ERR_MISALIGNED),
+    (dict(out=A + 8), _lib.POLAR_ERR_MISALIGNED),
+])
+def test_delta_sequence_validation_errors(kw, code):
+    assert dseq(**kw) == code
+    assert _lib.polar_last_error() != ""
+
+
+def test_delta_sequence_empty_and_null_params():
+    assert dseq(B=0, pool=None, slots=None, q=None) == _lib.POLAR_OK
+    assert dseq(T=0, pool=None, slots=None, q=None) == _lib.POLAR_OK
+    lib = _lib.load()
+    assert lib.polar_delta_sequence(None, 1, 1, 1, A, 1, A, A, A, A, A, A, A, None) == \
         _lib.POLAR_ERR_NULL_POINTER
 
 
