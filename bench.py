@@ -16,13 +16,16 @@ forward count).
 Besides the headline pair, the JSON line carries one object per further leg, each with its
 own roofline and, unless ``--no-cpu-baseline``, the oracle timed beside it: the forward at
 the 2K training shape and at 16K (``prefill_c2``, ``prefill_c3``), the variant modes, the
-paged chunk, the one-sequence decode, the backward and the memory step.
+paged chunk, the one-sequence decode, the backward, the memory step and the memory stream
+over whole sequences (``memory_sequence``, fp32 TFLOP/s of 7 d^2 per token and head).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                        [--legs all|LEG,LEG...]  (a subset of the extra legs, for profiling)
        python bench.py --copy-probe BYTES   (plain device copy, for counter calibration)
        python bench.py --memory-step-probe fused|ref --steps K
                                             (one form of the memory step, for counters)
+       python bench.py --memory-sequence-probe --steps K
+                                            (the memory-stream launch alone, for counters)
 """
 from __future__ import annotations
 
@@ -42,6 +45,7 @@ sys.path.insert(0, ROOT)
 METRIC = "Polar attn fwd TFLOP/s (bf16, T=64K) + paged decode GB/s at 256K KV"
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
+PEAK_FP32_TFLOPS = 157.3        # MI355X fp32 vector (published; counts packed fp32 FMA)
 
 
 # Sources each timed kernel is built from; a counter record stays valid while these are unchanged.
@@ -59,6 +63,7 @@ KERNEL_SOURCES = {
     "paged": _PREFILL_SRC,
     "append": ["polar_paged.hip", "polar_kernels.h"],
     "memory_step": ["polar_delta.hip", "polar_kernels.h"],
+    "memory_sequence": ["polar_delta.hip", "polar_kernels.h"],
 }
 
 
@@ -542,6 +547,102 @@ def measure_memory_step(dev, steps: int, warmup: int, with_cpu: bool = False):
     return rec
 
 
+SEQ_SHAPE = dict(B=32, T=2048, H=16)       # 32 training sequences of 2K tokens, 16 heads
+
+
+def delta_seq_flops(B, T, H, d=64):
+    """Algorithmic fp32 work of the memory stream: per (token, head) S k and S q (2 d^2
+    flops each) and S' = alpha S + u k^T (3 d^2), 7 d^2 in all."""
+    return 7.0 * d * d * B * T * H
+
+
+def _delta_seq_setup(dev):
+    import torch
+    import synth
+    d = synth.delta_seq_inputs(**SEQ_SHAPE, num_slots=64, dtype="bf16")
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    return d, (torch.from_numpy(d.pool).to(dev), torch.from_numpy(d.slots).to(dev), bf(d.q),
+               bf(d.k), bf(d.v), torch.from_numpy(d.alpha).to(dev), torch.from_numpy(d.beta).to(dev))
+
+
+def measure_memory_sequence(dev, steps: int, warmup: int, with_cpu: bool = False):
+    """The memory stream over 32 sequences x 2048 tokens x 16 heads in one launch, and the
+    same tokens as 2048 chained one-step launches beside it."""
+    import torch
+    from long_context_lm_amd import delta_sequence, delta_step
+    d, (pool, sl, q, k, v, al, be) = _delta_seq_setup(dev)
+    B, T, H = SEQ_SHAPE["B"], SEQ_SHAPE["T"], SEQ_SHAPE["H"]
+    for _ in range(warmup):
+        delta_sequence(pool, sl, q, k, v, al, be)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for e in ev:
+        e[0].record()
+        delta_sequence(pool, sl, q, k, v, al, be)
+        e[1].record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    # The same work as T step launches on per-token slices laid out beforehand.
+    qt, kt, vt = (x.transpose(0, 1).contiguous() for x in (q, k, v))
+    at, bt = al.transpose(0, 1).contiguous(), be.transpose(0, 1).contiguous()
+    delta_step(pool, sl, qt[0], kt[0], vt[0], at[0], bt[0])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for t in range(T):
+        delta_step(pool, sl, qt[t], kt[t], vt[t], at[t], bt[t])
+    e1.record()
+    torch.cuda.synchronize()
+    chained_ms = e0.elapsed_time(e1)
+    del qt, kt, vt, at, bt
+    fl = delta_seq_flops(B, T, H)
+    tf = fl / (ms * 1e-3) / 1e12
+    print(f"[bench] memory sequence: {ms:.3f} ms ({tf:.1f} TFLOP/s, "
+          f"{B * T / (ms * 1e-3) / 1e6:.1f} M tokens/s), {T} chained steps {chained_ms:.2f} ms",
+          file=sys.stderr, flush=True)
+    rec = {"workload": f"gated-delta memory stream over {B} sequences x {T} tokens x {H} heads, "
+                       "64x64 fp32 states in a 64-slot pool, bf16 q/k/v",
+           "value": round(tf, 2), "unit": "TFLOP/s", "ms": round(ms, 4),
+           "tokens_per_s": round(B * T / (ms * 1e-3), 0),
+           "chained_steps_ms": round(chained_ms, 3),
+           "roofline": {"bound": "alu", "achieved": round(tf, 2), "peak": PEAK_FP32_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(tf / PEAK_FP32_TFLOPS, 4),
+                        "traffic": traffic_record("memory_sequence")}}
+    if with_cpu:
+        def job():
+            import oracle
+            import synth
+            nb = 4
+            q1, k1, v1 = (synth.bf16_bits_to_f32(x[:nb]) for x in (d.q, d.k, d.v))
+            t0 = time.perf_counter()
+            oracle.delta_sequence_pool(d.pool, d.slots[:nb], q1, k1, v1, d.alpha[:nb],
+                                       d.beta[:nb])
+            t = time.perf_counter() - t0
+            rec["cpu_baseline"] = {"value": round(delta_seq_flops(nb, T, H) / t / 1e12, 6),
+                                   "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
+                                   "cpu": cpu_model(),
+                                   "sample": f"float64 stream of {nb} of the {B} sequences, all "
+                                             f"{T} tokens and {H} heads ({t:.1f} s)"}
+        CPU_JOBS.append(job)
+    return rec
+
+
+def memory_sequence_probe(steps: int):
+    """Run only the memory-stream launch (for per-launch HBM counters)."""
+    import torch
+    from long_context_lm_amd import _lib, delta_sequence
+    _lib.load()
+    d, (pool, sl, q, k, v, al, be) = _delta_seq_setup("cuda")
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        delta_sequence(pool, sl, q, k, v, al, be)
+    torch.cuda.synchronize()
+    print(json.dumps({"memory_sequence_probe": True, "steps": steps}))
+
+
 def memory_step_probe(which: str, steps: int):
     """Run only one form of the memory step (for per-step HBM counters)."""
     import torch
@@ -567,7 +668,8 @@ def copy_probe(nbytes: int):
     print(json.dumps({"copy_probe_bytes": nbytes}))
 
 
-EXTRA_LEGS = ("c2", "c3", "variants", "paged", "decode_b1", "backward", "memory_step")
+EXTRA_LEGS = ("c2", "c3", "variants", "paged", "decode_b1", "backward", "memory_step",
+              "memory_sequence")
 
 
 def main():
@@ -581,6 +683,7 @@ def main():
                          + ",".join(EXTRA_LEGS))
     ap.add_argument("--copy-probe", type=int, default=0)
     ap.add_argument("--memory-step-probe", choices=("fused", "ref"), default=None)
+    ap.add_argument("--memory-sequence-probe", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the Polar Attention path here is a single-GPU "
@@ -592,6 +695,9 @@ def main():
         return
     if args.memory_step_probe:
         memory_step_probe(args.memory_step_probe, args.steps)
+        return
+    if args.memory_sequence_probe:
+        memory_sequence_probe(args.steps)
         return
 
     import torch
@@ -699,6 +805,9 @@ def main():
         rec["backward"] = measure_backward(dev, max(1, args.steps // 2), args.warmup, cpu)
     if "memory_step" in legs:
         rec["memory_step"] = measure_memory_step(dev, args.steps, args.warmup, cpu)
+    if "memory_sequence" in legs:
+        torch.cuda.empty_cache()
+        rec["memory_sequence"] = measure_memory_sequence(dev, args.steps, args.warmup, cpu)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on bounded samples", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(pre, dec)
