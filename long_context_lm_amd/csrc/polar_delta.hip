@@ -16,6 +16,9 @@
 // over those 16 lanes in a fixed order that leaves the same value in all of them.
 #include "polar_kernels.h"
 
+#include <type_traits>
+
+
 namespace polar {
 namespace {
 
@@ -151,25 +154,30 @@ __global__ void __launch_bounds__(256) polar_delta_step_kernel(DeltaArgs a) {
 // The memory stream over a sequence: the same step for tokens t = 0..T-1 in order, the
 // state held in registers from its single read to its single write, o_t for every token.
 //
-// A workgroup of 4 waves owns one half (32 rows of d_v) of one (sequence, head) state; the
-// rows of the gated delta rule are independent given k, q and the row's v, so the two
-// halves need no communication.  Wave w holds rows 8 w .. 8 w + 7 of its half, lane l
-// columns 8 (l % 8) .. + 7 of row 8 w + l / 8: the row sums S k and S q reduce over the 8
-// lanes of a DPP half-row.  Tokens pass through LDS in chunks of C: the workgroup loads a
-// chunk's q and k (64 dims), v (its 32 rows), alpha and beta (256 / C threads per token),
-// L2-normalises q and k there (the step's x / sqrt(x.x + 1e-12)) and forms k.q once per
-// token; the next chunk's loads are issued before the current chunk is walked.  The walk
-// is the step's arithmetic, u = beta (v - alpha S k), o = alpha S q + u (k.q),
-// S' = alpha S + u k^T, token after token.  Tokens past the end of the sequence are staged
-// as alpha = 1, beta = 0, k = q = v = 0, which leaves S bit-for-bit unchanged, so every
-// chunk is walked in full.  o is identical in the 8 lanes of a row; over 8 tokens lane
-// c keeps the o of token c and writes it to LDS, and the chunk leaves in 128-byte rows.
-// Sum over the 8 lanes of a DPP half-row (every lane gets the same bits).
-__device__ __forceinline__ float row8_sum(float x) {
-  x = dpp_sum_step<0xB1>(x);    // quad_perm 1,0,3,2
-  x = dpp_sum_step<0x4E>(x);    // quad_perm 2,3,0,1
-  return dpp_sum_step<0x141>(x);  // row_half_mirror: quads 0<->1, 2<->3
-}
+// A workgroup of 4 waves owns one (sequence, head) state.  Lane l of wave w holds columns
+// CPL (l % LPR) .. + CPL - 1 of row CPL w + l / LPR (CPL = 16 columns, LPR = 4 lanes per
+// row): the row sums S k and S q reduce over the LPR lanes of a DPP quad.  Tokens pass
+// through LDS in chunks of C: the workgroup loads a chunk's q, k and v (64 dims each),
+// alpha and beta (256 / C threads per token), L2-normalises q and k there (the step's
+// x / sqrt(x.x + 1e-12)) and forms k.q once per token; the next chunk's loads are issued
+// before the current chunk is walked.  Sixteen columns per lane keep the per-token
+// overhead (two DPP steps per row sum, the scalars u and o) small beside the three
+// multiply-adds per state element; the arithmetic, not LDS, bounds the walk.
+//
+// The walk takes tokens in groups of 8 and defers the gate: with g_j the product of the
+// group's alpha up to token j and S = g_j R, the step u = beta (v - alpha S k),
+// o = alpha S q + u (k.q), S' = alpha S + u k^T becomes
+//   u = beta v - (beta g_j) (R k),   o = g_j (R q) + u (k.q),   R' = R + (u / g_j) k^T,
+// one multiply-add per state element per token instead of a multiply and a multiply-add;
+// S = g_7 R is restored at the end of the group.  The step's value is unchanged up to fp32
+// rounding.  A group where a running gate product leaves [2^-64, 2^64] (or is not a
+// number) takes the step as written, so no input overflows the deferred form.
+//
+// Tokens past the end of the sequence are staged as alpha = 1, beta = 0, k = q = v = 0,
+// which leaves the state bit-for-bit unchanged, so every chunk is walked in full.  o is
+// identical in the LPR lanes of a row; over a group lane c keeps the o of tokens c, c + 4,
+// writes them to LDS, and the chunk leaves in 256-byte rows.
+
 // Sum over groups of N (2, 4 or 8) neighbouring lanes.
 template <int N>
 __device__ __forceinline__ float group_sum(float x) {
@@ -179,8 +187,10 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// Per-token constants of the walk.  Deferred form: c1 = beta g, g, rg = 1 / g.  Step as
+// written: c1 = beta alpha, g = alpha, rg unused.  vs holds beta v in both.
 struct SeqTok {
-  float alpha, beta, kq, pad;
+  float c1, g, rg, kq;
 };
 
 // N consecutive elements of E, held raw between the global load and the conversion.
@@ -224,33 +234,40 @@ struct RawVec {
   }
 };
 
-template <class E, int C>
+template <class E, int C, int CPL>
 __global__ void __launch_bounds__(256) polar_delta_seq_kernel(DeltaSeqArgs a) {
   constexpr int D = kHeadDim;
+  constexpr int LPR = D / CPL;        // lanes per state row (the row sums reduce over them)
+  constexpr int RW = 4 * CPL;         // state rows per workgroup (4 waves, a row per lane)
+  constexpr int NP = D / RW;          // workgroups per state
+  constexpr int NSL = 8 / LPR;        // tokens of a group whose o one lane keeps
   constexpr int TPT = 256 / C;        // staging threads per token
   constexpr int DPT = D / TPT;        // q and k dims per staging thread
-  constexpr int VPT = 32 / TPT;       // v rows per staging thread
-  constexpr int OP = 36;              // o row pitch in LDS (16-byte aligned, spreads banks)
-  static_assert(C % 8 == 0 && TPT >= 2 && TPT <= 8, "chunk of 32..128 tokens");
-  __shared__ __attribute__((aligned(16))) float ks[C][D], qs[C][D], vs[C][32], os[C][OP];
+  constexpr int VPT = RW / TPT;       // v rows per staging thread
+  constexpr int OP = RW + 4;          // o row pitch in LDS (16-byte aligned, spreads banks)
+  static_assert(C % 8 == 0 && TPT >= 2 && TPT <= 8 && VPT >= 4, "chunk of 32..128 tokens");
+  static_assert(CPL == 8 || CPL == 16, "8 or 16 columns per lane");
+  __shared__ __attribute__((aligned(16))) float ks[C][D], qs[C][D], vs[C][RW], os[C][OP];
   __shared__ __attribute__((aligned(16))) SeqTok tk[C];
+  __shared__ int direct[C / 8];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int half = blockIdx.x & 1, bh = blockIdx.x >> 1;
+  const int part = blockIdx.x % NP, bh = blockIdx.x / NP;
   const int b = bh / a.H, h = bh % a.H;
   const int slot = a.slots[b];
   const bool ok = slot >= 0 && slot < a.num_slots;      // uniform over the workgroup
-  const int rl = wave * 8 + (lane >> 3), cg = lane & 7;   // walk: row in the half, columns
+  const int cg = lane % LPR;                              // walk: columns CPL cg .. + CPL-1
+  const int rw = wave * CPL + lane / LPR;                 // walk: row in the workgroup
   const int tt = tid / TPT, tq = tid % TPT;               // staging: token, part
 
-  float S[8];
+  float S[CPL];
   float *const sp =
-      a.pool + (((size_t)(ok ? slot : 0) * a.H + h) * D + half * 32 + rl) * D + cg * 8;
+      a.pool + (((size_t)(ok ? slot : 0) * a.H + h) * D + part * RW + rw) * D + cg * CPL;
   if (ok) {
-    const f32x4 s0 = *(const f32x4 *)sp, s1 = *(const f32x4 *)(sp + 4);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      S[e] = s0[e];
-      S[4 + e] = s1[e];
+    for (int c = 0; c < CPL / 4; ++c) {
+      const f32x4 x = *(const f32x4 *)(sp + 4 * c);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S[4 * c + e] = x[e];
     }
   }
 
@@ -266,7 +283,7 @@ __global__ void __launch_bounds__(256) polar_delta_seq_kernel(DeltaSeqArgs a) {
       const size_t tok = ((size_t)b * a.T + t) * a.H + h;
       rq.load((const E *)a.q + tok * D + DPT * tq);
       rk.load((const E *)a.k + tok * D + DPT * tq);
-      rv.load((const E *)a.v + tok * D + half * 32 + VPT * tq);
+      rv.load((const E *)a.v + tok * D + part * RW + VPT * tq);
       al = a.alpha[tok];
       be = a.beta[tok];
     }
@@ -289,6 +306,7 @@ __global__ void __launch_bounds__(256) polar_delta_seq_kernel(DeltaSeqArgs a) {
     kq = group_sum<TPT>(kq);
     const float rk = a.normalize ? rsqrtf(kk + 1e-12f) : 1.0f;
     const float rq = a.normalize ? rsqrtf(qq + 1e-12f) : 1.0f;
+    const float alive = live ? al : 1.0f, blive = live ? be : 0.0f;
     // A padded token's registers hold an earlier token (or zeros): select, never scale.
 #pragma unroll
     for (int i = 0; i < DPT / 4; ++i) {
@@ -305,12 +323,92 @@ __global__ void __launch_bounds__(256) polar_delta_seq_kernel(DeltaSeqArgs a) {
     for (int i = 0; i < VPT / 4; ++i) {
       f32x4 vw;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) vw[e] = live ? vf[4 * i + e] : 0.0f;
+      for (int e = 0; e < 4; ++e) vw[e] = live ? blive * vf[4 * i + e] : 0.0f;
       *(f32x4 *)&vs[tt][VPT * tq + 4 * i] = vw;
     }
-    if (tq == 0) tk[tt] = live ? SeqTok{al, be, kq * rk * rq, 0.f} : SeqTok{1.f, 0.f, 0.f, 0.f};
+    // The group of 8 tokens holding token tt lies in 8 TPT consecutive lanes of this wave
+    // (token j of the group at lanes base + j TPT): the gate products g_j and the group's
+    // g_7 are formed in the same order in every lane.
+    const int j = tt & 7, base = (lane / (8 * TPT)) * (8 * TPT);
+    float g = 1.0f, g7 = 1.0f;
+    bool tame = true;                       // every running product in [2^-64, 2^64]
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float ai = __shfl(alive, base + i * TPT);
+      g7 *= ai;
+      g = i <= j ? g7 : g;
+      tame = tame && g7 >= 0x1p-64f && g7 <= 0x1p64f;   // false for a NaN gate
+    }
+    const bool dir = !tame;
+    if (tq == 0) {
+      const float kqn = live ? kq * rk * rq : 0.0f;
+      tk[tt] = dir ? SeqTok{blive * alive, alive, 0.0f, kqn}
+                   : SeqTok{blive * g, g, 1.0f / g, kqn};
+      if (j == 0) direct[tt >> 3] = dir ? 1 : 0;
+    }
     // Every load of this chunk has been consumed: no global load is in flight past here.
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  };
+
+  // One group of 8 tokens from token t0 of the chunk.
+  struct Tok {
+    f32x4 k[CPL / 4], q[CPL / 4];
+    SeqTok c;
+    float bv;
+  };
+  auto read_tok = [&](int t, Tok &x) {
+#pragma unroll
+    for (int c = 0; c < CPL / 4; ++c) {
+      x.k[c] = *(const f32x4 *)&ks[t][cg * CPL + 4 * c];
+      x.q[c] = *(const f32x4 *)&qs[t][cg * CPL + 4 * c];
+    }
+    x.c = tk[t];
+    x.bv = vs[t][rw];
+  };
+  auto walk_group = [&](int t0, auto deferred) {
+    constexpr bool kDeferred = decltype(deferred)::value;
+    float osel[NSL], g7 = 1.0f;
+#pragma unroll
+    for (int n = 0; n < NSL; ++n) osel[n] = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      Tok cur;
+      read_tok(t0 + jj, cur);
+      float sk0 = 0.f, sk1 = 0.f, sq0 = 0.f, sq1 = 0.f;
+#pragma unroll
+      for (int c = 0; c < CPL / 4; c += 2)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sk0 = fmaf(S[4 * c + e], cur.k[c][e], sk0);
+          sk1 = fmaf(S[4 * c + 4 + e], cur.k[c + 1][e], sk1);
+          sq0 = fmaf(S[4 * c + e], cur.q[c][e], sq0);
+          sq1 = fmaf(S[4 * c + 4 + e], cur.q[c + 1][e], sq1);
+        }
+      const float sk = group_sum<LPR>(sk0 + sk1), sq = group_sum<LPR>(sq0 + sq1);
+      const float u = fmaf(-cur.c.c1, sk, cur.bv);
+      const float o = fmaf(cur.c.g, sq, u * cur.c.kq);
+      osel[jj / LPR] = cg == jj % LPR ? o : osel[jj / LPR];
+      if constexpr (kDeferred) {
+        const float w = u * cur.c.rg;
+#pragma unroll
+        for (int c = 0; c < CPL / 4; ++c)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) S[4 * c + e] = fmaf(w, cur.k[c][e], S[4 * c + e]);
+      } else {
+#pragma unroll
+        for (int c = 0; c < CPL / 4; ++c)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            S[4 * c + e] = fmaf(u, cur.k[c][e], cur.c.g * S[4 * c + e]);
+      }
+      g7 = cur.c.g;
+    }
+    if constexpr (kDeferred) {
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) S[e] *= g7;
+    }
+#pragma unroll
+    for (int n = 0; n < NSL; ++n) os[t0 + n * LPR + cg][rw] = osel[n];
   };
 
   fetch(0);
@@ -320,41 +418,16 @@ __global__ void __launch_bounds__(256) polar_delta_seq_kernel(DeltaSeqArgs a) {
     if (c0 + C < a.T) fetch(c0 + C);          // lands while this chunk is walked
     if (ok) {
       for (int t0 = 0; t0 < C; t0 += 8) {
-        float osel = 0.f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int t = t0 + j;
-          const f32x4 k0 = *(const f32x4 *)&ks[t][cg * 8];
-          const f32x4 k1 = *(const f32x4 *)&ks[t][cg * 8 + 4];
-          const f32x4 q0 = *(const f32x4 *)&qs[t][cg * 8];
-          const f32x4 q1 = *(const f32x4 *)&qs[t][cg * 8 + 4];
-          const SeqTok tok = tk[t];
-          const float vr = vs[t][rl];
-          float sk0 = 0.f, sk1 = 0.f, sq0 = 0.f, sq1 = 0.f;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            sk0 = fmaf(S[e], k0[e], sk0);
-            sk1 = fmaf(S[4 + e], k1[e], sk1);
-            sq0 = fmaf(S[e], q0[e], sq0);
-            sq1 = fmaf(S[4 + e], q1[e], sq1);
-          }
-          const float sk = row8_sum(sk0 + sk1), sq = row8_sum(sq0 + sq1);
-          const float u = tok.beta * (vr - tok.alpha * sk);
-          const float o = tok.alpha * sq + u * tok.kq;
-          osel = cg == j ? o : osel;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            S[e] = fmaf(u, k0[e], tok.alpha * S[e]);
-            S[4 + e] = fmaf(u, k1[e], tok.alpha * S[4 + e]);
-          }
-        }
-        os[t0 + cg][rl] = osel;
+        if (__builtin_amdgcn_readfirstlane(direct[t0 >> 3]))
+          walk_group(t0, std::false_type{});
+        else
+          walk_group(t0, std::true_type{});
       }
     }
     __syncthreads();
     // The chunk's outputs: TPT threads per token, VPT floats each.
     if (c0 + tt < a.T) {
-      float *op = a.out + (((size_t)b * a.T + c0 + tt) * a.H + h) * D + half * 32 + VPT * tq;
+      float *op = a.out + (((size_t)b * a.T + c0 + tt) * a.H + h) * D + part * RW + VPT * tq;
 #pragma unroll
       for (int i = 0; i < VPT / 4; ++i)
         *(f32x4 *)(op + 4 * i) =
@@ -362,23 +435,25 @@ __global__ void __launch_bounds__(256) polar_delta_seq_kernel(DeltaSeqArgs a) {
     }
   }
   if (ok) {
-    *(f32x4 *)sp = f32x4{S[0], S[1], S[2], S[3]};
-    *(f32x4 *)(sp + 4) = f32x4{S[4], S[5], S[6], S[7]};
+#pragma unroll
+    for (int c = 0; c < CPL / 4; ++c)
+      *(f32x4 *)(sp + 4 * c) = f32x4{S[4 * c], S[4 * c + 1], S[4 * c + 2], S[4 * c + 3]};
   }
 }
 
 }  // namespace
 
 hipError_t launch_delta_sequence(int dtype, const DeltaSeqArgs &a, hipStream_t stream) {
-  constexpr int C = 64;   // tokens per chunk
-  const long long wgs = 2LL * a.B * a.H;
+  constexpr int C = 32;     // tokens per chunk (34 KB of LDS)
+  constexpr int CPL = 16;   // state columns per lane: one workgroup per state
+  const long long wgs = (long long)(kHeadDim / (4 * CPL)) * a.B * a.H;
   if (wgs <= 0 || a.T <= 0) return hipSuccess;
   if (dtype == 1)
-    hipLaunchKernelGGL((polar_delta_seq_kernel<uint16_t, C>), dim3((unsigned)wgs), dim3(256), 0,
-                       stream, a);
+    hipLaunchKernelGGL((polar_delta_seq_kernel<uint16_t, C, CPL>), dim3((unsigned)wgs),
+                       dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((polar_delta_seq_kernel<float, C>), dim3((unsigned)wgs), dim3(256), 0,
-                       stream, a);
+    hipLaunchKernelGGL((polar_delta_seq_kernel<float, C, CPL>), dim3((unsigned)wgs), dim3(256),
+                       0, stream, a);
   return hipGetLastError();
 }
 
