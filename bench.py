@@ -26,6 +26,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                                             (one form of the memory step, for counters)
        python bench.py --memory-sequence-probe --steps K
                                             (the memory-stream launch alone, for counters)
+       python bench.py --counter-summary DIR  (profiles/ summaries from a rocprofv3 run)
 """
 from __future__ import annotations
 
@@ -64,6 +65,7 @@ KERNEL_SOURCES = {
     "append": ["polar_paged.hip", "polar_kernels.h"],
     "memory_step": ["polar_delta.hip", "polar_kernels.h"],
     "memory_sequence": ["polar_delta.hip", "polar_kernels.h"],
+    "fwd_train": _PREFILL_SRC,          # the training forward beside the backward
 }
 
 
@@ -668,6 +670,260 @@ def copy_probe(nbytes: int):
     print(json.dumps({"copy_probe_bytes": nbytes}))
 
 
+# ------------------------------------------------------------------ counter summaries
+# Which dispatches make up each leg: (kernel-name pattern, grid size or None, duration
+# class).  Dispatches of one kernel and grid are split into classes where their sorted
+# durations jump by more than 1.6x (the 2K and 16K forwards share a grid, as do the full
+# and windowed variants); class -1 is the longest, 0 the shortest.
+LEG_KERNELS = {
+    "prefill": [(r"polar_prefill_kernel<Bf16, 1, 8, 0,", 2097152, -1)],
+    "decode": [(r"polar_decode_split_kernel<Bf16>", 262144, -1),
+               (r"polar_decode_combine_kernel", 262144, -1)],
+    "variant": [(r"polar_rope_keys_kernel<unsigned short>", None, -1),
+                (r"polar_prefill_kernel<Bf16, 1, 8, 2,", 2097152, -1)],
+    "variant_window": [(r"polar_rope_keys_kernel<unsigned short>", None, -1),
+                       (r"polar_prefill_kernel<Bf16, 1, 8, 2,", 2097152, 0)],
+    "paged": [(r"polar_prefill_kernel<Bf16, 1, 16, 3,", None, -1)],
+    "append": [(r"polar_kv_append_kernel", None, -1)],
+    "prefill_c2": [(r"polar_prefill_kernel<Bf16, 1, 8, 0,", 524288, 0)],
+    "prefill_c3": [(r"polar_prefill_kernel<Bf16, 1, 8, 0,", 524288, -1)],
+    "decode_b1": [(r"polar_decode_split_kernel<Bf16>", 131072, -1),
+                  (r"polar_decode_combine_kernel", 16384, -1)],
+    "backward": [(r"polar_bwd_prep_kernel", None, -1), (r"polar_bwd_dq_kernel", None, -1),
+                 (r"polar_bwd_dkv_kernel", None, -1), (r"polar_bwd_dkv_add_kernel", None, -1),
+                 (r"polar_bwd_param_kernel", None, -1),
+                 (r"polar_bwd_param_final_kernel", None, -1)],
+    "fwd_train": [(r"polar_prefill_kernel<Bf16, 1, 8, 1,", None, -1)],
+    "memory_step": [(r"polar_delta_step_kernel<unsigned short, 4>", 262144, -1)],
+    "memory_sequence": [(r"polar_delta_seq_kernel<unsigned short,", None, -1)],
+}
+LEG_WORKLOAD = {
+    "prefill": "causal prefill B=1 T=65536 Hq=16 Hkv=4 d=64 bf16",
+    "decode": "paged decode B=16 L=262144 Hq=16 Hkv=4 d=64 page 64",
+    "variant": "RoPE + softmax-output variant prefill, T=65536 (key rotation included)",
+    "variant_window": "the same with a 4096-key window",
+    "paged": "last 4096-token chunk of T=65536 from 64-token pages",
+    "append": "KV append of that 4096-token chunk",
+    "prefill_c2": "causal prefill B=8 T=2048 (training shape)",
+    "prefill_c3": "causal prefill B=1 T=16384",
+    "decode_b1": "paged decode B=1 L=262144",
+    "backward": "backward B=8 T=2048, all cotangents, parameter gradients",
+    "fwd_train": "training forward B=8 T=2048 (saves lse, S, Q for the backward)",
+    "memory_step": "gated-delta step, 256 sequences x 16 heads",
+    "memory_sequence": "gated-delta stream, 32 sequences x 2048 tokens x 16 heads",
+}
+# Algorithmic bf16 flops of the legs whose MFMA counters are summarised.
+LEG_FLOPS = {"prefill": lambda: prefill_flops(1, 65536, 16, 64),
+             "prefill_c2": lambda: prefill_flops(8, 2048, 16, 64),
+             "prefill_c3": lambda: prefill_flops(1, 16384, 16, 64),
+             "fwd_train": lambda: prefill_flops(8, 2048, 16, 64),
+             "backward": lambda: backward_flops(8, 2048, 16, 64)}
+N_SIMD = 1024                    # 256 CUs x 4 SIMDs
+NOMINAL_GHZ = 2.4
+
+
+def _kernel_short(name: str) -> str:
+    """Demangled kernel name without namespaces and without the parameter list."""
+    name = name.replace("polar::(anonymous namespace)::", "").replace("polar::", "")
+    name = name.replace("void ", "")
+    depth = 0
+    for i in range(len(name) - 1, -1, -1):
+        if name[i] == ")":
+            depth += 1
+        elif name[i] == "(":
+            depth -= 1
+            if depth == 0:
+                return name[:i]
+    return name
+
+
+def _read_dispatches(path: str):
+    """{dispatch id: {"name", "grid", "ns", counter: value}} from a rocprofv3 CSV (kernel
+    trace or counter collection)."""
+    import csv
+    out = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            d = int(r["Dispatch_Id"])
+            if "Grid_Size" in r:
+                grid = int(r["Grid_Size"])
+            else:
+                grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+            e = out.setdefault(d, {"name": _kernel_short(r["Kernel_Name"]), "grid": grid,
+                                   "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+            if "Counter_Name" in r:
+                e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return out
+
+
+def _leg_dispatches(disp, pattern: str, grid, cls: int):
+    """Dispatch ids of one (kernel, grid, duration class), in dispatch order."""
+    import re
+    cand = sorted((e["ns"], d) for d, e in disp.items()
+                  if re.match(pattern, e["name"]) and (grid is None or e["grid"] == grid))
+    if not cand:
+        return []
+    classes = [[cand[0]]]
+    for item in cand[1:]:
+        if item[0] > 1.6 * classes[-1][-1][0]:
+            classes.append([item])
+        else:
+            classes[-1].append(item)
+    return sorted(d for _, d in classes[cls])
+
+
+def _mean(vals):
+    vals = list(vals)
+    return sum(vals) / len(vals) if vals else float("nan")
+
+
+def counter_summary(indir: str, outdir: str) -> None:
+    """Write the profiles/ summaries from one counter-collection directory: subfolders kt
+    (kernel trace), fetch, write, cfetch, cwrite (FETCH_SIZE / WRITE_SIZE of the run and of
+    a 1 GiB copy) and mfma1, mfma2 (MFMA, VALU, LDS and wait counters)."""
+    def csv_of(sub, kind):
+        hits = glob.glob(os.path.join(indir, sub, f"*_{kind}.csv"))
+        if len(hits) != 1:
+            raise SystemExit(f"expected one *_{kind}.csv under {indir}/{sub}, found {hits}")
+        return hits[0]
+    kt = _read_dispatches(csv_of("kt", "kernel_trace"))
+    fetch = _read_dispatches(csv_of("fetch", "counter_collection"))
+    write = _read_dispatches(csv_of("write", "counter_collection"))
+    cf = _read_dispatches(csv_of("cfetch", "counter_collection"))
+    cw = _read_dispatches(csv_of("cwrite", "counter_collection"))
+    m1 = _read_dispatches(csv_of("mfma1", "counter_collection"))
+    m2 = _read_dispatches(csv_of("mfma2", "counter_collection"))
+    copy_bytes = float(1 << 30)
+    cf_kib = max(e["FETCH_SIZE"] for e in cf.values() if "copyBuffer" in e["name"])
+    cw_kib = max(e["WRITE_SIZE"] for e in cw.values() if "copyBuffer" in e["name"])
+    f_fac, w_fac = copy_bytes / (cf_kib * 1024), copy_bytes / (cw_kib * 1024)
+    bench_cmd = "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline"
+    legs_cmd = bench_cmd + " --legs c2,c3,backward,memory_sequence"
+    head = [
+        "# rocprofv3 commands (run from /tmp with TMPDIR=/tmp; <R> is the repository, <O> the",
+        "# output directory; each --pmc pass is a run of its own):",
+        f"#   rocprofv3 --kernel-trace --stats --output-format csv -d <O>/kt -o kt -- {bench_cmd}",
+        f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <O>/fetch -o fetch -- {bench_cmd}",
+        f"#   rocprofv3 --pmc WRITE_SIZE GRBM_GUI_ACTIVE --output-format csv -d <O>/write -o write -- {bench_cmd}",
+        "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <O>/cfetch -o cfetch -- python3 bench.py --copy-probe 1073741824",
+        "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d <O>/cwrite -o cwrite -- python3 bench.py --copy-probe 1073741824",
+        "#   rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_MFMA "
+        f"SQ_INSTS_VALU SQ_INSTS_VALU_TRANS_F32 GRBM_GUI_ACTIVE --output-format csv -d <O>/mfma1 -o mfma1 -- {legs_cmd}",
+        "#   rocprofv3 --pmc SQ_VALU_MFMA_COEXEC_CYCLES SQ_ACTIVE_INST_VALU SQ_WAIT_INST_ANY SQ_WAVE_CYCLES "
+        f"SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE GRBM_GUI_ACTIVE --output-format csv -d <O>/mfma2 -o mfma2 -- {legs_cmd}",
+        "# summarised by: python3 bench.py --counter-summary <O>",
+        "# legs:",
+    ] + [f"#   {leg:16s} {desc}" for leg, desc in LEG_WORKLOAD.items()]
+    sha = {leg: src_hash(leg) for leg in KERNEL_SOURCES}
+    head += [f"# {leg} kernel sources sha256: {h}" for leg, h in sha.items()]
+
+    # Kernel trace: per leg and kernel, the dispatches' mean duration (the first dispatch of
+    # each class, a warmup, left out when there are more).
+    lines = head + ["", "# kernel trace: mean duration per launch over each leg's timed dispatches",
+                    f"{'leg':16s} {'kernel':52s} {'grid':>9s} {'n':>3s} {'mean_us':>10s} "
+                    f"{'min_us':>9s} {'max_us':>9s}"]
+    trace_us = {}
+    for leg, spec in LEG_KERNELS.items():
+        for pat, grid, cls in spec:
+            ids = _leg_dispatches(kt, pat, grid, cls)
+            if not ids:
+                continue
+            timed = ids[1:] if len(ids) > 1 else ids
+            ns = [kt[d]["ns"] for d in timed]
+            name = kt[ids[0]]["name"]
+            trace_us[(leg, name)] = _mean(ns) / 1e3
+            lines.append(f"{leg:16s} {name:52s} {kt[ids[0]]['grid']:9d} {len(timed):3d} "
+                         f"{_mean(ns) / 1e3:10.1f} {min(ns) / 1e3:9.1f} {max(ns) / 1e3:9.1f}")
+    with open(os.path.join(outdir, "kernel_trace_all_legs.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    # HBM traffic per leg (per launch of the leg's timed call).
+    lines = head + ["", f"plain copy of 1 GiB (__amd_rocclr_copyBuffer): FETCH_SIZE {cf_kib:.1f} KiB, "
+                        f"WRITE_SIZE {cw_kib:.1f} KiB",
+                    f"scale factors (true bytes / counter bytes): fetch {f_fac:.4f}, write {w_fac:.4f}",
+                    "", f"{'leg':16s} {'kernel':52s} {'FETCH_KiB':>12s} {'WRITE_KiB':>12s} "
+                        f"{'HBM_bytes_scaled':>16s} {'clock_GHz':>9s}"]
+    traffic = {"fetch_factor": f_fac, "write_factor": w_fac,
+               "source": "profiles/hbm_counters_all_legs.txt"}
+    for leg, spec in LEG_KERNELS.items():
+        fb = wb = 0.0
+        names = []
+        for pat, grid, cls in spec:
+            fi = _leg_dispatches(fetch, pat, grid, cls)
+            wi = _leg_dispatches(write, pat, grid, cls)
+            if not fi or not wi:
+                continue
+            fk = _mean(fetch[d]["FETCH_SIZE"] for d in fi)
+            wk = _mean(write[d]["WRITE_SIZE"] for d in wi)
+            ghz = _mean(write[d]["GRBM_GUI_ACTIVE"] / 8 / write[d]["ns"] for d in wi)
+            names.append(fetch[fi[0]]["name"])
+            fb += fk * 1024
+            wb += wk * 1024
+            lines.append(f"{leg:16s} {names[-1]:52s} {fk:12.1f} {wk:12.1f} "
+                         f"{fk * 1024 * f_fac + wk * 1024 * w_fac:16.4e} {ghz:9.3f}")
+        if names and leg in KERNEL_SOURCES:
+            traffic[leg] = {"src_sha256": sha[leg], "kernels": names, "fetch_bytes": fb,
+                            "write_bytes": wb}
+            lines.append(f"{leg:16s} {'(per launch of the leg)':52s} {fb / 1024:12.1f} "
+                         f"{wb / 1024:12.1f} {fb * f_fac + wb * w_fac:16.4e}")
+    lines.append("")
+    lines.append("# clock_GHz: GRBM_GUI_ACTIVE (summed over the 8 XCDs) / 8 / the dispatch's duration;")
+    lines.append("# the counter window exceeds a dispatch of a few tens of microseconds, so the")
+    lines.append("# figure is only meaningful for the long kernels.")
+    with open(os.path.join(outdir, "hbm_counters_all_legs.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    with open(os.path.join(outdir, "traffic.json"), "w") as f:
+        json.dump(traffic, f, indent=1)
+
+    # MFMA / VALU utilisation of the compute-bound kernels.
+    lines = head + [
+        "",
+        "# per SIMD per active cycle: cycles = GRBM_GUI_ACTIVE / 8 (one XCD's busy cycles) over",
+        f"# the dispatch, {N_SIMD} SIMDs.  mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x cycles);",
+        "# valu_busy = 4 SQ_ACTIVE_INST_VALU / (SIMDs x cycles) (the counter ticks per quad-cycle);",
+        "# coexec = SQ_VALU_MFMA_COEXEC_CYCLES / (SIMDs x cycles); wait = SQ_WAIT_INST_ANY /",
+        "# SQ_WAVE_CYCLES (share of wave time stalled on a dependency); flops = 512 x",
+        "# SQ_INSTS_VALU_MFMA_MOPS_BF16.  frac_at_clock = flops / (duration x SIMDs x clock x",
+        "# 1024 bf16 flops per SIMD-cycle); frac_nominal = the same at 2.4 GHz (2.5 PF/s).",
+        "# The clock (and every per-cycle figure) is only meaningful for dispatches longer",
+        "# than some tens of microseconds.",
+        "",
+        f"{'leg':12s} {'kernel':44s} {'us':>8s} {'GHz':>6s} {'flops':>10s} {'algo':>10s} "
+        f"{'fr_nom':>6s} {'fr_clk':>6s} {'mfma':>6s} {'valu':>6s} {'coex':>6s} {'trans%':>6s} "
+        f"{'wait':>6s} {'lds_cf':>7s}"]
+    for leg in ("prefill", "prefill_c2", "prefill_c3", "fwd_train", "backward", "decode",
+                "memory_sequence"):
+        for pat, grid, cls in LEG_KERNELS[leg]:
+            i1 = _leg_dispatches(m1, pat, grid, cls)
+            i2 = _leg_dispatches(m2, pat, grid, cls)
+            if not i1 or not i2:
+                continue
+            i1 = i1[1:] if len(i1) > 1 else i1
+            i2 = i2[1:] if len(i2) > 1 else i2
+            us = _mean(m1[d]["ns"] for d in i1) / 1e3
+            cyc1 = _mean(m1[d]["GRBM_GUI_ACTIVE"] / 8 for d in i1)
+            cyc2 = _mean(m2[d]["GRBM_GUI_ACTIVE"] / 8 for d in i2)
+            ghz = cyc1 / (us * 1e3)
+            fl = 512.0 * _mean(m1[d]["SQ_INSTS_VALU_MFMA_MOPS_BF16"] for d in i1)
+            busy = _mean(m1[d]["SQ_VALU_MFMA_BUSY_CYCLES"] for d in i1) / (N_SIMD * cyc1)
+            valu = 4 * _mean(m2[d]["SQ_ACTIVE_INST_VALU"] for d in i2) / (N_SIMD * cyc2)
+            coex = _mean(m2[d]["SQ_VALU_MFMA_COEXEC_CYCLES"] for d in i2) / (N_SIMD * cyc2)
+            trans = _mean(m1[d]["SQ_INSTS_VALU_TRANS_F32"] / max(m1[d]["SQ_INSTS_VALU"], 1)
+                          for d in i1)
+            wait = _mean(m2[d]["SQ_WAIT_INST_ANY"] / max(m2[d]["SQ_WAVE_CYCLES"], 1) for d in i2)
+            cf = _mean(m2[d]["SQ_LDS_BANK_CONFLICT"] / max(m2[d]["SQ_LDS_IDX_ACTIVE"], 1)
+                       for d in i2)
+            algo = LEG_FLOPS[leg]() if leg in LEG_FLOPS and len(LEG_KERNELS[leg]) == 1 else float("nan")
+            fr_nom = fl / (us * 1e-6) / 2.5e15
+            fr_clk = fl / (us * 1e-6 * N_SIMD * ghz * 1e9 * 1024)
+            lines.append(f"{leg:12s} {m1[i1[0]]['name'][:44]:44s} {us:8.1f} {ghz:6.3f} {fl:10.3e} "
+                         f"{algo:10.3e} {fr_nom:6.3f} {fr_clk:6.3f} {busy:6.3f} {valu:6.3f} "
+                         f"{coex:6.3f} {100 * trans:6.1f} {wait:6.3f} {cf:7.4f}")
+    with open(os.path.join(outdir, "mfma_valu_counters_prefill_backward_memory.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(f"wrote the summaries of {indir} to {outdir}")
+
+
 EXTRA_LEGS = ("c2", "c3", "variants", "paged", "decode_b1", "backward", "memory_step",
               "memory_sequence")
 
@@ -684,7 +940,12 @@ def main():
     ap.add_argument("--copy-probe", type=int, default=0)
     ap.add_argument("--memory-step-probe", choices=("fused", "ref"), default=None)
     ap.add_argument("--memory-sequence-probe", action="store_true")
+    ap.add_argument("--counter-summary", default=None,
+                    help="summarise a rocprofv3 collection directory into profiles/")
     args = ap.parse_args()
+    if args.counter_summary:
+        counter_summary(args.counter_summary, os.path.join(ROOT, "profiles"))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the Polar Attention path here is a single-GPU "
               "kernel library (see the sharding notes in DESIGN.md); run with --gpus 1.",
