@@ -35,6 +35,9 @@ struct PrefillArgs {
   const int32_t *page_table;              // [B,stride]
   const int32_t *start_pos;               // [B]
   int stride, num_pages, max_seq_len;
+  // Task and completion counters of this launch ([2], zero on entry, zero again when the
+  // last workgroup ends), or NULL: workgroup i then takes row block task i.
+  unsigned *ticket;
 };
 
 // dtype: 0 = f32, 1 = bf16 (same numbering as polar_dtype).

@@ -212,3 +212,25 @@ def test_lean_fewer_heads_per_block(gpu_lib, B, T, Hq, Hkv):
     one = gpu_prefill(_first_sequence(p))
     for key in ("dir", "count", "n_eff", "gate", "lse"):
         assert torch.equal(got[key][:1], one[key]), key
+
+
+def test_ticketed_task_order_batched(gpu_lib):
+    """B=4, T=16384: 4096 workgroups, the grid size from which plain prefills hand out row
+    blocks by ticket (workgroups take tasks in the order they start).  Sampled rows of the
+    first and last sequence against the oracle; the first sequence bit-identical to its own
+    launch (1024 workgroups, grid order); three launches in a row bit-identical (each
+    launch's counters are left at zero for the next one on their slot)."""
+    print("[case] prefill ticketed B=4 T=16384", flush=True)
+    p = synth.prefill_inputs("c3", B=4)
+    got = gpu_prefill(p)
+    rows = np.array([0, 1, 63, 64, 8191, 16383])
+    batches = np.array([0, 3])
+    want = oracle_prefill(p, rows=rows, batches=batches)
+    assert_close(select(got, batches=batches, rows=rows), want, p.count_vec, p.dtype,
+                 label="ticketed B=4 T=16384")
+    one = gpu_prefill(_first_sequence(p))
+    again = [gpu_prefill(p) for _ in range(2)]
+    for key in ("dir", "count", "n_eff", "gate", "lse"):
+        assert torch.equal(got[key][:1], one[key]), key
+        for x in again:
+            assert torch.equal(got[key], x[key]), key
