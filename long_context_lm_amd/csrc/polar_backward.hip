@@ -28,6 +28,8 @@
 //            dv^T += du^T P and dk^T += Q^T dS with du^T and Q^T from transposed tiles.
 //            Each key has one owner, so dk and dv need no atomics.
 //  4. parameter gradients: fixed-order two-level reductions over rows.
+#include <type_traits>
+
 #include "polar_kernels.h"
 #include "polar_mfma.h"
 
@@ -257,24 +259,31 @@ __global__ void __launch_bounds__(64 * kWaves) polar_bwd_dq_kernel(BwdArgs a) {
           const F va = *(const F *)(Vb + kb * 32 * KROW + ks * 16);
           P[kb] = Bf16::mma32(va, df[ks], ks == 0 ? zero : P[kb]);
         }
-      const bool diag = key0 + KT - 1 > wrow0;
+      // Tiles wholly below the wave's first row need no mask; the branch is per wave, so
+      // the mask's compares and selects stay out of the other tiles' code.
       F dl[2][2];
+      auto dlogits = [&](auto masked) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        float x[16];
+        for (int kb = 0; kb < 2; ++kb) {
+          float x[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float s = S[kb][r];
-          if (diag) {
-            const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * g32 + (r & 3);
-            if (key > row) s = -INFINITY;
+          for (int r = 0; r < 16; ++r) {
+            float s = S[kb][r];
+            if constexpr (decltype(masked)::value) {
+              const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * g32 + (r & 3);
+              if (key > row) s = -INFINITY;
+            }
+            const float p = fast_exp2(fmaf(s, cl2, -lse2));
+            x[r] = p * (P[kb][r] + fmaf(E, p, A));
           }
-          const float p = fast_exp2(fmaf(s, cl2, -lse2));
-          x[r] = p * (P[kb][r] + fmaf(E, p, A));
+          dl[kb][0] = Bf16::pack(x);
+          dl[kb][1] = Bf16::pack(x + 8);
         }
-        dl[kb][0] = Bf16::pack(x);
-        dl[kb][1] = Bf16::pack(x + 8);
-      }
+      };
+      if (key0 + KT - 1 > wrow0)
+        dlogits(std::true_type{});
+      else
+        dlogits(std::false_type{});
       const uint16_t *Tb = lds_at(&Kt[0][0], t_lane + buf * TBUF);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -506,24 +515,32 @@ polar_bwd_dkv_kernel(BwdArgs a) {
             S = Bf16::mma32(*(const F *)(Qb + ks * 16), kf[ks], ks == 0 ? zero : S);
             P = Bf16::mma32(*(const F *)(Cb + ks * 16), vf[ks], ks == 0 ? zero : P);
           }
-          const bool diag = r0row < kw0 + 31;
+          // Query tiles wholly below the wave's keys need no mask (branch per wave).
           float pv[16], dsv[16];
+          auto probs = [&](auto masked) {
 #pragma unroll
-          for (int a4 = 0; a4 < 4; ++a4) {
-            const int ri0 = 8 * a4 + 4 * g32;
-            const f32x4 cl = *(const f32x4 *)&Sc[buf][0][ri0];
-            const f32x4 ls = *(const f32x4 *)&Sc[buf][1][ri0];
-            const f32x4 ac = *(const f32x4 *)&Sc[buf][2][ri0];
-            const f32x4 ec = *(const f32x4 *)&Sc[buf][3][ri0];
+            for (int a4 = 0; a4 < 4; ++a4) {
+              const int ri0 = 8 * a4 + 4 * g32;
+              const f32x4 cl = *(const f32x4 *)&Sc[buf][0][ri0];
+              const f32x4 ls = *(const f32x4 *)&Sc[buf][1][ri0];
+              const f32x4 ac = *(const f32x4 *)&Sc[buf][2][ri0];
+              const f32x4 ec = *(const f32x4 *)&Sc[buf][3][ri0];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              const int r = 4 * a4 + c;
-              float p = fast_exp2(fmaf(S[r], cl[c], -ls[c]));
-              if (diag && r0row + ri0 + c < key) p = 0.f;
-              pv[r] = p;
-              dsv[r] = p * (P[r] + fmaf(ec[c], p, ac[c]));
+              for (int c = 0; c < 4; ++c) {
+                const int r = 4 * a4 + c;
+                float p = fast_exp2(fmaf(S[r], cl[c], -ls[c]));
+                if constexpr (decltype(masked)::value) {
+                  if (r0row + ri0 + c < key) p = 0.f;
+                }
+                pv[r] = p;
+                dsv[r] = p * (P[r] + fmaf(ec[c], p, ac[c]));
+              }
             }
-          }
+          };
+          if (r0row < kw0 + 31)
+            probs(std::true_type{});
+          else
+            probs(std::false_type{});
           // Rows whose arg-max key belongs to this wave (rare): add c*dm at that key.
           const int jl = __float_as_int(Sc[buf][5][c32]);
           if (__ballot(jl >= kw0 && jl < kw0 + 32) != 0) {
