@@ -1,5 +1,5 @@
 /*
- * libpolar — Polar Attention forward for AMD Instinct MI355X (gfx950).  C ABI, version 4
+ * libpolar — Polar Attention forward for AMD Instinct MI355X (gfx950).  C ABI, version 5
  * (POLAR_ABI_VERSION below; polar_abi_version() reports the loaded library's).
  *
  * The operation is the attention mixing step of the ATMA hybrid decoder as described in
@@ -49,8 +49,9 @@ extern "C" {
 /* 2: polar_variant gained the key-rotation workspace.
  * 3: polar_decode_workspace_bytes lost its page_size argument (the only page size is 64 and
  *    the workspace never depended on it).
- * 4: polar_delta_sequence (the memory stream over T tokens) added; nothing else changed. */
-#define POLAR_ABI_VERSION 4
+ * 4: polar_delta_sequence (the memory stream over T tokens) added; nothing else changed.
+ * 5: polar_attn_fwd_mixed (the three streams summed into one output) added. */
+#define POLAR_ABI_VERSION 5
 
 #if defined(__GNUC__)
 #define POLAR_API __attribute__((visibility("default")))
@@ -113,6 +114,27 @@ typedef struct {
 POLAR_API polar_status polar_attn_fwd(const polar_params *p, polar_dtype dt, int32_t B, int32_t T,
                             const void *q, const void *k, const void *v,
                             const polar_outputs *out, void *stream);
+
+/*
+ * The layer's output as the sum of its three streams (section 2.1 of the technical
+ * summary: content plus count plus memory), for callers that want only the sum:
+ *   mixed[b,t,h,:] = dir + count + memory[b,t,h,:]
+ * with dir and count exactly as polar_attn_fwd defines them for row t of head h, and
+ * memory the memory stream's output for the same token and head (polar_delta_sequence
+ * run with H = Hq heads).  Written once, in place of dir and count.
+ *   memory   optional device float32 [B,T,Hq,d], 16-byte aligned; NULL = no memory
+ *            stream.  May alias mixed (each element is read before it is written).
+ *   mixed    device float32 [B,T,Hq,d], 16-byte aligned.
+ *   out      the scalar outputs as for polar_attn_fwd (n_eff required, gate and lse
+ *            optional); out->dir and out->count must be NULL.
+ *   params.count_vec NULL = no count stream.
+ * Errors as for polar_attn_fwd, plus POLAR_ERR_UNSUPPORTED when out->dir or out->count is
+ * set.
+ */
+POLAR_API polar_status polar_attn_fwd_mixed(const polar_params *p, polar_dtype dt, int32_t B,
+                                            int32_t T, const void *q, const void *k,
+                                            const void *v, const float *memory, float *mixed,
+                                            const polar_outputs *out, void *stream);
 
 /*
  * Variant modes of the prefill (the comparison arms and position schemes the pages

@@ -28,7 +28,7 @@ POLAR_FLAG_LENGTH_TEMP = 1
 POLAR_FLAG_NULL_FLOOR = 2
 POLAR_DELTA_NORMALIZE_QK = 1
 
-EXPORTS = ("polar_attn_fwd", "polar_decode_workspace_bytes", "polar_attn_decode_paged",
+EXPORTS = ("polar_attn_fwd", "polar_attn_fwd_mixed", "polar_decode_workspace_bytes", "polar_attn_decode_paged",
            "polar_attn_decode_paged_noalloc",
            "polar_attn_fwd_train", "polar_bwd_workspace_bytes", "polar_attn_bwd",
            "polar_attn_fwd_variant", "polar_variant_workspace_bytes", "polar_kv_append",
@@ -134,6 +134,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.polar_delta_sequence.restype = I32
     lib.polar_delta_sequence.argtypes = [P(polar_delta_params), I32, I32, I32, VP, I32, VP, VP, VP,
                                          VP, VP, VP, VP, VP]
+    lib.polar_attn_fwd_mixed.restype = I32
+    lib.polar_attn_fwd_mixed.argtypes = [P(polar_params), I32, I32, I32, VP, VP, VP, VP, VP,
+                                         P(polar_outputs), VP]
     lib.polar_status_str.restype = ctypes.c_char_p
     lib.polar_status_str.argtypes = [I32]
     lib.polar_last_error.restype = ctypes.c_char_p
@@ -217,6 +220,11 @@ def polar_delta_step(params, dtype, B, state_pool, num_slots, slots, q, k, v, al
                      stream) -> int:
     return load().polar_delta_step(ctypes.byref(params), dtype, B, state_pool, num_slots, slots,
                                    q, k, v, alpha, beta, out, stream)
+
+
+def polar_attn_fwd_mixed(params, dtype, B, T, q, k, v, memory, mixed, outputs, stream) -> int:
+    return load().polar_attn_fwd_mixed(ctypes.byref(params), dtype, B, T, q, k, v, memory, mixed,
+                                       ctypes.byref(outputs), stream)
 
 
 def polar_delta_sequence(params, dtype, B, T, state_pool, num_slots, slots, q, k, v, alpha, beta,

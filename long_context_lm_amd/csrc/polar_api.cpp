@@ -68,7 +68,8 @@ struct PagedSrc {
 polar_status prefill(const polar_params *p, polar_dtype dt, int32_t B, int32_t T, const void *q,
                      const void *k, const void *v, const polar_outputs *out,
                      const polar_saved *saved, const polar_variant *var, void *stream,
-                     const PagedSrc *paged = nullptr) {
+                     const PagedSrc *paged = nullptr, float *mixed = nullptr,
+                     const float *memory = nullptr) {
   polar_status st = check_params(p, dt, out);
   if (st != POLAR_OK) return st;
   if (var) {
@@ -101,7 +102,7 @@ polar_status prefill(const polar_params *p, polar_dtype dt, int32_t B, int32_t T
     return fail(POLAR_ERR_BAD_SHAPE, "T*Hkv too large for one sequence (T=%d, Hkv=%d)", T,
                 p->n_kv_heads);
 
-  polar::PrefillArgs a;
+  polar::PrefillArgs a{};
   a.q = q;
   a.k = k;
   a.v = v;
@@ -113,6 +114,8 @@ polar_status prefill(const polar_params *p, polar_dtype dt, int32_t B, int32_t T
   a.n_eff = out->n_eff;
   a.gate = out->gate;
   a.lse = out->lse;
+  a.mixed = mixed;
+  a.memory = memory;
   a.u_norm = saved ? saved->u_norm : nullptr;
   a.arg_max = saved ? saved->arg_max : nullptr;
   a.attn = var ? var->attn : nullptr;
@@ -186,6 +189,26 @@ polar_status polar_attn_fwd(const polar_params *p, polar_dtype dt, int32_t B, in
                             const void *q, const void *k, const void *v,
                             const polar_outputs *out, void *stream) {
   return prefill(p, dt, B, T, q, k, v, out, nullptr, nullptr, stream);
+}
+
+polar_status polar_attn_fwd_mixed(const polar_params *p, polar_dtype dt, int32_t B, int32_t T,
+                                  const void *q, const void *k, const void *v,
+                                  const float *memory, float *mixed, const polar_outputs *out,
+                                  void *stream) {
+  if (!out) return fail(POLAR_ERR_NULL_POINTER, "outputs is NULL");
+  if (out->dir || out->count)
+    return fail(POLAR_ERR_UNSUPPORTED,
+                "outputs.dir and outputs.count must be NULL: the mixed output replaces them");
+  if (B > 0 && T > 0) {
+    if (!mixed) return fail(POLAR_ERR_NULL_POINTER, "mixed is NULL");
+    if (!aligned16(mixed) || (memory && !aligned16(memory)))
+      return fail(POLAR_ERR_MISALIGNED, "mixed and memory must be 16-byte aligned");
+    if (p && p->count_vec && !aligned16(p->count_vec))
+      return fail(POLAR_ERR_MISALIGNED, "count_vec must be 16-byte aligned");
+  }
+  polar_outputs o = *out;
+  o.dir = mixed;             // validated as the vector output
+  return prefill(p, dt, B, T, q, k, v, &o, nullptr, nullptr, stream, nullptr, mixed, memory);
 }
 
 size_t polar_variant_workspace_bytes(const polar_params *p, polar_dtype dt, int32_t B,

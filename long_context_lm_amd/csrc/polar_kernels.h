@@ -35,6 +35,11 @@ struct PrefillArgs {
   const int32_t *page_table;              // [B,stride]
   const int32_t *start_pos;               // [B]
   int stride, num_pages, max_seq_len;
+  // Mixed output (section 2.1's out = content + count + memory): when non-NULL, the kernel
+  // writes mixed = dir + count + memory [B,T,Hq,d] instead of dir and count; memory may be
+  // NULL (no memory stream).
+  float *mixed;
+  const float *memory;
   // Task and completion counters of this launch ([2], zero on entry, zero again when the
   // last workgroup ends), or NULL: workgroup i then takes row block task i.
   unsigned *ticket;

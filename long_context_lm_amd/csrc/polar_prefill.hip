@@ -35,7 +35,9 @@
 //    (kModeVariantRot); tiles that every row sees whole take the pipelined path;
 //  * paged instances (kMode == kModePaged) serve chunked prefill over a paged KV cache: the
 //    rows are C new tokens at positions start_pos[b].., and a 64-key tile is one page,
-//    read through the page table (pages with invalid ids are masked out).
+//    read through the page table (pages with invalid ids are masked out);
+//  * mixed instances (kMode == kModeMix) compute as the plain ones and write the sum of
+//    the three streams of section 2.1, dir + count + memory, instead of dir and count.
 #include <mutex>
 
 #include "polar_kernels.h"
@@ -73,6 +75,8 @@ constexpr int kModePlain = 0, kModeSave = 1, kModeVariant = 2, kModePaged = 3;
 // Variant whose keys still need RoPE (no rotated copy): they are rotated while staged
 // through registers, so this mode keeps the register staging path.
 constexpr int kModeVariantRot = 4;
+// Plain prefill writing dir + count + memory as one output (a.mixed).
+constexpr int kModeMix = 5;
 
 // RoPE rotation angle of pair t at position pos: revolutions = frac(pos * f_t) taken
 // exactly from the 64-bit fixed-point product, then the hardware sine and cosine, whose
@@ -104,6 +108,7 @@ __global__ void __launch_bounds__(64 * kWaves, kLean ? 4 : 1)
   constexpr bool kSave = kMode == kModeSave;
   constexpr bool kVar = kMode == kModeVariant || kMode == kModeVariantRot;
   constexpr bool kPaged = kMode == kModePaged;
+  constexpr bool kMix = kMode == kModeMix;
   static_assert(!kPaged || LdsCfg<TR>::kt == kPageSize, "a key tile is one page");
   constexpr int kThreads = 64 * kWaves;
   constexpr int kKT = LdsCfg<TR>::kt;                // keys per tile
@@ -858,17 +863,37 @@ __global__ void __launch_bounds__(64 * kWaves, kLean ? 4 : 1)
       const float th = (n2 - 1.0f) / (n2 + 1.0f);
       const float inv = nrm > 0.f ? rsqrtf(nrm) : 0.f;
       const size_t obase = ((size_t)b * a.T + row) * a.Hq + h;
-      float *dp = a.dir + obase * kD;
+      if constexpr (kMix) {
+        // The three streams summed: u/|u| + gate tanh(ln n_eff) w_h + memory.
+        const float cg = a.count_vec ? gate * th : 0.f;
+        const float *wp = a.count_vec ? a.count_vec + (size_t)h * kD : nullptr;
+        const float *mp = a.memory ? a.memory + obase * kD : nullptr;
+        float *xp = a.mixed + obase * kD;
 #pragma unroll
-      for (int db = 0; db < 2; ++db)
+        for (int db = 0; db < 2; ++db)
 #pragma unroll
-        for (int j4 = 0; j4 < 4; ++j4) {
-          const int dim0 = db * 32 + 8 * j4 + 4 * g32;
-          f32x4 val;
+          for (int j4 = 0; j4 < 4; ++j4) {
+            const int dim0 = db * 32 + 8 * j4 + 4 * g32;
+            const f32x4 w = a.count_vec ? *(const f32x4 *)(wp + dim0) : f32x4{0.f, 0.f, 0.f, 0.f};
+            const f32x4 m = a.memory ? *(const f32x4 *)(mp + dim0) : f32x4{0.f, 0.f, 0.f, 0.f};
+            f32x4 val;
 #pragma unroll
-          for (int c = 0; c < 4; ++c) val[c] = o[qb][db][4 * j4 + c] * inv;
-          *(f32x4 *)(dp + dim0) = val;
-        }
+            for (int c = 0; c < 4; ++c) val[c] = (o[qb][db][4 * j4 + c] * inv + cg * w[c]) + m[c];
+            *(f32x4 *)(xp + dim0) = val;
+          }
+      } else {
+        float *dp = a.dir + obase * kD;
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+          for (int j4 = 0; j4 < 4; ++j4) {
+            const int dim0 = db * 32 + 8 * j4 + 4 * g32;
+            f32x4 val;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) val[c] = o[qb][db][4 * j4 + c] * inv;
+            *(f32x4 *)(dp + dim0) = val;
+          }
+      }
       if constexpr (kVar) {
         if (a.attn) {
           const float is = 1.0f / St;
@@ -885,7 +910,7 @@ __global__ void __launch_bounds__(64 * kWaves, kLean ? 4 : 1)
             }
         }
       }
-      if (a.count) {
+      if (!kMix && a.count) {
         const float cg = gate * th;
         const float *wp = a.count_vec + (size_t)h * kD;
         float *cp = a.count + obase * kD;
@@ -1055,6 +1080,7 @@ hipError_t launch_prefill(int dtype, const PrefillArgs &args, hipStream_t stream
   dim3 grid((unsigned)blocks);
   const int mode = a.paged ? kModePaged
                  : a.variant ? ((a.rope && !a.k_rotated) ? kModeVariantRot : kModeVariant)
+                 : a.mixed ? kModeMix
                  : (a.u_norm != nullptr ? kModeSave : kModePlain);
   const dim3 bb(64 * kWavesBf16), bf(64 * kWavesF32);
   if (dtype == 1 && a.lean == 2) {
@@ -1074,6 +1100,9 @@ hipError_t launch_prefill(int dtype, const PrefillArgs &args, hipStream_t stream
     else if (mode == kModeSave)
       hipLaunchKernelGGL((polar_prefill_kernel<Bf16, 1, kWavesBf16, kModeSave, true>), grid,
                          bb, 0, stream, a);
+    else if (mode == kModeMix)
+      hipLaunchKernelGGL((polar_prefill_kernel<Bf16, 1, kWavesBf16, kModeMix, true>), grid,
+                         bb, 0, stream, a);
     else
       return hipErrorInvalidConfiguration;   // prefill_shape never picks it for other modes
   } else if (dtype == 1) {
@@ -1082,6 +1111,9 @@ hipError_t launch_prefill(int dtype, const PrefillArgs &args, hipStream_t stream
                          grid, bb, 0, stream, a);
     else if (mode == kModeSave)
       hipLaunchKernelGGL((polar_prefill_kernel<Bf16, kQbBf16, kWavesBf16, kModeSave, false>),
+                         grid, bb, 0, stream, a);
+    else if (mode == kModeMix)
+      hipLaunchKernelGGL((polar_prefill_kernel<Bf16, kQbBf16, kWavesBf16, kModeMix, false>),
                          grid, bb, 0, stream, a);
     else if (mode == kModeVariant)
       hipLaunchKernelGGL((polar_prefill_kernel<Bf16, kQbBf16, kWavesBf16, kModeVariant, false>),
@@ -1100,6 +1132,9 @@ hipError_t launch_prefill(int dtype, const PrefillArgs &args, hipStream_t stream
                          bf, 0, stream, a);
     else if (mode == kModeSave)
       hipLaunchKernelGGL((polar_prefill_kernel<F32, kQbF32, kWavesF32, kModeSave, false>), grid,
+                         bf, 0, stream, a);
+    else if (mode == kModeMix)
+      hipLaunchKernelGGL((polar_prefill_kernel<F32, kQbF32, kWavesF32, kModeMix, false>), grid,
                          bf, 0, stream, a);
     else if (mode == kModeVariant || mode == kModeVariantRot)   // fp32 always stages K itself
       hipLaunchKernelGGL((polar_prefill_kernel<F32, kQbF32, kWavesF32, kModeVariant, false>),

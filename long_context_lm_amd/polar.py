@@ -98,6 +98,32 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta=None, null_
     return out
 
 
+def attn_fwd_mixed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                   memory: Optional[torch.Tensor] = None, beta=None, null_bias=None,
+                   count_vec=None, train_len: int = 2048,
+                   flags: int = _lib.POLAR_FLAG_LENGTH_TEMP | _lib.POLAR_FLAG_NULL_FLOOR,
+                   want_gate: bool = True, want_lse: bool = True, stream=None) -> dict:
+    """The three streams summed (see polar_attn_fwd_mixed): "mixed" [B,T,Hq,d] = dir + count
+    + memory, plus the scalar outputs.  ``memory`` is the memory stream's output [B,T,Hq,d]
+    float32 (e.g. from :func:`delta_sequence` with Hq heads), or None."""
+    prm, keep, (B, T, Hq, Hkv, d) = _prefill_args(q, k, v, beta, null_bias, count_vec,
+                                                  train_len, flags)
+    dev = q.device
+    if memory is not None:
+        _check_aux(memory, "memory", dev, torch.float32, (B, T, Hq, d))
+    out = dict(mixed=torch.empty(B, T, Hq, d, device=dev, dtype=torch.float32),
+               n_eff=torch.empty(B, T, Hq, device=dev, dtype=torch.float32))
+    out["gate"] = torch.empty(B, T, Hq, device=dev, dtype=torch.float32) if want_gate else None
+    out["lse"] = torch.empty(B, T, Hq, device=dev, dtype=torch.float32) if want_lse else None
+    cout = _lib.polar_outputs(None, None, _ptr(out["n_eff"]), _ptr(out["gate"]),
+                              _ptr(out["lse"]))
+    s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+    _lib.check(_lib.polar_attn_fwd_mixed(prm, _DT[q.dtype], B, T, q.data_ptr(), k.data_ptr(),
+                                         v.data_ptr(), _ptr(memory), out["mixed"].data_ptr(),
+                                         cout, s))
+    return out
+
+
 def _prefill_args(q, k, v, beta, null_bias, count_vec, train_len, flags):
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _check_input(t, n)

@@ -13,7 +13,8 @@ and Gated-Delta Compression Memory" technical summary (gist.science), section 2.
   gated by a signal-detection confidence against an extreme-value-corrected null floor and
   mapped through tanh(log n_eff) onto a per-head vector.
 * out = content + count + memory; the memory stream is not part of this operation, so
-  ``dir`` (content) and ``count`` are returned separately.
+  ``dir`` (content) and ``count`` are returned separately, and ``three_streams`` forms the
+  sum from them and a memory-stream output.
 
 The pages fix no formula for the temperature, the floor or the gate.  Readings taken here
 (each one is listed with its reason in the design notes):
@@ -202,6 +203,19 @@ def polar_prefill(q, k, v, beta=None, null_bias=None, count_vec=None, train_len:
                 for key in out:
                     out[key][bi, r0:r1, hi] = res[key]
                 r0 = r1
+    return out
+
+
+def three_streams(fwd: dict, memory=None) -> np.ndarray:
+    """The layer output of section 2.1, out = content + count + memory, in float64: the
+    prefill's ``dir`` (content) plus its ``count`` (zero when the prefill had no count
+    vector) plus the memory stream's output for the same token and head (zero when None).
+    All three are [B,T,Hq,d]."""
+    out = np.asarray(fwd["dir"], np.float64).copy()
+    if fwd.get("count") is not None:
+        out = out + np.asarray(fwd["count"], np.float64)
+    if memory is not None:
+        out = out + np.asarray(memory, np.float64)
     return out
 
 

@@ -23,7 +23,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(_lib.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert _lib.polar_abi_version() == 4
+    assert _lib.polar_abi_version() == 5
 
 
 def test_status_strings():
@@ -89,6 +89,35 @@ def test_empty_prefill_is_a_valid_no_op():
         _lib.POLAR_OK
     # empty tensors may come as NULL pointers
     assert fwd(B=0, q=None, k=None, v=None, o=outs(dir=None, n_eff=None)) == _lib.POLAR_OK
+
+
+def mixed(p=None, dt=1, B=1, T=8, q=A, k=A, v=A, mem=A, mx=A, o=None):
+    p = params() if p is None else p
+    o = outs(dir=None, count=None) if o is None else o
+    return _lib.polar_attn_fwd_mixed(p, dt, B, T, q, k, v, mem, mx, o, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(o=outs()), _lib.POLAR_ERR_UNSUPPORTED),                  # dir and count set
+    (dict(o=outs(dir=None)), _lib.POLAR_ERR_UNSUPPORTED),          # count set
+    (dict(mx=None), _lib.POLAR_ERR_NULL_POINTER),
+    (dict(mx=A + 8), _lib.POLAR_ERR_MISALIGNED),
+    (dict(mem=A + 4), _lib.POLAR_ERR_MISALIGNED),
+    (dict(p=params(count_vec=A + 4)), _lib.POLAR_ERR_MISALIGNED),
+    (dict(o=outs(dir=None, count=None, n_eff=None)), _lib.POLAR_ERR_NULL_POINTER),
+    (dict(dt=7), _lib.POLAR_ERR_UNSUPPORTED),
+    (dict(p=params(n_q_heads=6, n_kv_heads=4)), _lib.POLAR_ERR_BAD_SHAPE),
+])
+def test_mixed_validation_errors(kw, code):
+    assert mixed(**kw) == code
+    assert _lib.polar_last_error() != ""
+
+
+def test_mixed_empty_and_optional_memory():
+    assert mixed(B=0, q=None, k=None, v=None, mem=None, mx=None) == _lib.POLAR_OK
+    assert mixed(T=0, q=None, k=None, v=None, mem=None, mx=None) == _lib.POLAR_OK
+    assert _lib.load().polar_attn_fwd_mixed(params(), 1, 1, 8, A, A, A, A, A, None, None) == \
+        _lib.POLAR_ERR_NULL_POINTER
 
 
 def dec(p=None, dt=1, B=2, q=A, kc=A, vc=A, num_pages=10, page=64, table=A, stride=4,
