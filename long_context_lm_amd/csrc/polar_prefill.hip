@@ -152,8 +152,19 @@ __global__ void __launch_bounds__(64 * kWaves, kLean ? 4 : 1)
   static_assert(!kSplit || kDepth == 1, "split instance loads one tile ahead");
   constexpr int kXchBytes = 8 * 36 * 64 * (int)sizeof(float);   // split merge: 36 values/lane
   constexpr int kRingBytes = kSlots * kSlotBytes;
-  constexpr int kSmemBytes = kSplit ? (2 * kRingBytes > kXchBytes ? 2 * kRingBytes : kXchBytes)
-                                    : kRingBytes;
+  // Lean instances (plain, training, mixed) write their vector outputs as whole 256-byte
+  // rows with non-temporal stores: each wave's 32 rows go through LDS (the registers hold 16-byte pieces of 32
+  // rows), in the ring's space once every tile load has landed.  Whole lines bypass the
+  // L2, so the launch does not end on a write-back of the outputs: at B = 8, T = 2K
+  // 125 -> 117 us.  (Non-temporal stores of the 16-byte pieces were 60% slower; whole rows
+  // through the L2 gained nothing.)
+  constexpr bool kRowStores =
+      kLean && (kMode == kModePlain || kMode == kModeSave || kMode == kModeMix);
+  constexpr int kOutPitch = kD + 4;                 // floats per staged row (spreads banks)
+  constexpr int kOutBytes = kRowStores ? kWaves * 32 * kOutPitch * (int)sizeof(float) : 0;
+  constexpr int kBase = kSplit ? (2 * kRingBytes > kXchBytes ? 2 * kRingBytes : kXchBytes)
+                               : kRingBytes;
+  constexpr int kSmemBytes = kBase > kOutBytes ? kBase : kOutBytes;
   __shared__ __attribute__((aligned(128))) char smem[kSmemBytes];
   auto Ks = reinterpret_cast<E (*)[kKT * KROW]>(smem);
   auto Vs = reinterpret_cast<E (*)[kD * VROW]>(smem + 4 * kKT * KROW * sizeof(E));
@@ -839,9 +850,17 @@ __global__ void __launch_bounds__(64 * kWaves, kLean ? 4 : 1)
   }
 
   // ---- epilogue ----
+  if constexpr (kRowStores) {
+    // The last step issued loads of a tile past the end: let them land before the ring's
+    // space is reused.
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    __syncthreads();
+  }
   const float bias = a.null_bias ? a.null_bias[h] : 0.0f;
+  float cgate[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
+    cgate[qb] = 0.f;
     const int row = wrow0 + qb * 32 + c32;
     const float St = half_sum(Ssum[qb]);
     const float Qt = half_sum(Qsum[qb]);
@@ -863,7 +882,19 @@ __global__ void __launch_bounds__(64 * kWaves, kLean ? 4 : 1)
       const float th = (n2 - 1.0f) / (n2 + 1.0f);
       const float inv = nrm > 0.f ? rsqrtf(nrm) : 0.f;
       const size_t obase = ((size_t)b * a.T + row) * a.Hq + h;
-      if constexpr (kMix) {
+      if constexpr (kRowStores) {
+        float *ep = reinterpret_cast<float *>(smem) + (wv * 32 + c32) * kOutPitch;
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+          for (int j4 = 0; j4 < 4; ++j4) {
+            const int dim0 = db * 32 + 8 * j4 + 4 * g32;
+            f32x4 val;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) val[c] = o[qb][db][4 * j4 + c] * inv;
+            *(f32x4 *)(ep + dim0) = val;
+          }
+      } else if constexpr (kMix) {
         // The three streams summed: u/|u| + gate tanh(ln n_eff) w_h + memory.
         const float cg = a.count_vec ? gate * th : 0.f;
         const float *wp = a.count_vec ? a.count_vec + (size_t)h * kD : nullptr;
@@ -910,7 +941,8 @@ __global__ void __launch_bounds__(64 * kWaves, kLean ? 4 : 1)
             }
         }
       }
-      if (!kMix && a.count) {
+      if constexpr (kRowStores) cgate[qb] = (!kMix || a.count_vec) ? gate * th : 0.f;
+      if (!kMix && !kRowStores && a.count) {
         const float cg = gate * th;
         const float *wp = a.count_vec + (size_t)h * kD;
         float *cp = a.count + obase * kD;
@@ -937,6 +969,37 @@ __global__ void __launch_bounds__(64 * kWaves, kLean ? 4 : 1)
         a.n_eff[obase] = neff;
         if (a.gate) a.gate[obase] = gate;
         if (a.lse) a.lse[obase] = lse;
+      }
+    }
+  }
+  if constexpr (kRowStores) {
+    // Four whole rows per store: lane l writes dims 4 (l % 16) .. + 3 of row 4 i + l / 16;
+    // count is gate tanh(ln n_eff) (held by the row's own lane) times the head's vector.
+    static_assert(!kRowStores || QB == 1, "row stores: one query block per wave");
+    __syncthreads();
+    const float *ep = reinterpret_cast<const float *>(smem) + wv * 32 * kOutPitch;
+    const int rq = lane >> 4, cc = (lane & 15) * 4;
+    const bool wcount = kMix ? a.count_vec != nullptr : a.count != nullptr;
+    const f32x4 w4 = wcount ? *(const f32x4 *)(a.count_vec + (size_t)h * kD + cc)
+                            : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 4 * i + rq;
+      const float cgr = __shfl(cgate[0], r);
+      if (wrow0 + r < a.T) {
+        const size_t ob = (((size_t)b * a.T + wrow0 + r) * a.Hq + h) * kD + cc;
+        const f32x4 dv = *(const f32x4 *)(ep + r * kOutPitch + cc);
+        if constexpr (kMix) {
+          // The three streams summed: u/|u| + gate tanh(ln n_eff) w_h + memory.
+          const f32x4 m = a.memory ? *(const f32x4 *)(a.memory + ob) : f32x4{0.f, 0.f, 0.f, 0.f};
+          f32x4 val;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) val[c] = (dv[c] + cgr * w4[c]) + m[c];
+          __builtin_nontemporal_store(val, (f32x4 *)(a.mixed + ob));
+        } else {
+          __builtin_nontemporal_store(dv, (f32x4 *)(a.dir + ob));
+          if (wcount) __builtin_nontemporal_store(w4 * cgr, (f32x4 *)(a.count + ob));
+        }
       }
     }
   }
