@@ -152,14 +152,14 @@ __global__ void __launch_bounds__(64 * kWaves, kLean ? 4 : 1)
   static_assert(!kSplit || kDepth == 1, "split instance loads one tile ahead");
   constexpr int kXchBytes = 8 * 36 * 64 * (int)sizeof(float);   // split merge: 36 values/lane
   constexpr int kRingBytes = kSlots * kSlotBytes;
-  // Lean instances (plain, training, mixed) write their vector outputs as whole 256-byte
-  // rows with non-temporal stores: each wave's 32 rows go through LDS (the registers hold 16-byte pieces of 32
+  // Lean instances (plain, training, mixed, variant) write their vector outputs as whole
+  // 256-byte rows with non-temporal stores: each wave's 32 rows go through LDS (the registers hold 16-byte pieces of 32
   // rows), in the ring's space once every tile load has landed.  Whole lines bypass the
   // L2, so the launch does not end on a write-back of the outputs: at B = 8, T = 2K
   // 125 -> 117 us.  (Non-temporal stores of the 16-byte pieces were 60% slower; whole rows
   // through the L2 gained nothing.)
-  constexpr bool kRowStores =
-      kLean && (kMode == kModePlain || kMode == kModeSave || kMode == kModeMix);
+  constexpr bool kRowStores = kLean && (kMode == kModePlain || kMode == kModeSave ||
+                                        kMode == kModeMix || kMode == kModeVariant);
   constexpr int kOutPitch = kD + 4;                 // floats per staged row (spreads banks)
   constexpr int kOutBytes = kRowStores ? kWaves * 32 * kOutPitch * (int)sizeof(float) : 0;
   constexpr int kBase = kSplit ? (2 * kRingBytes > kXchBytes ? 2 * kRingBytes : kXchBytes)
@@ -857,10 +857,13 @@ __global__ void __launch_bounds__(64 * kWaves, kLean ? 4 : 1)
     __syncthreads();
   }
   const float bias = a.null_bias ? a.null_bias[h] : 0.0f;
-  float cgate[QB];
+  // Row stores: per-row factors of the staged u (1/|u|, gate tanh(ln n_eff), 1/S).
+  float rinv[QB], cgate[QB], rinvs[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
+    rinv[qb] = 0.f;
     cgate[qb] = 0.f;
+    rinvs[qb] = 0.f;
     const int row = wrow0 + qb * 32 + c32;
     const float St = half_sum(Ssum[qb]);
     const float Qt = half_sum(Qsum[qb]);
@@ -883,6 +886,7 @@ __global__ void __launch_bounds__(64 * kWaves, kLean ? 4 : 1)
       const float inv = nrm > 0.f ? rsqrtf(nrm) : 0.f;
       const size_t obase = ((size_t)b * a.T + row) * a.Hq + h;
       if constexpr (kRowStores) {
+        // u itself: dir, attn and mixed are u times a per-row factor, applied at the store.
         float *ep = reinterpret_cast<float *>(smem) + (wv * 32 + c32) * kOutPitch;
 #pragma unroll
         for (int db = 0; db < 2; ++db)
@@ -891,9 +895,11 @@ __global__ void __launch_bounds__(64 * kWaves, kLean ? 4 : 1)
             const int dim0 = db * 32 + 8 * j4 + 4 * g32;
             f32x4 val;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) val[c] = o[qb][db][4 * j4 + c] * inv;
+            for (int c = 0; c < 4; ++c) val[c] = o[qb][db][4 * j4 + c];
             *(f32x4 *)(ep + dim0) = val;
           }
+        rinv[qb] = inv;
+        if constexpr (kVar) rinvs[qb] = 1.0f / St;
       } else if constexpr (kMix) {
         // The three streams summed: u/|u| + gate tanh(ln n_eff) w_h + memory.
         const float cg = a.count_vec ? gate * th : 0.f;
@@ -925,7 +931,7 @@ __global__ void __launch_bounds__(64 * kWaves, kLean ? 4 : 1)
             *(f32x4 *)(dp + dim0) = val;
           }
       }
-      if constexpr (kVar) {
+      if constexpr (kVar && !kRowStores) {
         if (a.attn) {
           const float is = 1.0f / St;
           float *ap = a.attn + obase * kD;
@@ -980,15 +986,23 @@ __global__ void __launch_bounds__(64 * kWaves, kLean ? 4 : 1)
     const float *ep = reinterpret_cast<const float *>(smem) + wv * 32 * kOutPitch;
     const int rq = lane >> 4, cc = (lane & 15) * 4;
     const bool wcount = kMix ? a.count_vec != nullptr : a.count != nullptr;
+    bool wattn = false;
+    if constexpr (kVar) wattn = a.attn != nullptr;
     const f32x4 w4 = wcount ? *(const f32x4 *)(a.count_vec + (size_t)h * kD + cc)
                             : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int r = 4 * i + rq;
-      const float cgr = __shfl(cgate[0], r);
+      const float cgr = __shfl(cgate[0], r), invr = __shfl(rinv[0], r);
+      float isr = 0.f;
+      if constexpr (kVar) isr = __shfl(rinvs[0], r);
       if (wrow0 + r < a.T) {
         const size_t ob = (((size_t)b * a.T + wrow0 + r) * a.Hq + h) * kD + cc;
-        const f32x4 dv = *(const f32x4 *)(ep + r * kOutPitch + cc);
+        const f32x4 u4 = *(const f32x4 *)(ep + r * kOutPitch + cc);
+        const f32x4 dv = u4 * invr;
+        if constexpr (kVar) {
+          if (wattn) __builtin_nontemporal_store(u4 * isr, (f32x4 *)(a.attn + ob));
+        }
         if constexpr (kMix) {
           // The three streams summed: u/|u| + gate tanh(ln n_eff) w_h + memory.
           const f32x4 m = a.memory ? *(const f32x4 *)(a.memory + ob) : f32x4{0.f, 0.f, 0.f, 0.f};
