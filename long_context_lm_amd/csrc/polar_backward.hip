@@ -65,6 +65,38 @@ __device__ __forceinline__ uint32_t pair_word(u32x2 w0, u32x2 w1, int e) {
                  : ((w0[e >> 1] & 0xFFFFu) | (w1[e >> 1] << 16));
 }
 
+// Gradient rows leave as whole 256-byte rows with non-temporal stores: a wave stages its
+// 32 rows (held in the 32x32 MFMA accumulator layout: lane l has row l % 32, dims
+// 32 db + 8 j4 + 4 (l / 32) + e in register 4 j4 + e of block db) in a wave-private LDS
+// area of 32 x kRowPitch floats, then stores four whole rows per instruction.  Whole lines
+// bypass the L2, so the launch does not end on a write-back of its outputs.
+constexpr int kRowPitch = kD + 4;
+__device__ __forceinline__ void stage_rows(float *st, const f32x16 (&acc)[2], float scale,
+                                           int lane) {
+  float *row = st + (lane & 31) * kRowPitch + 4 * (lane >> 5);
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4) {
+      f32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = acc[db][4 * j4 + e] * scale;
+      *(f32x4 *)(row + db * 32 + 8 * j4) = v;
+    }
+}
+// row_ptr(r): destination of row r (0..31) or NULL to skip it.
+template <class RowPtr>
+__device__ __forceinline__ void store_rows(const float *st, int lane, RowPtr row_ptr) {
+  const int cc = (lane & 15) * 4;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = 4 * i + (lane >> 4);
+    float *dst = row_ptr(r);
+    if (dst) __builtin_nontemporal_store(*(const f32x4 *)(st + r * kRowPitch + cc),
+                                         (f32x4 *)(dst + cc));
+  }
+}
+
 // ------------------------------------------------------------------ 1. per-row prep
 __global__ void __launch_bounds__(256) polar_bwd_prep_kernel(BwdArgs a) {
   const int tid = threadIdx.x, l16 = tid & 15;
@@ -332,19 +364,15 @@ __global__ void __launch_bounds__(64 * kWaves) polar_bwd_dq_kernel(BwdArgs a) {
     qd = half_sum(qd);
     if (valid && g32 == 0) a.rp[4 * rr] = tau * qd;
   }
-  if (valid) {
-    const float c = (a.beta ? a.beta[h] : 8.0f) * tau;
-    float *dqp = a.dq + rr * kD;
-#pragma unroll
-    for (int db = 0; db < 2; ++db)
-#pragma unroll
-      for (int j4 = 0; j4 < 4; ++j4) {
-        f32x4 val;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) val[e] = o[db][4 * j4 + e] * c;
-        *(f32x4 *)(dqp + db * 32 + 8 * j4 + 4 * g32) = val;
-      }
-  }
+  // dq = c o, through the wave's staging area (the tile buffers are free after the loop's
+  // last barrier; every staged load went through registers).
+  __shared__ __attribute__((aligned(16))) float Ost[kWaves][32 * kRowPitch];
+  stage_rows(Ost[wave], o, (a.beta ? a.beta[h] : 8.0f) * tau, lane);
+  __syncthreads();
+  store_rows(Ost[wave], lane, [&](int r) -> float * {
+    const int qrow = wrow0 + r;
+    return qrow < a.T ? a.dq + (((size_t)b * a.T + qrow) * a.Hq + h) * kD : nullptr;
+  });
 }
 
 // ------------------------------------------------------------------ 3. dk / dv
