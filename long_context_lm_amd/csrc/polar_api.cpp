@@ -259,12 +259,11 @@ polar_status polar_attn_bwd(const polar_params *p, polar_dtype dt, int32_t B, in
   if (B == 0 || T == 0) {
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = hipSuccess;
-    if (grads->d_beta && e == hipSuccess) e = hipMemsetAsync(grads->d_beta, 0, Hq * 4, s);
-    if (grads->d_null_bias && e == hipSuccess)
-      e = hipMemsetAsync(grads->d_null_bias, 0, Hq * 4, s);
+    if (grads->d_beta && e == hipSuccess) e = polar::launch_zero(grads->d_beta, Hq, s);
+    if (grads->d_null_bias && e == hipSuccess) e = polar::launch_zero(grads->d_null_bias, Hq, s);
     if (grads->d_count_vec && e == hipSuccess)
-      e = hipMemsetAsync(grads->d_count_vec, 0, (size_t)Hq * p->head_dim * 4, s);
-    if (e != hipSuccess) return fail(POLAR_ERR_HIP, "memset: %s", hipGetErrorString(e));
+      e = polar::launch_zero(grads->d_count_vec, (long long)Hq * p->head_dim, s);
+    if (e != hipSuccess) return fail(POLAR_ERR_HIP, "zero fill: %s", hipGetErrorString(e));
     return POLAR_OK;
   }
   if (!q || !k || !v) return fail(POLAR_ERR_NULL_POINTER, "q, k and v must be non-NULL");

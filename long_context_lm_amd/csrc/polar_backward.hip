@@ -753,6 +753,21 @@ int bwd_head_split(int G) {
   return 1;
 }
 
+// Zero fill by a kernel rather than hipMemsetAsync, so that a caller may capture the call in
+// a graph (a memset node there is avoided on purpose).
+__global__ void __launch_bounds__(256) polar_zero_kernel(float *p, long long n) {
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256)
+    p[i] = 0.f;
+}
+
+hipError_t launch_zero(float *p, long long n, hipStream_t stream) {
+  if (!p || n <= 0) return hipSuccess;
+  const long long blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(polar_zero_kernel, dim3((unsigned)(blocks < 1024 ? blocks : 1024)),
+                     dim3(256), 0, stream, p, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream) {
   const long long nrows = (long long)a.B * a.T * a.Hq;
   if (nrows <= 0) return hipSuccess;

@@ -149,5 +149,7 @@ int bwd_rows_per_block(int hb);
 int bwd_keys_per_block();
 int bwd_head_split(int G);                // workgroups sharing one key block (divides G)
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream);
+// p[0..n) = 0 with a kernel (capturable in a graph, unlike a memset node).
+hipError_t launch_zero(float *p, long long n, hipStream_t stream);
 
 }  // namespace polar
