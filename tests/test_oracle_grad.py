@@ -34,27 +34,35 @@ def _tiny(seed, B=1, T=6, Hq=2, Hkv=1, d=4):
     return q, k, v, beta, bias, w, cot
 
 
-def _loss_np(q, k, v, beta, bias, w, cot, train_len, flags):
-    out = oracle.polar_prefill(q, k, v, beta, bias, w, train_len, flags)
+def _loss_np(q, k, v, beta, bias, w, cot, train_len, flags, window=0, rope_theta=0.0):
+    out = oracle.polar_prefill(q, k, v, beta, bias, w, train_len, flags, window=window,
+                               rope_theta=rope_theta)
     return sum(float(np.sum(cot[n] * out[n])) for n in OUTS)
 
 
-@pytest.mark.parametrize("flags", [3, 0])
-def test_grad_matches_finite_differences(flags):
-    q, k, v, beta, bias, w, cot = _tiny(7 + flags)
+@pytest.mark.parametrize("flags,window,rope_theta", [
+    (3, 0, 0.0), (0, 0, 0.0),
+    (3, 3, 0.0),          # sliding window: rows 3.. lose their first keys, n = min(i+1, 3)
+    (3, 0, 7.0),          # RoPE (a small base, so that every pair turns noticeably)
+    (0, 2, 7.0),          # both
+])
+def test_grad_matches_finite_differences(flags, window, rope_theta):
+    q, k, v, beta, bias, w, cot = _tiny(7 + flags + window)
     train_len = 2                                  # tau > 1 from the third row on
-    g = oracle.polar_prefill_grad(q, k, v, cot, beta, bias, w, train_len, flags)
+    g = oracle.polar_prefill_grad(q, k, v, cot, beta, bias, w, train_len, flags,
+                                  window=window, rope_theta=rope_theta)
     args = dict(q=q, k=k, v=v, beta=beta, bias=bias, w=w)
     names = dict(q="dq", k="dk", v="dv", beta="d_beta", bias="d_null_bias", w="d_count_vec")
+    var = dict(window=window, rope_theta=rope_theta)
     eps = 1e-6
     for name, arr in args.items():
         fd = np.zeros(arr.shape)
         for idx in np.ndindex(arr.shape):
             saved = arr[idx]
             arr[idx] = saved + eps
-            lp = _loss_np(**args, cot=cot, train_len=train_len, flags=flags)
+            lp = _loss_np(**args, cot=cot, train_len=train_len, flags=flags, **var)
             arr[idx] = saved - eps
-            lm = _loss_np(**args, cot=cot, train_len=train_len, flags=flags)
+            lm = _loss_np(**args, cot=cot, train_len=train_len, flags=flags, **var)
             arr[idx] = saved
             fd[idx] = (lp - lm) / (2 * eps)
         got = g[names[name]].reshape(arr.shape)
@@ -147,6 +155,43 @@ def test_arg_max_keys_first_occurrence():
         for h in range(2):
             L = [beta[h] * float(q[0, i, h] @ k[0, jj, 0]) for jj in range(i + 1)]
             assert j[0, i, h] == L.index(max(L))
+
+
+def test_arg_max_keys_window():
+    """With a window W the maximum is taken over keys max(0, i-W+1)..i only."""
+    q, k, v, beta, bias, w, cot = _tiny(17, B=1, T=12, Hq=2, Hkv=1, d=4)
+    j = oracle.arg_max_keys(q, k, beta, 2048, 0, window=4)
+    for i in range(12):
+        for h in range(2):
+            lo = max(0, i - 3)
+            L = [float(q[0, i, h] @ k[0, jj, 0]) for jj in range(lo, i + 1)]
+            assert j[0, i, h] == lo + L.index(max(L))
+
+
+def test_rope_bf16_rounding_passes_gradients_through():
+    """With rope_bf16 the forward sees bfloat16-rounded rotations (equal to the numpy
+    oracle's rope_bf16 outputs) and the gradients are those of the rounded point taken as
+    exact: here, the direction cotangent against torch's SDPA backward on the rounded
+    rotations, carried back through the transposed rotation."""
+    q, k, v, beta, bias, w, cot = _tiny(19, B=1, T=9, Hq=2, Hkv=1, d=8)
+    g = oracle.polar_prefill_grad(q, k, v, dict(dir=cot["dir"]), np.full(2, 3.0), bias, w,
+                                  2048, 0, return_outputs=True, rope_theta=50.0,
+                                  rope_bf16=True)
+    ref = oracle.polar_prefill(q, k, v, np.full(2, 3.0), bias, w, 2048, 0, rope_theta=50.0,
+                               rope_bf16=True)
+    np.testing.assert_allclose(g["outputs"]["dir"], ref["dir"], rtol=1e-12, atol=1e-12)
+    qr = torch.tensor(oracle.round_bf16(oracle.rope(q, 50.0))).transpose(1, 2).requires_grad_(True)
+    kr = torch.tensor(oracle.round_bf16(oracle.rope(k, 50.0))).transpose(1, 2).requires_grad_(True)
+    vt = torch.tensor(v).transpose(1, 2)
+    u = torch.nn.functional.scaled_dot_product_attention(
+        qr, kr.repeat_interleave(2, dim=1), vt.repeat_interleave(2, dim=1), is_causal=True,
+        scale=3.0)
+    (torch.tensor(cot["dir"]).transpose(1, 2) * (u / u.norm(dim=-1, keepdim=True))).sum().backward()
+    # The transposed rotation is the rotation by the opposite angle.
+    dq = oracle.rope(qr.grad.transpose(1, 2).numpy(), 50.0, -np.arange(9.0))
+    dk = oracle.rope(kr.grad.transpose(1, 2).numpy(), 50.0, -np.arange(9.0))
+    np.testing.assert_allclose(g["dq"], dq, rtol=1e-10, atol=1e-10)
+    np.testing.assert_allclose(g["dk"], dk, rtol=1e-10, atol=1e-10)
 
 
 def test_cotangents_seeded():
