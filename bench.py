@@ -11,7 +11,7 @@ algorithmic flop count 4*d*Hq*T(T+1)/2 (QK^T and PV over visible pairs only); th
 figure (GB/s of K+V read once, plus table, queries and outputs) sits in ``decode``.  After
 the timed steps, the backward pass is timed on its own at the 2K training shape and
 reported in ``backward`` (TFLOP/s over the five products of the gradient, 2.5x the
-forward count).
+forward count); ``backward.variant`` times the same for the 512-key window + RoPE arm.
 
 Besides the headline pair, the JSON line carries one object per further leg, each with its
 own roofline and, unless ``--no-cpu-baseline``, the oracle timed beside it: the forward at
@@ -262,6 +262,7 @@ def measure_backward(dev, steps: int, warmup: int, with_cpu: bool):
                         "traffic": traffic_record("backward")}}
     print(f"[bench] backward mean {b_ms:.3f} ms ({tf:.1f} TFLOP/s), training forward "
           f"{f_ms:.3f} ms", file=sys.stderr, flush=True)
+    rec["variant"] = measure_backward_variant(dev, steps, warmup, q, k, v, kw, cot, p)
     if with_cpu:
         def job():
             import oracle
@@ -276,6 +277,47 @@ def measure_backward(dev, steps: int, warmup: int, with_cpu: bool):
                           f"({t:.1f} s)"}
         CPU_JOBS.append(job)
     return rec
+
+
+def measure_backward_variant(dev, steps: int, warmup: int, q, k, v, kw, cot, p,
+                             window: int = 512, theta: float = 10000.0):
+    """Training forward + backward of the window + RoPE arm at the same 2K shape: the
+    rotations of q and k, the windowed kernels and the inverse rotation of dq and dk."""
+    import torch
+    from long_context_lm_amd import attn_bwd, attn_fwd_train, bwd_workspace_bytes
+    from long_context_lm_amd import train_variant_workspace_bytes
+    vw = dict(window=window, rope_theta=theta)
+    wf = torch.empty(train_variant_workspace_bytes(p.Hq, p.Hkv, p.B, p.T, **vw),
+                     dtype=torch.uint8, device=dev)
+    wb = torch.empty(bwd_workspace_bytes(p.Hq, p.Hkv, p.B, p.T, **vw), dtype=torch.uint8,
+                     device=dev)
+    fwd = attn_fwd_train(q, k, v, workspace=wf, **vw, **kw)
+    for _ in range(warmup):
+        attn_fwd_train(q, k, v, workspace=wf, **vw, **kw)
+        attn_bwd(q, k, v, fwd, cot, workspace=wb, **vw, **kw)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for e in ev:
+        e[0].record()
+        fwd = attn_fwd_train(q, k, v, workspace=wf, **vw, **kw)
+        e[1].record()
+        attn_bwd(q, k, v, fwd, cot, workspace=wb, **vw, **kw)
+        e[2].record()
+    torch.cuda.synchronize()
+    f_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    b_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    Fb = 2.5 * 4.0 * p.d * p.B * p.Hq * visible_pairs(p.T, window)
+    tf = Fb / (b_ms * 1e-3) / 1e12
+    print(f"[bench] backward, window {window} + RoPE: {b_ms:.3f} ms ({tf:.1f} TFLOP/s), "
+          f"training forward {f_ms:.3f} ms", file=sys.stderr, flush=True)
+    return {"workload": f"backward of the {window}-key window + RoPE (theta {theta:g}) "
+                        "prefill at the same shape, rotations of q and k and the inverse "
+                        "rotation of dq and dk included",
+            "value": round(tf, 2), "unit": "TFLOP/s", "bwd_ms": round(b_ms, 4),
+            "fwd_train_ms": round(f_ms, 4),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                         "traffic": None}}
 
 
 def visible_pairs(T: int, window: int) -> float:
@@ -689,8 +731,10 @@ LEG_KERNELS = {
     "prefill_c3": [(r"polar_prefill_kernel<Bf16, 1, 8, 0,", 524288, -1)],
     "decode_b1": [(r"polar_decode_split_kernel<Bf16>", 131072, -1),
                   (r"polar_decode_combine_kernel", 16384, -1)],
-    "backward": [(r"polar_bwd_prep_kernel", None, -1), (r"polar_bwd_dq_kernel", None, -1),
-                 (r"polar_bwd_dkv_kernel", None, -1), (r"polar_bwd_dkv_add_kernel", None, -1),
+    "backward": [(r"polar_bwd_prep_kernel", None, -1),
+                 (r"polar_bwd_dq_kernel<8, false>", None, -1),
+                 (r"polar_bwd_dkv_kernel<4, 1, false>", None, -1),
+                 (r"polar_bwd_dkv_add_kernel", None, -1),
                  (r"polar_bwd_param_kernel", None, -1),
                  (r"polar_bwd_param_final_kernel", None, -1)],
     "fwd_train": [(r"polar_prefill_kernel<Bf16, 1, 8, 1,", None, -1)],

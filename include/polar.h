@@ -1,5 +1,5 @@
 /*
- * libpolar — Polar Attention forward for AMD Instinct MI355X (gfx950).  C ABI, version 5
+ * libpolar — Polar Attention forward for AMD Instinct MI355X (gfx950).  C ABI, version 6
  * (POLAR_ABI_VERSION below; polar_abi_version() reports the loaded library's).
  *
  * The operation is the attention mixing step of the ATMA hybrid decoder as described in
@@ -50,8 +50,10 @@ extern "C" {
  * 3: polar_decode_workspace_bytes lost its page_size argument (the only page size is 64 and
  *    the workspace never depended on it).
  * 4: polar_delta_sequence (the memory stream over T tokens) added; nothing else changed.
- * 5: polar_attn_fwd_mixed (the three streams summed into one output) added. */
-#define POLAR_ABI_VERSION 5
+ * 5: polar_attn_fwd_mixed (the three streams summed into one output) added.
+ * 6: the training forward and the backward of the window and RoPE variants added
+ *    (polar_attn_fwd_train_variant, polar_attn_bwd_variant and their workspace sizes). */
+#define POLAR_ABI_VERSION 6
 
 #if defined(__GNUC__)
 #define POLAR_API __attribute__((visibility("default")))
@@ -317,6 +319,53 @@ POLAR_API polar_status polar_attn_bwd(const polar_params *p, polar_dtype dt, int
                             const polar_outputs *fwd, const polar_saved *saved,
                             const polar_cotangents *cot, const polar_grads *grads,
                             void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Training forward and backward of the variant modes (the sliding-window and RoPE arms
+ * trained beside NoPE Polar Attention in the technical summary's section 3.1, "Ablation
+ * Insights").  var->window and
+ * var->rope_theta as for polar_attn_fwd_variant; var->attn must be NULL (the plain softmax
+ * read-out has no backward here: POLAR_ERR_UNSUPPORTED).  var == NULL, or window and
+ * rope_theta both 0, gives polar_attn_fwd_train and polar_attn_bwd.
+ *
+ * With RoPE both calls rotate q and k into their workspace first (rounded to the input
+ * type, as polar_attn_fwd_variant rotates them), run the causal kernels on the rotated
+ * vectors, and the backward turns dq and dk back by the transposed rotation, so its
+ * gradients are with respect to the unrotated q and k (the rounding of the rotated
+ * vectors is passed through unchanged).
+ *
+ * polar_train_variant_workspace_bytes: bytes polar_attn_fwd_train_variant needs in
+ *   var->workspace (16-byte aligned, contents scratch): B*T*(Hq+Hkv)*d elements of dt
+ *   with RoPE, 0 without (then var->workspace may be NULL).  0 also on invalid arguments.
+ * polar_attn_fwd_train_variant: as polar_attn_fwd_train (outputs, residuals, errors),
+ *   with the variant's window and rotation; its outputs are those of
+ *   polar_attn_fwd_variant for the same arguments.
+ * polar_bwd_variant_workspace_bytes: bytes of polar_attn_bwd_variant's workspace
+ *   (polar_bwd_workspace_bytes plus, with RoPE, room for the rotated q and k); 0 on
+ *   invalid arguments.  var->workspace is not used by the backward.
+ * polar_attn_bwd_variant: as polar_attn_bwd, for the outputs and residuals of
+ *   polar_attn_fwd_train_variant with the same var; bf16 inputs only.
+ */
+POLAR_API size_t polar_train_variant_workspace_bytes(const polar_params *p,
+                                                     const polar_variant *var, polar_dtype dt,
+                                                     int32_t B, int32_t T);
+POLAR_API polar_status polar_attn_fwd_train_variant(const polar_params *p,
+                                                    const polar_variant *var, polar_dtype dt,
+                                                    int32_t B, int32_t T, const void *q,
+                                                    const void *k, const void *v,
+                                                    const polar_outputs *out,
+                                                    const polar_saved *saved, void *stream);
+POLAR_API size_t polar_bwd_variant_workspace_bytes(const polar_params *p,
+                                                   const polar_variant *var, int32_t B,
+                                                   int32_t T);
+POLAR_API polar_status polar_attn_bwd_variant(const polar_params *p, const polar_variant *var,
+                                              polar_dtype dt, int32_t B, int32_t T,
+                                              const void *q, const void *k, const void *v,
+                                              const polar_outputs *fwd,
+                                              const polar_saved *saved,
+                                              const polar_cotangents *cot,
+                                              const polar_grads *grads, void *workspace,
+                                              size_t workspace_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------------
  * Paged KV cache: append and chunked prefill (the step before decode in section 2.2: new

@@ -34,6 +34,8 @@ EXPORTS = ("polar_attn_fwd", "polar_attn_fwd_mixed", "polar_decode_workspace_byt
            "polar_attn_fwd_variant", "polar_variant_workspace_bytes", "polar_kv_append",
            "polar_attn_prefill_paged",
            "polar_delta_step", "polar_delta_sequence",
+           "polar_train_variant_workspace_bytes", "polar_attn_fwd_train_variant",
+           "polar_bwd_variant_workspace_bytes", "polar_attn_bwd_variant",
            "polar_status_str", "polar_last_error", "polar_abi_version")
 
 
@@ -122,6 +124,20 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                            VP, VP, P(polar_outputs), VP]
     lib.polar_variant_workspace_bytes.restype = SZ
     lib.polar_variant_workspace_bytes.argtypes = [P(polar_params), I32, I32, I32]
+    lib.polar_train_variant_workspace_bytes.restype = SZ
+    lib.polar_train_variant_workspace_bytes.argtypes = [P(polar_params), P(polar_variant), I32,
+                                                        I32, I32]
+    lib.polar_attn_fwd_train_variant.restype = I32
+    lib.polar_attn_fwd_train_variant.argtypes = [P(polar_params), P(polar_variant), I32, I32,
+                                                 I32, VP, VP, VP, P(polar_outputs),
+                                                 P(polar_saved), VP]
+    lib.polar_bwd_variant_workspace_bytes.restype = SZ
+    lib.polar_bwd_variant_workspace_bytes.argtypes = [P(polar_params), P(polar_variant), I32,
+                                                      I32]
+    lib.polar_attn_bwd_variant.restype = I32
+    lib.polar_attn_bwd_variant.argtypes = [P(polar_params), P(polar_variant), I32, I32, I32, VP,
+                                           VP, VP, P(polar_outputs), P(polar_saved),
+                                           P(polar_cotangents), P(polar_grads), VP, SZ, VP]
     lib.polar_kv_append.restype = I32
     lib.polar_kv_append.argtypes = [P(polar_params), I32, I32, I32, VP, VP, VP, VP, I32, I32, VP,
                                     I32, VP, I32, VP]
@@ -246,6 +262,34 @@ def polar_attn_bwd(params, dtype, B, T, q, k, v, fwd, saved, cot, grads, workspa
     return load().polar_attn_bwd(ctypes.byref(params), dtype, B, T, q, k, v, ctypes.byref(fwd),
                                  ctypes.byref(saved), ctypes.byref(cot), ctypes.byref(grads),
                                  workspace, workspace_bytes, stream)
+
+
+def _var_ref(variant):
+    return None if variant is None else ctypes.byref(variant)
+
+
+def polar_train_variant_workspace_bytes(params, variant, dtype, B, T) -> int:
+    return load().polar_train_variant_workspace_bytes(ctypes.byref(params), _var_ref(variant),
+                                                      dtype, B, T)
+
+
+def polar_attn_fwd_train_variant(params, variant, dtype, B, T, q, k, v, outputs, saved,
+                                 stream) -> int:
+    return load().polar_attn_fwd_train_variant(ctypes.byref(params), _var_ref(variant), dtype,
+                                               B, T, q, k, v, ctypes.byref(outputs),
+                                               ctypes.byref(saved), stream)
+
+
+def polar_bwd_variant_workspace_bytes(params, variant, B, T) -> int:
+    return load().polar_bwd_variant_workspace_bytes(ctypes.byref(params), _var_ref(variant), B, T)
+
+
+def polar_attn_bwd_variant(params, variant, dtype, B, T, q, k, v, fwd, saved, cot, grads,
+                           workspace, workspace_bytes, stream) -> int:
+    return load().polar_attn_bwd_variant(ctypes.byref(params), _var_ref(variant), dtype, B, T, q,
+                                         k, v, ctypes.byref(fwd), ctypes.byref(saved),
+                                         ctypes.byref(cot), ctypes.byref(grads), workspace,
+                                         workspace_bytes, stream)
 
 
 def check(status: int) -> None:

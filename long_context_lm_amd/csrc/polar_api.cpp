@@ -60,6 +60,42 @@ float inv_log_train(const polar_params *p) {
   return (p->flags & POLAR_FLAG_LENGTH_TEMP) ? (float)(1.0 / log((double)p->train_len)) : 0.f;
 }
 
+// RoPE frequencies of the kernels: revolutions per position of pair t, rounded to 2^-64
+// units (< 1/(2 pi), so they fit); all zero when theta == 0.
+void fill_rope_f(uint64_t *f, float theta) {
+  for (int t = 0; t < polar::kHeadDim / 2; ++t) {
+    f[t] = 0;
+    if (theta > 0.f) {
+      const long double r = powl((long double)theta, -2.0L * t / polar::kHeadDim) /
+                            (2.0L * 3.14159265358979323846264338327950288L);
+      f[t] = (uint64_t)(r * 18446744073709551616.0L + 0.5L);
+    }
+  }
+}
+
+polar_status check_variant(const polar_variant *var) {
+  if (!var) return POLAR_OK;
+  if (var->window < 0) return fail(POLAR_ERR_BAD_SHAPE, "window (%d) must be >= 0", var->window);
+  if (!(var->rope_theta >= 0.f) || !isfinite(var->rope_theta) ||
+      (var->rope_theta > 0.f && var->rope_theta <= 1.f))
+    return fail(POLAR_ERR_BAD_SHAPE, "rope_theta must be 0 or a finite value > 1");
+  return POLAR_OK;
+}
+
+// Rotates x [B,T,H,d] of type dt by RoPE into out, with polar_attn_fwd_variant's rounding.
+hipError_t rotate_rows(polar_dtype dt, const void *x, void *out, int B, int T, int H,
+                       float theta, hipStream_t stream) {
+  polar::PrefillArgs r{};
+  r.k = x;
+  r.B = B;
+  r.T = T;
+  r.Hkv = H;
+  fill_rope_f(r.rope_f, theta);
+  return polar::launch_rope_keys((int)dt, r, out, stream);
+}
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
 struct PagedSrc {
   const int32_t *page_table, *start_pos;
   int stride, num_pages, max_seq_len;
@@ -73,10 +109,8 @@ polar_status prefill(const polar_params *p, polar_dtype dt, int32_t B, int32_t T
   polar_status st = check_params(p, dt, out);
   if (st != POLAR_OK) return st;
   if (var) {
-    if (var->window < 0) return fail(POLAR_ERR_BAD_SHAPE, "window (%d) must be >= 0", var->window);
-    if (!(var->rope_theta >= 0.f) || !isfinite(var->rope_theta) ||
-        (var->rope_theta > 0.f && var->rope_theta <= 1.f))
-      return fail(POLAR_ERR_BAD_SHAPE, "rope_theta must be 0 or a finite value > 1");
+    st = check_variant(var);
+    if (st != POLAR_OK) return st;
     if (var->attn && !aligned16(var->attn))
       return fail(POLAR_ERR_MISALIGNED, "variant attn output must be 16-byte aligned");
     if (var->workspace && !aligned16(var->workspace))
@@ -121,7 +155,11 @@ polar_status prefill(const polar_params *p, polar_dtype dt, int32_t B, int32_t T
   a.attn = var ? var->attn : nullptr;
   a.window = var ? var->window : 0;
   a.rope = (var && var->rope_theta > 0.f) ? 1 : 0;
-  a.variant = (a.attn || a.window > 0 || a.rope) ? 1 : 0;
+  // The training forward takes its window in the training instance (and its q and k
+  // already rotated, see polar_attn_fwd_train_variant).
+  a.variant = (!saved && (a.attn || a.window > 0 || a.rope)) ? 1 : 0;
+  if (saved && (a.attn || a.rope))
+    return fail(POLAR_ERR_UNSUPPORTED, "the training forward takes no attn output or rotation here");
   // Keys rotated once into the caller's workspace instead of in every staging workgroup.
   void *k_rot = nullptr;
   if (a.rope && var->workspace) {
@@ -137,16 +175,7 @@ polar_status prefill(const polar_params *p, polar_dtype dt, int32_t B, int32_t T
   a.stride = paged ? paged->stride : 0;
   a.num_pages = paged ? paged->num_pages : 0;
   a.max_seq_len = paged ? paged->max_seq_len : 0;
-  for (int t = 0; t < polar::kHeadDim / 2; ++t) {
-    a.rope_f[t] = 0;
-    if (a.rope) {
-      // revolutions per position of pair t, rounded to 2^-64 units (< 1/(2 pi), fits)
-      const long double f = powl((long double)var->rope_theta,
-                                 -2.0L * t / polar::kHeadDim) /
-                            (2.0L * 3.14159265358979323846264338327950288L);
-      a.rope_f[t] = (uint64_t)(f * 18446744073709551616.0L + 0.5L);
-    }
-  }
+  fill_rope_f(a.rope_f, a.rope ? var->rope_theta : 0.f);
   a.B = B;
   a.T = T;
   a.Hq = p->n_q_heads;
@@ -234,6 +263,55 @@ polar_status polar_attn_fwd_train(const polar_params *p, polar_dtype dt, int32_t
   return prefill(p, dt, B, T, q, k, v, out, saved, nullptr, stream);
 }
 
+size_t polar_train_variant_workspace_bytes(const polar_params *p, const polar_variant *var,
+                                           polar_dtype dt, int32_t B, int32_t T) {
+  if (!p || B < 0 || T < 0 || p->n_kv_heads < 1 || p->n_q_heads < 1 ||
+      (dt != POLAR_DTYPE_BF16 && dt != POLAR_DTYPE_F32) || check_variant(var) != POLAR_OK)
+    return 0;
+  if (!var || var->rope_theta == 0.f) return 0;
+  return (size_t)B * T * (p->n_q_heads + p->n_kv_heads) * polar::kHeadDim *
+         (dt == POLAR_DTYPE_BF16 ? 2 : 4);
+}
+
+polar_status polar_attn_fwd_train_variant(const polar_params *p, const polar_variant *var,
+                                          polar_dtype dt, int32_t B, int32_t T, const void *q,
+                                          const void *k, const void *v,
+                                          const polar_outputs *out, const polar_saved *saved,
+                                          void *stream) {
+  if (!saved) return fail(POLAR_ERR_NULL_POINTER, "saved is NULL");
+  polar_status st = check_variant(var);
+  if (st != POLAR_OK) return st;
+  if (var && var->attn)
+    return fail(POLAR_ERR_UNSUPPORTED, "the training forward takes no softmax read-out (var.attn)");
+  // The window goes to the training instance; a rotation is done here, into the workspace.
+  polar_variant w{};
+  w.window = var ? var->window : 0;
+  const float theta = var ? var->rope_theta : 0.f;
+  if (theta == 0.f) return prefill(p, dt, B, T, q, k, v, out, saved, &w, stream);
+  st = check_params(p, dt, out);
+  if (st != POLAR_OK) return st;
+  if (B < 0 || T < 0) return fail(POLAR_ERR_BAD_SHAPE, "B (%d) and T (%d) must be >= 0", B, T);
+  if (B == 0 || T == 0) return POLAR_OK;
+  if (!q || !k || !v) return fail(POLAR_ERR_NULL_POINTER, "q, k and v must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v))
+    return fail(POLAR_ERR_MISALIGNED, "q, k and v must be 16-byte aligned");
+  if (!var->workspace) return fail(POLAR_ERR_NULL_POINTER, "RoPE needs var.workspace");
+  if (!aligned16(var->workspace))
+    return fail(POLAR_ERR_MISALIGNED, "variant workspace must be 16-byte aligned");
+  const size_t need = polar_train_variant_workspace_bytes(p, var, dt, B, T);
+  if (var->workspace_bytes < need)
+    return fail(POLAR_ERR_WORKSPACE_TOO_SMALL, "variant workspace has %zu bytes, needs %zu",
+                var->workspace_bytes, need);
+  const size_t qbytes =
+      (size_t)B * T * p->n_q_heads * polar::kHeadDim * (dt == POLAR_DTYPE_BF16 ? 2 : 4);
+  char *qr = (char *)var->workspace, *kr = qr + qbytes;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = rotate_rows(dt, q, qr, B, T, p->n_q_heads, theta, s);
+  if (e == hipSuccess) e = rotate_rows(dt, k, kr, B, T, p->n_kv_heads, theta, s);
+  if (e != hipSuccess) return fail(POLAR_ERR_HIP, "rotation launch: %s", hipGetErrorString(e));
+  return prefill(p, dt, B, T, qr, kr, v, out, saved, &w, stream);
+}
+
 size_t polar_bwd_workspace_bytes(const polar_params *p, int32_t B, int32_t T) {
   if (!p || B < 1 || T < 1 || p->n_kv_heads < 1 || p->n_q_heads < 1 ||
       p->n_q_heads % p->n_kv_heads != 0 || !bwd_shape_ok(B, T, p->n_q_heads, p->n_kv_heads))
@@ -241,13 +319,20 @@ size_t polar_bwd_workspace_bytes(const polar_params *p, int32_t B, int32_t T) {
   return polar::bwd_ws_bytes(B, T, p->n_q_heads, p->n_kv_heads);
 }
 
-polar_status polar_attn_bwd(const polar_params *p, polar_dtype dt, int32_t B, int32_t T,
-                            const void *q, const void *k, const void *v,
-                            const polar_outputs *fwd, const polar_saved *saved,
-                            const polar_cotangents *cot, const polar_grads *grads,
-                            void *workspace, size_t workspace_bytes, void *stream) {
+// The backward, with the variant's window and rotation (var may be NULL).
+static polar_status bwd_impl(const polar_params *p, const polar_variant *var, polar_dtype dt,
+                             int32_t B, int32_t T, const void *q, const void *k, const void *v,
+                             const polar_outputs *fwd, const polar_saved *saved,
+                             const polar_cotangents *cot, const polar_grads *grads,
+                             void *workspace, size_t workspace_bytes, void *stream) {
   polar_status st = check_params(p, dt, fwd);
   if (st != POLAR_OK) return st;
+  st = check_variant(var);
+  if (st != POLAR_OK) return st;
+  if (var && var->attn)
+    return fail(POLAR_ERR_UNSUPPORTED, "the backward takes no softmax read-out (var.attn)");
+  const int window = var ? var->window : 0;
+  const float theta = var ? var->rope_theta : 0.f;
   if (dt != POLAR_DTYPE_BF16)
     return fail(POLAR_ERR_UNSUPPORTED, "the backward pass takes bf16 inputs only");
   if (!saved || !cot || !grads)
@@ -257,12 +342,12 @@ polar_status polar_attn_bwd(const polar_params *p, polar_dtype dt, int32_t B, in
     return fail(POLAR_ERR_NULL_POINTER, "cot.count given but params.count_vec is NULL");
   const int Hq = p->n_q_heads;
   if (B == 0 || T == 0) {
-    hipStream_t s = (hipStream_t)stream;
+    hipStream_t zs = (hipStream_t)stream;
     hipError_t e = hipSuccess;
-    if (grads->d_beta && e == hipSuccess) e = polar::launch_zero(grads->d_beta, Hq, s);
-    if (grads->d_null_bias && e == hipSuccess) e = polar::launch_zero(grads->d_null_bias, Hq, s);
+    if (grads->d_beta && e == hipSuccess) e = polar::launch_zero(grads->d_beta, Hq, zs);
+    if (grads->d_null_bias && e == hipSuccess) e = polar::launch_zero(grads->d_null_bias, Hq, zs);
     if (grads->d_count_vec && e == hipSuccess)
-      e = polar::launch_zero(grads->d_count_vec, (long long)Hq * p->head_dim, s);
+      e = polar::launch_zero(grads->d_count_vec, (long long)Hq * p->head_dim, zs);
     if (e != hipSuccess) return fail(POLAR_ERR_HIP, "zero fill: %s", hipGetErrorString(e));
     return POLAR_OK;
   }
@@ -286,10 +371,25 @@ polar_status polar_attn_bwd(const polar_params *p, polar_dtype dt, int32_t B, in
   if (!bwd_shape_ok(B, T, Hq, p->n_kv_heads))
     return fail(POLAR_ERR_BAD_SHAPE, "T*Hq too large for the backward (B=%d, T=%d, Hq=%d)", B,
                 T, Hq);
-  const size_t need = polar::bwd_ws_bytes(B, T, Hq, p->n_kv_heads);
+  const size_t base = polar::bwd_ws_bytes(B, T, Hq, p->n_kv_heads);
+  const size_t qbytes = (size_t)B * T * Hq * polar::kHeadDim * 2;
+  const size_t kbytes = (size_t)B * T * p->n_kv_heads * polar::kHeadDim * 2;
+  const size_t need = theta > 0.f ? align256(base) + align256(qbytes) + kbytes : base;
   if (workspace_bytes < need)
     return fail(POLAR_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed",
                 workspace_bytes, need);
+
+  hipStream_t s = (hipStream_t)stream;
+  if (theta > 0.f) {
+    // The kernels run on the rotated q and k, held after the backward's own workspace.
+    char *qr = (char *)workspace + align256(base);
+    char *kr = qr + align256(qbytes);
+    hipError_t e = rotate_rows(dt, q, qr, B, T, Hq, theta, s);
+    if (e == hipSuccess) e = rotate_rows(dt, k, kr, B, T, p->n_kv_heads, theta, s);
+    if (e != hipSuccess) return fail(POLAR_ERR_HIP, "rotation launch: %s", hipGetErrorString(e));
+    q = qr;
+    k = kr;
+  }
 
   polar::BwdArgs a;
   a.q = q;
@@ -328,14 +428,53 @@ polar_status polar_attn_bwd(const polar_params *p, polar_dtype dt, int32_t B, in
   a.hsplit = polar::bwd_head_split(a.G);
   a.inv_log_train = inv_log_train(p);
   a.null_floor = (p->flags & POLAR_FLAG_NULL_FLOOR) ? 1 : 0;
+  a.window = window;
   polar::bwd_ws_layout(a, workspace);
   const long long dq_blocks = (long long)a.n_row_blocks * a.Hkv * (a.G / a.hb) * B;
   const long long dkv_blocks = (long long)((a.n_key_blocks + 1) / 2) * a.hsplit * a.Hkv * B;
   if (dq_blocks > 0x7fffffffLL || dkv_blocks > 0x7fffffffLL)
     return fail(POLAR_ERR_BAD_SHAPE, "problem too large for one launch");
-  hipError_t err = polar::launch_bwd(a, (hipStream_t)stream);
+  hipError_t err = polar::launch_bwd(a, s);
   if (err != hipSuccess) return fail(POLAR_ERR_HIP, "backward launch: %s", hipGetErrorString(err));
+  if (theta > 0.f) {
+    // Gradients with respect to the unrotated q and k: the transposed rotation.
+    uint64_t f[polar::kHeadDim / 2];
+    fill_rope_f(f, theta);
+    err = polar::launch_unrope(grads->dq, B, T, Hq, f, s);
+    if (err == hipSuccess) err = polar::launch_unrope(grads->dk, B, T, p->n_kv_heads, f, s);
+    if (err != hipSuccess)
+      return fail(POLAR_ERR_HIP, "inverse rotation launch: %s", hipGetErrorString(err));
+  }
   return POLAR_OK;
+}
+
+polar_status polar_attn_bwd(const polar_params *p, polar_dtype dt, int32_t B, int32_t T,
+                            const void *q, const void *k, const void *v,
+                            const polar_outputs *fwd, const polar_saved *saved,
+                            const polar_cotangents *cot, const polar_grads *grads,
+                            void *workspace, size_t workspace_bytes, void *stream) {
+  return bwd_impl(p, nullptr, dt, B, T, q, k, v, fwd, saved, cot, grads, workspace,
+                  workspace_bytes, stream);
+}
+
+polar_status polar_attn_bwd_variant(const polar_params *p, const polar_variant *var,
+                                    polar_dtype dt, int32_t B, int32_t T, const void *q,
+                                    const void *k, const void *v, const polar_outputs *fwd,
+                                    const polar_saved *saved, const polar_cotangents *cot,
+                                    const polar_grads *grads, void *workspace,
+                                    size_t workspace_bytes, void *stream) {
+  return bwd_impl(p, var, dt, B, T, q, k, v, fwd, saved, cot, grads, workspace,
+                  workspace_bytes, stream);
+}
+
+size_t polar_bwd_variant_workspace_bytes(const polar_params *p, const polar_variant *var,
+                                         int32_t B, int32_t T) {
+  const size_t base = polar_bwd_workspace_bytes(p, B, T);
+  if (base == 0 || check_variant(var) != POLAR_OK) return 0;
+  if (!var || var->rope_theta == 0.f) return base;
+  const size_t qbytes = (size_t)B * T * p->n_q_heads * polar::kHeadDim * 2;
+  const size_t kbytes = (size_t)B * T * p->n_kv_heads * polar::kHeadDim * 2;
+  return align256(base) + align256(qbytes) + kbytes;
 }
 
 size_t polar_decode_workspace_bytes(const polar_params *p, int32_t B, int32_t max_seq_len) {

@@ -46,8 +46,13 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 using F = bf16x8;
 
-__device__ __forceinline__ float tau_of(int row, float inv_log_train) {
-  return inv_log_train > 0.f ? fmaxf(1.0f, logf((float)(row + 1)) * inv_log_train) : 1.0f;
+// Keys row i sees: i + 1, or min(i + 1, W) under a sliding window W.
+__device__ __forceinline__ int keys_seen(int row, int window) {
+  return window > 0 ? min(row + 1, window) : row + 1;
+}
+
+__device__ __forceinline__ float tau_of(int n, float inv_log_train) {
+  return inv_log_train > 0.f ? fmaxf(1.0f, logf((float)n) * inv_log_train) : 1.0f;
 }
 
 __device__ __forceinline__ const uint16_t *lds_at(const uint16_t *base, uint32_t off) {
@@ -134,7 +139,8 @@ __global__ void __launch_bounds__(256) polar_bwd_prep_kernel(BwdArgs a) {
   const float A = (a.c_lse ? a.c_lse[Rc] : 0.f) + 2.f * n * dn;
   const float E = -2.f * n2 * dn;
   const float beta = a.beta ? a.beta[h] : 8.0f;
-  const float tau = tau_of(i, a.inv_log_train);
+  const int nk = keys_seen(i, a.window);
+  const float tau = tau_of(nk, a.inv_log_train);
   const float c = beta * tau;
   if (!ok) return;
   bf16x4 o1, o2;
@@ -150,7 +156,7 @@ __global__ void __launch_bounds__(256) polar_bwd_prep_kernel(BwdArgs a) {
     const f32x4 r0 = {c * kLog2e, lse * kLog2e, c * A, c * E};
     const f32x4 r1 = {A, E, dm, __int_as_float(a.arg_max[Rc])};
     const float fl =
-        a.null_floor ? -dm * tau * 0.125f * sqrtf(2.f * logf((float)(i + 1))) : 0.f;
+        a.null_floor ? -dm * tau * 0.125f * sqrtf(2.f * logf((float)nk)) : 0.f;
     const f32x4 rp = {0.f, -dm, gate * th, fl};
     *(f32x4 *)(a.rows + 8 * Rc) = r0;
     *(f32x4 *)(a.rows + 8 * Rc + 4) = r1;
@@ -159,7 +165,8 @@ __global__ void __launch_bounds__(256) polar_bwd_prep_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------------------ 2. dq
-template <int kWaves>
+// kWin: the sliding-window instance (the causal one keeps the code it had without it).
+template <int kWaves, bool kWin>
 __global__ void __launch_bounds__(64 * kWaves) polar_bwd_dq_kernel(BwdArgs a) {
   constexpr int kThreads = 64 * kWaves;
   constexpr int KT = 64, KROW = 72, TROW = 72;
@@ -269,15 +276,20 @@ __global__ void __launch_bounds__(64 * kWaves) polar_bwd_dq_kernel(BwdArgs a) {
   const uint32_t t_lane = (uint32_t)((c32 * TROW + g32 * 8) * 2);
   constexpr uint32_t KBUF = KT * KROW * 2, TBUF = kD * TROW * 2;
 
-  stage_load(0);
+  // Under a sliding window the first tile is the one holding the workgroup's first
+  // visible key, and a wave skips the tiles wholly before its own first one.
+  const int W = kWin ? a.window : 0;
+  const int t_first = W > 0 ? max(0, row0 - W + 1) / KT : 0;
+  const int w_first = W > 0 ? wrow0 - W + 1 : 0;
+  stage_load(t_first);
   stage_store(0);
   __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
+  for (int t = t_first; t < ntiles; ++t) {
+    const int buf = (t - t_first) & 1;
     const bool more = t + 1 < ntiles;
     if (more) stage_load(t + 1);
     const int key0 = t * KT;
-    if (key0 <= w_last) {
+    if (key0 <= w_last && key0 + KT - 1 >= w_first) {
       const uint16_t *Kb = lds_at(&Ks[0][0], k_lane + buf * KBUF);
       const uint16_t *Vb = lds_at(&Vs[0][0], k_lane + buf * KBUF);
       const f32x16 zero = {};
@@ -303,7 +315,7 @@ __global__ void __launch_bounds__(64 * kWaves) polar_bwd_dq_kernel(BwdArgs a) {
             float s = S[kb][r];
             if constexpr (decltype(masked)::value) {
               const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * g32 + (r & 3);
-              if (key > row) s = -INFINITY;
+              if (key > row || (W > 0 && key <= row - W)) s = -INFINITY;
             }
             const float p = fast_exp2(fmaf(s, cl2, -lse2));
             x[r] = p * (P[kb][r] + fmaf(E, p, A));
@@ -312,7 +324,7 @@ __global__ void __launch_bounds__(64 * kWaves) polar_bwd_dq_kernel(BwdArgs a) {
           dl[kb][1] = Bf16::pack(x + 8);
         }
       };
-      if (key0 + KT - 1 > wrow0)
+      if (key0 + KT - 1 > wrow0 || (W > 0 && key0 <= wrow0 + 31 - W))
         dlogits(std::true_type{});
       else
         dlogits(std::false_type{});
@@ -345,7 +357,7 @@ __global__ void __launch_bounds__(64 * kWaves) polar_bwd_dq_kernel(BwdArgs a) {
         o[db][4 * j4 + 3] = fmaf(dm, bf16_hi(w[1]), o[db][4 * j4 + 3]);
       }
   }
-  const float tau = tau_of(valid ? row : 0, a.inv_log_train);
+  const float tau = tau_of(keys_seen(valid ? row : 0, a.window), a.inv_log_train);
   if (a.d_beta) {
     float qd = 0.f;
     if (valid) {
@@ -376,7 +388,7 @@ __global__ void __launch_bounds__(64 * kWaves) polar_bwd_dq_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------------------ 3. dk / dv
-template <int kWaves, int kDepth>
+template <int kWaves, int kDepth, bool kWin>
 __global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 polar_bwd_dkv_kernel(BwdArgs a) {
   constexpr int kThreads = 64 * kWaves;
@@ -411,6 +423,11 @@ polar_bwd_dkv_kernel(BwdArgs a) {
   const int g = bg % a.Hkv, b = bg / a.Hkv;
   const int nrt = (a.T + 31) / 32;
   const int rs = a.Hq * kD * 2;                     // bytes between rows of q / du
+  // Step s walks row tile rt_hi - s / GH: the last one that sees the key block (the last
+  // of the sequence, or under a sliding window W the one holding row k0 + KB - 2 + W),
+  // down to the key block's own.
+  const int W = kWin ? a.window : 0;
+  int rt_hi = nrt - 1;
 
   // Loop-invariant per-thread buffer offsets; the row tile and head move the resource
   // base, so rows past T fall outside the resource and load zeros.
@@ -432,7 +449,7 @@ polar_bwd_dkv_kernel(BwdArgs a) {
     u32x4 &qst = R.qst, &cst = R.cst;
     u32x2 *qtst = R.qtst, *dtst = R.dtst;
     f32x4 &sst = R.sst;
-    const int r0row = (nrt - 1 - s / GH) * 32;
+    const int r0row = (rt_hi - s / GH) * 32;
     const int h = g * a.G + hbase + s % GH;
     const size_t row0 = ((size_t)b * a.T + r0row) * a.Hq + h;
     const int nbytes = (int)(((size_t)(a.T - r0row) * a.Hq - h) * kD * 2);
@@ -460,7 +477,7 @@ polar_bwd_dkv_kernel(BwdArgs a) {
     const u32x4 &qst = R.qst, &cst = R.cst;
     const u32x2 *qtst = R.qtst, *dtst = R.dtst;
     f32x4 &sst = R.sst;
-    if (tid < 64 && (nrt - 1 - s / GH) * 32 + (tid & 31) >= a.T) {
+    if (tid < 64 && (rt_hi - s / GH) * 32 + (tid & 31) >= a.T) {
       const f32x4 pad0 = {1.f, INFINITY, 0.f, 0.f};
       const f32x4 pad1 = {0.f, 0.f, 0.f, __int_as_float(-1)};
       sst = tid < 32 ? pad0 : pad1;
@@ -490,6 +507,7 @@ polar_bwd_dkv_kernel(BwdArgs a) {
     const int kblk = half == 0 ? pair : a.n_key_blocks - 1 - pair;
     if (half == 1 && kblk == pair) break;            // odd count: the middle block once
     const int k0 = kblk * KB;
+    rt_hi = W > 0 ? min(nrt - 1, (k0 + KB - 2 + W) / 32) : nrt - 1;
     const int kw0 = k0 + wave * 32;
     const int key = kw0 + c32;
     const bool kvalid = key < a.T;
@@ -515,7 +533,7 @@ polar_bwd_dkv_kernel(BwdArgs a) {
         dV[db][r] = 0.f;
       }
 
-    const int nsteps = (nrt - k0 / 32) * GH;
+    const int nsteps = (rt_hi + 1 - k0 / 32) * GH;
     // Pipeline: step s computes from LDS buffer s&1; at its end, step s+1's staged set is
     // stored to the other buffer and refilled with step s+1+kDepth, so every load has
     // kDepth steps to arrive.  The step loop is unrolled by kDepth to keep set indices
@@ -532,8 +550,8 @@ polar_bwd_dkv_kernel(BwdArgs a) {
         const int s = s0 + u;
         if (s >= nsteps) break;
         const int buf = s & 1;
-        const int r0row = (nrt - 1 - s / GH) * 32;
-        if (r0row + 31 >= kw0 && kw0 < a.T) {
+        const int r0row = (rt_hi - s / GH) * 32;
+        if (r0row + 31 >= kw0 && kw0 < a.T && (W == 0 || r0row <= kw0 + 30 + W)) {
           const uint16_t *Qb = lds_at(&Qs[0][0], q_lane + buf * QBUF);
           const uint16_t *Cb = lds_at(&Cs[0][0], q_lane + buf * QBUF);
           const f32x16 zero = {};
@@ -558,14 +576,15 @@ polar_bwd_dkv_kernel(BwdArgs a) {
                 const int r = 4 * a4 + c;
                 float p = fast_exp2(fmaf(S[r], cl[c], -ls[c]));
                 if constexpr (decltype(masked)::value) {
-                  if (r0row + ri0 + c < key) p = 0.f;
+                  const int row = r0row + ri0 + c;
+                  if (row < key || (W > 0 && row - W >= key)) p = 0.f;
                 }
                 pv[r] = p;
                 dsv[r] = p * (P[r] + fmaf(ec[c], p, ac[c]));
               }
             }
           };
-          if (r0row < kw0 + 31)
+          if (r0row < kw0 + 31 || (W > 0 && r0row + 31 - W >= kw0))
             probs(std::true_type{});
           else
             probs(std::false_type{});
@@ -774,12 +793,19 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream) {
   hipLaunchKernelGGL(polar_bwd_prep_kernel, dim3((unsigned)((nrows + 15) / 16)), dim3(256), 0,
                      stream, a);
   const long long dq_blocks = (long long)a.n_row_blocks * a.Hkv * (a.G / a.hb) * a.B;
-  hipLaunchKernelGGL((polar_bwd_dq_kernel<kDqWaves>), dim3((unsigned)dq_blocks),
-                     dim3(64 * kDqWaves), 0, stream, a);
   const long long dkv_blocks =
       (long long)((a.n_key_blocks + 1) / 2) * a.hsplit * a.Hkv * a.B;
-  hipLaunchKernelGGL((polar_bwd_dkv_kernel<kDkvWaves, kDkvDepth>), dim3((unsigned)dkv_blocks),
-                     dim3(64 * kDkvWaves), 0, stream, a);
+  if (a.window > 0) {
+    hipLaunchKernelGGL((polar_bwd_dq_kernel<kDqWaves, true>), dim3((unsigned)dq_blocks),
+                       dim3(64 * kDqWaves), 0, stream, a);
+    hipLaunchKernelGGL((polar_bwd_dkv_kernel<kDkvWaves, kDkvDepth, true>),
+                       dim3((unsigned)dkv_blocks), dim3(64 * kDkvWaves), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((polar_bwd_dq_kernel<kDqWaves, false>), dim3((unsigned)dq_blocks),
+                       dim3(64 * kDqWaves), 0, stream, a);
+    hipLaunchKernelGGL((polar_bwd_dkv_kernel<kDkvWaves, kDkvDepth, false>),
+                       dim3((unsigned)dkv_blocks), dim3(64 * kDkvWaves), 0, stream, a);
+  }
   if (a.hsplit > 1) {
     const long long n4 = (long long)a.B * a.T * a.Hkv * kD / 4;
     hipLaunchKernelGGL(polar_bwd_dkv_add_kernel, dim3((unsigned)min((n4 + 255) / 256, 8192LL)),

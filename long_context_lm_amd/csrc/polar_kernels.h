@@ -57,6 +57,10 @@ hipError_t launch_prefill(int dtype, const PrefillArgs &a, hipStream_t stream);
 // Rotates the keys a.k [B,T,Hkv,d] by RoPE at positions 0..T-1 into k_out (same layout),
 // with exactly the arithmetic the prefill's staging applies.
 hipError_t launch_rope_keys(int dtype, const PrefillArgs &a, void *k_out, hipStream_t stream);
+// Gradients through RoPE: fp32 rows x [B,T,H,d] turned in place by the transposed rotation
+// (rope_f as in PrefillArgs).
+hipError_t launch_unrope(float *x, int B, int T, int H, const uint64_t *rope_f,
+                         hipStream_t stream);
 
 struct DecodeArgs {
   const void *q;                          // [B,Hq,d]
@@ -140,6 +144,7 @@ struct BwdArgs {
   int n_part;                             // parameter reduction: row chunks per head
   float inv_log_train;
   int null_floor;
+  int window;                             // W >= 1: row i sees keys i-W+1..i; 0: all
 };
 constexpr int kPartStride = 68;           // dw[64], dbeta, dbias, pad
 

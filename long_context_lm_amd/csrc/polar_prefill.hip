@@ -26,7 +26,7 @@
 //    Raising the reference rescales S and u by 2^(M_old-M_new) and Q by its square, the
 //    squared correction factor of section 2.2;
 //  * epilogue: n_eff = S^2/Q, lse, the floor gate, dir = u/|u|, count;
-//  * training instances (kMode == kModeSave) also keep, per lane, the first key attaining
+//  * training instances (kModeSave, kModeSaveWin) also keep, per lane, the first key attaining
 //    the lane's running maximum score and write |u| and that key (the row's arg-max) for
 //    the backward pass;
 //  * variant instances add a sliding window, RoPE and the plain softmax output: q is
@@ -77,6 +77,9 @@ constexpr int kModePlain = 0, kModeSave = 1, kModeVariant = 2, kModePaged = 3;
 constexpr int kModeVariantRot = 4;
 // Plain prefill writing dir + count + memory as one output (a.mixed).
 constexpr int kModeMix = 5;
+// The training instance under a sliding window (its own instance, so that the causal
+// training forward keeps the code it had without the window).
+constexpr int kModeSaveWin = 6;
 
 // RoPE rotation angle of pair t at position pos: revolutions = frac(pos * f_t) taken
 // exactly from the 64-bit fixed-point product, then the hardware sine and cosine, whose
@@ -105,10 +108,13 @@ __device__ __forceinline__ float rot_im(float x0, float x1, float c, float s) {
 template <class TR, int QB, int kWaves, int kMode, bool kLean>
 __global__ void __launch_bounds__(64 * kWaves, kLean ? 4 : 1)
     polar_prefill_kernel(PrefillArgs a) {
-  constexpr bool kSave = kMode == kModeSave;
+  constexpr bool kSave = kMode == kModeSave || kMode == kModeSaveWin;
   constexpr bool kVar = kMode == kModeVariant || kMode == kModeVariantRot;
   constexpr bool kPaged = kMode == kModePaged;
   constexpr bool kMix = kMode == kModeMix;
+  // The sliding window: variant instances, and the windowed training instance (which takes
+  // q and k already rotated when RoPE is on).
+  constexpr bool kWin = kVar || kMode == kModeSaveWin;
   static_assert(!kPaged || LdsCfg<TR>::kt == kPageSize, "a key tile is one page");
   constexpr int kThreads = 64 * kWaves;
   constexpr int kKT = LdsCfg<TR>::kt;                // keys per tile
@@ -158,7 +164,7 @@ __global__ void __launch_bounds__(64 * kWaves, kLean ? 4 : 1)
   // L2, so the launch does not end on a write-back of the outputs: at B = 8, T = 2K
   // 125 -> 117 us.  (Non-temporal stores of the 16-byte pieces were 60% slower; whole rows
   // through the L2 gained nothing.)
-  constexpr bool kRowStores = kLean && (kMode == kModePlain || kMode == kModeSave ||
+  constexpr bool kRowStores = kLean && (kMode == kModePlain || kSave ||
                                         kMode == kModeMix || kMode == kModeVariant);
   constexpr int kOutPitch = kD + 4;                 // floats per staged row (spreads banks)
   constexpr int kOutBytes = kRowStores ? kWaves * 32 * kOutPitch * (int)sizeof(float) : 0;
@@ -222,7 +228,7 @@ __global__ void __launch_bounds__(64 * kWaves, kLean ? 4 : 1)
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int row = wrow0 + qb * 32 + c32;
-    const int nk = (kVar && a.window > 0) ? min(row + 1, a.window) : pbase + row + 1;
+    const int nk = (kWin && a.window > 0) ? min(row + 1, a.window) : pbase + row + 1;
     const float tau =
         a.inv_log_train > 0.f ? fmaxf(1.0f, logf((float)nk) * a.inv_log_train) : 1.0f;
     cnat[qb] = beta * tau;
@@ -547,7 +553,7 @@ __global__ void __launch_bounds__(64 * kWaves, kLean ? 4 : 1)
         for (int r = 0; r < 16; ++r) {
           const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * g32 + (r & 3);
           bool masked = key > pbase + row;
-          if constexpr (kVar) masked = masked || (a.window > 0 && key <= row - a.window);
+          if constexpr (kWin) masked = masked || (a.window > 0 && key <= row - a.window);
           if (masked) S.v[qb][kb][r] = -INFINITY;
         }
     }
@@ -689,9 +695,9 @@ __global__ void __launch_bounds__(64 * kWaves, kLean ? 4 : 1)
   // Tiles [tf0, tf1) are seen whole by every row of the workgroup and take this pipelined
   // path; the others are masked one at a time.  With a sliding window the loop starts at
   // the first tile any row can see (t0) and the fully visible range starts at tf0.
-  const int t0 = (kVar && a.window > 0) ? max(0, row0 - a.window + 1) / kKT : 0;
+  const int t0 = (kWin && a.window > 0) ? max(0, row0 - a.window + 1) / kKT : 0;
   const int tf1 = min((pbase + row0 + 1) / kKT, ntiles);
-  const int tf0 = (kVar && a.window > 0)
+  const int tf0 = (kWin && a.window > 0)
                       ? min(tf1, (max(0, wg_last - a.window + 1) + kKT - 1) / kKT)
                       : t0;
 
@@ -728,7 +734,7 @@ __global__ void __launch_bounds__(64 * kWaves, kLean ? 4 : 1)
     if (stage) stage_load(t + kDepth);
     const int key0 = t * kKT;
     bool live = key0 <= w_last;
-    if constexpr (kVar) live = live && (a.window == 0 || key0 + kKT > wrow0 - a.window + 1);
+    if constexpr (kWin) live = live && (a.window == 0 || key0 + kKT > wrow0 - a.window + 1);
     if (live) {
       score(t % kSlots, Sa);
       mask(Sa, key0);
@@ -879,7 +885,7 @@ __global__ void __launch_bounds__(64 * kWaves, kLean ? 4 : 1)
       const float lse = (Mref[qb] + log2f(St)) * kLn2;
       const float m_nat = smax[qb] * cnat[qb];
       float floor_ = bias;
-      const int nk = (kVar && a.window > 0) ? min(row + 1, a.window) : pbase + row + 1;
+      const int nk = (kWin && a.window > 0) ? min(row + 1, a.window) : pbase + row + 1;
       if (a.null_floor) floor_ += cnat[qb] * 0.125f * sqrtf(2.0f * logf((float)nk));
       const float gate = 1.0f / (1.0f + expf(floor_ - m_nat));
       const float n2 = neff * neff;
@@ -1074,6 +1080,34 @@ constexpr int kWavesF32 = 4;
 // per CU the pipelined instances keep their two waves per SIMD busier.
 constexpr long long kLeanMinWorkgroups = 512;
 
+// The gradient with respect to the input of RoPE: fp32 rows [B,T,H,d] turned in place by
+// the transposed rotation, that is by the opposite angle (rope_cs's angle for pair t at
+// position p): (g0, g1) -> (g0 c + g1 s, g1 c - g0 s).  One thread per 16-byte chunk.
+struct RopeFreqs {
+  uint64_t f[kD / 2];
+};
+__global__ void __launch_bounds__(256)
+    polar_unrope_kernel(float *x, long long n, int T, int H, RopeFreqs fr) {
+  constexpr int kChunks = kD / 4;
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n;
+       i += (long long)gridDim.x * 256) {
+    const int part = (int)(i % kChunks);
+    const long long row = i / kChunks;                 // (b * T + pos) * H + h
+    const int pos = (int)((row / H) % T);
+    f32x4 *px = (f32x4 *)(x + row * kD) + part;
+    f32x4 w = *px;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      float c, sn;
+      rope_cs(fr.f[part * 2 + m], pos, c, sn);
+      const float g0 = w[2 * m], g1 = w[2 * m + 1];
+      w[2 * m] = fmaf(g0, c, g1 * sn);
+      w[2 * m + 1] = fmaf(g1, c, -(g0 * sn));
+    }
+    *px = w;
+  }
+}
+
 }  // namespace
 
 int prefill_heads_per_block(int G) {
@@ -1093,6 +1127,18 @@ PrefillShape prefill_shape(int dtype, const PrefillArgs &a) {
   // 16-wave workgroup: four waves per SIMD instead of two.
   if (a.paged) return {2, rows};
   return {0, rows};
+}
+
+hipError_t launch_unrope(float *x, int B, int T, int H, const uint64_t *rope_f,
+                         hipStream_t stream) {
+  const long long n = (long long)B * T * H * (kD / 4);
+  if (n <= 0) return hipSuccess;
+  RopeFreqs fr;
+  for (int t = 0; t < kD / 2; ++t) fr.f[t] = rope_f[t];
+  const long long need = (n + 255) / 256;
+  const unsigned blocks = (unsigned)(need < 65536 ? need : 65536);
+  hipLaunchKernelGGL(polar_unrope_kernel, dim3(blocks), dim3(256), 0, stream, x, n, T, H, fr);
+  return hipGetLastError();
 }
 
 hipError_t launch_rope_keys(int dtype, const PrefillArgs &a, void *k_out, hipStream_t stream) {
@@ -1159,7 +1205,8 @@ hipError_t launch_prefill(int dtype, const PrefillArgs &args, hipStream_t stream
   const int mode = a.paged ? kModePaged
                  : a.variant ? ((a.rope && !a.k_rotated) ? kModeVariantRot : kModeVariant)
                  : a.mixed ? kModeMix
-                 : (a.u_norm != nullptr ? kModeSave : kModePlain);
+                 : a.u_norm == nullptr ? kModePlain
+                 : (a.window > 0 ? kModeSaveWin : kModeSave);
   const dim3 bb(64 * kWavesBf16), bf(64 * kWavesF32);
   if (dtype == 1 && a.lean == 2) {
     if (mode != kModePaged) return hipErrorInvalidConfiguration;
@@ -1178,6 +1225,9 @@ hipError_t launch_prefill(int dtype, const PrefillArgs &args, hipStream_t stream
     else if (mode == kModeSave)
       hipLaunchKernelGGL((polar_prefill_kernel<Bf16, 1, kWavesBf16, kModeSave, true>), grid,
                          bb, 0, stream, a);
+    else if (mode == kModeSaveWin)
+      hipLaunchKernelGGL((polar_prefill_kernel<Bf16, 1, kWavesBf16, kModeSaveWin, true>), grid,
+                         bb, 0, stream, a);
     else if (mode == kModeMix)
       hipLaunchKernelGGL((polar_prefill_kernel<Bf16, 1, kWavesBf16, kModeMix, true>), grid,
                          bb, 0, stream, a);
@@ -1189,6 +1239,9 @@ hipError_t launch_prefill(int dtype, const PrefillArgs &args, hipStream_t stream
                          grid, bb, 0, stream, a);
     else if (mode == kModeSave)
       hipLaunchKernelGGL((polar_prefill_kernel<Bf16, kQbBf16, kWavesBf16, kModeSave, false>),
+                         grid, bb, 0, stream, a);
+    else if (mode == kModeSaveWin)
+      hipLaunchKernelGGL((polar_prefill_kernel<Bf16, kQbBf16, kWavesBf16, kModeSaveWin, false>),
                          grid, bb, 0, stream, a);
     else if (mode == kModeMix)
       hipLaunchKernelGGL((polar_prefill_kernel<Bf16, kQbBf16, kWavesBf16, kModeMix, false>),
@@ -1211,6 +1264,9 @@ hipError_t launch_prefill(int dtype, const PrefillArgs &args, hipStream_t stream
     else if (mode == kModeSave)
       hipLaunchKernelGGL((polar_prefill_kernel<F32, kQbF32, kWavesF32, kModeSave, false>), grid,
                          bf, 0, stream, a);
+    else if (mode == kModeSaveWin)
+      hipLaunchKernelGGL((polar_prefill_kernel<F32, kQbF32, kWavesF32, kModeSaveWin, false>),
+                         grid, bf, 0, stream, a);
     else if (mode == kModeMix)
       hipLaunchKernelGGL((polar_prefill_kernel<F32, kQbF32, kWavesF32, kModeMix, false>), grid,
                          bf, 0, stream, a);

@@ -140,8 +140,13 @@ def _prefill_args(q, k, v, beta, null_bias, count_vec, train_len, flags):
 def attn_fwd_train(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta=None,
                    null_bias=None, count_vec=None, train_len: int = 2048,
                    flags: int = _lib.POLAR_FLAG_LENGTH_TEMP | _lib.POLAR_FLAG_NULL_FLOOR,
-                   stream=None) -> dict:
-    """Prefill that also returns the residuals of the backward pass ("u_norm", "arg_max")."""
+                   window: int = 0, rope_theta: float = 0.0,
+                   workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """Prefill that also returns the residuals of the backward pass ("u_norm", "arg_max").
+
+    ``window`` and ``rope_theta`` select the variant modes (polar_attn_fwd_train_variant);
+    with RoPE, q and k are rotated into ``workspace`` (a uint8 device tensor of at least
+    train_variant_workspace_bytes(...) bytes, allocated here when None)."""
     prm, keep, (B, T, Hq, Hkv, d) = _prefill_args(q, k, v, beta, null_bias, count_vec,
                                                   train_len, flags)
     dev = q.device
@@ -150,9 +155,29 @@ def attn_fwd_train(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta=None,
     out["arg_max"] = torch.empty(B, T, Hq, device=dev, dtype=torch.int32)
     saved = _lib.polar_saved(_ptr(out["u_norm"]), _ptr(out["arg_max"]))
     s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
-    _lib.check(_lib.polar_attn_fwd_train(prm, _DT[q.dtype], B, T, q.data_ptr(), k.data_ptr(),
-                                         v.data_ptr(), cout, saved, s))
+    if window == 0 and rope_theta == 0.0:
+        _lib.check(_lib.polar_attn_fwd_train(prm, _DT[q.dtype], B, T, q.data_ptr(),
+                                             k.data_ptr(), v.data_ptr(), cout, saved, s))
+        return out
+    var = _lib.polar_variant(window, rope_theta, None, None, 0)
+    need = _lib.polar_train_variant_workspace_bytes(prm, var, _DT[q.dtype], B, T)
+    if need > 0:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        _check_aux(workspace, "workspace", dev, None)
+        var = _lib.polar_variant(window, rope_theta, None, workspace.data_ptr(),
+                                 workspace.numel() * workspace.element_size())
+    _lib.check(_lib.polar_attn_fwd_train_variant(prm, var, _DT[q.dtype], B, T, q.data_ptr(),
+                                                 k.data_ptr(), v.data_ptr(), cout, saved, s))
     return out
+
+
+def train_variant_workspace_bytes(Hq: int, Hkv: int, B: int, T: int, window: int = 0,
+                                  rope_theta: float = 0.0, dtype=torch.bfloat16,
+                                  d: int = 64) -> int:
+    prm = _lib.polar_params(Hq, Hkv, d, 2048, 0, None, None, None)
+    var = _lib.polar_variant(window, rope_theta, None, None, 0)
+    return _lib.polar_train_variant_workspace_bytes(prm, var, _DT[dtype], B, T)
 
 
 def attn_fwd_variant(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, window: int = 0,
@@ -194,19 +219,24 @@ def variant_workspace_bytes(Hq: int, Hkv: int, B: int, T: int, dtype=torch.bfloa
     return _lib.polar_variant_workspace_bytes(prm, _DT[dtype], B, T)
 
 
-def bwd_workspace_bytes(Hq: int, Hkv: int, B: int, T: int, d: int = 64) -> int:
+def bwd_workspace_bytes(Hq: int, Hkv: int, B: int, T: int, d: int = 64, window: int = 0,
+                        rope_theta: float = 0.0) -> int:
     prm = _lib.polar_params(Hq, Hkv, d, 2048, 0, None, None, None)
-    return _lib.polar_bwd_workspace_bytes(prm, B, T)
+    if window == 0 and rope_theta == 0.0:
+        return _lib.polar_bwd_workspace_bytes(prm, B, T)
+    var = _lib.polar_variant(window, rope_theta, None, None, 0)
+    return _lib.polar_bwd_variant_workspace_bytes(prm, var, B, T)
 
 
 def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, fwd: dict, cot: dict,
              beta=None, null_bias=None, count_vec=None, train_len: int = 2048,
              flags: int = _lib.POLAR_FLAG_LENGTH_TEMP | _lib.POLAR_FLAG_NULL_FLOOR,
              param_grads: bool = True, workspace: Optional[torch.Tensor] = None,
-             stream=None) -> dict:
+             window: int = 0, rope_theta: float = 0.0, stream=None) -> dict:
     """Backward of the causal prefill.
 
-    ``fwd`` is what attn_fwd_train returned for the same arguments; ``cot`` maps output
+    ``fwd`` is what attn_fwd_train returned for the same arguments (``window`` and
+    ``rope_theta`` included: they select polar_attn_bwd_variant); ``cot`` maps output
     names ("dir", "count", "n_eff", "gate", "lse") to float32 upstream gradients (missing
     names are zero).  Returns float32 dq, dk, dv and, with ``param_grads``, d_beta,
     d_null_bias and d_count_vec.
@@ -233,7 +263,10 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, fwd: dict, cot: 
     if param_grads:
         g.update(d_beta=torch.empty(Hq, **f32), d_null_bias=torch.empty(Hq, **f32),
                  d_count_vec=torch.empty(Hq, d, **f32))
-    need = _lib.polar_bwd_workspace_bytes(prm, B, T)
+    variant = window != 0 or rope_theta != 0.0
+    var = _lib.polar_variant(window, rope_theta, None, None, 0) if variant else None
+    need = (_lib.polar_bwd_variant_workspace_bytes(prm, var, B, T) if variant
+            else _lib.polar_bwd_workspace_bytes(prm, B, T))
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     _check_aux(workspace, "workspace", dev, None)
@@ -244,9 +277,15 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, fwd: dict, cot: 
     go = _lib.polar_grads(_ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g.get("d_beta")),
                           _ptr(g.get("d_null_bias")), _ptr(g.get("d_count_vec")))
     s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
-    _lib.check(_lib.polar_attn_bwd(prm, _DT[q.dtype], B, T, q.data_ptr(), k.data_ptr(),
-                                   v.data_ptr(), fo, sv, co, go, workspace.data_ptr(),
-                                   workspace.numel() * workspace.element_size(), s))
+    nbytes = workspace.numel() * workspace.element_size()
+    if variant:
+        _lib.check(_lib.polar_attn_bwd_variant(prm, var, _DT[q.dtype], B, T, q.data_ptr(),
+                                               k.data_ptr(), v.data_ptr(), fo, sv, co, go,
+                                               workspace.data_ptr(), nbytes, s))
+    else:
+        _lib.check(_lib.polar_attn_bwd(prm, _DT[q.dtype], B, T, q.data_ptr(), k.data_ptr(),
+                                       v.data_ptr(), fo, sv, co, go, workspace.data_ptr(),
+                                       nbytes, s))
     return g
 
 

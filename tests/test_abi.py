@@ -23,7 +23,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(_lib.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert _lib.polar_abi_version() == 5
+    assert _lib.polar_abi_version() == 6
 
 
 def test_status_strings():
@@ -291,6 +291,85 @@ def test_variant_empty_calls():
     assert var_fwd(window=16, theta=10000.0, attn=A, B=0) == _lib.POLAR_OK
     assert _lib.polar_attn_fwd_variant(params(), None, 1, 1, 0, A, A, A, outs(), None) == \
         _lib.POLAR_OK
+
+
+# ------------------------------------------------------------------ variant training + backward
+def train_var(window=0, theta=0.0, attn=None, ws=None, ws_bytes=0, dt=1, B=1, T=8, s=None,
+              o=None, q=A):
+    return _lib.polar_attn_fwd_train_variant(params(),
+                                             _lib.polar_variant(window, theta, attn, ws,
+                                                                ws_bytes),
+                                             dt, B, T, q, A, A, outs() if o is None else o,
+                                             saved() if s is None else s, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(window=-3), _lib.POLAR_ERR_BAD_SHAPE),
+    (dict(theta=0.9), _lib.POLAR_ERR_BAD_SHAPE),
+    (dict(attn=A), _lib.POLAR_ERR_UNSUPPORTED),             # no softmax read-out in training
+    (dict(window=4, o=outs(lse=None)), _lib.POLAR_ERR_NULL_POINTER),
+    (dict(theta=10000.0), _lib.POLAR_ERR_NULL_POINTER),     # RoPE needs the workspace
+    (dict(theta=10000.0, ws=A + 8, ws_bytes=1 << 20), _lib.POLAR_ERR_MISALIGNED),
+    # q and k rotated: 1 x 8 x (16 + 4) x 64 x 2 bytes = 20480
+    (dict(theta=10000.0, ws=A, ws_bytes=20479), _lib.POLAR_ERR_WORKSPACE_TOO_SMALL),
+    (dict(theta=10000.0, ws=A, ws_bytes=1 << 20, q=None), _lib.POLAR_ERR_NULL_POINTER),
+    (dict(theta=10000.0, ws=A, ws_bytes=1 << 20, dt=9), _lib.POLAR_ERR_UNSUPPORTED),
+])
+def test_train_variant_validation_errors(kw, code):
+    assert train_var(**kw) == code
+    assert _lib.polar_last_error() != ""
+
+
+def test_train_variant_null_saved_and_empty():
+    assert _lib.load().polar_attn_fwd_train_variant(
+        ctypes.byref(params()), None, 1, 1, 8, A, A, A, ctypes.byref(outs()), None, None) == \
+        _lib.POLAR_ERR_NULL_POINTER
+    assert train_var(window=4, theta=10000.0, B=0) == _lib.POLAR_OK
+
+
+def test_train_variant_workspace_bytes():
+    var = lambda w, t: _lib.polar_variant(w, t, None, None, 0)
+    f = _lib.polar_train_variant_workspace_bytes
+    assert f(params(), var(0, 10000.0), 1, 2, 100) == 2 * 100 * 20 * 64 * 2
+    assert f(params(), var(16, 10000.0), 0, 2, 100) == 2 * 100 * 20 * 64 * 4
+    assert f(params(), var(16, 0.0), 1, 2, 100) == 0          # no rotation, no workspace
+    assert f(params(), var(-1, 10000.0), 1, 2, 100) == 0
+    assert f(params(), var(0, 10000.0), 4, 2, 100) == 0
+
+
+def test_bwd_variant_workspace_bytes():
+    var = lambda w, t: _lib.polar_variant(w, t, None, None, 0)
+    f = _lib.polar_bwd_variant_workspace_bytes
+    base = _lib.polar_bwd_workspace_bytes(params(), 2, 300)
+    assert f(params(), var(64, 0.0), 2, 300) == base
+    assert f(params(), None, 2, 300) == base
+    rot = f(params(), var(0, 500.0), 2, 300)
+    q_bytes, k_bytes = 2 * 300 * 16 * 64 * 2, 2 * 300 * 4 * 64 * 2
+    assert rot >= base + q_bytes + k_bytes and rot <= base + q_bytes + k_bytes + 512
+    assert f(params(), var(0, 0.5), 2, 300) == 0
+    assert f(params(), var(0, 500.0), 0, 300) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(var=_lib.polar_variant(-1, 0.0, None, None, 0)), _lib.POLAR_ERR_BAD_SHAPE),
+    (dict(var=_lib.polar_variant(0, 1.0, None, None, 0)), _lib.POLAR_ERR_BAD_SHAPE),
+    (dict(var=_lib.polar_variant(8, 0.0, A, None, 0)), _lib.POLAR_ERR_UNSUPPORTED),
+    (dict(var=_lib.polar_variant(0, 500.0, None, None, 0), dt=0), _lib.POLAR_ERR_UNSUPPORTED),
+    # the base workspace is not enough once q and k are rotated into it
+    (dict(var=_lib.polar_variant(0, 500.0, None, None, 0), base_ws=True),
+     _lib.POLAR_ERR_WORKSPACE_TOO_SMALL),
+    (dict(var=_lib.polar_variant(16, 500.0, None, None, 0), g=grads(dq=None)),
+     _lib.POLAR_ERR_NULL_POINTER),
+])
+def test_bwd_variant_validation_errors(kw, code):
+    var = kw["var"]
+    p = params()
+    n = (_lib.polar_bwd_workspace_bytes(p, 1, 100) if kw.get("base_ws")
+         else _lib.polar_bwd_variant_workspace_bytes(p, var, 1, 100))
+    assert _lib.polar_attn_bwd_variant(p, var, kw.get("dt", 1), 1, 100, A, A, A, outs(),
+                                       saved(), cots(), kw.get("g", grads()), WS, n,
+                                       None) == code
+    assert _lib.polar_last_error() != ""
 
 
 # ------------------------------------------------------------------ paged append / chunks
