@@ -66,6 +66,9 @@ KERNEL_SOURCES = {
     "memory_step": ["polar_delta.hip", "polar_kernels.h"],
     "memory_sequence": ["polar_delta.hip", "polar_kernels.h"],
     "fwd_train": _PREFILL_SRC,          # the training forward beside the backward
+    # the window + RoPE arm: rotations, windowed training forward, windowed backward kernels
+    "backward_variant": ["polar_backward.hip", "polar_prefill.hip", "polar_mfma.h",
+                         "polar_kernels.h"],
 }
 
 
@@ -317,7 +320,7 @@ def measure_backward_variant(dev, steps: int, warmup: int, q, k, v, kw, cot, p,
             "fwd_train_ms": round(f_ms, 4),
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
-                         "traffic": None}}
+                         "traffic": traffic_record("backward_variant")}}
 
 
 def visible_pairs(T: int, window: int) -> float:
@@ -738,6 +741,11 @@ LEG_KERNELS = {
                  (r"polar_bwd_param_kernel", None, -1),
                  (r"polar_bwd_param_final_kernel", None, -1)],
     "fwd_train": [(r"polar_prefill_kernel<Bf16, 1, 8, 1,", None, -1)],
+    "backward_variant": [(r"polar_rope_qk_kernel<unsigned short>", None, -1),
+                         (r"polar_prefill_kernel<Bf16, 1, 8, 6,", None, -1),
+                         (r"polar_bwd_dq_kernel<8, true>", None, -1),
+                         (r"polar_bwd_dkv_kernel<4, 1, true>", None, -1),
+                         (r"polar_unrope_kernel", None, -1)],
     "memory_step": [(r"polar_delta_step_kernel<unsigned short, 4>", 262144, -1)],
     "memory_sequence": [(r"polar_delta_seq_kernel<unsigned short,", None, -1)],
 }
@@ -753,6 +761,9 @@ LEG_WORKLOAD = {
     "decode_b1": "paged decode B=1 L=262144",
     "backward": "backward B=8 T=2048, all cotangents, parameter gradients",
     "fwd_train": "training forward B=8 T=2048 (saves lse, S, Q for the backward)",
+    "backward_variant": "window 512 + RoPE arm at B=8 T=2048: q/k rotation, windowed "
+                        "training forward, windowed dq and dk/dv, inverse rotation (the "
+                        "prep, partial-add and parameter kernels are the backward leg's)",
     "memory_step": "gated-delta step, 256 sequences x 16 heads",
     "memory_sequence": "gated-delta stream, 32 sequences x 2048 tokens x 16 heads",
 }

@@ -82,16 +82,21 @@ polar_status check_variant(const polar_variant *var) {
   return POLAR_OK;
 }
 
-// Rotates x [B,T,H,d] of type dt by RoPE into out, with polar_attn_fwd_variant's rounding.
-hipError_t rotate_rows(polar_dtype dt, const void *x, void *out, int B, int T, int H,
-                       float theta, hipStream_t stream) {
-  polar::PrefillArgs r{};
-  r.k = x;
+// Rotates q [B,T,Hq,d] and k [B,T,Hkv,d] of type dt by RoPE into q_out and k_out, with
+// polar_attn_fwd_variant's rounding.
+hipError_t rotate_qk(polar_dtype dt, const void *q, const void *k, void *q_out, void *k_out,
+                     int B, int T, int Hq, int Hkv, float theta, hipStream_t stream) {
+  polar::RopeQk r{};
+  r.q = q;
+  r.k = k;
+  r.q_out = q_out;
+  r.k_out = k_out;
   r.B = B;
   r.T = T;
-  r.Hkv = H;
+  r.Hq = Hq;
+  r.Hkv = Hkv;
   fill_rope_f(r.rope_f, theta);
-  return polar::launch_rope_keys((int)dt, r, out, stream);
+  return polar::launch_rope_qk((int)dt, r, stream);
 }
 
 size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
@@ -306,8 +311,7 @@ polar_status polar_attn_fwd_train_variant(const polar_params *p, const polar_var
       (size_t)B * T * p->n_q_heads * polar::kHeadDim * (dt == POLAR_DTYPE_BF16 ? 2 : 4);
   char *qr = (char *)var->workspace, *kr = qr + qbytes;
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = rotate_rows(dt, q, qr, B, T, p->n_q_heads, theta, s);
-  if (e == hipSuccess) e = rotate_rows(dt, k, kr, B, T, p->n_kv_heads, theta, s);
+  const hipError_t e = rotate_qk(dt, q, k, qr, kr, B, T, p->n_q_heads, p->n_kv_heads, theta, s);
   if (e != hipSuccess) return fail(POLAR_ERR_HIP, "rotation launch: %s", hipGetErrorString(e));
   return prefill(p, dt, B, T, qr, kr, v, out, saved, &w, stream);
 }
@@ -384,8 +388,7 @@ static polar_status bwd_impl(const polar_params *p, const polar_variant *var, po
     // The kernels run on the rotated q and k, held after the backward's own workspace.
     char *qr = (char *)workspace + align256(base);
     char *kr = qr + align256(qbytes);
-    hipError_t e = rotate_rows(dt, q, qr, B, T, Hq, theta, s);
-    if (e == hipSuccess) e = rotate_rows(dt, k, kr, B, T, p->n_kv_heads, theta, s);
+    hipError_t e = rotate_qk(dt, q, k, qr, kr, B, T, Hq, p->n_kv_heads, theta, s);
     if (e != hipSuccess) return fail(POLAR_ERR_HIP, "rotation launch: %s", hipGetErrorString(e));
     q = qr;
     k = kr;
@@ -438,10 +441,15 @@ static polar_status bwd_impl(const polar_params *p, const polar_variant *var, po
   if (err != hipSuccess) return fail(POLAR_ERR_HIP, "backward launch: %s", hipGetErrorString(err));
   if (theta > 0.f) {
     // Gradients with respect to the unrotated q and k: the transposed rotation.
-    uint64_t f[polar::kHeadDim / 2];
-    fill_rope_f(f, theta);
-    err = polar::launch_unrope(grads->dq, B, T, Hq, f, s);
-    if (err == hipSuccess) err = polar::launch_unrope(grads->dk, B, T, p->n_kv_heads, f, s);
+    polar::Unrope u{};
+    u.dq = grads->dq;
+    u.dk = grads->dk;
+    u.B = B;
+    u.T = T;
+    u.Hq = Hq;
+    u.Hkv = p->n_kv_heads;
+    fill_rope_f(u.rope_f, theta);
+    err = polar::launch_unrope(u, s);
     if (err != hipSuccess)
       return fail(POLAR_ERR_HIP, "inverse rotation launch: %s", hipGetErrorString(err));
   }

@@ -57,10 +57,22 @@ hipError_t launch_prefill(int dtype, const PrefillArgs &a, hipStream_t stream);
 // Rotates the keys a.k [B,T,Hkv,d] by RoPE at positions 0..T-1 into k_out (same layout),
 // with exactly the arithmetic the prefill's staging applies.
 hipError_t launch_rope_keys(int dtype, const PrefillArgs &a, void *k_out, hipStream_t stream);
-// Gradients through RoPE: fp32 rows x [B,T,H,d] turned in place by the transposed rotation
-// (rope_f as in PrefillArgs).
-hipError_t launch_unrope(float *x, int B, int T, int H, const uint64_t *rope_f,
-                         hipStream_t stream);
+// The training arm with RoPE: q [B,T,Hq,d] and k [B,T,Hkv,d] rotated into q_out, k_out
+// (rope_f as in PrefillArgs), and the gradients dq, dk (fp32) turned back in place by the
+// transposed rotation.
+struct RopeQk {
+  const void *q, *k;
+  void *q_out, *k_out;
+  int B, T, Hq, Hkv;
+  uint64_t rope_f[kHeadDim / 2];
+};
+struct Unrope {
+  float *dq, *dk;
+  int B, T, Hq, Hkv;
+  uint64_t rope_f[kHeadDim / 2];
+};
+hipError_t launch_rope_qk(int dtype, const RopeQk &r, hipStream_t stream);
+hipError_t launch_unrope(const Unrope &u, hipStream_t stream);
 
 struct DecodeArgs {
   const void *q;                          // [B,Hq,d]

@@ -1034,10 +1034,35 @@ __global__ void __launch_bounds__(64 * kWaves, kLean ? 4 : 1)
   }
 }
 
-// Key rotation ahead of the variant prefill: one thread per 16-byte chunk of a key row (4
-// pairs for bf16, 2 for fp32), with the staging's arithmetic (rope_cs, the same explicit
-// FMAs, one rounding to the storage type), so the attention kernel sees the same rotated
-// keys either way.
+// One 16-byte chunk (part) of a row at position pos turned by RoPE: 4 pairs for bf16, 2 for
+// fp32, with the staging's arithmetic (rope_cs, the same explicit FMAs, one rounding to the
+// storage type), so every place that rotates a vector gets the same values.
+template <class E>
+__device__ __forceinline__ u32x4 rotate_chunk(u32x4 w, int part, int pos, const uint64_t *f) {
+  if constexpr (sizeof(E) == 2) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      float c, sn;
+      rope_cs(f[part * 4 + m], pos, c, sn);
+      const float x0 = __uint_as_float(w[m] << 16), x1 = __uint_as_float(w[m] & 0xFFFF0000u);
+      const bf16x2 r = {(__bf16)rot_re(x0, x1, c, sn), (__bf16)rot_im(x0, x1, c, sn)};
+      w[m] = __builtin_bit_cast(uint32_t, r);
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      float c, sn;
+      rope_cs(f[part * 2 + m], pos, c, sn);
+      const float x0 = __uint_as_float(w[2 * m]), x1 = __uint_as_float(w[2 * m + 1]);
+      w[2 * m] = __float_as_uint(rot_re(x0, x1, c, sn));
+      w[2 * m + 1] = __float_as_uint(rot_im(x0, x1, c, sn));
+    }
+  }
+  return w;
+}
+
+// Key rotation ahead of the variant prefill: one thread per 16-byte chunk of a key row, so
+// the attention kernel sees the keys it would have rotated while staging them.
 template <class E>
 __global__ void __launch_bounds__(256) polar_rope_keys_kernel(PrefillArgs a, E *k_out) {
   constexpr int kVec = 16 / (int)sizeof(E);            // elements per chunk
@@ -1048,27 +1073,30 @@ __global__ void __launch_bounds__(256) polar_rope_keys_kernel(PrefillArgs a, E *
     const int part = (int)(i % kChunks);
     const long long row = i / kChunks;                 // (b * T + pos) * Hkv + g
     const int pos = (int)((row / a.Hkv) % a.T);
-    u32x4 w = *(const u32x4 *)((const E *)a.k + row * kD + part * kVec);
-    if constexpr (sizeof(E) == 2) {
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        float c, sn;
-        rope_cs(a.rope_f[part * 4 + m], pos, c, sn);
-        const float x0 = __uint_as_float(w[m] << 16), x1 = __uint_as_float(w[m] & 0xFFFF0000u);
-        const bf16x2 r = {(__bf16)rot_re(x0, x1, c, sn), (__bf16)rot_im(x0, x1, c, sn)};
-        w[m] = __builtin_bit_cast(uint32_t, r);
-      }
-    } else {
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        float c, sn;
-        rope_cs(a.rope_f[part * 2 + m], pos, c, sn);
-        const float x0 = __uint_as_float(w[2 * m]), x1 = __uint_as_float(w[2 * m + 1]);
-        w[2 * m] = __float_as_uint(rot_re(x0, x1, c, sn));
-        w[2 * m + 1] = __float_as_uint(rot_im(x0, x1, c, sn));
-      }
-    }
-    *(u32x4 *)(k_out + row * kD + part * kVec) = w;
+    const u32x4 w = *(const u32x4 *)((const E *)a.k + row * kD + part * kVec);
+    *(u32x4 *)(k_out + row * kD + part * kVec) = rotate_chunk<E>(w, part, pos, a.rope_f);
+  }
+}
+
+// q [B,T,Hq,d] and k [B,T,Hkv,d] rotated in one launch (the training arm with RoPE): the
+// chunks of q first, then those of k.
+template <class E>
+__global__ void __launch_bounds__(256) polar_rope_qk_kernel(RopeQk r) {
+  constexpr int kVec = 16 / (int)sizeof(E);
+  constexpr int kChunks = kD / kVec;
+  const long long nq = (long long)r.B * r.T * r.Hq * kChunks;
+  const long long n = nq + (long long)r.B * r.T * r.Hkv * kChunks;
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n;
+       i += (long long)gridDim.x * 256) {
+    const bool isq = i < nq;
+    const long long j = isq ? i : i - nq;
+    const int H = isq ? r.Hq : r.Hkv;
+    const int part = (int)(j % kChunks);
+    const long long row = j / kChunks;                 // (b * T + pos) * H + h
+    const int pos = (int)((row / H) % r.T);
+    const E *src = (const E *)(isq ? r.q : r.k) + row * kD + part * kVec;
+    E *dst = (E *)(isq ? r.q_out : r.k_out) + row * kD + part * kVec;
+    *(u32x4 *)dst = rotate_chunk<E>(*(const u32x4 *)src, part, pos, r.rope_f);
   }
 }
 
@@ -1080,26 +1108,28 @@ constexpr int kWavesF32 = 4;
 // per CU the pipelined instances keep their two waves per SIMD busier.
 constexpr long long kLeanMinWorkgroups = 512;
 
-// The gradient with respect to the input of RoPE: fp32 rows [B,T,H,d] turned in place by
-// the transposed rotation, that is by the opposite angle (rope_cs's angle for pair t at
-// position p): (g0, g1) -> (g0 c + g1 s, g1 c - g0 s).  One thread per 16-byte chunk.
-struct RopeFreqs {
-  uint64_t f[kD / 2];
-};
-__global__ void __launch_bounds__(256)
-    polar_unrope_kernel(float *x, long long n, int T, int H, RopeFreqs fr) {
+// The gradient with respect to the input of RoPE: fp32 rows of dq [B,T,Hq,d] and dk
+// [B,T,Hkv,d] turned in place by the transposed rotation, that is by the opposite angle
+// (rope_cs's angle for pair t at position p): (g0, g1) -> (g0 c + g1 s, g1 c - g0 s).  One
+// thread per 16-byte chunk, dq's chunks first.
+__global__ void __launch_bounds__(256) polar_unrope_kernel(Unrope u) {
   constexpr int kChunks = kD / 4;
+  const long long nq = (long long)u.B * u.T * u.Hq * kChunks;
+  const long long n = nq + (long long)u.B * u.T * u.Hkv * kChunks;
   for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n;
        i += (long long)gridDim.x * 256) {
-    const int part = (int)(i % kChunks);
-    const long long row = i / kChunks;                 // (b * T + pos) * H + h
-    const int pos = (int)((row / H) % T);
-    f32x4 *px = (f32x4 *)(x + row * kD) + part;
+    const bool isq = i < nq;
+    const long long j = isq ? i : i - nq;
+    const int H = isq ? u.Hq : u.Hkv;
+    const int part = (int)(j % kChunks);
+    const long long row = j / kChunks;                 // (b * T + pos) * H + h
+    const int pos = (int)((row / H) % u.T);
+    f32x4 *px = (f32x4 *)((isq ? u.dq : u.dk) + row * kD) + part;
     f32x4 w = *px;
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       float c, sn;
-      rope_cs(fr.f[part * 2 + m], pos, c, sn);
+      rope_cs(u.rope_f[part * 2 + m], pos, c, sn);
       const float g0 = w[2 * m], g1 = w[2 * m + 1];
       w[2 * m] = fmaf(g0, c, g1 * sn);
       w[2 * m + 1] = fmaf(g1, c, -(g0 * sn));
@@ -1129,15 +1159,24 @@ PrefillShape prefill_shape(int dtype, const PrefillArgs &a) {
   return {0, rows};
 }
 
-hipError_t launch_unrope(float *x, int B, int T, int H, const uint64_t *rope_f,
-                         hipStream_t stream) {
-  const long long n = (long long)B * T * H * (kD / 4);
+hipError_t launch_rope_qk(int dtype, const RopeQk &r, hipStream_t stream) {
+  const long long n = (long long)r.B * r.T * (r.Hq + r.Hkv) * (kD / (dtype == 1 ? 8 : 4));
   if (n <= 0) return hipSuccess;
-  RopeFreqs fr;
-  for (int t = 0; t < kD / 2; ++t) fr.f[t] = rope_f[t];
   const long long need = (n + 255) / 256;
   const unsigned blocks = (unsigned)(need < 65536 ? need : 65536);
-  hipLaunchKernelGGL(polar_unrope_kernel, dim3(blocks), dim3(256), 0, stream, x, n, T, H, fr);
+  if (dtype == 1)
+    hipLaunchKernelGGL((polar_rope_qk_kernel<uint16_t>), dim3(blocks), dim3(256), 0, stream, r);
+  else
+    hipLaunchKernelGGL((polar_rope_qk_kernel<float>), dim3(blocks), dim3(256), 0, stream, r);
+  return hipGetLastError();
+}
+
+hipError_t launch_unrope(const Unrope &u, hipStream_t stream) {
+  const long long n = (long long)u.B * u.T * (u.Hq + u.Hkv) * (kD / 4);
+  if (n <= 0) return hipSuccess;
+  const long long need = (n + 255) / 256;
+  const unsigned blocks = (unsigned)(need < 65536 ? need : 65536);
+  hipLaunchKernelGGL(polar_unrope_kernel, dim3(blocks), dim3(256), 0, stream, u);
   return hipGetLastError();
 }
 
