@@ -49,6 +49,8 @@ namespace {
 constexpr int kD = kHeadDim;
 constexpr int kKTBf16 = 64;   // keys per tile (bf16 instances): one page of the paged cache
 constexpr float kLazyTheta = 8.0f;
+// Task queues of a ticketed launch; its counter set has one more word, the completion count.
+constexpr int kTicketQueues = 15;
 // The running reference before any visible key: finite, so that -M needs no select, and so
 // low that the first visible tile always raises it (the rescale factor is then 0).
 constexpr float kNoRef = -3.0e38f;
@@ -181,11 +183,15 @@ __global__ void __launch_bounds__(64 * kWaves, kLean ? 4 : 1)
   char *const gsmem = smem + grp * kRingBytes;       // this half's ring
   const int g32 = lane >> 5, c32 = lane & 31;
 
-  // Heaviest row blocks first; consecutive blocks cycle over (KV head, batch).  With a
-  // ticket counter, workgroups take tasks in the order they start rather than in
-  // workgroup order: the hardware deals workgroups to the eight XCDs round robin, and an
-  // XCD that runs faster then starts its next workgroups sooner and takes more of the
-  // work, instead of idling at the end while the slowest XCD finishes its fixed share.
+  // Heaviest row blocks first; consecutive blocks cycle over (batch, KV head), the
+  // task's group.  With tickets, workgroups take tasks in the order they start rather
+  // than in workgroup order, from queues of their own groups: the hardware deals
+  // workgroups to the eight XCDs round robin, so a workgroup's grid position fixes its
+  // group (and the K/V its XCD's L2 holds); it takes the next row block of its queue
+  // (the groups g with g % Q equal to its own), heaviest first, and once that queue is
+  // empty, the next of the other queues in turn.  An XCD that runs faster then starts its
+  // next workgroups sooner and takes more of its groups' work, and at the end the light
+  // tail of the others, instead of idling while the slowest XCD finishes its fixed share.
   const int n_hc = a.G / a.hb;
   const int NY = a.Hkv * n_hc;
   // Only the plain lean instance is ever launched with tickets (the others keep exactly
@@ -194,7 +200,22 @@ __global__ void __launch_bounds__(64 * kWaves, kLean ? 4 : 1)
   __shared__ int s_task;
   int id = blockIdx.x;
   if (kTicketed && a.ticket) {
-    if (tid == 0) s_task = (int)atomicAdd(a.ticket, 1u);
+    if (tid == 0) {
+      const int GY = a.B * NY;                           // groups
+      const int Q = min(GY, kTicketQueues);              // queues
+      const int home = (int)(blockIdx.x % (unsigned)GY) % Q;
+      int task = (int)blockIdx.x;        // unreachable fallback: a repeat writes equal values
+      for (int i = 0; i < Q; ++i) {
+        const int q = (home + i) % Q;
+        const int cnt = (GY - q + Q - 1) / Q;              // groups q, q + Q, ...
+        const unsigned j = atomicAdd(a.ticket + q, 1u);
+        if (j < (unsigned)(cnt * a.n_row_blocks)) {
+          task = (int)(j / cnt) * GY + q + Q * (int)(j % cnt);
+          break;
+        }
+      }
+      s_task = task;
+    }
     __syncthreads();
     id = s_task;
   }
@@ -1025,11 +1046,11 @@ __global__ void __launch_bounds__(64 * kWaves, kLean ? 4 : 1)
     }
   }
   // Every workgroup has taken its task once the completion count reaches the grid: the
-  // last one to finish leaves both counters at zero for the next launch on this slot.
+  // last one to finish leaves the counters at zero for the next launch on this slot.
   if (kTicketed && a.ticket && tid == 0) {
-    if (atomicAdd(a.ticket + 1, 1u) == gridDim.x - 1) {
-      atomicExch(a.ticket, 0u);
-      atomicExch(a.ticket + 1, 0u);
+    if (atomicAdd(a.ticket + kTicketQueues, 1u) == gridDim.x - 1) {
+#pragma unroll
+      for (int q = 0; q <= kTicketQueues; ++q) atomicExch(a.ticket + q, 0u);
     }
   }
 }
@@ -1194,13 +1215,14 @@ hipError_t launch_rope_keys(int dtype, const PrefillArgs &a, void *k_out, hipStr
   return hipGetLastError();
 }
 
-// Task counters for launches that hand out row blocks by ticket: one pair per launch, in a
-// ring of kTicketSlots pairs per device, each pair back at zero when its launch ends.  A
-// slot comes round again after kTicketSlots further launches on the device; only launches
-// that far apart and still running concurrently (a graph replayed beside itself on another
-// stream, say) could share one.
+// Task counters for launches that hand out row blocks by ticket: one set (the queue
+// counters and the completion count) per launch, in a ring of kTicketSlots sets per
+// device, each set back at zero when its launch ends.  A slot comes round again after
+// kTicketSlots further launches on the device; only launches that far apart and still
+// running concurrently (a graph replayed beside itself on another stream, say) could share
+// one.
 constexpr int kTicketSlots = 1024;
-static __device__ __align__(256) unsigned prefill_tickets[kTicketSlots][2];
+static __device__ __align__(256) unsigned prefill_tickets[kTicketSlots][kTicketQueues + 1];
 
 // The launches that take tasks by ticket: plain prefills of at least eight workgroups per
 // CU slot (T = 64K: 1.7% faster).  Below that the atomic at each workgroup's start costs
@@ -1224,7 +1246,7 @@ hipError_t ticket_slot(unsigned **slot) {
     if (err != hipSuccess) return err;
     base[dev] = (unsigned *)p;
   }
-  *slot = base[dev] + 2 * (next[dev]++ % kTicketSlots);
+  *slot = base[dev] + (kTicketQueues + 1) * (next[dev]++ % kTicketSlots);
   return hipSuccess;
 }
 
