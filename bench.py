@@ -167,6 +167,21 @@ def cpu_baseline(pre, dec):
                        "sample": f"decode, all {len(batches)} sequences ({t_dec:.1f} s)"}}
 
 
+def warm_up(fn, calls: int, min_ms: float = 100.0):
+    """``calls`` warmup calls, then more until the GPU has run this call for ``min_ms`` of
+    wall time: a GPU that sat idle while the host drew a leg's inputs runs its first
+    launches at a lower clock, and short legs would otherwise time that ramp."""
+    import torch
+    for _ in range(calls):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < min_ms:
+        for _ in range(4):
+            fn()
+        torch.cuda.synchronize()
+
+
 def measure_prefill_cfg(dev, name: str, steps: int, warmup: int, with_cpu: bool):
     """The causal forward on another of the pages' shapes: "c2" (B=8, T=2048, the training
     length, 5% planted near-copy keys) or "c3" (B=1, T=16384, 8x the training length, one
@@ -182,9 +197,7 @@ def measure_prefill_cfg(dev, name: str, steps: int, warmup: int, with_cpu: bool)
     q, k, v = to_dev(p.q), to_dev(p.k), to_dev(p.v)
     kw = dict(beta=torch.from_numpy(p.beta).to(dev), null_bias=torch.from_numpy(p.null_bias).to(dev),
               count_vec=torch.from_numpy(p.count_vec).to(dev), train_len=p.train_len, flags=p.flags)
-    for _ in range(warmup):
-        attn_fwd(q, k, v, **kw)
-    torch.cuda.synchronize()
+    warm_up(lambda: attn_fwd(q, k, v, **kw), warmup)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     for e in ev:
         e[0].record()
@@ -240,10 +253,8 @@ def measure_backward(dev, steps: int, warmup: int, with_cpu: bool):
     cot = {n: torch.from_numpy(x).to(dev) for n, x in cot_np.items()}
     ws = torch.empty(bwd_workspace_bytes(p.Hq, p.Hkv, p.B, p.T), dtype=torch.uint8, device=dev)
     fwd = attn_fwd_train(q, k, v, **kw)
-    for _ in range(warmup):
-        attn_fwd_train(q, k, v, **kw)
-        attn_bwd(q, k, v, fwd, cot, workspace=ws, **kw)
-    torch.cuda.synchronize()
+    warm_up(lambda: (attn_fwd_train(q, k, v, **kw), attn_bwd(q, k, v, fwd, cot, workspace=ws, **kw)),
+            warmup)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     for e in ev:
         e[0].record()
@@ -295,10 +306,8 @@ def measure_backward_variant(dev, steps: int, warmup: int, q, k, v, kw, cot, p,
     wb = torch.empty(bwd_workspace_bytes(p.Hq, p.Hkv, p.B, p.T, **vw), dtype=torch.uint8,
                      device=dev)
     fwd = attn_fwd_train(q, k, v, workspace=wf, **vw, **kw)
-    for _ in range(warmup):
-        attn_fwd_train(q, k, v, workspace=wf, **vw, **kw)
-        attn_bwd(q, k, v, fwd, cot, workspace=wb, **vw, **kw)
-    torch.cuda.synchronize()
+    warm_up(lambda: (attn_fwd_train(q, k, v, workspace=wf, **vw, **kw),
+                     attn_bwd(q, k, v, fwd, cot, workspace=wb, **vw, **kw)), warmup)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     for e in ev:
         e[0].record()
@@ -342,9 +351,7 @@ def measure_variants(dev, q, k, v, pkw, pre, steps: int, warmup: int, with_cpu: 
                      device=dev)
     for name, var in (("rope_softmax_out", dict(window=0, rope_theta=10000.0, workspace=ws)),
                       ("rope_window4096", dict(window=4096, rope_theta=10000.0, workspace=ws))):
-        for _ in range(warmup):
-            attn_fwd_variant(q, k, v, **var, **pkw)
-        torch.cuda.synchronize()
+        warm_up(lambda: attn_fwd_variant(q, k, v, **var, **pkw), warmup)
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
         for e in ev:
             e[0].record()
@@ -408,9 +415,7 @@ def measure_decode_b1(dev, steps: int, warmup: int, with_cpu: bool = False):
     ws = torch.empty(decode_workspace_bytes(d.Hq, d.Hkv, d.B, d.max_seq_len), dtype=torch.uint8,
                      device=dev)
     f = lambda: attn_decode_paged(qd, kc, vc, table, lens, d.max_seq_len, workspace=ws, **kw)
-    for _ in range(warmup):
-        f()
-    torch.cuda.synchronize()
+    warm_up(f, warmup)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     for e in ev:
         e[0].record()
@@ -464,10 +469,8 @@ def measure_paged(dev, pre, steps: int, warmup: int, with_cpu: bool = False):
     kw = dict(beta=torch.from_numpy(pre.beta).to(dev), count_vec=torch.from_numpy(pre.count_vec).to(dev),
               null_bias=torch.from_numpy(pre.null_bias).to(dev), train_len=pre.train_len,
               flags=pre.flags)
-    for _ in range(warmup):
-        kv_append(kn, vn, kc, vc, table, sp, ci.max_seq_len)
-        attn_prefill_paged(qn, kc, vc, table, sp, ci.max_seq_len, **kw)
-    torch.cuda.synchronize()
+    warm_up(lambda: (kv_append(kn, vn, kc, vc, table, sp, ci.max_seq_len),
+                     attn_prefill_paged(qn, kc, vc, table, sp, ci.max_seq_len, **kw)), warmup)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     for e in ev:
         e[0].record()
@@ -557,9 +560,7 @@ def measure_memory_step(dev, steps: int, warmup: int, with_cpu: bool = False):
     times = {}
     for name, fn in (("fused", lambda: delta_step(pool, sl, q, k, v, al, be)),
                      ("reference", lambda: delta_step_reference(pool, sl, q, k, v, al, be))):
-        for _ in range(warmup):
-            fn()
-        torch.cuda.synchronize()
+        warm_up(fn, warmup)
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
         for e in ev:
             e[0].record()
@@ -622,9 +623,7 @@ def measure_memory_sequence(dev, steps: int, warmup: int, with_cpu: bool = False
     from long_context_lm_amd import delta_sequence, delta_step
     d, (pool, sl, q, k, v, al, be) = _delta_seq_setup(dev)
     B, T, H = SEQ_SHAPE["B"], SEQ_SHAPE["T"], SEQ_SHAPE["H"]
-    for _ in range(warmup):
-        delta_sequence(pool, sl, q, k, v, al, be)
-    torch.cuda.synchronize()
+    warm_up(lambda: delta_sequence(pool, sl, q, k, v, al, be), warmup)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     for e in ev:
         e[0].record()

@@ -120,3 +120,28 @@ def test_variant_backward_training_shape(gpu_lib):
     want = _oracle_grads(p, cot, 512, 10000.0, batches=batches)
     sel = {n: got[n][batches] for n in ("dq", "dk", "dv")}
     assert_grads_close(sel, want, keys=("dq", "dk", "dv"), label="C2 W512 RoPE")
+
+
+def test_fp32_training_variant_forward(gpu_lib):
+    """fp32 inputs: the training forward of the window + RoPE arm (q and k rotated by the
+    rotation kernel, no rounding) against the oracle at the fp32 bound, and its outputs
+    against the fp32 variant forward (which rotates q at load) within fp32 rounding."""
+    from long_context_lm_amd import attn_fwd_train, attn_fwd_variant
+    from parity import TOL, assert_close
+    W, theta = 70, 10000.0
+    p = synth.prefill_inputs("c1", B=1, T=200, Hq=8, Hkv=2, dtype="f32")
+    q, k, v = (to_dev(getattr(p, n), p.dtype) for n in ("q", "k", "v"))
+    kw = dict(beta=p.beta, null_bias=p.null_bias, count_vec=p.count_vec,
+              train_len=p.train_len, flags=p.flags)
+    fwd = attn_fwd_train(q, k, v, window=W, rope_theta=theta, **kw)
+    ref = attn_fwd_variant(q, k, v, window=W, rope_theta=theta, want_attn=False, **kw)
+    torch.cuda.synchronize()
+    want = oracle.polar_prefill(p.as_f32("q"), p.as_f32("k"), p.as_f32("v"), p.beta,
+                                p.null_bias, p.count_vec, p.train_len, p.flags, window=W,
+                                rope_theta=theta)
+    assert_close(fwd, want, p.count_vec, "f32", label="fp32 train variant")
+    for n in OUTS:       # relative to each value's magnitude (n_eff runs to the hundreds)
+        d = float(((fwd[n] - ref[n]).abs() / ref[n].abs().clamp(min=1.0)).max())
+        assert d <= 1e-5, (n, d)
+    un = host(fwd["u_norm"])
+    assert np.max(np.abs(un - want["u_norm"]) / want["u_norm"]) < TOL["f32"]
