@@ -10,6 +10,12 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built libpolar")
+    # tests/test_host_asan.py runs the ABI tests again in a child process against a build
+    # whose host code carries AddressSanitizer; that child names the library here.
+    alt = os.environ.get("POLAR_TEST_LIBRARY")
+    if alt:
+        from long_context_lm_amd import _lib
+        print(f"[abi] library {_lib.load(alt)._name}", flush=True)
 
 
 @pytest.fixture(scope="session")
