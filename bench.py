@@ -1007,7 +1007,7 @@ def main():
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the Polar Attention path here is a single-GPU "
-              "kernel library (see the sharding notes in DESIGN.md); run with --gpus 1.",
+              "kernel library (one shard of a sharded job is one GPU at its real shape); run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
     if args.copy_probe:
