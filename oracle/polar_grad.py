@@ -10,7 +10,7 @@ oracle in ``polar_oracle``: length temperature, extreme-value floor, sigmoid gat
 tanh(log n_eff) count).  Gradients come from ``torch.autograd`` on the scalar
 
     L = sum(c_dir * dir) + sum(c_count * count) + sum(c_n_eff * n_eff)
-        + sum(c_gate * gate) + sum(c_lse * lse)
+        + sum(c_gate * gate) + sum(c_lse * lse) [+ sum(c_attn * attn)]
 
 for caller-given cotangents c_*, with respect to q, k, v and the per-head parameters
 beta, null_bias and count_vec.
@@ -43,7 +43,9 @@ import torch
 FLAG_LENGTH_TEMP = 1
 FLAG_NULL_FLOOR = 2
 
-_OUT = ("dir", "count", "n_eff", "gate", "lse")
+# The five Polar outputs, and the plain softmax read-out ("attn" = sum_j p_j v_j, the
+# "Softmax + Memory" arm of the pages' ablation), which may also carry a cotangent.
+_OUT = ("dir", "count", "n_eff", "gate", "lse", "attn")
 
 
 def _rows_forward(Qr, K, V, hi, lo, beta_h, bias_h, w_h, train_len: int, flags: int):
@@ -75,7 +77,7 @@ def _rows_forward(Qr, K, V, hi, lo, beta_h, bias_h, w_h, train_len: int, flags: 
         floor = floor + (beta_h * tau / math.sqrt(d)) * torch.sqrt(2.0 * torch.log(n))
     gate = torch.sigmoid(m - floor)
     count = (gate * torch.tanh(torch.log(n_eff)))[:, None] * w_h[None, :]
-    return dict(dir=dir_, count=count, n_eff=n_eff, gate=gate, lse=lse)
+    return dict(dir=dir_, count=count, n_eff=n_eff, gate=gate, lse=lse, attn=u)
 
 
 def _rotate(x, theta: float, bf16: bool):
@@ -101,8 +103,8 @@ def polar_prefill_grad(q, k, v, cot: dict, beta=None, null_bias=None, count_vec=
     """Gradients of the causal prefill with respect to q, k, v, beta, null_bias, count_vec.
 
     q [B,T,Hq,d], k and v [B,T,Hkv,d]; ``cot`` maps output names ("dir", "count",
-    "n_eff", "gate", "lse") to cotangents of the output shapes (a missing name means
-    zero).  ``window``, ``rope_theta`` and ``rope_bf16`` select the variant modes as in
+    "n_eff", "gate", "lse", and "attn" for the plain softmax read-out) to cotangents of
+    the output shapes (a missing name means zero).  ``window``, ``rope_theta`` and ``rope_bf16`` select the variant modes as in
     ``polar_prefill`` (0 = off).  Rows are processed in blocks of about ``max_elems``
     scores, each block's graph differentiated on its own; gradients accumulate in the
     leaves.  Returns float64 numpy arrays dq, dk, dv, d_beta [Hq], d_null_bias [Hq],
@@ -121,7 +123,7 @@ def polar_prefill_grad(q, k, v, cot: dict, beta=None, null_bias=None, count_vec=
     wt = f64(np.zeros((Hq, d)) if count_vec is None
              else np.asarray(count_vec).reshape(Hq, d)).requires_grad_(True)
     cts = {name: f64(cot[name]) for name in _OUT if cot.get(name) is not None}
-    outs = {name: np.zeros((B, T, Hq, d) if name in ("dir", "count") else (B, T, Hq))
+    outs = {name: np.zeros((B, T, Hq, d) if name in ("dir", "count", "attn") else (B, T, Hq))
             for name in _OUT} if return_outputs else None
     for b in range(B):
         for h in range(Hq):

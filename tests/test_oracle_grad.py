@@ -16,7 +16,7 @@ import torch
 import oracle
 import synth
 
-OUTS = ("dir", "count", "n_eff", "gate", "lse")
+OUTS = ("dir", "count", "n_eff", "gate", "lse", "attn")
 
 
 def _tiny(seed, B=1, T=6, Hq=2, Hkv=1, d=4):
@@ -30,7 +30,7 @@ def _tiny(seed, B=1, T=6, Hq=2, Hkv=1, d=4):
     w = rng.standard_normal((Hq, d))
     cot = dict(dir=rng.standard_normal((B, T, Hq, d)), count=rng.standard_normal((B, T, Hq, d)),
                n_eff=rng.standard_normal((B, T, Hq)), gate=rng.standard_normal((B, T, Hq)),
-               lse=rng.standard_normal((B, T, Hq)))
+               lse=rng.standard_normal((B, T, Hq)), attn=rng.standard_normal((B, T, Hq, d)))
     return q, k, v, beta, bias, w, cot
 
 
@@ -103,8 +103,36 @@ def test_direction_and_lse_grads_match_torch_sdpa():
     np.testing.assert_allclose(g["dv"], vt.grad.transpose(1, 2).numpy(), rtol=1e-10, atol=1e-10)
 
 
+def test_softmax_readout_grads_match_torch_sdpa():
+    """tau = 1: attn is exactly scaled-dot-product attention, so the gradients of an attn
+    cotangent are torch's SDPA backward (GQA expanded by repeat_interleave); with a window,
+    SDPA under the matching boolean mask."""
+    q, k, v, beta, bias, w, cot = _tiny(23, B=2, T=30, Hq=4, Hkv=2, d=8)
+    beta = np.full(4, 2.5)
+    for window in (0, 7):
+        g = oracle.polar_prefill_grad(q, k, v, dict(attn=cot["attn"]), beta, bias, w, 2048, 0,
+                                      window=window)
+        qt = torch.tensor(q).transpose(1, 2).contiguous().requires_grad_(True)
+        kt = torch.tensor(k).transpose(1, 2).contiguous().requires_grad_(True)
+        vt = torch.tensor(v).transpose(1, 2).contiguous().requires_grad_(True)
+        T = q.shape[1]
+        i = torch.arange(T)
+        allowed = i[None, :] <= i[:, None]
+        if window:
+            allowed &= i[None, :] > i[:, None] - window
+        u = torch.nn.functional.scaled_dot_product_attention(
+            qt, kt.repeat_interleave(2, dim=1), vt.repeat_interleave(2, dim=1),
+            attn_mask=allowed, scale=2.5)
+        (torch.tensor(cot["attn"]).transpose(1, 2) * u).sum().backward()
+        for name, t in (("dq", qt), ("dk", kt), ("dv", vt)):
+            np.testing.assert_allclose(g[name], t.grad.transpose(1, 2).numpy(), rtol=1e-10,
+                                       atol=1e-10)
+        assert np.all(g["d_count_vec"] == 0) and np.all(g["d_null_bias"] == 0)
+
+
 def test_single_key_closed_form():
-    """Row 0 sees one key: p = 1, n_eff = 1, dir = v0/|v0|, gate = sigmoid(beta q.k - b)."""
+    """Row 0 sees one key: p = 1, n_eff = 1, dir = v0/|v0|, attn = v0,
+    gate = sigmoid(beta q.k - b)."""
     q, k, v, beta, bias, w, cot = _tiny(5, T=1, Hq=2, Hkv=1, d=4)
     g = oracle.polar_prefill_grad(q, k, v, cot, beta, bias, w, 2048, 3)
     v0 = v[0, 0, 0]
@@ -119,6 +147,7 @@ def test_single_key_closed_form():
         dk += coef * beta[h] * q[0, 0, h]
         cd = cot["dir"][0, 0, h]
         dv += (cd - dir0 * (dir0 @ cd)) / np.linalg.norm(v0)
+        dv += cot["attn"][0, 0, h]                     # attn = v0, whatever the logit
         np.testing.assert_allclose(g["d_beta"][h], coef * s, atol=1e-13)
         np.testing.assert_allclose(g["d_null_bias"][h], -cot["gate"][0, 0, h] * gate * (1 - gate),
                                    atol=1e-13)
