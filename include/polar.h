@@ -1,5 +1,5 @@
 /*
- * libpolar — Polar Attention forward for AMD Instinct MI355X (gfx950).  C ABI, version 6
+ * libpolar — Polar Attention forward for AMD Instinct MI355X (gfx950).  C ABI, version 7
  * (POLAR_ABI_VERSION below; polar_abi_version() reports the loaded library's).
  *
  * The operation is the attention mixing step of the ATMA hybrid decoder as described in
@@ -52,8 +52,10 @@ extern "C" {
  * 4: polar_delta_sequence (the memory stream over T tokens) added; nothing else changed.
  * 5: polar_attn_fwd_mixed (the three streams summed into one output) added.
  * 6: the training forward and the backward of the window and RoPE variants added
- *    (polar_attn_fwd_train_variant, polar_attn_bwd_variant and their workspace sizes). */
-#define POLAR_ABI_VERSION 6
+ *    (polar_attn_fwd_train_variant, polar_attn_bwd_variant and their workspace sizes).
+ * 7: polar_cotangents gained attn, the gradient of the plain softmax read-out, and
+ *    polar_attn_fwd_train_variant writes that read-out (var.attn). */
+#define POLAR_ABI_VERSION 7
 
 #if defined(__GNUC__)
 #define POLAR_API __attribute__((visibility("default")))
@@ -266,13 +268,18 @@ typedef struct {
 
 /* Upstream gradients of the outputs, float32, device, in the polar_outputs layouts
  * ([B,T,Hq,d] for dir and count, [B,T,Hq] for the rest).  NULL means zero.  dir and
- * count must be 16-byte aligned; count != NULL needs params.count_vec. */
+ * count must be 16-byte aligned; count != NULL needs params.count_vec.
+ *   attn  [B,T,Hq,d], 16-byte aligned: gradient of the plain softmax read-out
+ *         u = sum_j p_j v_j (the polar_variant.attn output; u = dir * u_norm), for the
+ *         softmax arm the pages compare against.  Its term adds p_j (v_j - u) . attn to
+ *         the gradient of logit j and p_j attn to dv_j. */
 typedef struct {
   const float *dir;
   const float *count;
   const float *n_eff;
   const float *gate;
   const float *lse;
+  const float *attn;
 } polar_cotangents;
 
 /* Gradients written by polar_attn_bwd, float32, device.  dq [B,T,Hq,d], dk and dv
@@ -324,9 +331,12 @@ POLAR_API polar_status polar_attn_bwd(const polar_params *p, polar_dtype dt, int
  * Training forward and backward of the variant modes (the sliding-window and RoPE arms
  * trained beside NoPE Polar Attention in the technical summary's section 3.1, "Ablation
  * Insights").  var->window and
- * var->rope_theta as for polar_attn_fwd_variant; var->attn must be NULL (the plain softmax
- * read-out has no backward here: POLAR_ERR_UNSUPPORTED).  var == NULL, or window and
- * rope_theta both 0, gives polar_attn_fwd_train and polar_attn_bwd.
+ * var->rope_theta as for polar_attn_fwd_variant.  var == NULL, or window and rope_theta
+ * both 0 (and no attn), gives polar_attn_fwd_train and polar_attn_bwd.
+ *
+ * The plain softmax read-out: polar_attn_fwd_train_variant writes it to var->attn when
+ * that is non-NULL (as polar_attn_fwd_variant does), and its gradient enters the backward
+ * as cot->attn.  The backward takes no var->attn (POLAR_ERR_UNSUPPORTED).
  *
  * With RoPE both calls rotate q and k into their workspace first (rounded to the input
  * type, as polar_attn_fwd_variant rotates them), run the causal kernels on the rotated

@@ -39,6 +39,9 @@ EXPORTS = ("polar_attn_fwd", "polar_attn_fwd_mixed", "polar_decode_workspace_byt
            "polar_status_str", "polar_last_error", "polar_abi_version")
 
 
+ABI_VERSION = 7                            # POLAR_ABI_VERSION of include/polar.h
+
+
 class polar_params(ctypes.Structure):
     _fields_ = [("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("train_len", ctypes.c_int32),
@@ -70,7 +73,10 @@ class polar_saved(ctypes.Structure):
 class polar_cotangents(ctypes.Structure):
     _fields_ = [("dir", ctypes.c_void_p), ("count", ctypes.c_void_p),
                 ("n_eff", ctypes.c_void_p), ("gate", ctypes.c_void_p),
-                ("lse", ctypes.c_void_p)]
+                ("lse", ctypes.c_void_p), ("attn", ctypes.c_void_p)]
+
+
+COTANGENTS = tuple(name for name, _ in polar_cotangents._fields_)
 
 
 class polar_grads(ctypes.Structure):
@@ -159,6 +165,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.polar_last_error.argtypes = []
     lib.polar_abi_version.restype = I32
     lib.polar_abi_version.argtypes = []
+    if lib.polar_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{path} has C ABI version {lib.polar_abi_version()}, the binding "
+                           f"declares version {ABI_VERSION}: rebuild it")
     _lib = lib
     return lib
 

@@ -163,8 +163,8 @@ polar_status prefill(const polar_params *p, polar_dtype dt, int32_t B, int32_t T
   // The training forward takes its window in the training instance (and its q and k
   // already rotated, see polar_attn_fwd_train_variant).
   a.variant = (!saved && (a.attn || a.window > 0 || a.rope)) ? 1 : 0;
-  if (saved && (a.attn || a.rope))
-    return fail(POLAR_ERR_UNSUPPORTED, "the training forward takes no attn output or rotation here");
+  if (saved && a.rope)
+    return fail(POLAR_ERR_UNSUPPORTED, "the training forward takes no rotation here");
   // Keys rotated once into the caller's workspace instead of in every staging workgroup.
   void *k_rot = nullptr;
   if (a.rope && var->workspace) {
@@ -286,11 +286,13 @@ polar_status polar_attn_fwd_train_variant(const polar_params *p, const polar_var
   if (!saved) return fail(POLAR_ERR_NULL_POINTER, "saved is NULL");
   polar_status st = check_variant(var);
   if (st != POLAR_OK) return st;
-  if (var && var->attn)
-    return fail(POLAR_ERR_UNSUPPORTED, "the training forward takes no softmax read-out (var.attn)");
-  // The window goes to the training instance; a rotation is done here, into the workspace.
+  if (var && var->attn && !aligned16(var->attn))
+    return fail(POLAR_ERR_MISALIGNED, "variant attn output must be 16-byte aligned");
+  // The window and the read-out go to the training instance; a rotation is done here,
+  // into the workspace.
   polar_variant w{};
   w.window = var ? var->window : 0;
+  w.attn = var ? var->attn : nullptr;
   const float theta = var ? var->rope_theta : 0.f;
   if (theta == 0.f) return prefill(p, dt, B, T, q, k, v, out, saved, &w, stream);
   st = check_params(p, dt, out);
@@ -334,7 +336,8 @@ static polar_status bwd_impl(const polar_params *p, const polar_variant *var, po
   st = check_variant(var);
   if (st != POLAR_OK) return st;
   if (var && var->attn)
-    return fail(POLAR_ERR_UNSUPPORTED, "the backward takes no softmax read-out (var.attn)");
+    return fail(POLAR_ERR_UNSUPPORTED,
+                "the backward takes no var.attn (the read-out's gradient is cot.attn)");
   const int window = var ? var->window : 0;
   const float theta = var ? var->rope_theta : 0.f;
   if (dt != POLAR_DTYPE_BF16)
@@ -366,10 +369,10 @@ static polar_status bwd_impl(const polar_params *p, const polar_variant *var, po
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(fwd->dir) ||
       !aligned16(grads->dq) || !aligned16(grads->dk) || !aligned16(grads->dv) ||
       (cot->dir && !aligned16(cot->dir)) || (cot->count && !aligned16(cot->count)) ||
-      (cot->count && !aligned16(p->count_vec)))
+      (cot->attn && !aligned16(cot->attn)) || (cot->count && !aligned16(p->count_vec)))
     return fail(POLAR_ERR_MISALIGNED,
-                "q, k, v, fwd.dir, cot.dir, cot.count, count_vec, dq, dk, dv must be 16-byte "
-                "aligned");
+                "q, k, v, fwd.dir, cot.dir, cot.count, cot.attn, count_vec, dq, dk, dv must be "
+                "16-byte aligned");
   if (((uintptr_t)workspace & 255u) != 0)
     return fail(POLAR_ERR_MISALIGNED, "workspace must be 256-byte aligned");
   if (!bwd_shape_ok(B, T, Hq, p->n_kv_heads))
@@ -412,6 +415,7 @@ static polar_status bwd_impl(const polar_params *p, const polar_variant *var, po
   a.c_n_eff = cot->n_eff;
   a.c_gate = cot->gate;
   a.c_lse = cot->lse;
+  a.c_attn = cot->attn;
   a.dq = grads->dq;
   a.dk = grads->dk;
   a.dv = grads->dv;

@@ -4,17 +4,19 @@
 // The forward is section 2.1 of the ATMA technical summary (gist.science), "Polar
 // Attention: A Three-Channel Decomposition", as fused in section 2.2.  Differentiating it
 // row by row (row i of head h, c = beta_h * tau(i+1), l_j = c <q_i, k_j>, p = softmax(l)):
-//   du    = (I - dir dir^T) d_dir / |u|                      (dir = u/|u|)
+//   du    = (I - dir dir^T) d_dir / |u| + d_attn             (dir = u/|u|)
 //   th    = tanh(ln n_eff) = (n^2-1)/(n^2+1);  gc = d_count . w_h
 //   dgate = d_gate + gc th;  dn = d_n_eff + gc gate 4n/(n^2+1)^2
 //   dm    = dgate gate (1-gate)                              (gate = sigmoid(m - floor))
-//   A     = d_lse + 2 n dn;   E = -2 n^2 dn                  (n_eff = 1/sum p^2)
+//   A     = d_lse + 2 n dn - u . du;   E = -2 n^2 dn         (n_eff = 1/sum p^2)
 //   dl_j  = p_j (v_j . du + A + E p_j) + [j = j*] dm         (j* = first arg-max key)
 //   dq_i  = c sum_j dl_j k_j;  dk_j = sum_i c dl_ij q_i;  dv_j = sum_i p_ij du_i
 //   dbeta = sum_i [tau (q_i . sum_j dl_ij k_j) - dm (tau/sqrt(d)) sqrt(2 ln n)],
 //   dnull_bias = -sum_i dm,   dcount_vec = sum_i d_count_i gate th.
-// (u . du = 0, so the value term needs no row constant.)  p is recomputed from the saved
-// log-sum-exp, so no T x T quantity is stored.
+// d_attn is the cotangent of the plain softmax read-out u = sum_j p_j v_j (the softmax
+// arm).  u . du = u . d_attn in exact arithmetic (the direction part is orthogonal to u);
+// the prep kernel takes it of the rounded du the other kernels read.  p is recomputed
+// from the saved log-sum-exp, so no T x T quantity is stored.
 //
 // Kernels, in launch order:
 //  1. prep:  one 16-lane group per row: du (bf16), c*du (bf16) and the row scalars.
@@ -117,6 +119,7 @@ __global__ void __launch_bounds__(256) polar_bwd_prep_kernel(BwdArgs a) {
   const f32x4 cd = a.c_dir ? *(const f32x4 *)(a.c_dir + e0) : z4;
   const f32x4 cc = a.c_count ? *(const f32x4 *)(a.c_count + e0) : z4;
   const f32x4 w = a.c_count ? *(const f32x4 *)(a.count_vec + (size_t)h * kD + 4 * l16) : z4;
+  const f32x4 ca = a.c_attn ? *(const f32x4 *)(a.c_attn + e0) : z4;
   float dd = 0.f, gc = 0.f;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
@@ -130,30 +133,44 @@ __global__ void __launch_bounds__(256) polar_bwd_prep_kernel(BwdArgs a) {
   }
   const float U = a.u_norm[Rc], n = a.n_eff[Rc], gate = a.gate[Rc], lse = a.lse[Rc];
   const float inv = U > 0.f ? 1.0f / U : 0.f;
+  const float beta = a.beta ? a.beta[h] : 8.0f;
+  const int nk = keys_seen(i, a.window);
+  const float tau = tau_of(nk, a.inv_log_train);
+  const float c = beta * tau;
+  // du and c du as the MFMA kernels read them (bf16), and u . du of those rounded values:
+  // the row constant -u . du then cancels the value term's sum over keys exactly as it
+  // does in exact arithmetic (where it is -u . d_u, the direction part being orthogonal
+  // to u), instead of leaving the rounding of du times the mean logit and key.
+  bf16x4 o1, o2;
+  float ud = 0.f, ucd = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float du = (cd[k] - dir[k] * dd) * inv + ca[k];
+    o1[k] = (__bf16)du;
+    o2[k] = (__bf16)(c * du);
+    ud = fmaf(dir[k], (float)o1[k], ud);
+    ucd = fmaf(dir[k], (float)o2[k], ucd);
+  }
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) {
+    ud += __shfl_xor(ud, m);
+    ucd += __shfl_xor(ucd, m);
+  }
   const float n2 = n * n;
   const float th = (n2 - 1.f) / (n2 + 1.f);
   const float dth_dn = 4.f * n / ((n2 + 1.f) * (n2 + 1.f));
   const float dgate = (a.c_gate ? a.c_gate[Rc] : 0.f) + gc * th;
   const float dn = (a.c_n_eff ? a.c_n_eff[Rc] : 0.f) + gc * gate * dth_dn;
   const float dm = dgate * gate * (1.f - gate);
-  const float A = (a.c_lse ? a.c_lse[Rc] : 0.f) + 2.f * n * dn;
+  const float A0 = (a.c_lse ? a.c_lse[Rc] : 0.f) + 2.f * n * dn;
+  const float A = A0 - U * ud;             // with du (the dq kernel)
+  const float cA = c * A0 - U * ucd;       // with c du (the dk/dv kernel)
   const float E = -2.f * n2 * dn;
-  const float beta = a.beta ? a.beta[h] : 8.0f;
-  const int nk = keys_seen(i, a.window);
-  const float tau = tau_of(nk, a.inv_log_train);
-  const float c = beta * tau;
   if (!ok) return;
-  bf16x4 o1, o2;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const float du = (cd[k] - dir[k] * dd) * inv;
-    o1[k] = (__bf16)du;
-    o2[k] = (__bf16)(c * du);
-  }
   *(bf16x4 *)(a.du + e0) = o1;
   *(bf16x4 *)(a.cdu + e0) = o2;
   if (l16 == 0) {
-    const f32x4 r0 = {c * kLog2e, lse * kLog2e, c * A, c * E};
+    const f32x4 r0 = {c * kLog2e, lse * kLog2e, cA, c * E};
     const f32x4 r1 = {A, E, dm, __int_as_float(a.arg_max[Rc])};
     const float fl =
         a.null_floor ? -dm * tau * 0.125f * sqrtf(2.f * logf((float)nk)) : 0.f;

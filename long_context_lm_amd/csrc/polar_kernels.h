@@ -16,8 +16,9 @@ struct PrefillArgs {
   float *dir, *count, *n_eff, *gate, *lse;
   float *u_norm;                          // [B,T,Hq] |u| for the backward pass, or NULL
   int32_t *arg_max;                       // [B,T,Hq] first key of the row maximum (with u_norm)
+  // Softmax read-out sum p v [B,T,Hq,d], or NULL (variant and training instances):
+  float *attn;
   // Variant modes (variant instances only):
-  float *attn;                            // [B,T,Hq,d] plain softmax output sum p v, or NULL
   int variant;                            // 1: launch the variant instance
   int window;                             // W >= 1: row i sees keys i-W+1..i; 0: all
   int rope;                               // 1: rotate q and k by RoPE on load
@@ -134,7 +135,8 @@ hipError_t launch_delta_sequence(int dtype, const DeltaSeqArgs &a, hipStream_t s
 // r0 and r1 of a row are adjacent in `rows`):
 //   r0 = {c*log2(e), lse*log2(e), c*A, c*E}   r1 = {A, E, dm, arg-max key (int bits)}
 //   rp = {dbeta contribution of the dq kernel, -dm, gate*tanh(ln n_eff), floor term of dbeta}
-// with c = beta*tau and dl_j = p_j (v_j.du + A + E p_j) + [j = arg-max] dm.
+// with c = beta*tau and dl_j = p_j (v_j.du + A + E p_j) + [j = arg-max] dm (the u . du
+// inside A and c*A taken of the bf16 du and c*du the kernels read).
 struct BwdArgs {
   const void *q, *k, *v;                  // bf16 [B,T,Hq,d], [B,T,Hkv,d] x2
   const float *beta, *null_bias, *count_vec;
@@ -142,6 +144,7 @@ struct BwdArgs {
   const float *u_norm;                    // forward residuals
   const int32_t *arg_max;
   const float *c_dir, *c_count, *c_n_eff, *c_gate, *c_lse;   // cotangents (NULL = 0)
+  const float *c_attn;                    // cotangent of the read-out u = sum p v (NULL = 0)
   float *dq, *dk, *dv;                    // fp32 [B,T,Hq,d], [B,T,Hkv,d] x2
   float *d_beta, *d_null_bias, *d_count_vec;
   uint16_t *du, *cdu;                     // workspace: bf16 du and c*du [B,T,Hq,d]

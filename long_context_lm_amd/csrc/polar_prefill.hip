@@ -28,7 +28,7 @@
 //  * epilogue: n_eff = S^2/Q, lse, the floor gate, dir = u/|u|, count;
 //  * training instances (kModeSave, kModeSaveWin) also keep, per lane, the first key attaining
 //    the lane's running maximum score and write |u| and that key (the row's arg-max) for
-//    the backward pass;
+//    the backward pass, and, when asked, the softmax read-out u itself;
 //  * variant instances add a sliding window, RoPE and the plain softmax output: q is
 //    rotated as it is loaded, and K either arrives rotated (kModeVariant, rotated once by
 //    polar_rope_keys_kernel) or is rotated while each tile is staged through registers
@@ -117,6 +117,8 @@ __global__ void __launch_bounds__(64 * kWaves, kLean ? 4 : 1)
   // The sliding window: variant instances, and the windowed training instance (which takes
   // q and k already rotated when RoPE is on).
   constexpr bool kWin = kVar || kMode == kModeSaveWin;
+  // Instances that can also write the softmax read-out u (a.attn, when non-NULL).
+  constexpr bool kAttn = kVar || kSave;
   static_assert(!kPaged || LdsCfg<TR>::kt == kPageSize, "a key tile is one page");
   constexpr int kThreads = 64 * kWaves;
   constexpr int kKT = LdsCfg<TR>::kt;                // keys per tile
@@ -927,7 +929,7 @@ __global__ void __launch_bounds__(64 * kWaves, kLean ? 4 : 1)
             *(f32x4 *)(ep + dim0) = val;
           }
         rinv[qb] = inv;
-        if constexpr (kVar) rinvs[qb] = 1.0f / St;
+        if constexpr (kAttn) rinvs[qb] = 1.0f / St;
       } else if constexpr (kMix) {
         // The three streams summed: u/|u| + gate tanh(ln n_eff) w_h + memory.
         const float cg = a.count_vec ? gate * th : 0.f;
@@ -959,7 +961,7 @@ __global__ void __launch_bounds__(64 * kWaves, kLean ? 4 : 1)
             *(f32x4 *)(dp + dim0) = val;
           }
       }
-      if constexpr (kVar && !kRowStores) {
+      if constexpr (kAttn && !kRowStores) {
         if (a.attn) {
           const float is = 1.0f / St;
           float *ap = a.attn + obase * kD;
@@ -1015,7 +1017,7 @@ __global__ void __launch_bounds__(64 * kWaves, kLean ? 4 : 1)
     const int rq = lane >> 4, cc = (lane & 15) * 4;
     const bool wcount = kMix ? a.count_vec != nullptr : a.count != nullptr;
     bool wattn = false;
-    if constexpr (kVar) wattn = a.attn != nullptr;
+    if constexpr (kAttn) wattn = a.attn != nullptr;
     const f32x4 w4 = wcount ? *(const f32x4 *)(a.count_vec + (size_t)h * kD + cc)
                             : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1023,12 +1025,12 @@ __global__ void __launch_bounds__(64 * kWaves, kLean ? 4 : 1)
       const int r = 4 * i + rq;
       const float cgr = __shfl(cgate[0], r), invr = __shfl(rinv[0], r);
       float isr = 0.f;
-      if constexpr (kVar) isr = __shfl(rinvs[0], r);
+      if constexpr (kAttn) isr = __shfl(rinvs[0], r);
       if (wrow0 + r < a.T) {
         const size_t ob = (((size_t)b * a.T + wrow0 + r) * a.Hq + h) * kD + cc;
         const f32x4 u4 = *(const f32x4 *)(ep + r * kOutPitch + cc);
         const f32x4 dv = u4 * invr;
-        if constexpr (kVar) {
+        if constexpr (kAttn) {
           if (wattn) __builtin_nontemporal_store(u4 * isr, (f32x4 *)(a.attn + ob));
         }
         if constexpr (kMix) {

@@ -140,13 +140,14 @@ def _prefill_args(q, k, v, beta, null_bias, count_vec, train_len, flags):
 def attn_fwd_train(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta=None,
                    null_bias=None, count_vec=None, train_len: int = 2048,
                    flags: int = _lib.POLAR_FLAG_LENGTH_TEMP | _lib.POLAR_FLAG_NULL_FLOOR,
-                   window: int = 0, rope_theta: float = 0.0,
+                   window: int = 0, rope_theta: float = 0.0, want_attn: bool = False,
                    workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
     """Prefill that also returns the residuals of the backward pass ("u_norm", "arg_max").
 
     ``window`` and ``rope_theta`` select the variant modes (polar_attn_fwd_train_variant);
     with RoPE, q and k are rotated into ``workspace`` (a uint8 device tensor of at least
-    train_variant_workspace_bytes(...) bytes, allocated here when None)."""
+    train_variant_workspace_bytes(...) bytes, allocated here when None).  ``want_attn``
+    adds the plain softmax read-out "attn" [B,T,Hq,d]."""
     prm, keep, (B, T, Hq, Hkv, d) = _prefill_args(q, k, v, beta, null_bias, count_vec,
                                                   train_len, flags)
     dev = q.device
@@ -155,17 +156,20 @@ def attn_fwd_train(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta=None,
     out["arg_max"] = torch.empty(B, T, Hq, device=dev, dtype=torch.int32)
     saved = _lib.polar_saved(_ptr(out["u_norm"]), _ptr(out["arg_max"]))
     s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
-    if window == 0 and rope_theta == 0.0:
+    if window == 0 and rope_theta == 0.0 and not want_attn:
         _lib.check(_lib.polar_attn_fwd_train(prm, _DT[q.dtype], B, T, q.data_ptr(),
                                              k.data_ptr(), v.data_ptr(), cout, saved, s))
         return out
-    var = _lib.polar_variant(window, rope_theta, None, None, 0)
+    if want_attn:
+        out["attn"] = torch.empty(B, T, Hq, d, device=dev, dtype=torch.float32)
+    attn = _ptr(out.get("attn"))
+    var = _lib.polar_variant(window, rope_theta, attn, None, 0)
     need = _lib.polar_train_variant_workspace_bytes(prm, var, _DT[q.dtype], B, T)
     if need > 0:
         if workspace is None:
             workspace = torch.empty(need, dtype=torch.uint8, device=dev)
         _check_aux(workspace, "workspace", dev, None)
-        var = _lib.polar_variant(window, rope_theta, None, workspace.data_ptr(),
+        var = _lib.polar_variant(window, rope_theta, attn, workspace.data_ptr(),
                                  workspace.numel() * workspace.element_size())
     _lib.check(_lib.polar_attn_fwd_train_variant(prm, var, _DT[q.dtype], B, T, q.data_ptr(),
                                                  k.data_ptr(), v.data_ptr(), cout, saved, s))
@@ -237,8 +241,8 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, fwd: dict, cot: 
 
     ``fwd`` is what attn_fwd_train returned for the same arguments (``window`` and
     ``rope_theta`` included: they select polar_attn_bwd_variant); ``cot`` maps output
-    names ("dir", "count", "n_eff", "gate", "lse") to float32 upstream gradients (missing
-    names are zero).  Returns float32 dq, dk, dv and, with ``param_grads``, d_beta,
+    names ("dir", "count", "n_eff", "gate", "lse", and "attn" for the softmax read-out) to
+    float32 upstream gradients (missing names are zero).  Returns float32 dq, dk, dv and, with ``param_grads``, d_beta,
     d_null_bias and d_count_vec.
     """
     prm, keep, (B, T, Hq, Hkv, d) = _prefill_args(q, k, v, beta, null_bias, count_vec,
@@ -250,12 +254,12 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, fwd: dict, cot: 
                           ("u_norm", f32t, (B, T, Hq)), ("arg_max", torch.int32, (B, T, Hq))):
         _check_aux(fwd.get(name), f"fwd[{name!r}]", dev, dt, shp)
     cts = {}
-    for name in ("dir", "count", "n_eff", "gate", "lse"):
+    for name in _lib.COTANGENTS:
         c = cot.get(name)
         cts[name] = None if c is None else torch.as_tensor(
             c, dtype=torch.float32, device=dev).contiguous()
         if c is not None:
-            want = (B, T, Hq, d) if name in ("dir", "count") else (B, T, Hq)
+            want = (B, T, Hq, d) if name in ("dir", "count", "attn") else (B, T, Hq)
             _check_aux(cts[name], f"cot[{name!r}]", dev, f32t, want)
     f32 = dict(device=dev, dtype=torch.float32)
     g = dict(dq=torch.empty(B, T, Hq, d, **f32), dk=torch.empty(B, T, Hkv, d, **f32),
@@ -273,7 +277,7 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, fwd: dict, cot: 
     fo = _lib.polar_outputs(_ptr(fwd["dir"]), None, _ptr(fwd["n_eff"]), _ptr(fwd["gate"]),
                             _ptr(fwd["lse"]))
     sv = _lib.polar_saved(_ptr(fwd["u_norm"]), _ptr(fwd["arg_max"]))
-    co = _lib.polar_cotangents(*(_ptr(cts[n]) for n in ("dir", "count", "n_eff", "gate", "lse")))
+    co = _lib.polar_cotangents(*(_ptr(cts[n]) for n in _lib.COTANGENTS))
     go = _lib.polar_grads(_ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g.get("d_beta")),
                           _ptr(g.get("d_null_bias")), _ptr(g.get("d_count_vec")))
     s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream

@@ -104,8 +104,8 @@ def polar_prefill_grad(q, k, v, cot: dict, beta=None, null_bias=None, count_vec=
 
     q [B,T,Hq,d], k and v [B,T,Hkv,d]; ``cot`` maps output names ("dir", "count",
     "n_eff", "gate", "lse", and "attn" for the plain softmax read-out) to cotangents of
-    the output shapes (a missing name means zero).  ``window``, ``rope_theta`` and ``rope_bf16`` select the variant modes as in
-    ``polar_prefill`` (0 = off).  Rows are processed in blocks of about ``max_elems``
+    the output shapes (a missing name means zero).  ``window``, ``rope_theta`` and
+    ``rope_bf16`` select the variant modes as in ``polar_prefill`` (0 = off).  Rows are processed in blocks of about ``max_elems``
     scores, each block's graph differentiated on its own; gradients accumulate in the
     leaves.  Returns float64 numpy arrays dq, dk, dv, d_beta [Hq], d_null_bias [Hq],
     d_count_vec [Hq,d] (and the forward outputs when ``return_outputs``).

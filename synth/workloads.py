@@ -297,25 +297,32 @@ def decode_inputs(name: str = "c5", B: Optional[int] = None, L: Optional[int] = 
 # --------------------------------------------------------------------------- gradients
 @dataclasses.dataclass
 class Cotangents:
-    """Upstream gradients of the five prefill outputs (float32, standard normal)."""
+    """Upstream gradients of the five prefill outputs, and optionally of the plain softmax
+    read-out (float32, standard normal)."""
     d_dir: np.ndarray          # [B,T,Hq,d]
     d_count: np.ndarray        # [B,T,Hq,d]
     d_n_eff: np.ndarray        # [B,T,Hq]
     d_gate: np.ndarray         # [B,T,Hq]
     d_lse: np.ndarray          # [B,T,Hq]
+    d_attn: Optional[np.ndarray] = None    # [B,T,Hq,d]
 
     def as_dict(self) -> dict:
-        return dict(dir=self.d_dir, count=self.d_count, n_eff=self.d_n_eff, gate=self.d_gate,
-                    lse=self.d_lse)
+        out = dict(dir=self.d_dir, count=self.d_count, n_eff=self.d_n_eff, gate=self.d_gate,
+                   lse=self.d_lse)
+        if self.d_attn is not None:
+            out["attn"] = self.d_attn
+        return out
 
 
 def cotangents(B: int, T: int, Hq: int, d: int = 64, seed: int = 2001,
-               n_eff_scale: float = 1.0) -> Cotangents:
-    """Seeded upstream gradients for the backward pass: one child stream per output."""
-    s = np.random.SeedSequence(seed).spawn(5)
+               n_eff_scale: float = 1.0, attn: bool = False) -> Cotangents:
+    """Seeded upstream gradients for the backward pass: one child stream per output (the
+    read-out's is the sixth, so asking for it leaves the other five unchanged)."""
+    s = np.random.SeedSequence(seed).spawn(6)
     return Cotangents(d_dir=_normal(s[0], (B, T, Hq, d)), d_count=_normal(s[1], (B, T, Hq, d)),
                       d_n_eff=(np.float32(n_eff_scale) * _normal(s[2], (B, T, Hq))).astype(np.float32),
-                      d_gate=_normal(s[3], (B, T, Hq)), d_lse=_normal(s[4], (B, T, Hq)))
+                      d_gate=_normal(s[3], (B, T, Hq)), d_lse=_normal(s[4], (B, T, Hq)),
+                      d_attn=_normal(s[5], (B, T, Hq, d)) if attn else None)
 
 
 

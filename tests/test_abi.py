@@ -23,7 +23,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(_lib.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert _lib.polar_abi_version() == 6
+    assert _lib.polar_abi_version() == 7 == _lib.ABI_VERSION
 
 
 def test_status_strings():
@@ -175,9 +175,10 @@ def saved(**kw):
 
 
 def cots(**kw):
-    d = dict(dir=A, count=A, n_eff=A, gate=A, lse=A)
+    d = dict(dir=A, count=A, n_eff=A, gate=A, lse=A, attn=A)
     d.update(kw)
-    return _lib.polar_cotangents(d["dir"], d["count"], d["n_eff"], d["gate"], d["lse"])
+    return _lib.polar_cotangents(d["dir"], d["count"], d["n_eff"], d["gate"], d["lse"],
+                                 d["attn"])
 
 
 def grads(**kw):
@@ -221,6 +222,7 @@ def test_bwd_workspace_bytes():
     (dict(ws=WS + 16), _lib.POLAR_ERR_MISALIGNED),
     (dict(g=grads(dk=A + 4)), _lib.POLAR_ERR_MISALIGNED),
     (dict(c=cots(dir=A + 8)), _lib.POLAR_ERR_MISALIGNED),
+    (dict(c=cots(attn=A + 4)), _lib.POLAR_ERR_MISALIGNED),
     (dict(ws_bytes=1024), _lib.POLAR_ERR_WORKSPACE_TOO_SMALL),
 ])
 def test_bwd_validation_errors(kw, code):
@@ -306,7 +308,8 @@ def train_var(window=0, theta=0.0, attn=None, ws=None, ws_bytes=0, dt=1, B=1, T=
 @pytest.mark.parametrize("kw,code", [
     (dict(window=-3), _lib.POLAR_ERR_BAD_SHAPE),
     (dict(theta=0.9), _lib.POLAR_ERR_BAD_SHAPE),
-    (dict(attn=A), _lib.POLAR_ERR_UNSUPPORTED),             # no softmax read-out in training
+    (dict(attn=A + 4), _lib.POLAR_ERR_MISALIGNED),          # the read-out, misaligned
+    (dict(theta=10000.0, ws=A, ws_bytes=1 << 20, attn=A + 8), _lib.POLAR_ERR_MISALIGNED),
     (dict(window=4, o=outs(lse=None)), _lib.POLAR_ERR_NULL_POINTER),
     (dict(theta=10000.0), _lib.POLAR_ERR_NULL_POINTER),     # RoPE needs the workspace
     (dict(theta=10000.0, ws=A + 8, ws_bytes=1 << 20), _lib.POLAR_ERR_MISALIGNED),
@@ -325,6 +328,7 @@ def test_train_variant_null_saved_and_empty():
         ctypes.byref(params()), None, 1, 1, 8, A, A, A, ctypes.byref(outs()), None, None) == \
         _lib.POLAR_ERR_NULL_POINTER
     assert train_var(window=4, theta=10000.0, B=0) == _lib.POLAR_OK
+    assert train_var(attn=A, T=0) == _lib.POLAR_OK          # the read-out, empty call
 
 
 def test_train_variant_workspace_bytes():
@@ -353,6 +357,7 @@ def test_bwd_variant_workspace_bytes():
 @pytest.mark.parametrize("kw,code", [
     (dict(var=_lib.polar_variant(-1, 0.0, None, None, 0)), _lib.POLAR_ERR_BAD_SHAPE),
     (dict(var=_lib.polar_variant(0, 1.0, None, None, 0)), _lib.POLAR_ERR_BAD_SHAPE),
+    # the read-out's gradient comes in cot.attn, never var.attn
     (dict(var=_lib.polar_variant(8, 0.0, A, None, 0)), _lib.POLAR_ERR_UNSUPPORTED),
     (dict(var=_lib.polar_variant(0, 500.0, None, None, 0), dt=0), _lib.POLAR_ERR_UNSUPPORTED),
     # the base workspace is not enough once q and k are rotated into it
