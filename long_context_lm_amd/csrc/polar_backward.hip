@@ -571,6 +571,8 @@ polar_bwd_dkv_kernel(BwdArgs a) {
         if (r0row + 31 >= kw0 && kw0 < a.T && (W == 0 || r0row <= kw0 + 30 + W)) {
           const uint16_t *Qb = lds_at(&Qs[0][0], q_lane + buf * QBUF);
           const uint16_t *Cb = lds_at(&Cs[0][0], q_lane + buf * QBUF);
+          // The arg-max key of row c32, read ahead of the products that hide its latency.
+          const int jl = __float_as_int(Sc[buf][5][c32]);
           const f32x16 zero = {};
           f32x16 S, P;
 #pragma unroll
@@ -606,7 +608,6 @@ polar_bwd_dkv_kernel(BwdArgs a) {
           else
             probs(std::false_type{});
           // Rows whose arg-max key belongs to this wave (rare): add c*dm at that key.
-          const int jl = __float_as_int(Sc[buf][5][c32]);
           if (__ballot(jl >= kw0 && jl < kw0 + 32) != 0) {
 #pragma unroll
             for (int a4 = 0; a4 < 4; ++a4) {
