@@ -19,15 +19,16 @@
 // from the saved log-sum-exp, so no T x T quantity is stored.
 //
 // Kernels, in launch order:
-//  1. prep:  one 16-lane group per row: du (bf16), c*du (bf16) and the row scalars.
+//  1. prep:  one 16-lane group per row: du (bf16) and the row scalars.
 //  2. dq:    one wave per 32 rows of a head (lane = query, as in the forward): per 64-key
 //            tile S^T = K Q^T and dP^T = V du^T on MFMA, dl on the VALU, then
 //            dq^T += K^T dl^T with K^T from a transposed LDS tile.
 //  3. dk/dv: one wave per 32 keys (lane = key), keys and values resident in registers;
 //            a workgroup owns two key blocks (i and its mirror, for causal balance) and
 //            walks, from the last one down, every query tile of the G heads sharing the KV
-//            head that can see their keys.  S' = Q K^T and c dP' = (c du) V^T on MFMA, then
-//            dv^T += du^T P and dk^T += Q^T dS with du^T and Q^T from transposed tiles.
+//            head that can see their keys.  S' = Q K^T and dP' = du V^T on MFMA (the row's
+//            c applied on the VALU), then dv^T += du^T P and dk^T += Q^T dS with du^T and
+//            Q^T from transposed tiles.
 //            Each key has one owner, so dk and dv need no atomics.
 //  4. parameter gradients: fixed-order two-level reductions over rows.
 #include <type_traits>
@@ -137,40 +138,32 @@ __global__ void __launch_bounds__(256) polar_bwd_prep_kernel(BwdArgs a) {
   const int nk = keys_seen(i, a.window);
   const float tau = tau_of(nk, a.inv_log_train);
   const float c = beta * tau;
-  // du and c du as the MFMA kernels read them (bf16), and u . du of those rounded values:
-  // the row constant -u . du then cancels the value term's sum over keys exactly as it
-  // does in exact arithmetic (where it is -u . d_u, the direction part being orthogonal
-  // to u), instead of leaving the rounding of du times the mean logit and key.
-  bf16x4 o1, o2;
-  float ud = 0.f, ucd = 0.f;
+  // du as the MFMA kernels read it (bf16), and u . du of that rounded value: the row
+  // constant -u . du then cancels the value term's sum over keys exactly as it does in
+  // exact arithmetic (where it is -u . d_u, the direction part being orthogonal to u),
+  // instead of leaving the rounding of du times the mean logit and key.
+  bf16x4 o1;
+  float ud = 0.f;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const float du = (cd[k] - dir[k] * dd) * inv + ca[k];
     o1[k] = (__bf16)du;
-    o2[k] = (__bf16)(c * du);
     ud = fmaf(dir[k], (float)o1[k], ud);
-    ucd = fmaf(dir[k], (float)o2[k], ucd);
   }
 #pragma unroll
-  for (int m = 1; m < 16; m <<= 1) {
-    ud += __shfl_xor(ud, m);
-    ucd += __shfl_xor(ucd, m);
-  }
+  for (int m = 1; m < 16; m <<= 1) ud += __shfl_xor(ud, m);
   const float n2 = n * n;
   const float th = (n2 - 1.f) / (n2 + 1.f);
   const float dth_dn = 4.f * n / ((n2 + 1.f) * (n2 + 1.f));
   const float dgate = (a.c_gate ? a.c_gate[Rc] : 0.f) + gc * th;
   const float dn = (a.c_n_eff ? a.c_n_eff[Rc] : 0.f) + gc * gate * dth_dn;
   const float dm = dgate * gate * (1.f - gate);
-  const float A0 = (a.c_lse ? a.c_lse[Rc] : 0.f) + 2.f * n * dn;
-  const float A = A0 - U * ud;             // with du (the dq kernel)
-  const float cA = c * A0 - U * ucd;       // with c du (the dk/dv kernel)
+  const float A = (a.c_lse ? a.c_lse[Rc] : 0.f) + 2.f * n * dn - U * ud;
   const float E = -2.f * n2 * dn;
   if (!ok) return;
   *(bf16x4 *)(a.du + e0) = o1;
-  *(bf16x4 *)(a.cdu + e0) = o2;
   if (l16 == 0) {
-    const f32x4 r0 = {c * kLog2e, lse * kLog2e, cA, c * E};
+    const f32x4 r0 = {c * kLog2e, lse * kLog2e, c * A, c * E};
     const f32x4 r1 = {A, E, dm, __int_as_float(a.arg_max[Rc])};
     const float fl =
         a.null_floor ? -dm * tau * 0.125f * sqrtf(2.f * logf((float)nk)) : 0.f;
@@ -413,7 +406,7 @@ polar_bwd_dkv_kernel(BwdArgs a) {
   constexpr int KB = 32 * kWaves;                   // keys per key block
   constexpr int QROW = 72, TROW = 40;
   __shared__ __attribute__((aligned(16))) uint16_t Qs[2][32 * QROW];   // q rows
-  __shared__ __attribute__((aligned(16))) uint16_t Cs[2][32 * QROW];   // c*du rows
+  __shared__ __attribute__((aligned(16))) uint16_t Cs[2][32 * QROW];   // du rows
   __shared__ __attribute__((aligned(16))) uint16_t Qt[2][kD * TROW];   // q^T
   __shared__ __attribute__((aligned(16))) uint16_t Dt[2][kD * TROW];   // du^T
   // Row scalars: cl2, lse2, c*A, c*E, dm, arg-max key (bits).
@@ -454,7 +447,7 @@ polar_bwd_dkv_kernel(BwdArgs a) {
   const int voff_p1 = voff_p0 + rs;
   const int voff_s = (tid & 31) * a.Hq * 32 + (tid >> 5) * 16;   // r0 (tid < 32) or r1
 
-  // Staged query-side data of one step: q and c*du row chunks, q and du pair tasks, and
+  // Staged query-side data of one step: q and du row chunks, q and du pair tasks, and
   // (threads < 64) one row record.  kDepth sets are in flight.
   struct Stage {
     u32x4 qst, cst;
@@ -474,10 +467,8 @@ polar_bwd_dkv_kernel(BwdArgs a) {
         (void *)((const uint16_t *)a.q + row0 * kD), 0, nbytes, kBufferFlags);
     const auto dr = __builtin_amdgcn_make_buffer_rsrc((void *)(a.du + row0 * kD), 0, nbytes,
                                                       kBufferFlags);
-    const auto cr = __builtin_amdgcn_make_buffer_rsrc((void *)(a.cdu + row0 * kD), 0, nbytes,
-                                                      kBufferFlags);
     qst = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(qr, voff_c, 0, 0));
-    cst = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(cr, voff_c, 0, 0));
+    cst = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(dr, voff_c, 0, 0));
     qtst[0] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(qr, voff_p0, 0, 0));
     qtst[1] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(qr, voff_p1, 0, 0));
     dtst[0] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(dr, voff_p0, 0, 0));
@@ -599,7 +590,8 @@ polar_bwd_dkv_kernel(BwdArgs a) {
                   if (row < key || (W > 0 && row - W >= key)) p = 0.f;
                 }
                 pv[r] = p;
-                dsv[r] = p * (P[r] + fmaf(ec[c], p, ac[c]));
+                // c dl / p = c (du . v_j) + c A + c E p, with c = cl ln 2.
+                dsv[r] = p * fmaf(cl[c] * kLn2, P[r], fmaf(ec[c], p, ac[c]));
               }
             }
           };
@@ -758,7 +750,7 @@ int n_parts(int B, int T) {
 
 size_t bwd_ws_bytes(int B, int T, int Hq, int Hkv) {
   const size_t nrows = (size_t)B * T * Hq;
-  return 2 * align256(nrows * kD * 2) + align256(nrows * 32) + align256(nrows * 16) +
+  return align256(nrows * kD * 2) + align256(nrows * 32) + align256(nrows * 16) +
          align256((size_t)Hq * n_parts(B, T) * kPartStride * 4) +
          2 * align256((size_t)(kDkvSplitMax - 1) * B * T * Hkv * kD * 4);
 }
@@ -767,8 +759,6 @@ void bwd_ws_layout(BwdArgs &a, void *ws) {
   const size_t nrows = (size_t)a.B * a.T * a.Hq;
   char *p = (char *)ws;
   a.du = (uint16_t *)p;
-  p += align256(nrows * kD * 2);
-  a.cdu = (uint16_t *)p;
   p += align256(nrows * kD * 2);
   a.rows = (float *)p;
   p += align256(nrows * 32);

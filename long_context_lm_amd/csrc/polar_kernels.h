@@ -136,7 +136,7 @@ hipError_t launch_delta_sequence(int dtype, const DeltaSeqArgs &a, hipStream_t s
 //   r0 = {c*log2(e), lse*log2(e), c*A, c*E}   r1 = {A, E, dm, arg-max key (int bits)}
 //   rp = {dbeta contribution of the dq kernel, -dm, gate*tanh(ln n_eff), floor term of dbeta}
 // with c = beta*tau and dl_j = p_j (v_j.du + A + E p_j) + [j = arg-max] dm (the u . du
-// inside A and c*A taken of the bf16 du and c*du the kernels read).
+// inside A taken of the bf16 du the kernels read).
 struct BwdArgs {
   const void *q, *k, *v;                  // bf16 [B,T,Hq,d], [B,T,Hkv,d] x2
   const float *beta, *null_bias, *count_vec;
@@ -147,7 +147,7 @@ struct BwdArgs {
   const float *c_attn;                    // cotangent of the read-out u = sum p v (NULL = 0)
   float *dq, *dk, *dv;                    // fp32 [B,T,Hq,d], [B,T,Hkv,d] x2
   float *d_beta, *d_null_bias, *d_count_vec;
-  uint16_t *du, *cdu;                     // workspace: bf16 du and c*du [B,T,Hq,d]
+  uint16_t *du;                           // workspace: bf16 du [B,T,Hq,d]
   float *rows;                            // workspace: per-row r0, r1 (8 floats)
   float *rp;                              // workspace: per-row float4
   float *part;                            // workspace: [Hq][n_part][kPartStride]
@@ -164,7 +164,7 @@ struct BwdArgs {
 constexpr int kPartStride = 68;           // dw[64], dbeta, dbias, pad
 
 size_t bwd_ws_bytes(int B, int T, int Hq, int Hkv);
-void bwd_ws_layout(BwdArgs &a, void *ws);  // sets du, cdu, rows, rp, part, dk/dv parts, n_part
+void bwd_ws_layout(BwdArgs &a, void *ws);  // sets du, rows, rp, part, dk/dv parts, n_part
 int bwd_rows_per_block(int hb);
 int bwd_keys_per_block();
 int bwd_head_split(int G);                // workgroups sharing one key block (divides G)
