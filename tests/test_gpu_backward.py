@@ -57,6 +57,8 @@ def test_forward_train_matches_forward_and_oracle(gpu_lib):
     (1, 100, 16, 2, 3, 16, False),     # G = 8
     (1, 1, 4, 1, 3, 2048, False),      # a single row
     (1, 65, 4, 1, 3, 8, True),         # one key past a 64-key tile
+    (1, 150, 32, 4, 3, 64, False),     # 32 heads: prep walks 16-head slabs token by token
+    (2, 130, 6, 2, 3, 64, True),       # 6 heads (G = 3): prep's one-row fallback, no head split
 ])
 def test_backward_parity(gpu_lib, B, T, Hq, Hkv, flags, train_len, rand):
     print(f"[case] bwd B={B} T={T} Hq={Hq} Hkv={Hkv} flags={flags} L={train_len}", flush=True)
