@@ -50,7 +50,7 @@ PEAK_FP32_TFLOPS = 157.3        # MI355X fp32 vector (published; counts packed f
 
 
 # Sources each timed kernel is built from; a counter record stays valid while these are unchanged.
-_PREFILL_SRC = ["polar_prefill.hip", "polar_mfma.h", "polar_kernels.h"]
+_PREFILL_SRC = ["polar_prefill.hip", "polar_mfma.h", "polar_kernels.h", "polar_rope.h"]
 _DECODE_SRC = ["polar_decode.hip", "polar_mfma.h", "polar_kernels.h"]
 KERNEL_SOURCES = {
     "prefill": _PREFILL_SRC,
@@ -58,7 +58,7 @@ KERNEL_SOURCES = {
     "prefill_c3": _PREFILL_SRC,
     "decode": _DECODE_SRC,
     "decode_b1": _DECODE_SRC,
-    "backward": ["polar_backward.hip", "polar_mfma.h", "polar_kernels.h"],
+    "backward": ["polar_backward.hip", "polar_mfma.h", "polar_kernels.h", "polar_rope.h"],
     "variant": _PREFILL_SRC,            # key rotation + variant prefill, full causal range
     "variant_window": _PREFILL_SRC,     # key rotation + variant prefill, 4096-key window
     "paged": _PREFILL_SRC,
@@ -68,7 +68,7 @@ KERNEL_SOURCES = {
     "fwd_train": _PREFILL_SRC,          # the training forward beside the backward
     # the window + RoPE arm: rotations, windowed training forward, windowed backward kernels
     "backward_variant": ["polar_backward.hip", "polar_prefill.hip", "polar_mfma.h",
-                         "polar_kernels.h"],
+                         "polar_kernels.h", "polar_rope.h"],
 }
 
 
@@ -296,7 +296,7 @@ def measure_backward(dev, steps: int, warmup: int, with_cpu: bool):
 def measure_backward_variant(dev, steps: int, warmup: int, q, k, v, kw, cot, p,
                              window: int = 512, theta: float = 10000.0):
     """Training forward + backward of the window + RoPE arm at the same 2K shape: the
-    rotations of q and k, the windowed kernels and the inverse rotation of dq and dk."""
+    rotations of q and k and the windowed kernels (which turn dq and dk back)."""
     import torch
     from long_context_lm_amd import attn_bwd, attn_fwd_train, bwd_workspace_bytes
     from long_context_lm_amd import train_variant_workspace_bytes
@@ -735,7 +735,7 @@ LEG_KERNELS = {
                   (r"polar_decode_combine_kernel", 16384, -1)],
     "backward": [(r"polar_bwd_prep_kernel", None, -1),
                  (r"polar_bwd_dq_kernel<8, false>", None, -1),
-                 (r"polar_bwd_dkv_kernel<4, 1, false>", None, -1),
+                 (r"polar_bwd_dkv_kernel<4, 1, false, false>", None, -1),
                  (r"polar_bwd_dkv_add_kernel", None, -1),
                  (r"polar_bwd_param_kernel", None, -1),
                  (r"polar_bwd_param_final_kernel", None, -1)],
@@ -743,8 +743,7 @@ LEG_KERNELS = {
     "backward_variant": [(r"polar_rope_qk_kernel<unsigned short>", None, -1),
                          (r"polar_prefill_kernel<Bf16, 1, 8, 6,", None, -1),
                          (r"polar_bwd_dq_kernel<8, true>", None, -1),
-                         (r"polar_bwd_dkv_kernel<4, 1, true>", None, -1),
-                         (r"polar_unrope_kernel", None, -1)],
+                         (r"polar_bwd_dkv_kernel<4, 1, true, true>", None, -1)],
     "memory_step": [(r"polar_delta_step_kernel<unsigned short, 4>", 262144, -1)],
     "memory_sequence": [(r"polar_delta_seq_kernel<unsigned short,", None, -1)],
 }
@@ -761,8 +760,9 @@ LEG_WORKLOAD = {
     "backward": "backward B=8 T=2048, all cotangents, parameter gradients",
     "fwd_train": "training forward B=8 T=2048 (saves lse, S, Q for the backward)",
     "backward_variant": "window 512 + RoPE arm at B=8 T=2048: q/k rotation, windowed "
-                        "training forward, windowed dq and dk/dv, inverse rotation (the "
-                        "prep, partial-add and parameter kernels are the backward leg's)",
+                        "training forward, windowed dq and dk/dv turning dq and dk back "
+                        "(the prep, partial-add and parameter kernels are the backward "
+                        "leg's)",
     "memory_step": "gated-delta step, 256 sequences x 16 heads",
     "memory_sequence": "gated-delta stream, 32 sequences x 2048 tokens x 16 heads",
 }

@@ -436,27 +436,17 @@ static polar_status bwd_impl(const polar_params *p, const polar_variant *var, po
   a.inv_log_train = inv_log_train(p);
   a.null_floor = (p->flags & POLAR_FLAG_NULL_FLOOR) ? 1 : 0;
   a.window = window;
+  a.rope = theta > 0.f ? 1 : 0;
+  fill_rope_f(a.rope_f, theta);
   polar::bwd_ws_layout(a, workspace);
   const long long dq_blocks = (long long)a.n_row_blocks * a.Hkv * (a.G / a.hb) * B;
   const long long dkv_blocks = (long long)((a.n_key_blocks + 1) / 2) * a.hsplit * a.Hkv * B;
   if (dq_blocks > 0x7fffffffLL || dkv_blocks > 0x7fffffffLL)
     return fail(POLAR_ERR_BAD_SHAPE, "problem too large for one launch");
+  // With RoPE the dq and dk/dv kernels turn their outputs back by the transposed rotation,
+  // so the gradients are with respect to the unrotated q and k.
   hipError_t err = polar::launch_bwd(a, s);
   if (err != hipSuccess) return fail(POLAR_ERR_HIP, "backward launch: %s", hipGetErrorString(err));
-  if (theta > 0.f) {
-    // Gradients with respect to the unrotated q and k: the transposed rotation.
-    polar::Unrope u{};
-    u.dq = grads->dq;
-    u.dk = grads->dk;
-    u.B = B;
-    u.T = T;
-    u.Hq = Hq;
-    u.Hkv = p->n_kv_heads;
-    fill_rope_f(u.rope_f, theta);
-    err = polar::launch_unrope(u, s);
-    if (err != hipSuccess)
-      return fail(POLAR_ERR_HIP, "inverse rotation launch: %s", hipGetErrorString(err));
-  }
   return POLAR_OK;
 }
 

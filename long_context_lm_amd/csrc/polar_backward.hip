@@ -35,6 +35,7 @@
 
 #include "polar_kernels.h"
 #include "polar_mfma.h"
+#include "polar_rope.h"
 
 namespace polar {
 namespace {
@@ -92,16 +93,18 @@ __device__ __forceinline__ void stage_rows(float *st, const f32x16 (&acc)[2], fl
       *(f32x4 *)(row + db * 32 + 8 * j4) = v;
     }
 }
-// row_ptr(r): destination of row r (0..31) or NULL to skip it.
-template <class RowPtr>
-__device__ __forceinline__ void store_rows(const float *st, int lane, RowPtr row_ptr) {
+// row_ptr(r): destination of row r (0..31) or NULL to skip it; fix(v, r, dim0): the four
+// values of row r from dim0 on, as stored.
+template <class RowPtr, class Fix>
+__device__ __forceinline__ void store_rows(const float *st, int lane, RowPtr row_ptr, Fix fix) {
   const int cc = (lane & 15) * 4;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int r = 4 * i + (lane >> 4);
     float *dst = row_ptr(r);
-    if (dst) __builtin_nontemporal_store(*(const f32x4 *)(st + r * kRowPitch + cc),
-                                         (f32x4 *)(dst + cc));
+    if (dst)
+      __builtin_nontemporal_store(fix(*(const f32x4 *)(st + r * kRowPitch + cc), r, cc),
+                                  (f32x4 *)(dst + cc));
   }
 }
 
@@ -391,14 +394,22 @@ __global__ void __launch_bounds__(64 * kWaves) polar_bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float Ost[kWaves][32 * kRowPitch];
   stage_rows(Ost[wave], o, (a.beta ? a.beta[h] : 8.0f) * tau, lane);
   __syncthreads();
-  store_rows(Ost[wave], lane, [&](int r) -> float * {
-    const int qrow = wrow0 + r;
-    return qrow < a.T ? a.dq + (((size_t)b * a.T + qrow) * a.Hq + h) * kD : nullptr;
-  });
+  // Under RoPE, dq with respect to the unrotated q: each row turned back at its position.
+  store_rows(
+      Ost[wave], lane,
+      [&](int r) -> float * {
+        const int qrow = wrow0 + r;
+        return qrow < a.T ? a.dq + (((size_t)b * a.T + qrow) * a.Hq + h) * kD : nullptr;
+      },
+      [&](f32x4 v, int r, int dim0) {
+        return a.rope ? unrotate4(v, dim0, wrow0 + r, a.rope_f) : v;
+      });
 }
 
 // ------------------------------------------------------------------ 3. dk / dv
-template <int kWaves, int kDepth, bool kWin>
+// kRope: the instance that turns dk back by the transposed rotation (its own instance, so
+// that the others keep their registers).
+template <int kWaves, int kDepth, bool kWin, bool kRope>
 __global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 polar_bwd_dkv_kernel(BwdArgs a) {
   constexpr int kThreads = 64 * kWaves;
@@ -646,6 +657,9 @@ polar_bwd_dkv_kernel(BwdArgs a) {
             kv[e] = dK[db][4 * j4 + e];
             vv[e] = dV[db][4 * j4 + e];
           }
+          // Under RoPE, dk with respect to the unrotated k (partials too: the turn is
+          // linear, so the partial add sums turned vectors).
+          if constexpr (kRope) kv = unrotate4(kv, d0, key, a.rope_f);
           const size_t pofs = (size_t)(hpart - 1) * a.B * a.T * a.Hkv * kD;
           *(f32x4 *)((hpart == 0 ? a.dk : a.dk_part + pofs) + ob + d0) = kv;
           *(f32x4 *)((hpart == 0 ? a.dv : a.dv_part + pofs) + ob + d0) = vv;
@@ -803,16 +817,24 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream) {
   const long long dq_blocks = (long long)a.n_row_blocks * a.Hkv * (a.G / a.hb) * a.B;
   const long long dkv_blocks =
       (long long)((a.n_key_blocks + 1) / 2) * a.hsplit * a.Hkv * a.B;
+  const dim3 gq((unsigned)dq_blocks), bq(64 * kDqWaves);
+  const dim3 gk((unsigned)dkv_blocks), bk(64 * kDkvWaves);
   if (a.window > 0) {
-    hipLaunchKernelGGL((polar_bwd_dq_kernel<kDqWaves, true>), dim3((unsigned)dq_blocks),
-                       dim3(64 * kDqWaves), 0, stream, a);
-    hipLaunchKernelGGL((polar_bwd_dkv_kernel<kDkvWaves, kDkvDepth, true>),
-                       dim3((unsigned)dkv_blocks), dim3(64 * kDkvWaves), 0, stream, a);
+    hipLaunchKernelGGL((polar_bwd_dq_kernel<kDqWaves, true>), gq, bq, 0, stream, a);
+    if (a.rope)
+      hipLaunchKernelGGL((polar_bwd_dkv_kernel<kDkvWaves, kDkvDepth, true, true>), gk, bk, 0,
+                         stream, a);
+    else
+      hipLaunchKernelGGL((polar_bwd_dkv_kernel<kDkvWaves, kDkvDepth, true, false>), gk, bk, 0,
+                         stream, a);
   } else {
-    hipLaunchKernelGGL((polar_bwd_dq_kernel<kDqWaves, false>), dim3((unsigned)dq_blocks),
-                       dim3(64 * kDqWaves), 0, stream, a);
-    hipLaunchKernelGGL((polar_bwd_dkv_kernel<kDkvWaves, kDkvDepth, false>),
-                       dim3((unsigned)dkv_blocks), dim3(64 * kDkvWaves), 0, stream, a);
+    hipLaunchKernelGGL((polar_bwd_dq_kernel<kDqWaves, false>), gq, bq, 0, stream, a);
+    if (a.rope)
+      hipLaunchKernelGGL((polar_bwd_dkv_kernel<kDkvWaves, kDkvDepth, false, true>), gk, bk, 0,
+                         stream, a);
+    else
+      hipLaunchKernelGGL((polar_bwd_dkv_kernel<kDkvWaves, kDkvDepth, false, false>), gk, bk,
+                         0, stream, a);
   }
   if (a.hsplit > 1) {
     const long long n4 = (long long)a.B * a.T * a.Hkv * kD / 4;

@@ -59,21 +59,15 @@ hipError_t launch_prefill(int dtype, const PrefillArgs &a, hipStream_t stream);
 // with exactly the arithmetic the prefill's staging applies.
 hipError_t launch_rope_keys(int dtype, const PrefillArgs &a, void *k_out, hipStream_t stream);
 // The training arm with RoPE: q [B,T,Hq,d] and k [B,T,Hkv,d] rotated into q_out, k_out
-// (rope_f as in PrefillArgs), and the gradients dq, dk (fp32) turned back in place by the
-// transposed rotation.
+// (rope_f as in PrefillArgs).  The backward kernels turn dq and dk back themselves
+// (BwdArgs::rope).
 struct RopeQk {
   const void *q, *k;
   void *q_out, *k_out;
   int B, T, Hq, Hkv;
   uint64_t rope_f[kHeadDim / 2];
 };
-struct Unrope {
-  float *dq, *dk;
-  int B, T, Hq, Hkv;
-  uint64_t rope_f[kHeadDim / 2];
-};
 hipError_t launch_rope_qk(int dtype, const RopeQk &r, hipStream_t stream);
-hipError_t launch_unrope(const Unrope &u, hipStream_t stream);
 
 struct DecodeArgs {
   const void *q;                          // [B,Hq,d]
@@ -160,6 +154,10 @@ struct BwdArgs {
   float inv_log_train;
   int null_floor;
   int window;                             // W >= 1: row i sees keys i-W+1..i; 0: all
+  // 1: q and k are RoPE-rotated (rope_f as in PrefillArgs); dq and dk leave the kernels
+  // turned back by the transposed rotation.
+  int rope;
+  uint64_t rope_f[kHeadDim / 2];
 };
 constexpr int kPartStride = 68;           // dw[64], dbeta, dbias, pad
 

@@ -42,6 +42,7 @@
 
 #include "polar_kernels.h"
 #include "polar_mfma.h"
+#include "polar_rope.h"
 
 namespace polar {
 namespace {
@@ -82,17 +83,6 @@ constexpr int kModeMix = 5;
 // The training instance under a sliding window (its own instance, so that the causal
 // training forward keeps the code it had without the window).
 constexpr int kModeSaveWin = 6;
-
-// RoPE rotation angle of pair t at position pos: revolutions = frac(pos * f_t) taken
-// exactly from the 64-bit fixed-point product, then the hardware sine and cosine, whose
-// argument is in revolutions (the rotated values are rounded to bf16 afterwards, far
-// coarser than their error).
-__device__ __forceinline__ void rope_cs(uint64_t f, int pos, float &c, float &s) {
-  const uint32_t hi = (uint32_t)(((uint64_t)(uint32_t)pos * f) >> 32);
-  const float rev = (float)hi * 2.3283064365386963e-10f;
-  s = __builtin_amdgcn_sinf(rev);
-  c = __builtin_amdgcn_cosf(rev);
-}
 
 // The rotated pair, with the contraction spelled out so that every place that rotates a
 // key rounds the same way: (x0 c - x1 s, x0 s + x1 c).
@@ -1131,36 +1121,6 @@ constexpr int kWavesF32 = 4;
 // per CU the pipelined instances keep their two waves per SIMD busier.
 constexpr long long kLeanMinWorkgroups = 512;
 
-// The gradient with respect to the input of RoPE: fp32 rows of dq [B,T,Hq,d] and dk
-// [B,T,Hkv,d] turned in place by the transposed rotation, that is by the opposite angle
-// (rope_cs's angle for pair t at position p): (g0, g1) -> (g0 c + g1 s, g1 c - g0 s).  One
-// thread per 16-byte chunk, dq's chunks first.
-__global__ void __launch_bounds__(256) polar_unrope_kernel(Unrope u) {
-  constexpr int kChunks = kD / 4;
-  const long long nq = (long long)u.B * u.T * u.Hq * kChunks;
-  const long long n = nq + (long long)u.B * u.T * u.Hkv * kChunks;
-  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n;
-       i += (long long)gridDim.x * 256) {
-    const bool isq = i < nq;
-    const long long j = isq ? i : i - nq;
-    const int H = isq ? u.Hq : u.Hkv;
-    const int part = (int)(j % kChunks);
-    const long long row = j / kChunks;                 // (b * T + pos) * H + h
-    const int pos = (int)((row / H) % u.T);
-    f32x4 *px = (f32x4 *)((isq ? u.dq : u.dk) + row * kD) + part;
-    f32x4 w = *px;
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      float c, sn;
-      rope_cs(u.rope_f[part * 2 + m], pos, c, sn);
-      const float g0 = w[2 * m], g1 = w[2 * m + 1];
-      w[2 * m] = fmaf(g0, c, g1 * sn);
-      w[2 * m + 1] = fmaf(g1, c, -(g0 * sn));
-    }
-    *px = w;
-  }
-}
-
 }  // namespace
 
 int prefill_heads_per_block(int G) {
@@ -1191,15 +1151,6 @@ hipError_t launch_rope_qk(int dtype, const RopeQk &r, hipStream_t stream) {
     hipLaunchKernelGGL((polar_rope_qk_kernel<uint16_t>), dim3(blocks), dim3(256), 0, stream, r);
   else
     hipLaunchKernelGGL((polar_rope_qk_kernel<float>), dim3(blocks), dim3(256), 0, stream, r);
-  return hipGetLastError();
-}
-
-hipError_t launch_unrope(const Unrope &u, hipStream_t stream) {
-  const long long n = (long long)u.B * u.T * (u.Hq + u.Hkv) * (kD / 4);
-  if (n <= 0) return hipSuccess;
-  const long long need = (n + 255) / 256;
-  const unsigned blocks = (unsigned)(need < 65536 ? need : 65536);
-  hipLaunchKernelGGL(polar_unrope_kernel, dim3(blocks), dim3(256), 0, stream, u);
   return hipGetLastError();
 }
 
