@@ -94,9 +94,8 @@ __device__ __forceinline__ float rot_im(float x0, float x1, float c, float s) {
 }
 
 // kLean: each tile's scores are used in the step that issues them (see kAhead below).  Lean
-// instances are held to 128 registers (four waves per SIMD); the training instance, whose
-// arg-max tracking needs a few more, spills 7 outside the key loop's vector work, which
-// costs less than the occupancy.
+// instances are held to 128 registers (four waves per SIMD), the training instances with
+// their arg-max tracking included.
 template <class TR, int QB, int kWaves, int kMode, bool kLean>
 __global__ void __launch_bounds__(64 * kWaves, kLean ? 4 : 1)
     polar_prefill_kernel(PrefillArgs a) {
@@ -592,14 +591,16 @@ __global__ void __launch_bounds__(64 * kWaves, kLean ? 4 : 1)
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S.v[qb][kb][r]);
       if (mx > lbest[qb]) {
         asm volatile("");     // a branch, not selects: lanes rarely improve after a few tiles
-        int key = 0;
+        // The offset of the lowest register holding the maximum, as a small literal (one
+        // select per register), then the lane's base key added once.
+        int off = 0;
 #pragma unroll
         for (int kb = NKB - 1; kb >= 0; --kb)
 #pragma unroll
           for (int r = 15; r >= 0; --r)
-            if (S.v[qb][kb][r] == mx) key = key0 + kb * 32 + 8 * (r >> 2) + 4 * g32 + (r & 3);
+            if (S.v[qb][kb][r] == mx) off = kb * 32 + 8 * (r >> 2) + (r & 3);
         lbest[qb] = mx;
-        lkey[qb] = key;
+        lkey[qb] = key0 + 4 * g32 + off;
       }
     }
   };
