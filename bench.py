@@ -323,8 +323,8 @@ def measure_backward_variant(dev, steps: int, warmup: int, q, k, v, kw, cot, p,
     print(f"[bench] backward, window {window} + RoPE: {b_ms:.3f} ms ({tf:.1f} TFLOP/s), "
           f"training forward {f_ms:.3f} ms", file=sys.stderr, flush=True)
     return {"workload": f"backward of the {window}-key window + RoPE (theta {theta:g}) "
-                        "prefill at the same shape, rotations of q and k and the inverse "
-                        "rotation of dq and dk included",
+                        "prefill at the same shape, the rotation of q and k included (the "
+                        "kernels turn dq and dk back as they store them)",
             "value": round(tf, 2), "unit": "TFLOP/s", "bwd_ms": round(b_ms, 4),
             "fwd_train_ms": round(f_ms, 4),
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
