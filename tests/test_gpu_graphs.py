@@ -101,6 +101,30 @@ def test_variant_backward_replays(gpu_lib):
         torch.cuda.synchronize()
 
 
+def test_readout_training_replays(gpu_lib):
+    """The softmax read-out's training forward (writing u) and its backward (taking u's
+    gradient) captured together."""
+    p = synth.prefill_inputs("c2", B=2, T=300)
+    q, k, v = (to_dev(getattr(p, n), p.dtype) for n in ("q", "k", "v"))
+    kw = dict(beta=torch.from_numpy(p.beta).cuda(), null_bias=torch.from_numpy(p.null_bias).cuda(),
+              count_vec=torch.from_numpy(p.count_vec).cuda(), train_len=p.train_len, flags=p.flags)
+    cot = {n: torch.from_numpy(x).cuda()
+           for n, x in synth.cotangents(p.B, p.T, p.Hq, p.d, attn=True).as_dict().items()}
+    wb = torch.empty(bwd_workspace_bytes(p.Hq, p.Hkv, p.B, p.T), dtype=torch.uint8, device="cuda")
+
+    def step():
+        fwd = attn_fwd_train(q, k, v, want_attn=True, **kw)
+        return {**fwd, **attn_bwd(q, k, v, fwd, cot, workspace=wb, **kw)}
+    eager = step()
+    g, out = _capture(step)
+    for _ in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        _same(eager, out)
+        attn_fwd(q, k, v, **kw)
+        torch.cuda.synchronize()
+
+
 def test_decode_replays(gpu_lib):
     d = synth.decode_inputs("c5", B=2, L=5000)
     qd, kc, vc = to_dev(d.q, d.dtype), to_dev(d.k_pool, d.dtype), to_dev(d.v_pool, d.dtype)
