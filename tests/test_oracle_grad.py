@@ -229,3 +229,14 @@ def test_cotangents_seeded():
     assert all(np.array_equal(getattr(a, f), getattr(b, f)) for f in
                ("d_dir", "d_count", "d_n_eff", "d_gate", "d_lse"))
     assert a.d_dir.dtype == np.float32 and a.d_dir.shape == (1, 8, 2, 4)
+
+
+def test_readout_cotangent_leaves_the_others_unchanged():
+    """Asking for the read-out's cotangent draws it from a sixth child stream: the five
+    others are the same arrays, and "attn" appears in the dict only when asked for."""
+    a = synth.cotangents(2, 8, 3, 4, seed=11)
+    b = synth.cotangents(2, 8, 3, 4, seed=11, attn=True)
+    assert "attn" not in a.as_dict() and b.as_dict()["attn"].shape == (2, 8, 3, 4)
+    for n, x in a.as_dict().items():
+        assert np.array_equal(x, b.as_dict()[n]), n
+    assert not np.array_equal(b.d_attn, b.d_dir)

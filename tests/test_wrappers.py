@@ -46,3 +46,4 @@ def test_per_head_parameters_hold_one_value_per_head():
         polar._head_params(None, None, np.ones((16, 32), np.float32), 16, 64, cpu)
     b, nb, w = polar._head_params(np.ones(16), np.zeros(16), np.ones((16, 64)), 16, 64, cpu)
     assert b.dtype == torch.float32 and w.is_contiguous() and w.numel() == 1024
+
